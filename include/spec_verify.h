@@ -1,0 +1,171 @@
+/*
+ * spec_verify.h — C ABI of the batched speculative-decoding verifier for
+ * AMD MI355X (gfx950).
+ *
+ * The operation is the verification step of speculative decoding as the
+ * pages define it:
+ *   - "EAGLE-3 speculative decoding review" (6unoyunr.github.io), section
+ *     "Speculative Decoding" (the draft / verify / accept-or-reject cycle),
+ *     the section asking whether a small draft hurts quality (greedy rule,
+ *     acceptance probability A(x) = min(1, p(x)/q(x)), residual
+ *     p_residual = norm(max(0, p - q))), and the section on the full EAGLE-3
+ *     inference loop (tree verification, strict acceptance);
+ *   - the speculative-decoding chapter of an LLM-serving book
+ *     (froggydisk.github.io), sections on how it works and on the acceptance
+ *     rule that preserves the output distribution.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless the parameter name ends in _host.
+ *  - Tensors are dense, row-major, the vocabulary axis V contiguous.  bf16
+ *    tensors hold IEEE bfloat16 bit patterns.
+ *  - All buffers are owned by the caller.  The library never allocates,
+ *    frees or synchronises inside a call; kernels are enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL = the default stream) and the
+ *    outputs are valid once that stream has been synchronised.
+ *  - `ws` is a caller-owned device workspace of at least
+ *    spec_workspace_bytes(B, n_pos, V) bytes.  It must be zero-filled before
+ *    its first use.  Its first 1 MiB holds completion counters at fixed
+ *    places, which every call leaves at zero again, so one workspace can be
+ *    reused for calls of any shape without clearing it.  Calls that share a
+ *    workspace must be ordered on one stream.
+ *  - Return value: SPEC_OK, or a negative code.  Any code other than
+ *    SPEC_EHIP means the arguments were rejected on the host and nothing was
+ *    enqueued.  SPEC_EHIP reports a failed HIP launch.
+ *  - Inputs must be finite except that -inf marks a masked token.  Every
+ *    row must hold at least one finite value.
+ *  - A draft or node token outside [0, V) is a rejection (sampling) or a
+ *    mismatch (greedy); it is never used as an index.
+ *  - Sizes: 0 <= B <= 65536, 0 <= k <= 1023, 1 <= V <= 2^30, 1 <= n_nodes <= 1024.
+ *    B == 0 is a no-op that returns SPEC_OK.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of logit / probability tensors. */
+enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+/* What the sampling rows hold.
+ * SPEC_LOGITS: raw logits; p = softmax(target / T), q = softmax(draft / T).
+ * SPEC_PROBS:  float32 probabilities used as given (T must be 1). */
+enum { SPEC_LOGITS = 0, SPEC_PROBS = 1 };
+
+enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,     /* null pointer, size or scalar out of range */
+  SPEC_EDTYPE = -2,     /* unsupported dtype / kind combination */
+  SPEC_EWORKSPACE = -3, /* workspace null or smaller than required */
+  SPEC_EHIP = -4,       /* a HIP launch failed */
+  SPEC_ETREE = -5       /* parent array is not a tree in BFS-compatible order */
+};
+
+/* Human-readable text for a return code (static storage). */
+const char* spec_strerror(int code);
+
+/* Workspace bytes needed by any entry point for B requests of n_pos
+ * positions (k + 1 for chains, n_nodes for trees) over a vocabulary of V.
+ * Returns 0 for invalid sizes. */
+size_t spec_workspace_bytes(int B, int n_pos, int V);
+
+/* Uniforms from a seed.  out[i] = (SplitMix64 output number counter0 + i of
+ * the stream seeded with `seed`) >> 40, times 2^-24: a float in [0, 1) on
+ * the 2^-24 grid.  SplitMix64 as in Steele, Lea & Flood (OOPSLA 2014):
+ * output(ctr) = mix(seed + (ctr + 1) * 0x9E3779B97F4A7C15 mod 2^64).
+ * The pages tie reproducible sampling to the seed and to the order in which
+ * random numbers are used (EAGLE-3 review, sections on interpreting
+ * losslessness and on lossless versus numerically identical output); this
+ * counter form makes each value independent of the order of use.
+ * out: device float[n].  n >= 0. */
+int spec_fill_uniforms(uint64_t seed, uint64_t counter0, int64_t n, float* out,
+                       void* stream);
+
+/* Greedy chain verification (EAGLE-3 review, greedy bullets of the section
+ * on whether a small draft hurts quality; serving chapter, last sentence of
+ * the acceptance-rule section).  For each request b:
+ *   a_i = argmax_j target[b, i, j] (lowest j on ties), i = 0..k;
+ *   n_b = first i < k with draft_tokens[b, i] != a_i, or k;
+ *   accepted_len[b] = n_b;
+ *   out_tokens[b, 0..n_b-1] = draft_tokens[b, 0..n_b-1];
+ *   out_tokens[b, n_b] = a_{n_b};  out_tokens[b, n_b+1..k] = -1.
+ * target: [B, k+1, V] of `dtype` (SPEC_F32 or SPEC_BF16).
+ * draft_tokens: int32 [B, k] (may be NULL when k == 0).
+ * accepted_len: int32 [B].  out_tokens: int32 [B, k+1]. */
+int spec_verify_greedy(const void* target, int dtype, int B, int k, int V,
+                       const int32_t* draft_tokens, int32_t* accepted_len,
+                       int32_t* out_tokens, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Sampling chain verification with the rule min(1, p(x)/q(x)) (EAGLE-3
+ * review, equation A(x) and the residual equation; serving chapter,
+ * acceptance-rule section; stop at the first rejection and the bonus token:
+ * EAGLE-3 review "Speculative Decoding" step 3, serving chapter "how it
+ * works").  For each request b, positions i = 0..k-1 in order:
+ *   x = draft_tokens[b, i];  accept iff 0 <= x < V and u_acc < p_i(x)/q_i(x)
+ *   (a zero q_i(x) accepts iff p_i(x) > 0);
+ *   at the first rejection n: draw t from normalise(max(0, p_n - q_n)) by
+ *   inverse CDF with u_res (t = min{ j : C_j > u_res * C_{V-1} }, C the
+ *   running sum over ascending token id); if that residual has zero mass,
+ *   draw from p_n with the same u_res;
+ *   if all k are accepted: n = k and t is drawn from p_k the same way.
+ *   accepted_len[b] = n; out_tokens[b] = draft_tokens[b, 0..n-1], t, then -1.
+ * Uniforms: u_acc = u[b, i, 0], u_res = u[b, n, 1], where u is `uniforms`
+ * (device float [B, k+1, 2]) or, when `uniforms` is NULL, the values
+ * spec_fill_uniforms(seed, counter0, ...) would write to such an array.
+ * dtype/kind: SPEC_LOGITS with SPEC_F32 or SPEC_BF16 (temperature > 0,
+ * finite, 1/temperature finite); SPEC_PROBS with SPEC_F32 (temperature 1).
+ * target: [B, k+1, V]; draft: [B, k, V] (may be NULL when k == 0).
+ * probe (nullable): float [B, k+1, 4]; for i < k, probe[b,i,0] = p_i(x_i)
+ * and probe[b,i,1] = q_i(x_i) (0 for an out-of-range token); probe[b,n,2] =
+ * total mass of the distribution drawn from at position n (the residual mass
+ * sum max(0, p_n - q_n) after a rejection, sum p_k for the bonus draw); all
+ * other entries 0.
+ * Arithmetic: row statistics (max, log-sum-exp) in float32 with float64
+ * merges; the acceptance ratio in float64; the residual / bonus draw fully
+ * in float64. */
+int spec_verify_sample(const void* target, const void* draft, int dtype, int kind,
+                       int B, int k, int V, const int32_t* draft_tokens,
+                       const float* uniforms, uint64_t seed, uint64_t counter0,
+                       float temperature, int32_t* accepted_len,
+                       int32_t* out_tokens, float* probe, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Greedy tree verification (EAGLE-3 review, section on the full inference
+ * loop: tree attention gives the target's distribution after every node, and
+ * strict acceptance keeps the longest prefix that matches the target's
+ * choice).  Node 0 is the root; node j > 0 has parent parent_host[j] < j and
+ * carries token node_tokens[b, j] (column 0 is ignored).  target[b, j] is
+ * the target's distribution after node j's prefix.  Let a_j = argmax
+ * target[b, j] (lowest id on ties).  Node j > 0 is accepted iff its parent
+ * is accepted and node_tokens[b, j] == a_{parent(j)}; the root is accepted.
+ * d* = the deepest accepted node (lowest index among equal depths).
+ *   accepted_len[b] = depth(d*);
+ *   out_tokens[b] = tokens of the nodes on the root->d* path (root
+ *   excluded), then a_{d*}, then -1 up to D+1 entries (D = tree depth);
+ *   out_path[b] (nullable) = node ids of the path from the root (0 first),
+ *   then -1 up to D+1 entries.
+ * parent_host: HOST int32 [n_nodes], parent[0] = -1, 0 <= parent[j] < j;
+ * read during the call only.  target: [B, n_nodes, V] of dtype.
+ * node_tokens: int32 [B, n_nodes].  accepted_len: int32 [B].
+ * out_tokens, out_path: int32 [B, D+1]. */
+int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes,
+                            int V, const int32_t* parent_host,
+                            const int32_t* node_tokens, int32_t* accepted_len,
+                            int32_t* out_tokens, int32_t* out_path, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Depth D of the tree described by parent_host (see above), or a negative
+ * error code if the array is malformed.  Host only. */
+int spec_tree_depth(const int32_t* parent_host, int n_nodes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -104,6 +104,9 @@ class RequestResult:
     accepted: int
     tokens: list
     decisions: list = field(default_factory=list)
+    # total weight of the distribution the final token was drawn from, in
+    # probability units: sum max(0, p_n - q_n) after a rejection, sum p_k for
+    # the bonus draw
     residual_mass: float = float("nan")
     path: list = field(default_factory=list)
 
@@ -230,7 +233,7 @@ def verify_sample_request(target: np.ndarray, draft: np.ndarray,
     t, m2, total = inverse_cdf(p, float(u[k, 1]))
     decisions.append(Decision("resample", k, m2, t))
     toks = [int(v) for v in draft_tokens[:k]] + [t]
-    return RequestResult(k, toks, decisions, residual_mass=0.0)
+    return RequestResult(k, toks, decisions, residual_mass=total)
 
 
 def verify_sample(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,

@@ -1,0 +1,266 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Integer outputs must match bit-exactly, except that a disagreement is
+allowed when its first differing decision lies within 1e-5 of its boundary
+in the oracle (flagged); unflagged mismatches must be zero.  Probabilities
+reported by the probe must agree within 1e-5 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.rng as R
+import oracle.verify as O
+import verify_accept_sampling_amd as S
+import workloads as W
+from parity_helpers import (PROB_TOL, check_chain_structure, check_probe, compare_sample,
+                            ints_to_device, to_device)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# uniforms
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("seed,ctr,n", [(0, 0, 1000), (2003, 0, 64 * 9 * 2),
+                                        (12345678901234567, 2 ** 63 + 11, 4097),
+                                        (7, 2 ** 64 - 5, 300), (99, 5, 1)])
+def test_uniforms_bit_exact(seed, ctr, n):
+    g = S.spec_fill_uniforms(seed, ctr, n).cpu().numpy().astype(np.float64)
+    assert np.array_equal(g, R.uniforms(seed, ctr, n))
+
+
+# ---------------------------------------------------------------------------
+# greedy chain
+# ---------------------------------------------------------------------------
+
+
+def _run_greedy(wl):
+    acc_o, out_o, _ = O.verify_greedy(wl.target, wl.draft_tokens, wl.dtype)
+    acc_g, out_g = S.spec_verify_greedy(to_device(wl.target, wl.dtype),
+                                        ints_to_device(wl.draft_tokens))
+    torch.cuda.synchronize()
+    acc_g, out_g = acc_g.cpu().numpy(), out_g.cpu().numpy()
+    assert np.array_equal(acc_g, acc_o)
+    assert np.array_equal(out_g, out_o)
+    check_chain_structure(acc_g, out_g, wl.draft_tokens, wl.V)
+
+
+def test_greedy_chain_v1000_full():
+    _say("greedy chain B=1 k=4 V=1000 f32")
+    _run_greedy(W.greedy_chain())
+
+
+@pytest.mark.parametrize("B,k,V,dtype", [(37, 6, 50_000, "bf16"), (5, 8, 128256, "bf16"),
+                                         (9, 3, 1001, "f32"), (9, 3, 1001, "bf16"),
+                                         (3, 2, 7, "f32"), (4, 0, 300, "bf16"),
+                                         (2, 1, 1, "f32"), (1, 200, 64, "f32"),
+                                         (64, 8, 32768, "f32")])
+def test_greedy_chain_shapes(B, k, V, dtype):
+    _say(f"greedy chain B={B} k={k} V={V} {dtype}")
+    _run_greedy(W.greedy_chain(B=B, k=k, V=V, seed=B * 1000 + V, dtype=dtype))
+
+
+def test_greedy_chain_ties_masks_and_bad_tokens():
+    rng = np.random.default_rng(5)
+    B, k, V = 40, 5, 3000
+    z = np.round(rng.standard_normal((B, k + 1, V)) * 1.2).astype(np.float32)  # many ties
+    z[rng.random(z.shape) < 0.3] = -np.inf
+    amax = np.argmax(z[:, :k], axis=-1)
+    toks = np.where(rng.random((B, k)) < 0.8, amax, rng.integers(0, V, (B, k))).astype(np.int32)
+    toks[0, 0] = -1
+    toks[1, 2] = V
+    toks[2, 1] = 2 ** 31 - 1
+    wl = W.ChainWorkload("ties", z, None, toks, "logits", "f32", 1.0, 0)
+    _run_greedy(wl)
+    wl_bf = W.ChainWorkload("ties_bf16", W.f32_to_bf16_bits(z), None, toks, "logits", "bf16",
+                            1.0, 0)
+    _run_greedy(wl_bf)
+
+
+# ---------------------------------------------------------------------------
+# tree greedy
+# ---------------------------------------------------------------------------
+
+
+def _run_tree(wl):
+    acc_o, out_o, path_o, _ = O.verify_tree_greedy(wl.target, wl.parent, wl.node_tokens,
+                                                   wl.dtype)
+    acc_g, out_g, path_g = S.spec_verify_tree_greedy(to_device(wl.target, wl.dtype), wl.parent,
+                                                     ints_to_device(wl.node_tokens))
+    torch.cuda.synchronize()
+    assert np.array_equal(acc_g.cpu().numpy(), acc_o)
+    assert np.array_equal(out_g.cpu().numpy(), out_o)
+    assert np.array_equal(path_g.cpu().numpy(), path_o)
+
+
+def test_tree_greedy_v128256_full():
+    _say("tree greedy B=16 N=61 V=128256 bf16")
+    _run_tree(W.tree_greedy())
+
+
+@pytest.mark.parametrize("B,V,dtype,p", [(64, 12, "f32", 0.8), (32, 1000, "bf16", 0.9),
+                                         (8, 30001, "bf16", 0.9), (5, 4096, "f32", 1.0)])
+def test_tree_greedy_small(B, V, dtype, p):
+    _say(f"tree greedy B={B} V={V} {dtype}")
+    _run_tree(W.tree_greedy(B=B, V=V, seed=V, p_match=p, dtype=dtype))
+
+
+def test_tree_shapes_chain_single_and_deep():
+    # chain-shaped tree equals chain greedy
+    wl = W.greedy_chain(B=20, k=7, V=500, seed=3, p_match=0.85)
+    parent = np.arange(-1, wl.k, dtype=np.int32)
+    nt = np.concatenate([np.zeros((wl.B, 1), np.int32), wl.draft_tokens], axis=1)
+    tw = W.TreeWorkload("chain", wl.target, parent, nt, "f32")
+    _run_tree(tw)
+    acc_c, out_c = S.spec_verify_greedy(to_device(wl.target, "f32"),
+                                        ints_to_device(wl.draft_tokens))
+    acc_t, out_t, _ = S.spec_verify_tree_greedy(to_device(wl.target, "f32"), parent,
+                                                ints_to_device(nt))
+    assert torch.equal(acc_c, acc_t) and torch.equal(out_c, out_t)
+    # root only
+    _run_tree(W.tree_greedy(B=3, V=100, seed=4, parent=np.array([-1], np.int32)))
+    # deep chain of 1024 nodes, every draft correct
+    deep = W.tree_greedy(B=2, V=16, seed=6, parent=np.arange(-1, 1023, dtype=np.int32),
+                         p_match=1.0, dtype="f32")
+    _run_tree(deep)
+    # wide star with duplicate siblings
+    star = np.array([-1] + [0] * 300 + list(range(1, 301)), dtype=np.int32)
+    _run_tree(W.tree_greedy(B=4, V=8, seed=7, parent=star, p_match=0.5, dtype="f32"))
+
+
+# ---------------------------------------------------------------------------
+# sampling chain
+# ---------------------------------------------------------------------------
+
+
+def _run_sample(wl, seed=None, counter0=0, requests=None, use_array=True, max_mismatch=0):
+    seed = wl.uniform_seed if seed is None else seed
+    u = R.chain_uniforms(seed, wl.B, wl.k, counter0)
+    tgt = to_device(wl.target, wl.dtype)
+    dft = to_device(wl.draft, wl.dtype) if wl.k > 0 else None
+    toks = ints_to_device(wl.draft_tokens)
+    if use_array:
+        ug = S.spec_fill_uniforms(seed, counter0, wl.B * (wl.k + 1) * 2).view(wl.B, wl.k + 1, 2)
+        acc_g, out_g, pr_g = S.spec_verify_sample(tgt, dft, toks, wl.temperature, uniforms=ug,
+                                                  kind=wl.kind, probe=True)
+    else:
+        acc_g, out_g, pr_g = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=seed,
+                                                  counter0=counter0, kind=wl.kind, probe=True)
+    torch.cuda.synchronize()
+    acc_g, out_g, pr_g = acc_g.cpu().numpy(), out_g.cpu().numpy(), pr_g.cpu().numpy()
+    check_chain_structure(acc_g, out_g, wl.draft_tokens, wl.V)
+    reqs = list(range(wl.B)) if requests is None else list(requests)
+    acc_o, out_o, res = O.verify_sample(wl.target, wl.draft, wl.draft_tokens, u,
+                                        wl.temperature, wl.kind, wl.dtype, requests=reqs)
+    st = compare_sample(acc_g, out_g, acc_o, out_o, res, reqs)
+    worst = check_probe(pr_g, wl, acc_g, acc_o, res, reqs)
+    _say(f"  {wl.name}: {st} probe_max_abs_err={worst:.3g}")
+    assert st["unflagged"] == 0, st["unflagged_requests"]
+    assert st["mismatches"] <= max_mismatch, st
+    assert worst <= PROB_TOL
+    return acc_g, out_g
+
+
+def test_sample_chain_v32000_full():
+    _say("sample chain B=8 k=4 V=32000 bf16 T=1")
+    _run_sample(W.sample_chain_v32000())
+
+
+def test_sample_chain_llama3_full():
+    _say("sample chain B=64 k=8 V=128256 bf16 T=0.7")
+    wl = W.sample_chain_llama3()
+    a1, o1 = _run_sample(wl, use_array=False)
+    # the inline counter uniforms and an explicit uniform array agree exactly
+    a2, o2 = _run_sample(wl, use_array=True)
+    assert np.array_equal(a1, a2) and np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("B,k,V,dtype,T", [(50, 3, 1001, "f32", 1.0), (40, 5, 4000, "bf16", 0.3),
+                                           (30, 4, 32000, "f32", 2.5), (16, 0, 5000, "bf16", 1.0),
+                                           (20, 1, 17, "bf16", 0.8), (8, 12, 65536, "bf16", 1.0)])
+def test_sample_chain_shapes(B, k, V, dtype, T):
+    _say(f"sample chain B={B} k={k} V={V} {dtype} T={T}")
+    wl = W.sample_chain(B, k, V, seed=B + k + V, uniform_seed=77 + V, target_std=2.0,
+                        noise_std=1.0, temperature=T, dtype=dtype)
+    _run_sample(wl)
+
+
+def test_sample_identical_draft_accepts_everything():
+    wl = W.sample_chain(24, 6, 3000, seed=1, uniform_seed=2, target_std=2.0, noise_std=1.0,
+                        temperature=0.9, dtype="bf16")
+    wl.draft = wl.target[:, : wl.k].copy()
+    acc, _ = _run_sample(wl)
+    assert np.all(acc == wl.k)
+
+
+def test_sample_masks_and_bad_tokens():
+    rng = np.random.default_rng(11)
+    wl = W.sample_chain(32, 4, 2048, seed=9, uniform_seed=10, target_std=2.0, noise_std=1.0,
+                        temperature=1.0, dtype="f32")
+    t = wl.target.copy()
+    d = wl.draft.copy()
+    t[rng.random(t.shape) < 0.2] = -np.inf
+    d[rng.random(d.shape) < 0.2] = -np.inf
+    wl.target, wl.draft = t, d
+    toks = wl.draft_tokens.copy()
+    toks[0, 0] = -5
+    toks[1, 1] = 2048
+    toks[2, 3] = 2 ** 31 - 1
+    wl.draft_tokens = toks
+    _run_sample(wl)
+
+
+def test_sample_probs_small_and_empty_residual():
+    wl = W.controlled_acceptance(B=90, k=4, V=1000, seed=21, uniform_seed=22, logit_std=1.0)
+    _run_sample(wl)
+    # q >= p elementwise (q carries extra mass): rejections have an empty residual
+    rng = np.random.default_rng(3)
+    B, k, V = 16, 2, 64
+    p = rng.dirichlet(np.ones(V), size=(B, k + 1)).astype(np.float32)
+    q = (p[:, :k] * np.float32(1.5)).astype(np.float32)
+    toks = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    wl2 = W.ChainWorkload("empty_residual", p, q, toks, "probs", "f32", 1.0, 5)
+    acc, out = _run_sample(wl2)
+    assert (acc < k).any()
+
+
+@pytest.fixture(scope="module")
+def controlled_full():
+    _say("generating controlled-acceptance B=512 k=8 V=128256 f32 probs")
+    return W.controlled_acceptance()
+
+
+def test_sample_controlled_acceptance_full(controlled_full):
+    _say("sample probs B=512 k=8 V=128256")
+    _run_sample(controlled_full)
+
+
+def test_workspace_reuse_with_stale_partials():
+    """A workspace whose non-counter bytes hold garbage (as left by calls of
+    other shapes) gives the same results: only the fixed counter region must
+    be zero."""
+    ws = S.Workspace(DEV)
+    buf = ws.get(S.spec_workspace_bytes(64, 9, 128256))
+    buf[1 << 20:].fill_(0xA5)
+    wl = W.sample_chain(12, 5, 20000, seed=4, uniform_seed=5, target_std=2.0, noise_std=1.0,
+                        temperature=0.8, dtype="bf16")
+    tgt, dft = to_device(wl.target, "bf16"), to_device(wl.draft, "bf16")
+    toks = ints_to_device(wl.draft_tokens)
+    ref = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=5)
+    g = W.greedy_chain(B=7, k=3, V=999, seed=3)
+    gref = S.spec_verify_greedy(to_device(g.target, "f32"), ints_to_device(g.draft_tokens))
+    for _ in range(3):
+        got = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=5, workspace=ws)
+        assert all(torch.equal(a, b) for a, b in zip(ref, got))
+        ggot = S.spec_verify_greedy(to_device(g.target, "f32"), ints_to_device(g.draft_tokens),
+                                    workspace=ws)
+        assert all(torch.equal(a, b) for a, b in zip(gref, ggot))
+        buf[1 << 20:].fill_(0x5A)

@@ -1,0 +1,272 @@
+"""Batched speculative-decoding verification on AMD MI355X (gfx950).
+
+Thin Python binding of libspecverify.so: every function has the name of the
+C entry point it calls and only marshals arguments (torch tensors in device
+memory, the current HIP stream, a zero-filled workspace).  All verification
+work runs in the library's HIP kernels; there is no fallback: if the library
+is missing or a call fails, an exception is raised.
+
+    spec_workspace_bytes(B, n_pos, V)
+    spec_fill_uniforms(seed, counter0, n, out=None)
+    spec_verify_greedy(target, draft_tokens)
+    spec_verify_sample(target, draft, draft_tokens, temperature, ...)
+    spec_verify_tree_greedy(target, parent, node_tokens)
+    spec_tree_depth(parent)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "SpecVerifyError", "Workspace", "library_path", "load_library", "declared_symbols",
+    "spec_workspace_bytes", "spec_fill_uniforms", "spec_verify_greedy",
+    "spec_verify_sample", "spec_verify_tree_greedy", "spec_tree_depth", "spec_strerror",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "spec_verify.h")
+
+SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_LOGITS, SPEC_PROBS = 0, 1
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libspecverify.so")
+
+
+def declared_symbols() -> list:
+    """Names of the functions declared in include/spec_verify.h."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+def load_library():
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          f"or python -m verify_accept_sampling_amd._build")
+    lib = ctypes.CDLL(path)
+    c_int, c_size, c_u64, c_i64, c_f, vp = (ctypes.c_int, ctypes.c_size_t, ctypes.c_uint64,
+                                            ctypes.c_int64, ctypes.c_float, ctypes.c_void_p)
+    lib.spec_strerror.argtypes = [c_int]
+    lib.spec_strerror.restype = ctypes.c_char_p
+    lib.spec_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    lib.spec_workspace_bytes.restype = c_size
+    lib.spec_fill_uniforms.argtypes = [c_u64, c_u64, c_i64, vp, vp]
+    lib.spec_fill_uniforms.restype = c_int
+    lib.spec_tree_depth.argtypes = [vp, c_int]
+    lib.spec_tree_depth.restype = c_int
+    lib.spec_verify_greedy.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]
+    lib.spec_verify_greedy.restype = c_int
+    lib.spec_verify_sample.argtypes = [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp, c_u64,
+                                       c_u64, c_f, vp, vp, vp, vp, c_size, vp]
+    lib.spec_verify_sample.restype = c_int
+    lib.spec_verify_tree_greedy.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
+                                            vp, c_size, vp]
+    lib.spec_verify_tree_greedy.restype = c_int
+    _lib = lib
+    return lib
+
+
+def spec_strerror(code: int) -> str:
+    return load_library().spec_strerror(int(code)).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        raise SpecVerifyError(code, spec_strerror(code))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def spec_workspace_bytes(B: int, n_pos: int, V: int) -> int:
+    return int(load_library().spec_workspace_bytes(int(B), int(n_pos), int(V)))
+
+
+class Workspace:
+    """Zero-filled device workspace, grown on demand (zeroed again on growth)."""
+
+    def __init__(self, device=None):
+        self.device = torch.device(device if device is not None else "cuda")
+        self.buf = torch.zeros(0, dtype=torch.uint8, device=self.device)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8,
+                                   device=self.device)
+        return self.buf
+
+    def reset(self):
+        self.buf.zero_()
+
+
+_default_ws = {}
+
+
+def _workspace(ws: Optional[Workspace], device, nbytes: int) -> torch.Tensor:
+    if ws is None:
+        key = torch.device(device).index
+        ws = _default_ws.get(key)
+        if ws is None:
+            ws = _default_ws[key] = Workspace(device)
+    return ws.get(nbytes)
+
+
+def spec_fill_uniforms(seed: int, counter0: int, n: int,
+                       out: Optional[torch.Tensor] = None, device="cuda") -> torch.Tensor:
+    if out is None:
+        out = torch.empty(int(n), dtype=torch.float32, device=device)
+    _need_cuda(out, "out")
+    if out.dtype != torch.float32 or out.numel() < n:
+        raise ValueError("out must be float32 with at least n elements")
+    lib = load_library()
+    _check(lib.spec_fill_uniforms(int(seed) & (2 ** 64 - 1), int(counter0) & (2 ** 64 - 1),
+                                  int(n), _ptr(out), _stream(out.device)))
+    return out
+
+
+def spec_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
+                       workspace: Optional[Workspace] = None):
+    """Greedy chain verification.  target [B, k+1, V] (f32/bf16), draft_tokens
+    int32 [B, k].  Returns (accepted_len [B], out_tokens [B, k+1])."""
+    _need_cuda(target, "target")
+    B, kp1, V = target.shape
+    k = kp1 - 1
+    _need_cuda(draft_tokens, "draft_tokens")
+    if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, k):
+        raise ValueError("draft_tokens must be int32 [B, k]")
+    acc = torch.empty(B, dtype=torch.int32, device=target.device)
+    out = torch.empty(B, kp1, dtype=torch.int32, device=target.device)
+    lib = load_library()
+    nbytes = spec_workspace_bytes(B, kp1, V)
+    ws = _workspace(workspace, target.device, nbytes)
+    _check(lib.spec_verify_greedy(_ptr(target), _dtype_code(target), B, k, V, _ptr(draft_tokens),
+                                  _ptr(acc), _ptr(out), _ptr(ws), ws.numel(),
+                                  _stream(target.device)))
+    return acc, out
+
+
+def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
+                       draft_tokens: torch.Tensor, temperature: float = 1.0,
+                       uniforms: Optional[torch.Tensor] = None, seed: int = 0,
+                       counter0: int = 0, kind: str = "logits", probe: bool = False,
+                       workspace: Optional[Workspace] = None):
+    """Sampling chain verification with min(1, p/q) acceptance.
+
+    target [B, k+1, V], draft [B, k, V] (f32/bf16 logits, or f32 probabilities
+    with kind="probs"), draft_tokens int32 [B, k], uniforms float32
+    [B, k+1, 2] or None (then derived from seed/counter0 inside the kernels).
+    Returns (accepted_len, out_tokens) or, with probe=True,
+    (accepted_len, out_tokens, probe [B, k+1, 4])."""
+    _need_cuda(target, "target")
+    B, kp1, V = target.shape
+    k = kp1 - 1
+    dev = target.device
+    if k > 0:
+        _need_cuda(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, k, V):
+            raise ValueError("draft must match target's dtype with shape [B, k, V]")
+        _need_cuda(draft_tokens, "draft_tokens")
+        if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, k):
+            raise ValueError("draft_tokens must be int32 [B, k]")
+    if uniforms is not None:
+        _need_cuda(uniforms, "uniforms")
+        if uniforms.dtype != torch.float32 or uniforms.numel() != B * kp1 * 2:
+            raise ValueError("uniforms must be float32 [B, k+1, 2]")
+    kind_code = {"logits": SPEC_LOGITS, "probs": SPEC_PROBS}[kind]
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty(B, kp1, dtype=torch.int32, device=dev)
+    pr = torch.empty(B, kp1, 4, dtype=torch.float32, device=dev) if probe else None
+    lib = load_library()
+    nbytes = spec_workspace_bytes(B, kp1, V)
+    ws = _workspace(workspace, dev, nbytes)
+    _check(lib.spec_verify_sample(
+        _ptr(target), _ptr(draft if k > 0 else None), _dtype_code(target), kind_code, B, k, V,
+        _ptr(draft_tokens if k > 0 else None), _ptr(uniforms),
+        int(seed) & (2 ** 64 - 1), int(counter0) & (2 ** 64 - 1), float(temperature),
+        _ptr(acc), _ptr(out), _ptr(pr), _ptr(ws), ws.numel(), _stream(dev)))
+    if probe:
+        return acc, out, pr
+    return acc, out
+
+
+def _parent_array(parent) -> "ctypes.Array":
+    vals = [int(v) for v in (parent.tolist() if hasattr(parent, "tolist") else parent)]
+    return (ctypes.c_int32 * len(vals))(*vals), len(vals)
+
+
+def spec_tree_depth(parent: Sequence[int]) -> int:
+    arr, n = _parent_array(parent)
+    d = int(load_library().spec_tree_depth(ctypes.cast(arr, ctypes.c_void_p), n))
+    if d < 0:
+        _check(d)
+    return d
+
+
+def spec_verify_tree_greedy(target: torch.Tensor, parent: Sequence[int],
+                            node_tokens: torch.Tensor, want_path: bool = True,
+                            workspace: Optional[Workspace] = None):
+    """Greedy tree verification.  target [B, N, V], parent (host sequence of
+    N ints), node_tokens int32 [B, N].  Returns (accepted_len [B],
+    out_tokens [B, D+1], out_path [B, D+1] or None)."""
+    _need_cuda(target, "target")
+    B, N, V = target.shape
+    _need_cuda(node_tokens, "node_tokens")
+    if node_tokens.dtype != torch.int32 or tuple(node_tokens.shape) != (B, N):
+        raise ValueError("node_tokens must be int32 [B, N]")
+    arr, n = _parent_array(parent)
+    if n != N:
+        raise ValueError("parent must have one entry per node")
+    D = spec_tree_depth(parent)
+    dev = target.device
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
+    path = torch.empty(B, D + 1, dtype=torch.int32, device=dev) if want_path else None
+    lib = load_library()
+    nbytes = spec_workspace_bytes(B, N, V)
+    ws = _workspace(workspace, dev, nbytes)
+    _check(lib.spec_verify_tree_greedy(_ptr(target), _dtype_code(target), B, N, V,
+                                       ctypes.cast(arr, ctypes.c_void_p), _ptr(node_tokens),
+                                       _ptr(acc), _ptr(out), _ptr(path), _ptr(ws), ws.numel(),
+                                       _stream(dev)))
+    return acc, out, path

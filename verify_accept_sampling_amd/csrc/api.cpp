@@ -1,0 +1,153 @@
+// C ABI of the verifier: argument validation, workspace layout and dispatch
+// to the gfx950 kernels.  Nothing is enqueued unless every check passes.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/spec_verify.h"
+#include "internal.h"
+
+using namespace specv;
+
+namespace {
+
+bool valid_dtype(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
+
+// Largest number of threads a one-dimensional grid may hold.
+constexpr long kMaxGridThreads = 0xFFFFFFFFL;
+
+int check_workspace(void* ws, size_t ws_bytes, int B, int n_pos, int V, WsLayout* L) {
+  *L = ws_layout(B, n_pos, V);
+  if (ws == nullptr || ws_bytes < L->total) return SPEC_EWORKSPACE;
+  return SPEC_OK;
+}
+
+int check_grid(long blocks) {
+  return (blocks * kThreads <= kMaxGridThreads) ? SPEC_OK : SPEC_EINVAL;
+}
+
+long row_chunks_for(int V) { return (V + kRowChunkElems - 1) / kRowChunkElems; }
+
+int tree_depth_checked(const int32_t* parent, int n_nodes) {
+  if (parent == nullptr || n_nodes < 1 || n_nodes > kMaxNodes) return SPEC_EINVAL;
+  if (parent[0] != -1) return SPEC_ETREE;
+  int depth[kMaxNodes];
+  depth[0] = 0;
+  int D = 0;
+  for (int j = 1; j < n_nodes; ++j) {
+    const int p = parent[j];
+    if (p < 0 || p >= j) return SPEC_ETREE;
+    depth[j] = depth[p] + 1;
+    if (depth[j] > D) D = depth[j];
+  }
+  return D;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_strerror(int code) {
+  switch (code) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument (null pointer, size or scalar out of range)";
+    case SPEC_EDTYPE: return "unsupported dtype / kind combination";
+    case SPEC_EWORKSPACE: return "workspace missing or smaller than spec_workspace_bytes()";
+    case SPEC_EHIP: return "HIP launch failed";
+    case SPEC_ETREE: return "parent array is not a tree with parent[0] = -1 and parent[j] < j";
+    default: return "unknown error code";
+  }
+}
+
+size_t spec_workspace_bytes(int B, int n_pos, int V) {
+  if (B < 0 || B > kMaxB || n_pos < 1 || n_pos > kMaxNodes || V < 1 || V > kMaxV) return 0;
+  return ws_layout(B, n_pos, V).total;
+}
+
+int spec_fill_uniforms(uint64_t seed, uint64_t counter0, int64_t n, float* out, void* stream) {
+  if (n < 0) return SPEC_EINVAL;
+  if (n == 0) return SPEC_OK;
+  if (out == nullptr) return SPEC_EINVAL;
+  if (launch_fill_uniforms(seed, counter0, n, out, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return SPEC_EHIP;
+  return SPEC_OK;
+}
+
+int spec_tree_depth(const int32_t* parent_host, int n_nodes) {
+  return tree_depth_checked(parent_host, n_nodes);
+}
+
+int spec_verify_greedy(const void* target, int dtype, int B, int k, int V,
+                       const int32_t* draft_tokens, int32_t* accepted_len, int32_t* out_tokens,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return SPEC_EDTYPE;
+  if (B < 0 || B > kMaxB || k < 0 || k > kMaxK || V < 1 || V > kMaxV) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (target == nullptr || accepted_len == nullptr || out_tokens == nullptr) return SPEC_EINVAL;
+  if (k > 0 && draft_tokens == nullptr) return SPEC_EINVAL;
+  if (check_grid((long)B * (k + 1) * row_chunks_for(V)) != SPEC_OK) return SPEC_EINVAL;
+  WsLayout L;
+  if (int rc = check_workspace(ws, ws_bytes, B, k + 1, V, &L)) return rc;
+  if (launch_greedy_chain(target, dtype, B, k, V, draft_tokens, accepted_len, out_tokens, ws, L,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPEC_EHIP;
+  return SPEC_OK;
+}
+
+int spec_verify_sample(const void* target, const void* draft, int dtype, int kind, int B, int k,
+                       int V, const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
+                       uint64_t counter0, float temperature, int32_t* accepted_len,
+                       int32_t* out_tokens, float* probe, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!valid_dtype(dtype) || (kind != SPEC_LOGITS && kind != SPEC_PROBS)) return SPEC_EDTYPE;
+  if (kind == SPEC_PROBS && dtype != SPEC_F32) return SPEC_EDTYPE;
+  if (B < 0 || B > kMaxB || k < 0 || k > kMaxK || V < 1 || V > kMaxV) return SPEC_EINVAL;
+  if (kind == SPEC_LOGITS) {
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return SPEC_EINVAL;
+    const float c = 1.4426950408889634f / temperature;
+    if (!std::isfinite(c) || !std::isfinite(1.0 / (double)temperature)) return SPEC_EINVAL;
+  } else if (temperature != 1.f) {
+    return SPEC_EINVAL;
+  }
+  if (B == 0) return SPEC_OK;
+  if (target == nullptr || accepted_len == nullptr || out_tokens == nullptr) return SPEC_EINVAL;
+  if (k > 0 && (draft == nullptr || draft_tokens == nullptr)) return SPEC_EINVAL;
+  const long C2 = (V + kResChunkElems - 1) / kResChunkElems;
+  if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V)) != SPEC_OK) return SPEC_EINVAL;
+  if (check_grid((long)B * C2) != SPEC_OK) return SPEC_EINVAL;
+  WsLayout L;
+  if (int rc = check_workspace(ws, ws_bytes, B, k + 1, V, &L)) return rc;
+  if (launch_sample(target, draft, dtype, kind, B, k, V, draft_tokens, uniforms, seed, counter0,
+                    temperature, accepted_len, out_tokens, probe, ws, L,
+                    static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPEC_EHIP;
+  return SPEC_OK;
+}
+
+int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes, int V,
+                            const int32_t* parent_host, const int32_t* node_tokens,
+                            int32_t* accepted_len, int32_t* out_tokens, int32_t* out_path,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return SPEC_EDTYPE;
+  if (B < 0 || B > kMaxB || n_nodes < 1 || n_nodes > kMaxNodes || V < 1 || V > kMaxV)
+    return SPEC_EINVAL;
+  const int D = tree_depth_checked(parent_host, n_nodes);
+  if (D < 0) return D;
+  if (B == 0) return SPEC_OK;
+  if (target == nullptr || node_tokens == nullptr || accepted_len == nullptr ||
+      out_tokens == nullptr)
+    return SPEC_EINVAL;
+  if (check_grid((long)B * n_nodes * row_chunks_for(V)) != SPEC_OK) return SPEC_EINVAL;
+  WsLayout L;
+  if (int rc = check_workspace(ws, ws_bytes, B, n_nodes, V, &L)) return rc;
+  TreeArgs tree;
+  std::memset(&tree, 0, sizeof(tree));
+  for (int j = 0; j < n_nodes; ++j) tree.parent[j] = static_cast<int16_t>(parent_host[j]);
+  if (launch_tree_greedy(target, dtype, B, n_nodes, V, tree, D, node_tokens, accepted_len,
+                         out_tokens, out_path, ws, L, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return SPEC_EHIP;
+  return SPEC_OK;
+}
+
+}  // extern "C"

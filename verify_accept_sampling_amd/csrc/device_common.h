@@ -1,0 +1,225 @@
+// Device helpers for the gfx950 verification kernels: row addressing,
+// 16-byte vector loads, wave64 / work-group reductions and scans, the
+// counter-based SplitMix64 uniform, and the last-work-group ticket.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace specv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Elements per 16-byte vector for each input dtype (0 = f32, 1 = bf16).
+template <int DT>
+struct Elems {
+  static constexpr int kVec = DT == 1 ? 8 : 4;
+  static constexpr int kBytes = DT == 1 ? 2 : 4;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// One element of a row as float.
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* row, long j) {
+  if constexpr (DT == 1) {
+    const uint16_t h = reinterpret_cast<const uint16_t*>(row)[j];
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+  } else {
+    return reinterpret_cast<const float*>(row)[j];
+  }
+}
+
+// NE elements starting at element index e0 (NE == Elems<DT>::kVec: one
+// 16-byte load that must be 16-byte aligned; NE == 1: one scalar load).
+template <int DT, int NE>
+__device__ __forceinline__ void load_group(const void* row, long e0, float (&x)[NE]) {
+  if constexpr (NE == 1) {
+    x[0] = load_elem<DT>(row, e0);
+  } else {
+    static_assert(NE == Elems<DT>::kVec, "vector group must be 16 bytes");
+    const u32x4 w = *reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const char*>(row) + e0 * Elems<DT>::kBytes);
+    if constexpr (DT == 1) {
+      x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+      x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+      x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+      x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    } else {
+      x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+      x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 shuffles
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ double shfl_up_d(double v, int d) { return __shfl_up(v, d, 64); }
+
+// ---------------------------------------------------------------------------
+// (max, sum of exp2((x - max) * c)) pairs: the streaming softmax statistic
+// ---------------------------------------------------------------------------
+
+// Combine two (m, s) pairs, s measured relative to m in base-2 units scaled
+// by c.  -inf maxima (no finite element yet) carry s = 0.
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2, float c) {
+  const float mn = fmaxf(m, m2);
+  const float base = (mn == -INFINITY) ? 0.f : mn;
+  s = s * __builtin_amdgcn_exp2f((m - base) * c) + s2 * __builtin_amdgcn_exp2f((m2 - base) * c);
+  m = mn;
+}
+
+// Work-group reduction of (m, s); result valid in thread 0.
+__device__ __forceinline__ void block_reduce_ms(float& m, float& s, float c) {
+  __shared__ float sm[kWaves], ss[kWaves];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = shfl_xor_f(m, o);
+    const float s2 = shfl_xor_f(s, o);
+    ms_merge(m, s, m2, s2, c);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) { sm[wave] = m; ss[wave] = s; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = sm[0]; s = ss[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) ms_merge(m, s, sm[w], ss[w], c);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// (value, index) argmax with lowest index on ties
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void am_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+// Work-group argmax; result valid in thread 0.
+__device__ __forceinline__ void block_reduce_am(float& v, int& i) {
+  __shared__ float sv[kWaves];
+  __shared__ int si[kWaves];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v2 = shfl_xor_f(v, o);
+    const int i2 = shfl_xor_i(i, o);
+    am_merge(v, i, v2, i2);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) { sv[wave] = v; si[wave] = i; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    v = sv[0]; i = si[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) am_merge(v, i, sv[w], si[w]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float64 sums and scans over a work-group
+// ---------------------------------------------------------------------------
+
+// Sum over the work-group (fixed order); result broadcast to all threads.
+__device__ __forceinline__ double block_sum_d(double v) {
+  __shared__ double sd[kWaves];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += shfl_xor_d(v, o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sd[wave] = v;
+  __syncthreads();
+  double t = sd[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) t += sd[w];
+  return t;
+}
+
+// Exclusive scan of one double per thread across the work-group.
+// Returns the exclusive prefix for this thread.
+__device__ __forceinline__ double block_exclusive_scan_d(double v) {
+  __shared__ double wsum[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = shfl_up_d(inc, d);
+    if (lane >= d) inc += o;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  return base + (inc - v);
+}
+
+// Minimum of an int over the work-group, broadcast.
+__device__ __forceinline__ int block_min_i(int v) {
+  __shared__ int si[kWaves];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, shfl_xor_i(v, o));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) si[wave] = v;
+  __syncthreads();
+  int t = si[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) t = min(t, si[w]);
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// SplitMix64 uniform (Steele, Lea & Flood 2014), counter form
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float splitmix_uniform(uint64_t seed, uint64_t ctr) {
+  uint64_t z = seed + (ctr + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z = z ^ (z >> 31);
+  return static_cast<float>(static_cast<uint32_t>(z >> 40)) * 0x1.0p-24f;
+}
+
+// Uniform for (request b, position i, slot) from an array or from the seed.
+__device__ __forceinline__ float get_uniform(const float* u, uint64_t seed, uint64_t ctr0,
+                                             int b, int i, int slot, int k) {
+  const long idx = ((long)b * (k + 1) + i) * 2 + slot;
+  if (u != nullptr) return u[idx];
+  return splitmix_uniform(seed, ctr0 + (uint64_t)idx);
+}
+
+// ---------------------------------------------------------------------------
+// Last-work-group ticket: every work-group of a group calls this once after
+// publishing its partial result; exactly one (the last) gets true.  The
+// counter is reset to zero by the last work-group so the workspace is left
+// clean for the next call.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bool last_block_ticket(unsigned* counter, unsigned total) {
+  __shared__ int is_last;
+  __threadfence();  // publish this work-group's partials (device scope)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(counter, 1u);
+    is_last = (prev == total - 1u);
+    if (is_last) atomicExch(counter, 0u);
+  }
+  __syncthreads();
+  const bool last = is_last != 0;
+  if (last) __threadfence();  // acquire the other work-groups' partials
+  return last;
+}
+
+}  // namespace specv
