@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched sampling verification step on one MI355X.
+
+Workload: B=64 requests, k=8 drafts, V=128256 (Llama-3 vocabulary), bf16
+target logits N(0, 3^2) with 20 peak tokens per row boosted by +8, draft =
+target + N(0, 1.5^2), temperature 0.7, draft tokens drawn from the draft
+distribution, uniforms from the SplitMix64 counter (fresh per step).
+
+One step = one spec_verify_sample call: the float32 row-statistics pass over
+all 17 rows per request, the float64 min(1, p/q) tests, and the float64
+residual / bonus draw.  Inputs are resident in HBM; `--copies` input copies
+are rotated so the 256 MB Infinity Cache cannot serve a step from the
+previous one.
+
+Prints one JSON line: verified positions per second (B * (k+1) target
+positions per step) and, for the dominant kernel (the row-statistics pass),
+algorithmic HBM bytes per launch over its average event-timed duration
+against the 8 TB/s peak; plus the float64 oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B=64 k=8 V=128256"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_b64_k8_v128256_traffic.json")
+KERNEL_SOURCES = ["verify_accept_sampling_amd/csrc/sample.hip",
+                  "verify_accept_sampling_amd/csrc/device_common.h",
+                  "verify_accept_sampling_amd/csrc/internal.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_per_launch: float):
+    """HBM bytes per launch of the row-statistics kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The float64 oracle, as it stands, on the same workload: request after
+    request (repeating the batch with fresh uniforms) until the time budget
+    is spent, on one host thread."""
+    import oracle.rng as R
+    import oracle.verify as O
+
+    t0 = time.perf_counter()
+    done = 0
+    rep = 0
+    while time.perf_counter() - t0 < budget_s:
+        u = R.chain_uniforms(wl.uniform_seed, wl.B, wl.k, rep * wl.B * (wl.k + 1) * 2)
+        for b in range(wl.B):
+            O.verify_sample(wl.target, wl.draft, wl.draft_tokens, u, wl.temperature, wl.kind,
+                            wl.dtype, requests=[b])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        rep += 1
+    dt = time.perf_counter() - t0
+    return {"value": done * (wl.k + 1) / dt, "unit": "verified positions/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} requests of the B=64, k=8, V=128256 bf16 workload "
+                      f"(batch repeated with fresh uniforms), {dt:.1f} s on 1 host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the verifier is batch-parallel and this build "
+              "runs on a single MI355X (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import verify_accept_sampling_amd as S
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating B=64 k=8 V=128256 bf16 workload", file=sys.stderr, flush=True)
+    wl = W.sample_chain_llama3()
+    B, k, V = wl.B, wl.k, wl.V
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    tgt0, dft0 = dev_bf16(wl.target), dev_bf16(wl.draft)
+    copies = [(tgt0, dft0)] + [(tgt0.clone(), dft0.clone()) for _ in range(args.copies - 1)]
+    toks = torch.from_numpy(wl.draft_tokens).to(dev)
+    ws = S.Workspace(dev)
+    n_u = B * (k + 1) * 2
+
+    def step(i):
+        t, d = copies[i % len(copies)]
+        return S.spec_verify_sample(t, d, toks, wl.temperature, seed=wl.uniform_seed,
+                                    counter0=i * n_u, workspace=ws)
+
+    print(f"bench: warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    S.spec_profile_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    accs = []
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        acc, _ = step(args.warmup + i)
+        accs.append(acc)
+    end.record()
+    torch.cuda.synchronize()
+    S.spec_profile_enable(False)
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    kern = {}
+    for name in ("row_pass", "draw"):
+        n, ms = S.spec_profile_read(name)
+        kern[name] = {"launches": n, "avg_us": (ms / n * 1e3) if n else None}
+    print(f"bench: timed {args.steps} steps, {ms_step * 1e3:.1f} us/step", file=sys.stderr,
+          flush=True)
+
+    acc_all = torch.stack(accs).cpu().numpy()
+    row_bytes = V * 2
+    pass1_bytes = B * (2 * k + 1) * row_bytes
+    rejected = (acc_all < k).sum(axis=1)
+    draw_bytes = (rejected * 2 + (B - rejected)) * row_bytes
+    search_bytes = (rejected * 2 + (B - rejected)) * min(V, 4096) * 2
+    step_bytes = float(np.mean(pass1_bytes + draw_bytes + search_bytes))
+    avg_row_us = kern["row_pass"]["avg_us"]
+    achieved = pass1_bytes / (avg_row_us * 1e-6) / 1e9
+    traffic = measured_traffic(pass1_bytes)
+    positions = B * (k + 1)
+    result = {
+        "metric": METRIC,
+        "value": positions / (ms_step * 1e-3),
+        "unit": "verified positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "sample_chain_b64_k8_v128256_bf16_t0.7", "B": B, "k": k, "V": V,
+                   "logits": "bf16", "temperature": wl.temperature, "input_copies": len(copies),
+                   "draw_arithmetic": "f64"},
+        "roofline": {"bound": "hbm", "kernel": "k_row_stats", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": pass1_bytes},
+        "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_algorithmic_bytes": step_bytes,
+        "kernels_avg_us": {n: v["avg_us"] for n, v in kern.items()},
+        "mean_accepted": float(acc_all.mean()),
+        "mean_emitted": float(acc_all.mean() + 1),
+    }
+    if not args.no_cpu_baseline:
+        print(f"bench: cpu baseline ({args.cpu_seconds:.0f} s budget)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

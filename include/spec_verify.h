@@ -25,9 +25,10 @@
  *    outputs are valid once that stream has been synchronised.
  *  - `ws` is a caller-owned device workspace of at least
  *    spec_workspace_bytes(B, n_pos, V) bytes.  It must be zero-filled before
- *    its first use.  Its first 1 MiB holds completion counters at fixed
- *    places, which every call leaves at zero again, so one workspace can be
- *    reused for calls of any shape without clearing it.  Calls that share a
+ *    its first use.  Its first 512 KiB hold per-request completion counters
+ *    at fixed places, which every call leaves at zero again, so one
+ *    workspace serves calls of any shape without clearing it; the rest is
+ *    scratch that each call writes before reading.  Calls that share a
  *    workspace must be ordered on one stream.
  *  - Return value: SPEC_OK, or a negative code.  Any code other than
  *    SPEC_EHIP means the arguments were rejected on the host and nothing was
@@ -127,8 +128,8 @@ int spec_verify_greedy(const void* target, int dtype, int B, int k, int V,
  * sum max(0, p_n - q_n) after a rejection, sum p_k for the bonus draw); all
  * other entries 0.
  * Arithmetic: row statistics (max, log-sum-exp) in float32 with float64
- * merges; the acceptance ratio in float64; the residual / bonus draw fully
- * in float64. */
+ * merges; the acceptance ratio in float64; the residual / bonus draw in
+ * float64 (normalisers, weights and running sums). */
 int spec_verify_sample(const void* target, const void* draft, int dtype, int kind,
                        int B, int k, int V, const int32_t* draft_tokens,
                        const float* uniforms, uint64_t seed, uint64_t counter0,
@@ -163,6 +164,21 @@ int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes,
 /* Depth D of the tree described by parent_host (see above), or a negative
  * error code if the array is malformed.  Host only. */
 int spec_tree_depth(const int32_t* parent_host, int n_nodes);
+
+/* Optional per-kernel timing for measurement tools (not part of the
+ * verification itself).  spec_profile_enable(1) clears the totals and, from
+ * then on, brackets every kernel the library enqueues with two HIP events on
+ * the same stream; spec_profile_enable(0) stops recording.  spec_profile_read
+ * waits for the recorded events and returns, for one kernel kind, the number
+ * of timed launches and their summed event time in milliseconds.  Kinds: */
+enum {
+  SPEC_KERNEL_ROW_PASS = 0, /* row pass over every logit row + per-request finish
+                               (acceptance tests, greedy rule, tree walk) */
+  SPEC_KERNEL_DRAW = 1,     /* float64 residual / bonus pass + inverse-CDF draw */
+  SPEC_KERNEL_UNIFORMS = 2  /* spec_fill_uniforms */
+};
+int spec_profile_enable(int on);
+int spec_profile_read(int kind, long* launches, double* total_ms);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ __all__ = [
     "SpecVerifyError", "Workspace", "library_path", "load_library", "declared_symbols",
     "spec_workspace_bytes", "spec_fill_uniforms", "spec_verify_greedy",
     "spec_verify_sample", "spec_verify_tree_greedy", "spec_tree_depth", "spec_strerror",
+    "spec_profile_enable", "spec_profile_read", "KERNEL_KINDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -83,8 +84,29 @@ def load_library():
     lib.spec_verify_tree_greedy.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                             vp, c_size, vp]
     lib.spec_verify_tree_greedy.restype = c_int
+    lib.spec_profile_enable.argtypes = [c_int]
+    lib.spec_profile_enable.restype = c_int
+    lib.spec_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_long),
+                                      ctypes.POINTER(ctypes.c_double)]
+    lib.spec_profile_read.restype = c_int
     _lib = lib
     return lib
+
+
+KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2}
+
+
+def spec_profile_enable(on: bool = True) -> None:
+    """Start (clearing the totals) or stop per-kernel event timing."""
+    _check(load_library().spec_profile_enable(1 if on else 0))
+
+
+def spec_profile_read(kind: str):
+    """(launches, total milliseconds) of one kernel kind since enabling."""
+    n = ctypes.c_long(0)
+    ms = ctypes.c_double(0.0)
+    _check(load_library().spec_profile_read(KERNEL_KINDS[kind], ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
 
 
 def spec_strerror(code: int) -> str:
@@ -124,7 +146,10 @@ def spec_workspace_bytes(B: int, n_pos: int, V: int) -> int:
 
 
 class Workspace:
-    """Zero-filled device workspace, grown on demand (zeroed again on growth)."""
+    """Zero-filled device workspace, grown on demand (zeroed again on growth).
+
+    Calls leave its completion counters at zero, so it needs no clearing
+    between calls of any shape."""
 
     def __init__(self, device=None):
         self.device = torch.device(device if device is not None else "cuda")
@@ -135,9 +160,6 @@ class Workspace:
             self.buf = torch.zeros(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8,
                                    device=self.device)
         return self.buf
-
-    def reset(self):
-        self.buf.zero_()
 
 
 _default_ws = {}

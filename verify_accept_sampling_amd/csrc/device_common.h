@@ -1,6 +1,20 @@
 // Device helpers for the gfx950 verification kernels: row addressing,
 // 16-byte vector loads, wave64 / work-group reductions and scans, the
-// counter-based SplitMix64 uniform, and the last-work-group ticket.
+// counter-based SplitMix64 uniform, and the completion tickets that let the
+// last work-group of a request finish it.
+//
+// Completion tickets without device-scope fences.  On this part a
+// device-scope release (an L2 write-back) inside a streaming kernel costs
+// about 1 us per work-group per XCD, so no kernel here uses one.  Instead a
+// work-group publishes its partial result with device-scope relaxed atomic
+// stores, which compile to stores with the sc1 bit: written through to the
+// device coherence point, past the XCD's L2.  It then waits until those
+// stores have completed (s_waitcnt vmcnt(0)) and only then increments the
+// request's counter with a device-scope atomic.  The work-group that
+// receives the last ticket reads the partials with device-scope relaxed
+// atomic loads (sc1: served from the coherence point, not from a stale L2
+// line).  Every partial was complete before its ticket was taken, and the
+// last ticket is taken after every other ticket, so the reader sees them all.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,6 +24,50 @@
 #include "internal.h"
 
 namespace specv {
+
+// ---------------------------------------------------------------------------
+// Coherent publication and completion tickets
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_d(double* p, double v) {
+  st_dev(reinterpret_cast<uint64_t*>(p), static_cast<uint64_t>(__double_as_longlong(v)));
+}
+__device__ __forceinline__ double ld_dev_d(const double* p) {
+  return __longlong_as_double(static_cast<long long>(ld_dev(reinterpret_cast<const uint64_t*>(p))));
+}
+__device__ __forceinline__ uint64_t pack2(float a, float b) {
+  return static_cast<uint64_t>(__float_as_uint(a)) |
+         (static_cast<uint64_t>(__float_as_uint(b)) << 32);
+}
+__device__ __forceinline__ float unpack_lo(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v)); }
+__device__ __forceinline__ float unpack_hi(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
+
+// One thread per work-group calls this after its coherent stores.  Returns
+// true for the last of `total` arrivals; that caller also resets the counter
+// to zero for the next call.
+__device__ __forceinline__ bool arrive(unsigned* counter, unsigned total) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const unsigned t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool last = (t == total - 1u);
+  if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
+// Work-group form: thread 0 arrives; the answer is broadcast.
+__device__ __forceinline__ bool block_arrive(unsigned* counter, unsigned total) {
+  __shared__ int s_last;
+  if (threadIdx.x == 0) s_last = arrive(counter, total) ? 1 : 0;
+  __syncthreads();
+  return s_last != 0;
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -36,14 +94,16 @@ __device__ __forceinline__ float load_elem(const void* row, long j) {
 
 // NE elements starting at element index e0 (NE == Elems<DT>::kVec: one
 // 16-byte load that must be 16-byte aligned; NE == 1: one scalar load).
-template <int DT, int NE>
+// NT: non-temporal load (streamed data that is read once).
+template <int DT, int NE, bool NT = false>
 __device__ __forceinline__ void load_group(const void* row, long e0, float (&x)[NE]) {
   if constexpr (NE == 1) {
     x[0] = load_elem<DT>(row, e0);
   } else {
     static_assert(NE == Elems<DT>::kVec, "vector group must be 16 bytes");
-    const u32x4 w = *reinterpret_cast<const u32x4*>(
+    const u32x4* ptr = reinterpret_cast<const u32x4*>(
         reinterpret_cast<const char*>(row) + e0 * Elems<DT>::kBytes);
+    const u32x4 w = NT ? __builtin_nontemporal_load(ptr) : *ptr;
     if constexpr (DT == 1) {
       x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
       x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
@@ -146,6 +206,31 @@ __device__ __forceinline__ double block_sum_d(double v) {
   return t;
 }
 
+// Sums of five doubles per thread over the work-group, in place (every
+// thread receives the totals).
+__device__ __forceinline__ void block_sum_d5(double (&v)[5]) {
+  __shared__ double sd[kWaves][5];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int q = 0; q < 5; ++q) v[q] += shfl_xor_d(v[q], o);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < 5; ++q) sd[wave][q] = v[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    double t = sd[0][q];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += sd[w][q];
+    v[q] = t;
+  }
+}
+
 // Exclusive scan of one double per thread across the work-group.
 // Returns the exclusive prefix for this thread.
 __device__ __forceinline__ double block_exclusive_scan_d(double v) {
@@ -198,28 +283,6 @@ __device__ __forceinline__ float get_uniform(const float* u, uint64_t seed, uint
   const long idx = ((long)b * (k + 1) + i) * 2 + slot;
   if (u != nullptr) return u[idx];
   return splitmix_uniform(seed, ctr0 + (uint64_t)idx);
-}
-
-// ---------------------------------------------------------------------------
-// Last-work-group ticket: every work-group of a group calls this once after
-// publishing its partial result; exactly one (the last) gets true.  The
-// counter is reset to zero by the last work-group so the workspace is left
-// clean for the next call.
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ bool last_block_ticket(unsigned* counter, unsigned total) {
-  __shared__ int is_last;
-  __threadfence();  // publish this work-group's partials (device scope)
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(counter, 1u);
-    is_last = (prev == total - 1u);
-    if (is_last) atomicExch(counter, 0u);
-  }
-  __syncthreads();
-  const bool last = is_last != 0;
-  if (last) __threadfence();  // acquire the other work-groups' partials
-  return last;
 }
 
 }  // namespace specv

@@ -1,9 +1,10 @@
-// Greedy chain and greedy tree verification for gfx950.
+// Greedy chain and greedy tree verification for gfx950, one launch per call.
 //
-// One launch per call.  Work-group (chunk, row) streams one chunk of one
-// logit row with 16-byte loads and reduces it to (max value, lowest index).
-// The last work-group to finish a request (ticket counter) merges the chunk
-// partials of that request's rows and applies the greedy rule:
+// Work-group (chunk, row) streams one chunk of one logit row with 16-byte
+// non-temporal loads and reduces it to (max value, lowest index), publishes
+// that partial and takes its request's completion ticket.  The last
+// work-group of a request merges the partials of the request's rows and
+// applies the greedy rule:
 //   chain: the first draft token that differs from the target argmax ends
 //          the accepted prefix and the argmax there is emitted
 //          ("EAGLE-3 speculative decoding review", greedy bullets of the
@@ -18,59 +19,60 @@
 
 namespace specv {
 
-struct ArgmaxPart {
-  float v;
-  int i;
-};
+// Groups in flight per thread in the streaming loop.
+constexpr int kUnrollArgmax = kRowUnroll;
 
-// Unroll depth of the streaming loops: groups in flight per thread.
-constexpr int kUnrollArgmax = 4;
-
-// Argmax of row elements [chunk range) for this thread (ascending order, so
-// a strict '>' keeps the lowest index).  NE = elements per load.
-template <int DT, int NE>
-__device__ __forceinline__ void argmax_sweep(const void* row, long n_groups, long g0, long g1,
-                                             float& bv, int& bi) {
-  bv = -INFINITY;
-  bi = INT_MAX;
-  for (long g = g0 + threadIdx.x; g < g1; g += (long)kThreads * kUnrollArgmax) {
-    float x[kUnrollArgmax][NE];
+// Fold one group of NE elements (group index gi) into the running argmax;
+// a strict '>' keeps the lowest index because groups arrive in ascending
+// order within a thread.
+template <int NE>
+__device__ __forceinline__ void argmax_update(float& bv, int& bi, const float (&x)[NE], long gi) {
+  float lm = x[0];
 #pragma unroll
-    for (int u = 0; u < kUnrollArgmax; ++u) {
-      const long gg = g + (long)u * kThreads;
-      if (gg < g1) {
-        load_group<DT, NE>(row, gg * NE, x[u]);
-      } else {
+  for (int e = 1; e < NE; ++e) lm = fmaxf(lm, x[e]);
+  if (lm > bv) {
+    int first = NE - 1;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) x[u][e] = -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnrollArgmax; ++u) {
-      float lm = x[u][0];
-#pragma unroll
-      for (int e = 1; e < NE; ++e) lm = fmaxf(lm, x[u][e]);
-      if (lm > bv) {
-        int first = NE - 1;
-#pragma unroll
-        for (int e = NE - 1; e >= 0; --e)
-          if (x[u][e] == lm) first = e;
-        bv = lm;
-        bi = static_cast<int>((g + (long)u * kThreads) * NE + first);
-      }
-    }
+    for (int e = NE - 1; e >= 0; --e)
+      if (x[e] == lm) first = e;
+    bv = lm;
+    bi = static_cast<int>(gi * NE + first);
   }
-  (void)n_groups;
 }
 
-// Stream the (chunk, row) of this work-group and publish its partial.
-// Returns the request index of the row.
+// Argmax of this thread's groups in [g0, g1) (ascending, so a strict '>'
+// keeps the lowest index).  NE = elements per load.
 template <int DT, int NE>
-__device__ __forceinline__ int argmax_chunk(const void* target, int n_pos, int V, int C1,
-                                            ArgmaxPart* part) {
-  const int blk = blockIdx.x;
-  const int chunk = blk % C1;
-  const long row = blk / C1;
+__device__ __forceinline__ void argmax_sweep(const void* row, long g0, long g1, float& bv,
+                                             int& bi) {
+  bv = -INFINITY;
+  bi = INT_MAX;
+  long g = g0 + threadIdx.x;
+  // Main loop: kUnrollArgmax loads issued back to back, no bounds branch.
+  for (; g + (long)(kUnrollArgmax - 1) * kThreads < g1; g += (long)kThreads * kUnrollArgmax) {
+    float x[kUnrollArgmax][NE];
+#pragma unroll
+    for (int u = 0; u < kUnrollArgmax; ++u)
+      load_group<DT, NE, true>(row, (g + (long)u * kThreads) * NE, x[u]);
+#pragma unroll
+    for (int u = 0; u < kUnrollArgmax; ++u) argmax_update<NE>(bv, bi, x[u], g + (long)u * kThreads);
+  }
+  for (; g < g1; g += kThreads) {
+    float x[NE];
+    load_group<DT, NE, true>(row, g * NE, x);
+    argmax_update<NE>(bv, bi, x, g);
+  }
+}
+
+// Stream this work-group's (chunk, row), publish its (value, index) partial
+// and take the request's ticket.  Returns true in the request's last
+// work-group.
+template <int DT, int NE>
+__device__ __forceinline__ bool argmax_chunk(const void* target, int n_pos, int V, int C1,
+                                            uint64_t* part, unsigned* counters, int& b) {
+  const int chunk = blockIdx.x % C1;
+  const long row = blockIdx.x / C1;
+  b = static_cast<int>(row / n_pos);
   const long n_groups = V / NE;
   const long gpc = (n_groups + C1 - 1) / C1;
   const long g0 = (long)chunk * gpc;
@@ -78,32 +80,25 @@ __device__ __forceinline__ int argmax_chunk(const void* target, int n_pos, int V
   const void* rp = reinterpret_cast<const char*>(target) + row * (long)V * Elems<DT>::kBytes;
   float bv;
   int bi;
-  argmax_sweep<DT, NE>(rp, n_groups, g0, g1, bv, bi);
+  argmax_sweep<DT, NE>(rp, g0, g1, bv, bi);
   block_reduce_am(bv, bi);
-  if (threadIdx.x == 0) part[row * C1 + chunk] = ArgmaxPart{bv, bi};
-  return static_cast<int>(row / n_pos);
+  if (threadIdx.x == 0) st_dev(&part[row * C1 + chunk], pack2(bv, __int_as_float(bi)));
+  return block_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(n_pos * C1));
 }
 
-// In the last work-group of request b: merge every row's chunk partials into
-// amax[0..n_pos-1] (shared memory).  All-(-inf) rows resolve to index 0.
-__device__ __forceinline__ void merge_argmax_rows(const ArgmaxPart* part, int b, int n_pos,
-                                                  int C1, int* amax) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int j = wave; j < n_pos; j += kWaves) {
+// Merge every row's chunk partials of request b into amax[0..n_pos-1]
+// (shared memory), one thread per row.  All-(-inf) rows resolve to index 0.
+__device__ __forceinline__ void merge_argmax_rows(const uint64_t* part, int b, int n_pos, int C1,
+                                                  int* amax) {
+  for (int j = threadIdx.x; j < n_pos; j += kThreads) {
     const long row = (long)b * n_pos + j;
     float v = -INFINITY;
     int i = INT_MAX;
-    for (int c = lane; c < C1; c += 64) {
-      const ArgmaxPart p = part[row * C1 + c];
-      am_merge(v, i, p.v, p.i);
+    for (int c = 0; c < C1; ++c) {
+      const uint64_t p = ld_dev(&part[row * C1 + c]);
+      am_merge(v, i, unpack_lo(p), __float_as_int(unpack_hi(p)));
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float v2 = shfl_xor_f(v, o);
-      const int i2 = shfl_xor_i(i, o);
-      am_merge(v, i, v2, i2);
-    }
-    if (lane == 0) amax[j] = (i == INT_MAX) ? 0 : i;
+    amax[j] = (i == INT_MAX) ? 0 : i;
   }
   __syncthreads();
 }
@@ -112,15 +107,13 @@ template <int DT, int NE>
 __global__ __launch_bounds__(kThreads) void k_greedy_chain(
     const void* __restrict__ target, int k, int V, int C1,
     const int32_t* __restrict__ draft_tokens, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ out_tokens, ArgmaxPart* __restrict__ part,
+    int32_t* __restrict__ out_tokens, uint64_t* __restrict__ part,
     unsigned* __restrict__ counters) {
   const int n_pos = k + 1;
-  const int b = argmax_chunk<DT, NE>(target, n_pos, V, C1, part);
-  if (!last_block_ticket(&counters[(long)b * kCountersPerReq + 0], (unsigned)(n_pos * C1)))
-    return;
+  int b;
+  if (!argmax_chunk<DT, NE>(target, n_pos, V, C1, part, counters, b)) return;
   __shared__ int amax[kMaxK + 1];
   merge_argmax_rows(part, b, n_pos, C1, amax);
-  // first mismatch: minimum over positions that differ
   int first = k;
   for (int i = threadIdx.x; i < k; i += kThreads)
     if (draft_tokens[(long)b * k + i] != amax[i]) first = min(first, i);
@@ -139,10 +132,9 @@ __global__ __launch_bounds__(kThreads) void k_tree_greedy(
     const void* __restrict__ target, int n_nodes, int V, int C1, TreeArgs tree, int D,
     const int32_t* __restrict__ node_tokens, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_path,
-    ArgmaxPart* __restrict__ part, unsigned* __restrict__ counters) {
-  const int b = argmax_chunk<DT, NE>(target, n_nodes, V, C1, part);
-  if (!last_block_ticket(&counters[(long)b * kCountersPerReq + 0], (unsigned)(n_nodes * C1)))
-    return;
+    uint64_t* __restrict__ part, unsigned* __restrict__ counters) {
+  int b;
+  if (!argmax_chunk<DT, NE>(target, n_nodes, V, C1, part, counters, b)) return;
   __shared__ int amax[kMaxNodes];
   __shared__ int tok[kMaxNodes];
   __shared__ int path[kMaxNodes];
@@ -207,10 +199,11 @@ hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int 
                                hipStream_t s) {
   const int C1 = row_chunks(V);
   char* w = static_cast<char*>(ws);
-  auto* part = reinterpret_cast<ArgmaxPart*>(w + L.part1);
+  auto* part = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const dim3 grid((unsigned)((long)B * (k + 1) * C1)), block(kThreads);
   const bool vec = rows_aligned(target, V, dtype);
+  prof_before(kProfRowPass, s);
   if (dtype == 1) {
     if (vec)
       hipLaunchKernelGGL((k_greedy_chain<1, 8>), grid, block, 0, s, target, k, V, C1,
@@ -226,6 +219,7 @@ hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int 
       hipLaunchKernelGGL((k_greedy_chain<0, 1>), grid, block, 0, s, target, k, V, C1,
                          draft_tokens, accepted_len, out_tokens, part, cnt);
   }
+  prof_after(kProfRowPass, s);
   return hipGetLastError();
 }
 
@@ -235,10 +229,11 @@ hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
                               void* ws, const WsLayout& L, hipStream_t s) {
   const int C1 = row_chunks(V);
   char* w = static_cast<char*>(ws);
-  auto* part = reinterpret_cast<ArgmaxPart*>(w + L.part1);
+  auto* part = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const dim3 grid((unsigned)((long)B * n_nodes * C1)), block(kThreads);
   const bool vec = rows_aligned(target, V, dtype);
+  prof_before(kProfRowPass, s);
   if (dtype == 1) {
     if (vec)
       hipLaunchKernelGGL((k_tree_greedy<1, 8>), grid, block, 0, s, target, n_nodes, V, C1,
@@ -258,6 +253,7 @@ hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
                          tree, depth, node_tokens, accepted_len, out_tokens, out_path, part,
                          cnt);
   }
+  prof_after(kProfRowPass, s);
   return hipGetLastError();
 }
 

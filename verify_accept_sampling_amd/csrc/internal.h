@@ -12,46 +12,68 @@ namespace specv {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-// Elements per work-group chunk of the pass over every row.
-constexpr int kRowChunkElems = 16384;
+// Elements per work-group chunk of the pass over every row (tunable at
+// build time).
+#ifndef SPEC_ROW_CHUNK
+#define SPEC_ROW_CHUNK 65536
+#endif
+constexpr int kRowChunkElems = SPEC_ROW_CHUNK;
+// 16-byte loads in flight per thread in the row pass.
+#ifndef SPEC_ROW_UNROLL
+#define SPEC_ROW_UNROLL 8
+#endif
+constexpr int kRowUnroll = SPEC_ROW_UNROLL;
 // Smallest chunk the workspace is sized for (leaves room to retune).
 constexpr int kRowChunkElemsMin = 2048;
 // Elements per work-group chunk of the float64 residual / bonus pass:
 // 256 threads x 16 consecutive elements.
 constexpr int kSegPerThread = 16;
 constexpr int kResChunkElems = kThreads * kSegPerThread;
+// Chunks of the float64 draw pass handled by one work-group (tunable).
+#ifndef SPEC_DRAW_CHUNKS_PER_GROUP
+#define SPEC_DRAW_CHUNKS_PER_GROUP 4
+#endif
+constexpr int kDrawChunksPerGroup = SPEC_DRAW_CHUNKS_PER_GROUP;
 
 constexpr int kMaxK = 1023;
 constexpr int kMaxNodes = 1024;
 constexpr int kMaxV = 1 << 30;
+constexpr int kMaxB = 65536;
 
-// Per-request state handed from one kernel of a call to the next.
+// Per-request state handed from the row pass to the draw pass.
 struct ReqState {
-  int n;        // accepted length (first rejection or k)
-  int mode;     // kModeResidual or kModeBonus
-  float mp;     // max logit of the target row drawn from (offset for exp)
-  float mq;     // max logit of the draft row (residual mode)
-  double sp;    // float64 normaliser sum exp((z - mp) / T) of the target row
-  double sq;    // float64 normaliser of the draft row
-  double pad[2];
+  int n;         // accepted length (first rejection or k)
+  int mode;      // kModeResidual or kModeBonus
+  float mp;      // max logit of the target row drawn from (offset for exp)
+  float mq;      // max logit of the draft row (residual mode)
+  double rho32;  // S_p / S_q of the rejected rows from the float32 statistics
 };
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
 
-// Counters per request: [0] row pass, [1] normaliser pass, [2] draw pass.
-constexpr int kCountersPerReq = 4;
+// Chunk partial of the float64 draw pass.
+struct DrawPart {
+  double sp;    // sum of e^{(z - mp)/T} (probabilities: sum of p) over the chunk
+  double sq;    // sum of e^{(y - mq)/T} over the chunk (residual mode)
+  double w;     // sum of the draw weights at rho32
+  double dq;    // d w / d rho at rho32: minus the sum of e^{(y-mq)/T} where the weight is positive
+  double flag;  // 1 if an element lies so close to the rho32 kink that the
+                // linear correction to the exact rho may not hold
+  double pad;
+};
 
-// Workspace layout.  The ticket counters sit at a fixed place (the first
-// kMaxB * kCountersPerReq words) whatever the call's shape, so a workspace
-// reused across shapes never reads another call's partial results as a
-// counter; every call leaves the counters it used at zero.
-constexpr int kMaxB = 65536;
+// Completion counters per request: [0] row pass, [1] draw pass.
+constexpr int kCountersPerReq = 2;
 
+// Workspace layout.  The completion counters sit at a fixed place (the
+// first kMaxB * kCountersPerReq words) whatever the call's shape; they must
+// be zero before the first call and every call leaves them at zero.  The
+// other regions are written before they are read within each call.
 struct WsLayout {
   size_t count;  // uint32 [kMaxB * kCountersPerReq], always at offset 0
-  size_t part1;  // float2 [rows * chunks]: (max, sum) or (value, index)
+  size_t part1;  // uint64 [rows * row_chunks]: packed (max, sum) or (value, index)
   size_t state;  // ReqState [B]
-  size_t part2;  // double2 [B * res_chunks]
+  size_t part2;  // DrawPart [B * res_chunks]
   size_t total;
 };
 
@@ -64,7 +86,7 @@ inline int res_chunks(int V) { return (V + kResChunkElems - 1) / kResChunkElems;
 
 inline WsLayout ws_layout(int B, int n_pos, int V) {
   WsLayout L;
-  size_t rows = (size_t)B * (size_t)n_pos * 2;
+  const size_t rows = (size_t)B * (size_t)n_pos * 2;
   size_t off = 0;
   L.count = off;
   off = align_up(off + (size_t)kMaxB * kCountersPerReq * 4, 256);
@@ -73,7 +95,7 @@ inline WsLayout ws_layout(int B, int n_pos, int V) {
   L.state = off;
   off = align_up(off + (size_t)B * sizeof(ReqState), 256);
   L.part2 = off;
-  off = align_up(off + (size_t)B * (size_t)res_chunks(V) * 16, 256);
+  off = align_up(off + (size_t)B * (size_t)res_chunks(V) * sizeof(DrawPart), 256);
   L.total = off;
   return L;
 }
@@ -82,6 +104,15 @@ inline WsLayout ws_layout(int B, int n_pos, int V) {
 struct TreeArgs {
   int16_t parent[kMaxNodes];
 };
+
+// Kernel kinds for the optional event timing (same values as the public
+// SPEC_KERNEL_* constants).
+constexpr int kProfRowPass = 0;   // row statistics / argmax sweep + per-request finish
+constexpr int kProfDraw = 1;      // float64 residual / bonus pass + inverse-CDF draw
+constexpr int kProfUniforms = 2;  // spec_fill_uniforms
+constexpr int kProfKinds = 3;
+void prof_before(int kind, hipStream_t s);
+void prof_after(int kind, hipStream_t s);
 
 // Launch wrappers (defined in the .hip files).  Each returns a hipError_t.
 hipError_t launch_fill_uniforms(uint64_t seed, uint64_t counter0, int64_t n,

@@ -1,0 +1,108 @@
+// Optional per-kernel timing with HIP events.  While enabled, every kernel a
+// spec_* call enqueues is bracketed by two events recorded on the same
+// stream; spec_profile_read synchronises the recorded events and reports, per
+// kernel kind, the launch count and the summed event time.  Disabled (the
+// default), the hooks cost one branch per launch.
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "../../include/spec_verify.h"
+#include "internal.h"
+
+namespace specv {
+namespace {
+
+struct Pair {
+  hipEvent_t a = nullptr, b = nullptr;
+  int kind = -1;
+  bool used = false;
+};
+
+std::mutex g_mu;
+std::atomic<bool> g_on{false};
+std::vector<Pair> g_pairs;
+size_t g_next = 0;
+int g_open = -1;  // index of the pair whose start has been recorded
+double g_ms[kProfKinds] = {0};
+long g_count[kProfKinds] = {0};
+
+// Fold every recorded pair into the totals (synchronising its end event).
+void drain_locked() {
+  for (auto& p : g_pairs) {
+    if (!p.used) continue;
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      g_ms[p.kind] += ms;
+      g_count[p.kind] += 1;
+    }
+    p.used = false;
+  }
+  g_next = 0;
+}
+
+}  // namespace
+
+void prof_before(int kind, hipStream_t s) {
+  if (!g_on) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on) return;
+  if (g_next == g_pairs.size()) drain_locked();
+  Pair& p = g_pairs[g_next];
+  p.kind = kind;
+  if (hipEventRecord(p.a, s) != hipSuccess) return;
+  g_open = static_cast<int>(g_next);
+}
+
+void prof_after(int kind, hipStream_t s) {
+  if (!g_on) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on || g_open < 0 || g_pairs[g_open].kind != kind) return;
+  if (hipEventRecord(g_pairs[g_open].b, s) == hipSuccess) {
+    g_pairs[g_open].used = true;
+    ++g_next;
+  }
+  g_open = -1;
+}
+
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" {
+
+int spec_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (on) {
+    if (g_pairs.empty()) {
+      g_pairs.resize(2048);
+      for (auto& p : g_pairs) {
+        if (hipEventCreate(&p.a) != hipSuccess || hipEventCreate(&p.b) != hipSuccess)
+          return SPEC_EHIP;
+      }
+    }
+    for (int i = 0; i < kProfKinds; ++i) {
+      g_ms[i] = 0.0;
+      g_count[i] = 0;
+    }
+    for (auto& p : g_pairs) p.used = false;
+    g_next = 0;
+    g_open = -1;
+    g_on = true;
+  } else {
+    g_on = false;
+  }
+  return SPEC_OK;
+}
+
+int spec_profile_read(int kind, long* launches, double* total_ms) {
+  if (kind < 0 || kind >= kProfKinds || launches == nullptr || total_ms == nullptr)
+    return SPEC_EINVAL;
+  std::lock_guard<std::mutex> lk(g_mu);
+  drain_locked();
+  *launches = g_count[kind];
+  *total_ms = g_ms[kind];
+  return SPEC_OK;
+}
+
+}  // extern "C"

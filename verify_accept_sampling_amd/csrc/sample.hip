@@ -5,36 +5,52 @@
 // rejection and drawing a bonus token when every draft passes (EAGLE-3
 // review "Speculative Decoding" step 3; serving chapter "how it works").
 //
-// Logits path, three launches on the caller's stream:
+// Logits path, two launches on the caller's stream:
 //   1. k_row_stats: work-group (chunk, row) streams one chunk of one of the
-//      request's 2k+1 rows (k+1 target, k draft) with 16-byte loads and
-//      reduces it to (max, sum 2^((x - max) c)), c = log2(e)/T, in float32.
-//      The request's last work-group merges the chunk partials in float64,
-//      evaluates every acceptance ratio p_i(x_i)/q_i(x_i) from the gathered
-//      logits, finds the first rejection n and writes the accepted prefix.
-//   2. k_res_norm: only for requests that rejected; recomputes the float64
-//      normalisers of target row n and draft row n.
-//   3. k_res_draw: float64 weights of the row drawn from (residual
-//      max(0, p_n - q_n), or p_k for the bonus), one inclusive scan per
-//      chunk, and in the request's last work-group the cross-chunk prefix and
-//      the inverse-CDF search inside the chunk that holds the draw.
-// Probabilities path (rows already normalised): a gather-only acceptance
-// kernel replaces launches 1-2.
+//      request's 2k+1 rows (k+1 target, k draft) with 16-byte non-temporal
+//      loads and reduces it to (max, sum 2^((x - max) c)), c = log2(e)/T, in
+//      float32; it publishes the pair and takes the request's ticket.  The
+//      request's last work-group merges the pairs (float64), evaluates every
+//      acceptance ratio p_i(x_i)/q_i(x_i) from the gathered logits, finds the
+//      first rejection n and writes the accepted prefix and the request state.
+//   2. k_draw: work-group (request, chunk) over the row(s) the final token is
+//      drawn from -- target and draft row n after a rejection, target row k
+//      for the bonus -- in float64: the normaliser partials S_p, S_q and the
+//      draw weights, evaluated at the float32 estimate rho32 of S_p/S_q with
+//      their derivative in rho.  The request's last work-group forms the
+//      float64 rho, moves every chunk total to it (linear in rho unless an
+//      element sits at the kink of max(0, .), in which case the chunk is
+//      recomputed), locates the chunk holding the inverse-CDF point and
+//      searches it with the exact weights.
+// Probabilities path (rows given as distributions): k_draw alone, each
+// work-group first repeating the (gather-only) acceptance tests.
 #include <climits>
 
 #include "device_common.h"
+#include "device_math.h"
 
 namespace specv {
 
-struct MSPart {
-  float m;
-  float s;
-};
+constexpr int kUnrollStats = kRowUnroll;
 
-constexpr int kUnrollStats = 4;
+// An element whose two terms differ by less than this fraction (relative to
+// rho32 e^{(y-mq)/T}) may change sides of max(0, .) between rho32 and the
+// float64 rho; its chunk is then recomputed exactly.  rho32 is within about
+// 1e-6 of rho.
+constexpr double kKinkBand = 1e-5;
+
+// Row r of request b: r <= k is target row r, r > k is draft row r-k-1.
+template <int DT>
+__device__ __forceinline__ const void* stat_row(const void* target, const void* draft, int b,
+                                                int r, int k, int V) {
+  const long eb = Elems<DT>::kBytes;
+  if (r <= k)
+    return reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + r) * V * eb;
+  return reinterpret_cast<const char*>(draft) + ((long)b * k + (r - k - 1)) * V * eb;
+}
 
 // ---------------------------------------------------------------------------
-// 1. Row statistics
+// 1. Row statistics and acceptance
 // ---------------------------------------------------------------------------
 
 template <int NE>
@@ -51,28 +67,34 @@ __device__ __forceinline__ void ms_update(float& m, float& s, const float (&x)[N
   m = mn;
 }
 
-// Row r of request b: r <= k is target row r, r > k is draft row r-k-1.
-template <int DT>
-__device__ __forceinline__ const void* stat_row(const void* target, const void* draft, int b,
-                                                int r, int k, int V) {
-  const long eb = Elems<DT>::kBytes;
-  if (r <= k)
-    return reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + r) * V * eb;
-  return reinterpret_cast<const char*>(draft) + ((long)b * k + (r - k - 1)) * V * eb;
+// Merged maximum and normaliser (float64, relative to that maximum) of one
+// row from its chunk partials, by one thread: each partial is loaded once and
+// folded in with the pairwise (max, sum) rule.
+__device__ __forceinline__ void merge_row_thread(const uint64_t* part, long base_idx, int C1,
+                                                 float c, float& M, double& S) {
+  M = -INFINITY;
+  S = 0.0;
+  for (int cc = 0; cc < C1; ++cc) {
+    const uint64_t pp = ld_dev(&part[base_idx + cc]);
+    const float m2 = unpack_lo(pp);
+    const double s2 = (double)unpack_hi(pp);
+    const float mn = fmaxf(M, m2);
+    const float base = (mn == -INFINITY) ? 0.f : mn;
+    S = S * exp2((double)((M - base) * c)) + s2 * exp2((double)((m2 - base) * c));
+    M = mn;
+  }
 }
 
 template <int DT, int NE>
 __global__ __launch_bounds__(kThreads) void k_row_stats(
     const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C1,
-    float c, double inv_t, const int32_t* __restrict__ draft_tokens,
-    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
-    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probe, MSPart* __restrict__ part, ReqState* __restrict__ state,
-    unsigned* __restrict__ counters) {
+    float c, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
+    uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ out_tokens, float* __restrict__ probe, uint64_t* __restrict__ part,
+    ReqState* __restrict__ state, unsigned* __restrict__ counters) {
   const int R = 2 * k + 1;
-  const int blk = blockIdx.x;
-  const int chunk = blk % C1;
-  const long rowid = blk / C1;
+  const int chunk = blockIdx.x % C1;
+  const long rowid = blockIdx.x / C1;
   const int b = static_cast<int>(rowid / R);
   const int r = static_cast<int>(rowid % R);
   {
@@ -82,131 +104,56 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     const long g0 = (long)chunk * gpc;
     const long g1 = min(g0 + gpc, n_groups);
     float m = -INFINITY, s = 0.f;
-    for (long g = g0 + threadIdx.x; g < g1; g += (long)kThreads * kUnrollStats) {
+    long g = g0 + threadIdx.x;
+    // Main loop: kUnrollStats loads issued back to back, no bounds branch.
+    for (; g + (long)(kUnrollStats - 1) * kThreads < g1; g += (long)kThreads * kUnrollStats) {
       float x[kUnrollStats][NE];
 #pragma unroll
-      for (int u = 0; u < kUnrollStats; ++u) {
-        const long gg = g + (long)u * kThreads;
-        if (gg < g1) {
-          load_group<DT, NE>(rp, gg * NE, x[u]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < NE; ++e) x[u][e] = -INFINITY;
-        }
-      }
+      for (int u = 0; u < kUnrollStats; ++u)
+        load_group<DT, NE, true>(rp, (g + (long)u * kThreads) * NE, x[u]);
 #pragma unroll
       for (int u = 0; u < kUnrollStats; ++u) ms_update<NE>(m, s, x[u], c);
     }
+    for (; g < g1; g += kThreads) {
+      float x[NE];
+      load_group<DT, NE, true>(rp, g * NE, x);
+      ms_update<NE>(m, s, x, c);
+    }
     block_reduce_ms(m, s, c);
-    if (threadIdx.x == 0) part[rowid * C1 + chunk] = MSPart{m, s};
+    if (threadIdx.x == 0) st_dev(&part[rowid * C1 + chunk], pack2(m, s));
   }
-  if (!last_block_ticket(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
+  if (!block_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
 
-  // ---- last work-group of request b: merge, accept scan, emit prefix ----
-  // One wave per draft position: merge the chunk partials of target row i
-  // and draft row i (float64 sums), then test draft token i.
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int first = k;
-  for (int i = wave; i < k; i += kWaves) {
-    float mrow[2];
-    double l2s[2];
-#pragma unroll
-    for (int side = 0; side < 2; ++side) {
-      const long base_idx = ((long)b * R + (side == 0 ? i : k + 1 + i)) * C1;
-      float M = -INFINITY;
-      for (int cc = lane; cc < C1; cc += 64) M = fmaxf(M, part[base_idx + cc].m);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-      const float mb = (M == -INFINITY) ? 0.f : M;
-      double S = 0.0;
-      for (int cc = lane; cc < C1; cc += 64) {
-        const MSPart pp = part[base_idx + cc];
-        S += (double)pp.s * exp2((double)((pp.m - mb) * c));
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) S += shfl_xor_d(S, o);
-      mrow[side] = M;
-      l2s[side] = log2(S);
-    }
-    if (lane == 0) {
-      const int x = draft_tokens[(long)b * k + i];
-      float pv = 0.f, qv = 0.f;
-      bool accept = false;
-      if (x >= 0 && x < V) {
-        const float zp = load_elem<DT>(stat_row<DT>(target, draft, b, i, k, V), x);
-        const float zq = load_elem<DT>(stat_row<DT>(target, draft, b, k + 1 + i, k, V), x);
-        // log2 p_i(x) and log2 q_i(x) from the row statistics
-        const double lp = (double)((zp - mrow[0]) * c) - l2s[0];
-        const double lq = (double)((zq - mrow[1]) * c) - l2s[1];
-        const double ratio = exp2(lp - lq);
-        const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
-        accept = (double)u < ratio;
-        pv = (float)exp2(lp);
-        qv = (float)exp2(lq);
-      }
-      if (!accept) first = min(first, i);
-      if (probe) {
-        float* pr = probe + ((long)b * (k + 1) + i) * 4;
-        pr[0] = pv; pr[1] = qv; pr[2] = 0.f; pr[3] = 0.f;
-      }
-    }
+  // ---- last work-group of request b: acceptance tests ----
+  // Every row of the request is merged by its own thread (one round of
+  // coherent loads) while the logits at the draft tokens are gathered; then
+  // thread i tests draft i.
+  __shared__ float s_m[2 * kMaxK + 1];
+  __shared__ double s_s[2 * kMaxK + 1];
+  for (int rr = threadIdx.x; rr < R; rr += kThreads) {
+    float M;
+    double S;
+    merge_row_thread(part, ((long)b * R + rr) * C1, C1, c, M, S);
+    s_m[rr] = M;
+    s_s[rr] = S;
   }
-  const int n = block_min_i(first);
-  if (probe && threadIdx.x == 0) {
-    float* pr = probe + ((long)b * (k + 1) + k) * 4;
-    pr[0] = 0.f; pr[1] = 0.f; pr[2] = 0.f; pr[3] = 0.f;
-  }
-  for (int i = threadIdx.x; i <= k; i += kThreads) {
-    if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
-    else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
-  }
-  // Maxima of the rows the draw uses: target row n and (rejection) draft row n.
-  if (wave == 0) {
-    float mrow[2] = {0.f, 0.f};
-#pragma unroll
-    for (int side = 0; side < 2; ++side) {
-      if (side == 1 && n == k) break;
-      const long base_idx = ((long)b * R + (side == 0 ? n : k + 1 + n)) * C1;
-      float M = -INFINITY;
-      for (int cc = lane; cc < C1; cc += 64) M = fmaxf(M, part[base_idx + cc].m);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-      mrow[side] = M;
-    }
-    if (lane == 0) {
-      accepted_len[b] = n;
-      ReqState st;
-      st.n = n;
-      st.mode = n < k ? kModeResidual : kModeBonus;
-      st.mp = mrow[0];
-      st.mq = mrow[1];
-      st.sp = 0.0;
-      st.sq = 0.0;
-      st.pad[0] = st.pad[1] = 0.0;
-      state[b] = st;
-    }
-  }
-  (void)inv_t;
-}
-
-// Probabilities path: rows are given distributions; the acceptance test
-// u * q(x) < p(x) is exact in float64 for float32 inputs.
-__global__ __launch_bounds__(kThreads) void k_accept_probs(
-    const float* __restrict__ target, const float* __restrict__ draft, int k, int V,
-    const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms, uint64_t seed,
-    uint64_t ctr0, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probe, ReqState* __restrict__ state) {
-  const int b = blockIdx.x;
+  __syncthreads();
   int first = k;
   for (int i = threadIdx.x; i < k; i += kThreads) {
     const int x = draft_tokens[(long)b * k + i];
     float pv = 0.f, qv = 0.f;
     bool accept = false;
     if (x >= 0 && x < V) {
-      pv = target[((long)b * (k + 1) + i) * V + x];
-      qv = draft[((long)b * k + i) * V + x];
+      const float zp = load_elem<DT>(stat_row<DT>(target, draft, b, i, k, V), x);
+      const float zq = load_elem<DT>(stat_row<DT>(target, draft, b, k + 1 + i, k, V), x);
+      // log2 p_i(x) and log2 q_i(x) from the row statistics
+      const double lp = (double)((zp - s_m[i]) * c) - log2(s_s[i]);
+      const double lq = (double)((zq - s_m[k + 1 + i]) * c) - log2(s_s[k + 1 + i]);
+      const double ratio = exp2(lp - lq);
       const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
-      accept = (double)u * (double)qv < (double)pv;
+      accept = (double)u < ratio;
+      pv = (float)exp2(lp);
+      qv = (float)exp2(lq);
     }
     if (!accept) first = min(first, i);
     if (probe) {
@@ -215,32 +162,79 @@ __global__ __launch_bounds__(kThreads) void k_accept_probs(
     }
   }
   const int n = block_min_i(first);
-  if (probe && threadIdx.x == 0) {
-    float* pr = probe + ((long)b * (k + 1) + k) * 4;
-    pr[0] = 0.f; pr[1] = 0.f; pr[2] = 0.f; pr[3] = 0.f;
-  }
   for (int i = threadIdx.x; i <= k; i += kThreads) {
     if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
     else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
   }
+  // State for the draw: maxima of target row n and (rejection) draft row n,
+  // and the float32-based normaliser ratio of that pair.
   if (threadIdx.x == 0) {
+    const float mp = s_m[n];
+    const float mq = n < k ? s_m[k + 1 + n] : 0.f;
+    const double sq = n < k ? s_s[k + 1 + n] : 1.0;
     accepted_len[b] = n;
-    ReqState st;
-    st.n = n;
-    st.mode = n < k ? kModeResidual : kModeBonus;
-    st.mp = 0.f; st.mq = 0.f; st.sp = 0.0; st.sq = 0.0;
-    st.pad[0] = st.pad[1] = 0.0;
-    state[b] = st;
+    state[b] = ReqState{n, n < k ? kModeResidual : kModeBonus, mp, mq, s_s[n] / sq};
+    if (probe) {
+      float* pr = probe + ((long)b * (k + 1) + k) * 4;
+      pr[0] = 0.f; pr[1] = 0.f; pr[2] = 0.f; pr[3] = 0.f;
+    }
   }
 }
 
+// Acceptance tests on probability rows: u * q(x) < p(x), exact in float64
+// for float32 inputs.  Every thread returns n; with `write` the accepted
+// prefix and the probe values are stored, except probe[b, n, 2], which the
+// request's finishing work-group owns.
+__device__ int accept_scan_probs(const float* target, const float* draft, int b, int k, int V,
+                                 const int32_t* draft_tokens, const float* uniforms,
+                                 uint64_t seed, uint64_t ctr0, bool write,
+                                 int32_t* accepted_len, int32_t* out_tokens, float* probe) {
+  // k <= 1023, so each thread handles at most 4 positions.
+  float pv[4] = {0.f, 0.f, 0.f, 0.f}, qv[4] = {0.f, 0.f, 0.f, 0.f};
+  int first = k;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int i = threadIdx.x + s * kThreads;
+    if (i >= k) break;
+    const int x = draft_tokens[(long)b * k + i];
+    bool accept = false;
+    if (x >= 0 && x < V) {
+      pv[s] = target[((long)b * (k + 1) + i) * V + x];
+      qv[s] = draft[((long)b * k + i) * V + x];
+      const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
+      accept = (double)u * (double)qv[s] < (double)pv[s];
+    }
+    if (!accept) first = min(first, i);
+  }
+  const int n = block_min_i(first);
+  if (write) {
+    if (probe) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int i = threadIdx.x + s * kThreads;
+        if (i > k) break;
+        float* pr = probe + ((long)b * (k + 1) + i) * 4;
+        pr[0] = i < k ? pv[s] : 0.f;
+        pr[1] = i < k ? qv[s] : 0.f;
+        if (i != n) pr[2] = 0.f;
+        pr[3] = 0.f;
+      }
+    }
+    for (int i = threadIdx.x; i <= k; i += kThreads) {
+      if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
+      else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
+    }
+    if (threadIdx.x == 0) accepted_len[b] = n;
+  }
+  return n;
+}
+
 // ---------------------------------------------------------------------------
-// 2. Float64 normalisers of the rejected target / draft rows
+// 2. Float64 draw pass
 // ---------------------------------------------------------------------------
 
-// Load this thread's 16-element segment [j0, j0 + 16) of a row as floats;
-// elements at or beyond V read as -inf (logits) / 0 (probabilities) via
-// `fill`.
+// This thread's 16-element segment [j0, j0 + 16) of a row as floats;
+// elements at or beyond V read as `fill`.
 template <int DT, int NE>
 __device__ __forceinline__ void load_segment(const void* row, long j0, int V, float fill,
                                              float (&x)[kSegPerThread]) {
@@ -259,203 +253,254 @@ __device__ __forceinline__ void load_segment(const void* row, long j0, int V, fl
   }
 }
 
-template <int DT, int NE>
-__global__ __launch_bounds__(kThreads) void k_res_norm(
-    const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C2,
-    double inv_t, ReqState* __restrict__ state, double2* __restrict__ part2,
-    unsigned* __restrict__ counters) {
-  const int b = blockIdx.x / C2;
-  const int chunk = blockIdx.x % C2;
-  const ReqState st = state[b];
-  if (st.mode != kModeResidual) return;  // uniform over the request's work-groups
-  const int n = st.n;
-  const long eb = Elems<DT>::kBytes;
-  const void* prow = reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + n) * V * eb;
-  const void* qrow = reinterpret_cast<const char*>(draft) + ((long)b * k + n) * V * eb;
-  const long j0 = (long)chunk * kResChunkElems + (long)threadIdx.x * kSegPerThread;
-  float zp[kSegPerThread], zq[kSegPerThread];
-  load_segment<DT, NE>(prow, j0, V, -INFINITY, zp);
-  load_segment<DT, NE>(qrow, j0, V, -INFINITY, zq);
-  const double mp = st.mp, mq = st.mq;
-  double sp = 0.0, sq = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSegPerThread; ++e) {
-    sp += exp(((double)zp[e] - mp) * inv_t);
-    sq += exp(((double)zq[e] - mq) * inv_t);
-  }
-  sp = block_sum_d(sp);
-  sq = block_sum_d(sq);
-  if (threadIdx.x == 0) part2[(long)b * C2 + chunk] = make_double2(sp, sq);
-  if (!last_block_ticket(&counters[(long)b * kCountersPerReq + 1], (unsigned)C2)) return;
-  if (threadIdx.x == 0) {
-    double tp = 0.0, tq = 0.0;
-    for (int cc = 0; cc < C2; ++cc) {
-      const double2 v = part2[(long)b * C2 + cc];
-      tp += v.x;
-      tq += v.y;
-    }
-    state[b].sp = tp;
-    state[b].sq = tq;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 3. Float64 residual / bonus weights, scan and inverse-CDF draw
-// ---------------------------------------------------------------------------
-
-enum WeightMode { kWResidual = 0, kWBonusOrP = 1 };
-
-struct ChunkResult {
-  double total;  // chunk total (value of the chunk's last running sum)
-  int token;     // first element whose running sum exceeds thr, or INT_MAX
-};
-
-// Weights of one chunk for this work-group, their running sums, the chunk
-// total, and (search) the first element j with P + running_sum_j > thr.
-// Every chunk total and every searched running sum comes from this one
-// function, so the pass that finds the chunk and the pass that searches it
-// evaluate identical operations.
+// Per-element float64 terms of the draw.  KIND 0 (logits): ea = e^{(z-mp)/T},
+// eb = e^{(y-mq)/T}.  KIND 1 (probabilities): ea = p, eb = q.  `resid`
+// selects whether the draft row is read.
 template <int DT, int NE, int KIND>
-__device__ __attribute__((noinline)) ChunkResult chunk_pass(
-    const void* prow, const void* qrow, int V, int chunk, int wmode, double mp, double mq,
-    double inv_t, double rho, bool search, double P, double thr) {
-  const long j0 = (long)chunk * kResChunkElems + (long)threadIdx.x * kSegPerThread;
+__device__ __forceinline__ void segment_terms(const void* prow, const void* qrow, long j0, int V,
+                                              bool resid, double mp, double mq, double inv_t,
+                                              const double* tab, double (&ea)[kSegPerThread],
+                                              double (&eb)[kSegPerThread]) {
   const float fill = KIND == 0 ? -INFINITY : 0.f;
   float zp[kSegPerThread], zq[kSegPerThread];
   load_segment<DT, NE>(prow, j0, V, fill, zp);
-  if (wmode == kWResidual) load_segment<DT, NE>(qrow, j0, V, fill, zq);
-  double w[kSegPerThread];
+  if (resid) load_segment<DT, NE>(qrow, j0, V, fill, zq);
 #pragma unroll
   for (int e = 0; e < kSegPerThread; ++e) {
-    double we;
     if (KIND == 0) {
-      const double ep = exp(((double)zp[e] - mp) * inv_t);
-      if (wmode == kWResidual) {
-        const double eq = exp(((double)zq[e] - mq) * inv_t);
-        we = fmax(0.0, ep - rho * eq);
-      } else {
-        we = ep;
-      }
+      ea[e] = exp_nonpos(((double)zp[e] - mp) * inv_t, tab);
+      eb[e] = resid ? exp_nonpos(((double)zq[e] - mq) * inv_t, tab) : 0.0;
     } else {
-      we = (wmode == kWResidual) ? fmax(0.0, (double)zp[e] - (double)zq[e]) : (double)zp[e];
+      ea[e] = (double)zp[e];
+      eb[e] = resid ? (double)zq[e] : 0.0;
+    }
+  }
+}
+
+// Search one chunk with the exact weights: w = max(0, ea - rho eb)
+// (residual) or w = ea.  Returns the first element whose running sum, added
+// to the prefix P of the earlier chunks, exceeds thr, falling back to the
+// chunk's last positive-weight element (only reachable through a last-bit
+// difference between the chunk total used to locate it and the sums here).
+template <int DT, int NE, int KIND>
+__device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk, bool resid,
+                            double mp, double mq, double inv_t, double rho, double P, double thr,
+                            const double* tab) {
+  const long j0 = (long)chunk * kResChunkElems + (long)threadIdx.x * kSegPerThread;
+  // Runs once per request on a cold instruction cache: the segment is loaded
+  // up front, then the float64 work is a rolled loop so that its code stays
+  // small.
+  const float fill = KIND == 0 ? -INFINITY : 0.f;
+  float zp[kSegPerThread], zq[kSegPerThread];
+  load_segment<DT, NE>(prow, j0, V, fill, zp);
+  if (resid) load_segment<DT, NE>(qrow, j0, V, fill, zq);
+  double w[kSegPerThread];
+  double tsum = 0.0;
+#pragma unroll 1
+  for (int e = 0; e < kSegPerThread; ++e) {
+    const double a = KIND == 0 ? exp_nonpos(((double)zp[e] - mp) * inv_t, tab) : (double)zp[e];
+    double we = a;
+    if (resid) {
+      const double bq = KIND == 0 ? exp_nonpos(((double)zq[e] - mq) * inv_t, tab) : (double)zq[e];
+      we = fmax(0.0, a - rho * bq);
     }
     w[e] = we;
+    tsum += we;
   }
-  double tsum = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSegPerThread; ++e) tsum += w[e];
   const double excl = block_exclusive_scan_d(tsum);
-  // The chunk total is the running sum at the chunk's last element inside
-  // the row, so the element that made the chunk qualify also qualifies here.
-  const long j_last = min((long)(chunk + 1) * kResChunkElems, (long)V) - 1;
-  __shared__ double s_total;
-  int tok = INT_MAX;
+  int tok = INT_MAX, lastpos = -1;
   double run = 0.0;
 #pragma unroll
   for (int e = 0; e < kSegPerThread; ++e) {
     run += w[e];
-    const double local = excl + run;
-    if (j0 + e == j_last) s_total = local;
-    if (search && tok == INT_MAX && j0 + e <= j_last && P + local > thr)
-      tok = static_cast<int>(j0 + e);
+    if (j0 + e < V) {
+      if (w[e] > 0.0) lastpos = static_cast<int>(j0 + e);
+      if (tok == INT_MAX && P + (excl + run) > thr) tok = static_cast<int>(j0 + e);
+    }
   }
-  __syncthreads();
-  ChunkResult res;
-  res.total = s_total;
-  res.token = search ? block_min_i(tok) : INT_MAX;
-  return res;
+  tok = block_min_i(tok);
+  lastpos = -block_min_i(-lastpos);
+  return tok == INT_MAX ? lastpos : tok;
+}
+
+// Exact chunk total with the float64 rho (for chunks flagged at the kink).
+template <int DT, int NE, int KIND>
+__device__ double chunk_total_exact(const void* prow, const void* qrow, int V, int chunk,
+                                    double mp, double mq, double inv_t, double rho,
+                                    const double* tab) {
+  const long j0 = (long)chunk * kResChunkElems + (long)threadIdx.x * kSegPerThread;
+  double ea[kSegPerThread], eb[kSegPerThread];
+  segment_terms<DT, NE, KIND>(prow, qrow, j0, V, true, mp, mq, inv_t, tab, ea, eb);
+  double t = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSegPerThread; ++e) t += fmax(0.0, ea[e] - rho * eb[e]);
+  return block_sum_d(t);
 }
 
 template <int DT, int NE, int KIND>
-__global__ __launch_bounds__(kThreads) void k_res_draw(
+__global__ __launch_bounds__(kThreads) void k_draw(
     const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C2,
-    double inv_t, const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    double inv_t, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
+    uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, float* __restrict__ probe,
-    const ReqState* __restrict__ state, double2* __restrict__ part2,
+    const ReqState* __restrict__ state, DrawPart* __restrict__ part,
     unsigned* __restrict__ counters) {
-  const int b = blockIdx.x / C2;
-  const int own = blockIdx.x % C2;
-  const ReqState st = state[b];
-  const int n = st.n;
-  const long eb = Elems<DT>::kBytes;
-  const void* prow = reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + n) * V * eb;
-  const void* qrow = st.mode == kModeResidual
-                         ? reinterpret_cast<const char*>(draft) + ((long)b * k + n) * V * eb
-                         : nullptr;
-  const double rho = (KIND == 0 && st.mode == kModeResidual) ? st.sp / st.sq : 0.0;
-  int wmode = st.mode == kModeResidual ? kWResidual : kWBonusOrP;
-  const double2* pc = part2 + (long)b * C2;
-  double2* pw = part2 + (long)b * C2;
+  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  const int b = blockIdx.x / G2;
+  const int chunk = blockIdx.x % G2;  // this work-group's group of chunks
+  __shared__ double tab[32];
+  if (KIND == 0 && threadIdx.x < 32) tab[threadIdx.x] = kExp2Frac32[threadIdx.x];
+  int n;
+  double mp = 0.0, mq = 0.0, rho32 = 1.0;
+  if (KIND == 0) {
+    const ReqState st = state[b];
+    n = st.n;
+    mp = st.mp;
+    mq = st.mq;
+    rho32 = st.rho32;
+  } else {
+    n = accept_scan_probs(static_cast<const float*>(target), static_cast<const float*>(draft), b,
+                          k, V, draft_tokens, uniforms, seed, ctr0, chunk == 0, accepted_len,
+                          out_tokens, probe);
+  }
+  __syncthreads();
+  const bool resid = n < k;
+  const long eb_bytes = Elems<DT>::kBytes;
+  const void* prow =
+      reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + n) * V * eb_bytes;
+  const void* qrow =
+      resid ? reinterpret_cast<const char*>(draft) + ((long)b * k + n) * V * eb_bytes : nullptr;
 
-  // Phases: 0 = own chunk total; 1 = fallback totals (zero residual);
-  // 2 = search.  One call site of chunk_pass serves all of them.
-  int phase = 0;
-  int chunk = own;
-  double P = 0.0, thr = 0.0, mass = 0.0;
-  __shared__ int s_chunk;
-  __shared__ double s_P, s_thr, s_mass;
-  __shared__ int s_phase;
-  for (;;) {
-    const ChunkResult cr = chunk_pass<DT, NE, KIND>(prow, qrow, V, chunk, wmode, st.mp, st.mq,
-                                                    inv_t, rho, phase == 2, P, thr);
-    if (phase == 2) {
-      if (threadIdx.x == 0) {
-        const int t = (cr.token == INT_MAX) ? -1 : cr.token;
-        out_tokens[(long)b * (k + 1) + n] = t;
-        if (probe) probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
-      }
-      return;
-    }
-    if (phase == 0) {
-      if (threadIdx.x == 0) pw[own].x = cr.total;
-      if (!last_block_ticket(&counters[(long)b * kCountersPerReq + 2], (unsigned)C2)) return;
-    } else {
-      if (threadIdx.x == 0) pw[chunk].y = cr.total;
-      __syncthreads();
-      if (chunk + 1 < C2) {
-        ++chunk;
-        continue;
-      }
-    }
-    // Cross-chunk prefix (sequential, float64) and the chunk holding the draw.
-    if (threadIdx.x == 0) {
-      const float u = get_uniform(uniforms, seed, ctr0, b, n, 1, k);
-      double tot = 0.0;
-      for (int cc = 0; cc < C2; ++cc) tot += (phase == 0) ? pc[cc].x : pc[cc].y;
-      int next_phase = 2, cs = C2 - 1;
-      double Pc = 0.0, th = (double)u * tot;
-      if (phase == 0 && !(tot > 0.0)) {
-        next_phase = 1;  // zero residual: draw from p_n instead
-      } else {
-        double run = 0.0;
-        for (int cc = 0; cc < C2; ++cc) {
-          const double wc = (phase == 0) ? pc[cc].x : pc[cc].y;
-          if (run + wc > th) { cs = cc; break; }
-          run += wc;
+  // ---- this work-group's chunks: normaliser partials and draw weights at rho32 ----
+  for (int ci = 0; ci < kDrawChunksPerGroup; ++ci) {
+    const int cc = chunk * kDrawChunksPerGroup + ci;
+    if (cc >= C2) break;  // block-uniform
+    const long j0 = (long)cc * kResChunkElems + (long)threadIdx.x * kSegPerThread;
+    double ea[kSegPerThread], eb[kSegPerThread];
+    segment_terms<DT, NE, KIND>(prow, qrow, j0, V, resid, mp, mq, inv_t, tab, ea, eb);
+    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};  // sp, sq, w, dq, flag
+#pragma unroll
+    for (int e = 0; e < kSegPerThread; ++e) {
+      v[0] += ea[e];
+      v[1] += eb[e];
+      if (resid) {
+        const double d = ea[e] - rho32 * eb[e];
+        if (d > 0.0) {
+          v[2] += d;
+          v[3] -= eb[e];
         }
-        Pc = run;
+        if (KIND == 0 && fabs(d) <= kKinkBand * rho32 * eb[e] && eb[e] > 0.0) v[4] = 1.0;
+      } else {
+        v[2] += ea[e];
       }
-      if (phase == 0) {
-        if (KIND == 0) s_mass = (st.mode == kModeResidual) ? tot / st.sp : 1.0;
-        else s_mass = tot;
+    }
+    block_sum_d5(v);
+    if (threadIdx.x == 0) {
+      DrawPart* p = &part[(long)b * C2 + cc];
+      st_dev_d(&p->sp, v[0]);
+      st_dev_d(&p->sq, v[1]);
+      st_dev_d(&p->w, v[2]);
+      st_dev_d(&p->dq, v[3]);
+      st_dev_d(&p->flag, v[4]);
+    }
+  }
+  if (!block_arrive(&counters[(long)b * kCountersPerReq + 1], (unsigned)G2)) return;
+
+  // ---- last work-group of request b: exact rho, chunk totals, draw ----
+  DrawPart* rp = part + (long)b * C2;
+  __shared__ double s_rho, s_sp;
+  {
+    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int cc = threadIdx.x; cc < C2; cc += kThreads) {
+      v[0] += ld_dev_d(&rp[cc].sp);
+      v[1] += ld_dev_d(&rp[cc].sq);
+    }
+    block_sum_d5(v);
+    if (threadIdx.x == 0) {
+      s_sp = v[0];
+      s_rho = (KIND == 0 && resid) ? v[0] / v[1] : 1.0;
+    }
+  }
+  __syncthreads();
+  const double rho = s_rho, sp_tot = s_sp;
+  // Chunk totals at the exact rho: linear correction, or recomputation for
+  // the (rare) chunks with an element at the kink.  Written back in place.
+  // Chunks are handled 256 at a time, one per thread.
+  if (KIND == 0 && resid) {
+    __shared__ int s_kink[kThreads];
+    for (int base = 0; base < C2; base += kThreads) {
+      const int cc = base + threadIdx.x;
+      int kink = 0;
+      if (cc < C2) {
+        kink = ld_dev_d(&rp[cc].flag) > 0.0;
+        if (!kink) st_dev_d(&rp[cc].w, fmax(0.0, ld_dev_d(&rp[cc].w) + (rho - rho32) * ld_dev_d(&rp[cc].dq)));
       }
-      s_phase = next_phase;
-      s_chunk = cs;
-      s_P = Pc;
-      s_thr = th;
+      s_kink[threadIdx.x] = kink;
+      if (__syncthreads_count(kink) > 0) {
+        for (int j = 0; j < kThreads && base + j < C2; ++j) {
+          if (!s_kink[j]) continue;  // block-uniform
+          const double wt =
+              chunk_total_exact<DT, NE, KIND>(prow, qrow, V, base + j, mp, mq, inv_t, rho, tab);
+          if (threadIdx.x == 0) st_dev_d(&rp[base + j].w, fmax(0.0, wt));
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // Prefix of the chunk totals (residual weights, or the target weights when
+  // the residual is empty) by a tiled work-group scan; the same scan runs
+  // twice, first for the total and then to find the chunk holding u * total.
+  const float u = get_uniform(uniforms, seed, ctr0, b, n, 1, k);
+  int mode = resid ? 0 : 1;  // 0: residual weights, 1: target weights
+  double grand = 0.0;
+  for (int pass = 0; pass < 2; ++pass) {
+    double running = 0.0;
+    for (int base = 0; base < C2; base += kThreads) {
+      const int cc = base + threadIdx.x;
+      const double wc = cc < C2 ? (mode == 0 ? ld_dev_d(&rp[cc].w) : ld_dev_d(&rp[cc].sp)) : 0.0;
+      running += block_sum_d(wc);
+    }
+    grand = running;
+    if (!(grand > 0.0) && mode == 0) mode = 1;  // zero residual: draw from p_n
+    else break;
+  }
+  const double thr = (double)u * grand;
+  __shared__ double s_P;
+  __shared__ int s_cs;
+  if (threadIdx.x == 0) { s_cs = C2 - 1; s_P = 0.0; }
+  {
+    double running = 0.0;
+    int found = 0;
+    for (int base = 0; base < C2 && !found; base += kThreads) {
+      const int cc = base + threadIdx.x;
+      const double wc = cc < C2 ? (mode == 0 ? ld_dev_d(&rp[cc].w) : ld_dev_d(&rp[cc].sp)) : 0.0;
+      const double excl = running + block_exclusive_scan_d(wc);
+      const int hit = (cc < C2 && excl + wc > thr) ? cc : INT_MAX;
+      const int first_hit = block_min_i(hit);
+      if (first_hit != INT_MAX) {
+        if (cc == first_hit) { s_cs = cc; s_P = excl; }
+        found = 1;
+      } else if (cc == C2 - 1) {
+        s_P = excl;  // no hit (last-bit case): search the last chunk from its prefix
+      }
+      running += block_sum_d(wc);
     }
     __syncthreads();
-    if (phase == 0) mass = s_mass;
-    phase = s_phase;
-    if (phase == 1) {
-      wmode = kWBonusOrP;
-      chunk = 0;
-    } else {
-      chunk = s_chunk;
-      P = s_P;
-      thr = s_thr;
+  }
+  const double s_thr = thr, s_grand = grand;
+  const int s_mode = mode;
+  int t = search_chunk<DT, NE, KIND>(prow, qrow, V, s_cs, s_mode == 0, mp, mq, inv_t, rho, s_P,
+                                     s_thr, tab);
+  if (threadIdx.x == 0) {
+    if (!(s_grand > 0.0)) t = -1;  // rows without mass (invalid input)
+    out_tokens[(long)b * (k + 1) + n] = t;
+    if (probe) {
+      // Mass of the distribution drawn from, in probability units.
+      double mass;
+      if (KIND == 0) mass = resid ? (s_mode == 0 ? s_grand / sp_tot : 0.0) : 1.0;
+      else mass = s_mode == 0 ? s_grand : (resid ? 0.0 : s_grand);
+      probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
-    __syncthreads();
   }
 }
 
@@ -480,20 +525,39 @@ static void launch_logits(const void* target, const void* draft, int B, int k, i
   const int C2 = res_chunks(V);
   const float c = 1.4426950408889634f / temperature;
   const double inv_t = 1.0 / (double)temperature;
-  auto* part = reinterpret_cast<MSPart*>(w + L.part1);
+  auto* p1 = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* st = reinterpret_cast<ReqState*>(w + L.state);
-  auto* p2 = reinterpret_cast<double2*>(w + L.part2);
+  auto* p2 = reinterpret_cast<DrawPart*>(w + L.part2);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const long R = 2L * k + 1;
+  prof_before(kProfRowPass, s);
   hipLaunchKernelGGL((k_row_stats<DT, NE>), dim3((unsigned)(B * R * C1)), dim3(kThreads), 0, s,
-                     target, draft, k, V, C1, c, inv_t, draft_tokens, uniforms, seed, ctr0,
-                     accepted_len, out_tokens, probe, part, st, cnt);
-  if (k > 0)
-    hipLaunchKernelGGL((k_res_norm<DT, NE>), dim3((unsigned)(B * C2)), dim3(kThreads), 0, s,
-                       target, draft, k, V, C2, inv_t, st, p2, cnt);
-  hipLaunchKernelGGL((k_res_draw<DT, NE, 0>), dim3((unsigned)(B * C2)), dim3(kThreads), 0, s,
-                     target, draft, k, V, C2, inv_t, uniforms, seed, ctr0, out_tokens, probe,
-                     st, p2, cnt);
+                     target, draft, k, V, C1, c, draft_tokens, uniforms, seed, ctr0,
+                     accepted_len, out_tokens, probe, p1, st, cnt);
+  prof_after(kProfRowPass, s);
+  prof_before(kProfDraw, s);
+  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  hipLaunchKernelGGL((k_draw<DT, NE, 0>), dim3((unsigned)(B * G2)), dim3(kThreads), 0, s, target,
+                     draft, k, V, C2, inv_t, draft_tokens, uniforms, seed, ctr0, accepted_len,
+                     out_tokens, probe, st, p2, cnt);
+  prof_after(kProfDraw, s);
+}
+
+template <int NE>
+static void launch_probs(const void* target, const void* draft, int B, int k, int V,
+                         const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
+                         uint64_t ctr0, int32_t* accepted_len, int32_t* out_tokens,
+                         float* probe, char* w, const WsLayout& L, hipStream_t s) {
+  const int C2 = res_chunks(V);
+  auto* st = reinterpret_cast<ReqState*>(w + L.state);
+  auto* p2 = reinterpret_cast<DrawPart*>(w + L.part2);
+  auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
+  prof_before(kProfDraw, s);
+  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  hipLaunchKernelGGL((k_draw<0, NE, 1>), dim3((unsigned)(B * G2)), dim3(kThreads), 0, s, target,
+                     draft, k, V, C2, 1.0, draft_tokens, uniforms, seed, ctr0, accepted_len,
+                     out_tokens, probe, st, p2, cnt);
+  prof_after(kProfDraw, s);
 }
 
 hipError_t launch_sample(const void* target, const void* draft, int dtype, int kind, int B,
@@ -504,25 +568,13 @@ hipError_t launch_sample(const void* target, const void* draft, int dtype, int k
   char* w = static_cast<char*>(ws);
   const bool vec = rows_aligned(target, V, dtype) && (k == 0 || rows_aligned(draft, V, dtype));
   if (kind == 1) {
-    auto* st = reinterpret_cast<ReqState*>(w + L.state);
-    auto* p2 = reinterpret_cast<double2*>(w + L.part2);
-    auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
-    const int C2 = res_chunks(V);
-    hipLaunchKernelGGL(k_accept_probs, dim3((unsigned)B), dim3(kThreads), 0, s,
-                       static_cast<const float*>(target), static_cast<const float*>(draft), k, V,
-                       draft_tokens, uniforms, seed, counter0, accepted_len, out_tokens, probe,
-                       st);
     if (vec)
-      hipLaunchKernelGGL((k_res_draw<0, 4, 1>), dim3((unsigned)(B * C2)), dim3(kThreads), 0, s,
-                         target, draft, k, V, C2, 1.0, uniforms, seed, counter0, out_tokens,
-                         probe, st, p2, cnt);
+      launch_probs<4>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+                      accepted_len, out_tokens, probe, w, L, s);
     else
-      hipLaunchKernelGGL((k_res_draw<0, 1, 1>), dim3((unsigned)(B * C2)), dim3(kThreads), 0, s,
-                         target, draft, k, V, C2, 1.0, uniforms, seed, counter0, out_tokens,
-                         probe, st, p2, cnt);
-    return hipGetLastError();
-  }
-  if (dtype == 1) {
+      launch_probs<1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+                      accepted_len, out_tokens, probe, w, L, s);
+  } else if (dtype == 1) {
     if (vec)
       launch_logits<1, 8>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
                           temperature, accepted_len, out_tokens, probe, w, L, s);
