@@ -72,19 +72,27 @@ def compare_sample(acc_g, out_g, acc_o, out_o, results, requests):
     return st
 
 
-def check_probe(probe_g, wl, acc_g, acc_o, results, requests):
+def check_probe(probe_g, wl, acc_g, acc_o, results, requests, detail=None):
     """p_i(x_i), q_i(x_i) within PROB_TOL of the oracle's float64 values, and
-    the mass of the drawn-from distribution at the stop position."""
+    the mass of the drawn-from distribution at the stop position.  Returns the
+    largest absolute difference; `detail` (a list) receives where it is."""
     worst = 0.0
+    where = None
     for b in requests:
         pv, qv = O.probe_values(wl.target, wl.draft, wl.draft_tokens, wl.temperature,
                                 wl.kind, wl.dtype, b)
         k = wl.k
-        dp = np.abs(probe_g[b, :k, 0].astype(np.float64) - pv)
-        dq = np.abs(probe_g[b, :k, 1].astype(np.float64) - qv)
-        worst = max(worst, float(dp.max(initial=0.0)), float(dq.max(initial=0.0)))
+        for i in range(k):
+            for f, ref in ((0, pv[i]), (1, qv[i])):
+                d = abs(float(probe_g[b, i, f]) - ref)
+                if d > worst:
+                    worst, where = d, (b, i, f, float(probe_g[b, i, f]), ref)
         n = int(acc_o[b])
         m = results[b].residual_mass
         if math.isfinite(m) and int(acc_g[b]) == n:
-            worst = max(worst, abs(float(probe_g[b, n, 2]) - m))
+            d = abs(float(probe_g[b, n, 2]) - m)
+            if d > worst:
+                worst, where = d, (b, n, 2, float(probe_g[b, n, 2]), m)
+    if detail is not None:
+        detail.append(where)
     return worst

@@ -1,6 +1,6 @@
 """Accuracy of the float64 exponential used by the draw pass (CPU build of
-the same header): Tang's table-driven method against the C library's long
-double expl, over the whole non-positive range it serves."""
+the same header): Tang's table-driven method, 2^(t/64) for t <= 0, against
+the C library's long double exp2l, over the whole range it serves."""
 import os
 import shutil
 import subprocess
@@ -19,32 +19,33 @@ DRIVER = r"""
 #include "device_math.h"
 int main() {
   std::mt19937_64 g(12345);
-  std::uniform_real_distribution<double> wide(-745.0, 0.0), narrow(-40.0, 0.0);
-  double worst = 0.0, worst_x = 0.0;
+  const double tmin = -745.0 * 0x1.71547652b82fep+6;
+  std::uniform_real_distribution<double> wide(tmin, 0.0), narrow(-4000.0, 0.0);
+  double worst = 0.0, worst_t = 0.0;
   long n = 0;
-  auto check = [&](double x) {
-    const double got = specv::exp_nonpos(x, specv::kExp2Frac32);
-    const long double ref = expl((long double)x);
+  auto check = [&](double t) {
+    const double got = specv::exp2_64(t, specv::kExp2Frac64);
+    const long double ref = exp2l((long double)t / 64.0L);
     if (ref < 2.2250738585072014e-308L) {  // subnormal results: absolute bound
       const long double err = fabsl((long double)got - ref) / 4.9406564584124654e-324L;
-      if (err > 2.0) { std::printf("BAD subnormal x=%a got=%a\n", x, got); }
+      if (err > 2.0) { std::printf("BAD subnormal t=%a got=%a\n", t, got); }
       return;
     }
     const long double ulp = (long double)std::nextafter((double)ref, 1e300) - (long double)(double)ref;
     const double e = (double)(fabsl((long double)got - ref) / ulp);
-    if (e > worst) { worst = e; worst_x = x; }
+    if (e > worst) { worst = e; worst_t = t; }
     ++n;
   };
   for (int i = 0; i < 2000000; ++i) check(wide(g));
   for (int i = 0; i < 2000000; ++i) check(narrow(g));
-  for (int i = 0; i < 100000; ++i) check(-std::ldexp((double)i, -20));
-  const double specials[] = {0.0, -0.0, -1e-300, -1e-17, -0.5, -1.0, -700.0, -708.4, -744.0, -745.1};
-  for (double x : specials) check(x);
-  std::printf("checked %ld worst_ulp %.3f at %a\n", n, worst, worst_x);
+  for (int i = 0; i < 100000; ++i) check(-std::ldexp((double)i, -14));
+  const double specials[] = {0.0, -0.0, -1e-300, -1e-17, -0.5, -1.0, -64.0, -65.5, tmin, tmin + 1};
+  for (double t : specials) check(t);
+  std::printf("checked %ld worst_ulp %.3f at %a\n", n, worst, worst_t);
   std::printf("minus_inf %a below_range %a zero %a\n",
-              specv::exp_nonpos(-INFINITY, specv::kExp2Frac32),
-              specv::exp_nonpos(-800.0, specv::kExp2Frac32),
-              specv::exp_nonpos(0.0, specv::kExp2Frac32));
+              specv::exp2_64(-INFINITY, specv::kExp2Frac64),
+              specv::exp2_64(-800.0 * 0x1.71547652b82fep+6, specv::kExp2Frac64),
+              specv::exp2_64(0.0, specv::kExp2Frac64));
   return 0;
 }
 """

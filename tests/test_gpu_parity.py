@@ -161,8 +161,9 @@ def _run_sample(wl, seed=None, counter0=0, requests=None, use_array=True, max_mi
     acc_o, out_o, res = O.verify_sample(wl.target, wl.draft, wl.draft_tokens, u,
                                         wl.temperature, wl.kind, wl.dtype, requests=reqs)
     st = compare_sample(acc_g, out_g, acc_o, out_o, res, reqs)
-    worst = check_probe(pr_g, wl, acc_g, acc_o, res, reqs)
-    _say(f"  {wl.name}: {st} probe_max_abs_err={worst:.3g}")
+    where = []
+    worst = check_probe(pr_g, wl, acc_g, acc_o, res, reqs, where)
+    _say(f"  {wl.name}: {st} probe_max_abs_err={worst:.3g} at (b, i, field, gpu, oracle)={where[0]}")
     assert st["unflagged"] == 0, st["unflagged_requests"]
     assert st["mismatches"] <= max_mismatch, st
     assert worst <= PROB_TOL

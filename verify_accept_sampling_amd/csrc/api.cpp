@@ -112,7 +112,7 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
   if (B == 0) return SPEC_OK;
   if (target == nullptr || accepted_len == nullptr || out_tokens == nullptr) return SPEC_EINVAL;
   if (k > 0 && (draft == nullptr || draft_tokens == nullptr)) return SPEC_EINVAL;
-  const long C2 = (V + kResChunkElems - 1) / kResChunkElems;
+  const long C2 = (V + kDrawChunk - 1) / kDrawChunk;
   if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V)) != SPEC_OK) return SPEC_EINVAL;
   if (check_grid((long)B * C2) != SPEC_OK) return SPEC_EINVAL;
   WsLayout L;

@@ -129,22 +129,42 @@ __device__ __forceinline__ double shfl_up_d(double v, int d) { return __shfl_up(
 // (max, sum of exp2((x - max) * c)) pairs: the streaming softmax statistic
 // ---------------------------------------------------------------------------
 
-// Combine two (m, s) pairs, s measured relative to m in base-2 units scaled
-// by c.  -inf maxima (no finite element yet) carry s = 0.
-__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2, float c) {
+// Float32 product rounded on its own.  The compiler's default contraction
+// would fuse a plain `a * b` into a following add (and HIP's __fmul_rn is a
+// plain multiply), giving fma(a, b, z): then fl(m c) - fl(m c) is no longer
+// exactly 0 but the rounding error of m c, and merges that should leave a
+// sum untouched scale it by 2^(that error) at every reduction level.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
+// Combine two (m, s) pairs, each s (float64) relative to 2^fl32(m c).
+// -inf maxima (no finite element yet) carry s = 0.
+__device__ __forceinline__ void ms_merge(float& m, double& s, float m2, double s2, float c) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  // Each s is relative to exactly the rounded product fl32(m c); the side
+  // that holds the new maximum keeps a factor of exactly 1.
   const float mn = fmaxf(m, m2);
-  const float base = (mn == -INFINITY) ? 0.f : mn;
-  s = s * __builtin_amdgcn_exp2f((m - base) * c) + s2 * __builtin_amdgcn_exp2f((m2 - base) * c);
+  const float mcn = mul_rn(mn, c);
+  s = s * (double)__builtin_amdgcn_exp2f(mul_rn(m, c) - mcn) +
+      s2 * (double)__builtin_amdgcn_exp2f(mul_rn(m2, c) - mcn);
   m = mn;
 }
 
 // Work-group reduction of (m, s); result valid in thread 0.
-__device__ __forceinline__ void block_reduce_ms(float& m, float& s, float c) {
-  __shared__ float sm[kWaves], ss[kWaves];
+__device__ __forceinline__ void block_reduce_ms(float& m, double& s, float c) {
+  __shared__ float sm[kWaves];
+  __shared__ double ss[kWaves];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float m2 = shfl_xor_f(m, o);
-    const float s2 = shfl_xor_f(s, o);
+    const double s2 = shfl_xor_d(s, o);
     ms_merge(m, s, m2, s2, c);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -25,15 +25,19 @@ constexpr int kRowChunkElems = SPEC_ROW_CHUNK;
 constexpr int kRowUnroll = SPEC_ROW_UNROLL;
 // Smallest chunk the workspace is sized for (leaves room to retune).
 constexpr int kRowChunkElemsMin = 2048;
-// Elements per work-group chunk of the float64 residual / bonus pass:
-// 256 threads x 16 consecutive elements.
+// Float64 residual / bonus pass: the row is cut into chunks of
+// kDrawChunk elements, one wave per chunk (64 lanes x 16 consecutive
+// elements); a work-group of kThreads/64 waves handles kDrawChunksPerWave
+// consecutive chunks per wave.
 constexpr int kSegPerThread = 16;
-constexpr int kResChunkElems = kThreads * kSegPerThread;
-// Chunks of the float64 draw pass handled by one work-group (tunable).
-#ifndef SPEC_DRAW_CHUNKS_PER_GROUP
-#define SPEC_DRAW_CHUNKS_PER_GROUP 4
+constexpr int kDrawChunk = 64 * kSegPerThread;
+#ifndef SPEC_DRAW_CHUNKS_PER_WAVE
+#define SPEC_DRAW_CHUNKS_PER_WAVE 2
 #endif
-constexpr int kDrawChunksPerGroup = SPEC_DRAW_CHUNKS_PER_GROUP;
+constexpr int kDrawChunksPerWave = SPEC_DRAW_CHUNKS_PER_WAVE;
+constexpr int kDrawChunksPerGroup = kWaves * kDrawChunksPerWave;
+// Elements per thread when a whole work-group searches one chunk.
+constexpr int kSearchPerThread = kDrawChunk / kThreads;
 
 constexpr int kMaxK = 1023;
 constexpr int kMaxNodes = 1024;
@@ -82,7 +86,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int row_chunks_max(int V) {
   return (V + kRowChunkElemsMin - 1) / kRowChunkElemsMin;
 }
-inline int res_chunks(int V) { return (V + kResChunkElems - 1) / kResChunkElems; }
+inline int res_chunks(int V) { return (V + kDrawChunk - 1) / kDrawChunk; }
 
 inline WsLayout ws_layout(int B, int n_pos, int V) {
   WsLayout L;

@@ -53,23 +53,34 @@ __device__ __forceinline__ const void* stat_row(const void* target, const void* 
 // 1. Row statistics and acceptance
 // ---------------------------------------------------------------------------
 
+// Streaming softmax statistic of a chunk: running maximum m and
+// s = sum 2^(x c - mc) with mc = fl32(m c), the rounded product (each
+// element costs one fused multiply-add; merges recompute mc from m, so its
+// rounding cancels exactly).  Each group of NE terms is added in float32
+// and the group sums in float64: a float32 running sum near 1 would absorb
+// the many terms far below its last bit.
 template <int NE>
-__device__ __forceinline__ void ms_update(float& m, float& s, const float (&x)[NE], float c) {
+__device__ __forceinline__ void ms_update(float& m, float& mc, double& s, const float (&x)[NE],
+                                          float c) {
   float lm = x[0];
 #pragma unroll
   for (int e = 1; e < NE; ++e) lm = fmaxf(lm, x[e]);
-  const float mn = fmaxf(m, lm);
-  const float base = (mn == -INFINITY) ? 0.f : mn;
-  float acc = s * __builtin_amdgcn_exp2f((m - base) * c);
+  if (lm > m) {  // rare after the first groups
+    const float mcn = mul_rn(lm, c);
+    s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f(mc - mcn);
+    m = lm;
+    mc = mcn;
+  }
+  if (m == -INFINITY) return;  // only -inf so far
+  float g = 0.f;
 #pragma unroll
-  for (int e = 0; e < NE; ++e) acc += __builtin_amdgcn_exp2f((x[e] - base) * c);
-  s = acc;
-  m = mn;
+  for (int e = 0; e < NE; ++e) g += __builtin_amdgcn_exp2f(fmaf(x[e], c, -mc));
+  s += (double)g;
 }
 
-// Merged maximum and normaliser (float64, relative to that maximum) of one
-// row from its chunk partials, by one thread: each partial is loaded once and
-// folded in with the pairwise (max, sum) rule.
+// Merged maximum M and normaliser S = sum 2^(x c - fl32(M c)) (float64) of
+// one row from its chunk partials, by one thread: each partial is loaded
+// once and folded in.
 __device__ __forceinline__ void merge_row_thread(const uint64_t* part, long base_idx, int C1,
                                                  float c, float& M, double& S) {
   M = -INFINITY;
@@ -78,9 +89,15 @@ __device__ __forceinline__ void merge_row_thread(const uint64_t* part, long base
     const uint64_t pp = ld_dev(&part[base_idx + cc]);
     const float m2 = unpack_lo(pp);
     const double s2 = (double)unpack_hi(pp);
+    if (m2 == -INFINITY) continue;
+    if (M == -INFINITY) {
+      M = m2;
+      S = s2;
+      continue;
+    }
     const float mn = fmaxf(M, m2);
-    const float base = (mn == -INFINITY) ? 0.f : mn;
-    S = S * exp2((double)((M - base) * c)) + s2 * exp2((double)((m2 - base) * c));
+    const double mcn = (double)mul_rn(mn, c);
+    S = S * exp2((double)mul_rn(M, c) - mcn) + s2 * exp2((double)mul_rn(m2, c) - mcn);
     M = mn;
   }
 }
@@ -103,7 +120,8 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     const long gpc = (n_groups + C1 - 1) / C1;
     const long g0 = (long)chunk * gpc;
     const long g1 = min(g0 + gpc, n_groups);
-    float m = -INFINITY, s = 0.f;
+    float m = -INFINITY, mc = -INFINITY;
+    double s = 0.0;
     long g = g0 + threadIdx.x;
     // Main loop: kUnrollStats loads issued back to back, no bounds branch.
     for (; g + (long)(kUnrollStats - 1) * kThreads < g1; g += (long)kThreads * kUnrollStats) {
@@ -112,15 +130,15 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
       for (int u = 0; u < kUnrollStats; ++u)
         load_group<DT, NE, true>(rp, (g + (long)u * kThreads) * NE, x[u]);
 #pragma unroll
-      for (int u = 0; u < kUnrollStats; ++u) ms_update<NE>(m, s, x[u], c);
+      for (int u = 0; u < kUnrollStats; ++u) ms_update<NE>(m, mc, s, x[u], c);
     }
     for (; g < g1; g += kThreads) {
       float x[NE];
       load_group<DT, NE, true>(rp, g * NE, x);
-      ms_update<NE>(m, s, x, c);
+      ms_update<NE>(m, mc, s, x, c);
     }
     block_reduce_ms(m, s, c);
-    if (threadIdx.x == 0) st_dev(&part[rowid * C1 + chunk], pack2(m, s));
+    if (threadIdx.x == 0) st_dev(&part[rowid * C1 + chunk], pack2(m, (float)s));
   }
   if (!block_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
 
@@ -147,8 +165,9 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
       const float zp = load_elem<DT>(stat_row<DT>(target, draft, b, i, k, V), x);
       const float zq = load_elem<DT>(stat_row<DT>(target, draft, b, k + 1 + i, k, V), x);
       // log2 p_i(x) and log2 q_i(x) from the row statistics
-      const double lp = (double)((zp - s_m[i]) * c) - log2(s_s[i]);
-      const double lq = (double)((zq - s_m[k + 1 + i]) * c) - log2(s_s[k + 1 + i]);
+      const double lp = ((double)zp * c - (double)mul_rn(s_m[i], c)) - log2(s_s[i]);
+      const double lq =
+          ((double)zq * c - (double)mul_rn(s_m[k + 1 + i], c)) - log2(s_s[k + 1 + i]);
       const double ratio = exp2(lp - lq);
       const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
       accept = (double)u < ratio;
@@ -171,9 +190,12 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
   if (threadIdx.x == 0) {
     const float mp = s_m[n];
     const float mq = n < k ? s_m[k + 1 + n] : 0.f;
-    const double sq = n < k ? s_s[k + 1 + n] : 1.0;
+    // S relative to 2^(m c) instead of 2^fl32(m c): ratio of the pair.
+    const double sp = s_s[n] * exp2((double)mul_rn(mp, c) - (double)mp * c);
+    const double sq =
+        n < k ? s_s[k + 1 + n] * exp2((double)mul_rn(mq, c) - (double)mq * c) : 1.0;
     accepted_len[b] = n;
-    state[b] = ReqState{n, n < k ? kModeResidual : kModeBonus, mp, mq, s_s[n] / sq};
+    state[b] = ReqState{n, n < k ? kModeResidual : kModeBonus, mp, mq, sp / sq};
     if (probe) {
       float* pr = probe + ((long)b * (k + 1) + k) * 4;
       pr[0] = 0.f; pr[1] = 0.f; pr[2] = 0.f; pr[3] = 0.f;
@@ -233,13 +255,14 @@ __device__ int accept_scan_probs(const float* target, const float* draft, int b,
 // 2. Float64 draw pass
 // ---------------------------------------------------------------------------
 
-// This thread's 16-element segment [j0, j0 + 16) of a row as floats;
-// elements at or beyond V read as `fill`.
-template <int DT, int NE>
-__device__ __forceinline__ void load_segment(const void* row, long j0, int V, float fill,
-                                             float (&x)[kSegPerThread]) {
+// NN consecutive elements from j0 as floats (NN a multiple of NE); elements
+// at or beyond V read as `fill`.
+template <int DT, int NE, int NN>
+__device__ __forceinline__ void load_run(const void* row, long j0, int V, float fill,
+                                         float (&x)[NN]) {
+  static_assert(NN % NE == 0, "run length must be a multiple of the load width");
 #pragma unroll
-  for (int g = 0; g < kSegPerThread / NE; ++g) {
+  for (int g = 0; g < NN / NE; ++g) {
     const long e0 = j0 + (long)g * NE;
     float t[NE];
     if (e0 + NE <= V) {
@@ -253,65 +276,115 @@ __device__ __forceinline__ void load_segment(const void* row, long j0, int V, fl
   }
 }
 
-// Per-element float64 terms of the draw.  KIND 0 (logits): ea = e^{(z-mp)/T},
-// eb = e^{(y-mq)/T}.  KIND 1 (probabilities): ea = p, eb = q.  `resid`
-// selects whether the draft row is read.
+// Float64 term of one element.  KIND 0 (logits): e^{(z - m)/T}, evaluated as
+// 2^(t/64) with t = z c1 + c0, c1 = 64/(T ln 2), c0 = -m c1; KIND 1
+// (probabilities): the value itself.
+template <int KIND>
+__device__ __forceinline__ double draw_term(float z, double c1, double c0, const double* tab) {
+  return KIND == 0 ? exp2_64(fma((double)z, c1, c0), tab) : (double)z;
+}
+
+// Sums of one chunk by one wave (lane l covers the 16 elements from
+// chunk * kDrawChunk + 16 l), reduced across the wave (valid in every lane):
+//   v[0] = sum a, v[1] = sum b (a, b the target and draft terms),
+//   v[2] = sum of the draw weights at rho32 (max(0, a - rho32 b), or a for
+//          the bonus), v[3] = their derivative in rho (minus the sum of b
+//          where the weight is positive), v[4] = 1 if an element lies within
+//          the kink band of max(0, .).
 template <int DT, int NE, int KIND>
-__device__ __forceinline__ void segment_terms(const void* prow, const void* qrow, long j0, int V,
-                                              bool resid, double mp, double mq, double inv_t,
-                                              const double* tab, double (&ea)[kSegPerThread],
-                                              double (&eb)[kSegPerThread]) {
+__device__ __forceinline__ void wave_chunk_sums(const void* prow, const void* qrow, int V,
+                                                int chunk, bool resid, double c1, double c0p,
+                                                double c0q, double rho32, const double* tab,
+                                                double (&v)[5]) {
+  const int lane = threadIdx.x & 63;
+  const long j0 = (long)chunk * kDrawChunk + (long)lane * kSegPerThread;
   const float fill = KIND == 0 ? -INFINITY : 0.f;
   float zp[kSegPerThread], zq[kSegPerThread];
-  load_segment<DT, NE>(prow, j0, V, fill, zp);
-  if (resid) load_segment<DT, NE>(qrow, j0, V, fill, zq);
+  load_run<DT, NE, kSegPerThread>(prow, j0, V, fill, zp);
+  if (resid) load_run<DT, NE, kSegPerThread>(qrow, j0, V, fill, zq);
+#pragma unroll
+  for (int q = 0; q < 5; ++q) v[q] = 0.0;
 #pragma unroll
   for (int e = 0; e < kSegPerThread; ++e) {
-    if (KIND == 0) {
-      ea[e] = exp_nonpos(((double)zp[e] - mp) * inv_t, tab);
-      eb[e] = resid ? exp_nonpos(((double)zq[e] - mq) * inv_t, tab) : 0.0;
+    const double a = draw_term<KIND>(zp[e], c1, c0p, tab);
+    v[0] += a;
+    if (resid) {
+      const double bq = draw_term<KIND>(zq[e], c1, c0q, tab);
+      v[1] += bq;
+      const double d = a - rho32 * bq;
+      if (d > 0.0) {
+        v[2] += d;
+        v[3] -= bq;
+      }
+      if (KIND == 0 && bq > 0.0 && fabs(d) <= kKinkBand * rho32 * bq) v[4] = 1.0;
     } else {
-      ea[e] = (double)zp[e];
-      eb[e] = resid ? (double)zq[e] : 0.0;
+      v[2] += a;
     }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int q = 0; q < 5; ++q) v[q] += shfl_xor_d(v[q], o);
   }
 }
 
-// Search one chunk with the exact weights: w = max(0, ea - rho eb)
-// (residual) or w = ea.  Returns the first element whose running sum, added
-// to the prefix P of the earlier chunks, exceeds thr, falling back to the
-// chunk's last positive-weight element (only reachable through a last-bit
-// difference between the chunk total used to locate it and the sums here).
-template <int DT, int NE, int KIND>
-__device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk, bool resid,
-                            double mp, double mq, double inv_t, double rho, double P, double thr,
-                            const double* tab) {
-  const long j0 = (long)chunk * kResChunkElems + (long)threadIdx.x * kSegPerThread;
-  // Runs once per request on a cold instruction cache: the segment is loaded
-  // up front, then the float64 work is a rolled loop so that its code stays
-  // small.
+// kSearchPerThread consecutive elements of a chunk for this thread of a
+// whole work-group: [chunk * kDrawChunk + kSearchPerThread t, ...).
+template <int DT, int KIND>
+__device__ __forceinline__ void search_terms(const void* prow, const void* qrow, int V, int chunk,
+                                             bool resid, double c1, double c0p, double c0q,
+                                             double rho, const double* tab,
+                                             double (&w)[kSearchPerThread], long& j0) {
+  j0 = (long)chunk * kDrawChunk + (long)threadIdx.x * kSearchPerThread;
   const float fill = KIND == 0 ? -INFINITY : 0.f;
-  float zp[kSegPerThread], zq[kSegPerThread];
-  load_segment<DT, NE>(prow, j0, V, fill, zp);
-  if (resid) load_segment<DT, NE>(qrow, j0, V, fill, zq);
-  double w[kSegPerThread];
-  double tsum = 0.0;
-#pragma unroll 1
-  for (int e = 0; e < kSegPerThread; ++e) {
-    const double a = KIND == 0 ? exp_nonpos(((double)zp[e] - mp) * inv_t, tab) : (double)zp[e];
-    double we = a;
-    if (resid) {
-      const double bq = KIND == 0 ? exp_nonpos(((double)zq[e] - mq) * inv_t, tab) : (double)zq[e];
-      we = fmax(0.0, a - rho * bq);
-    }
-    w[e] = we;
-    tsum += we;
+  float zp[kSearchPerThread], zq[kSearchPerThread];
+#pragma unroll
+  for (int e = 0; e < kSearchPerThread; ++e) {
+    zp[e] = (j0 + e < V) ? load_elem<DT>(prow, j0 + e) : fill;
+    zq[e] = (resid && j0 + e < V) ? load_elem<DT>(qrow, j0 + e) : fill;
   }
+  // Runs once per request on a cold instruction cache: rolled.
+#pragma unroll 1
+  for (int e = 0; e < kSearchPerThread; ++e) {
+    const double a = draw_term<KIND>(zp[e], c1, c0p, tab);
+    w[e] = resid ? fmax(0.0, a - rho * draw_term<KIND>(zq[e], c1, c0q, tab)) : a;
+  }
+}
+
+// Exact chunk total with the float64 rho (for chunks flagged at the kink).
+template <int DT, int KIND>
+__device__ double chunk_total_exact(const void* prow, const void* qrow, int V, int chunk,
+                                    double c1, double c0p, double c0q, double rho,
+                                    const double* tab) {
+  double w[kSearchPerThread];
+  long j0;
+  search_terms<DT, KIND>(prow, qrow, V, chunk, true, c1, c0p, c0q, rho, tab, w, j0);
+  double t = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSearchPerThread; ++e) t += w[e];
+  return block_sum_d(t);
+}
+
+// Search one chunk with the exact weights.  Returns the first element whose
+// running sum, added to the prefix P of the earlier chunks, exceeds thr,
+// falling back to the chunk's last positive-weight element (reachable only
+// through a last-bit difference between the chunk total used to locate it
+// and the sums here).
+template <int DT, int KIND>
+__device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk, bool resid,
+                            double c1, double c0p, double c0q, double rho, double P, double thr,
+                            const double* tab) {
+  double w[kSearchPerThread];
+  long j0;
+  search_terms<DT, KIND>(prow, qrow, V, chunk, resid, c1, c0p, c0q, rho, tab, w, j0);
+  double tsum = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSearchPerThread; ++e) tsum += w[e];
   const double excl = block_exclusive_scan_d(tsum);
   int tok = INT_MAX, lastpos = -1;
   double run = 0.0;
 #pragma unroll
-  for (int e = 0; e < kSegPerThread; ++e) {
+  for (int e = 0; e < kSearchPerThread; ++e) {
     run += w[e];
     if (j0 + e < V) {
       if (w[e] > 0.0) lastpos = static_cast<int>(j0 + e);
@@ -323,18 +396,11 @@ __device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk
   return tok == INT_MAX ? lastpos : tok;
 }
 
-// Exact chunk total with the float64 rho (for chunks flagged at the kink).
-template <int DT, int NE, int KIND>
-__device__ double chunk_total_exact(const void* prow, const void* qrow, int V, int chunk,
-                                    double mp, double mq, double inv_t, double rho,
-                                    const double* tab) {
-  const long j0 = (long)chunk * kResChunkElems + (long)threadIdx.x * kSegPerThread;
-  double ea[kSegPerThread], eb[kSegPerThread];
-  segment_terms<DT, NE, KIND>(prow, qrow, j0, V, true, mp, mq, inv_t, tab, ea, eb);
-  double t = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSegPerThread; ++e) t += fmax(0.0, ea[e] - rho * eb[e]);
-  return block_sum_d(t);
+// Wait until this wave's earlier stores have completed.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <int DT, int NE, int KIND>
@@ -347,9 +413,9 @@ __global__ __launch_bounds__(kThreads) void k_draw(
     unsigned* __restrict__ counters) {
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
   const int b = blockIdx.x / G2;
-  const int chunk = blockIdx.x % G2;  // this work-group's group of chunks
-  __shared__ double tab[32];
-  if (KIND == 0 && threadIdx.x < 32) tab[threadIdx.x] = kExp2Frac32[threadIdx.x];
+  const int grp = blockIdx.x % G2;
+  __shared__ double tab[64];
+  if (KIND == 0 && threadIdx.x < 64) tab[threadIdx.x] = kExp2Frac64[threadIdx.x];
   int n;
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
@@ -360,42 +426,26 @@ __global__ __launch_bounds__(kThreads) void k_draw(
     rho32 = st.rho32;
   } else {
     n = accept_scan_probs(static_cast<const float*>(target), static_cast<const float*>(draft), b,
-                          k, V, draft_tokens, uniforms, seed, ctr0, chunk == 0, accepted_len,
+                          k, V, draft_tokens, uniforms, seed, ctr0, grp == 0, accepted_len,
                           out_tokens, probe);
   }
   __syncthreads();
   const bool resid = n < k;
+  const double c1 = inv_t * kInvLn2x64, c0p = -mp * c1, c0q = -mq * c1;
   const long eb_bytes = Elems<DT>::kBytes;
   const void* prow =
       reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + n) * V * eb_bytes;
   const void* qrow =
       resid ? reinterpret_cast<const char*>(draft) + ((long)b * k + n) * V * eb_bytes : nullptr;
 
-  // ---- this work-group's chunks: normaliser partials and draw weights at rho32 ----
-  for (int ci = 0; ci < kDrawChunksPerGroup; ++ci) {
-    const int cc = chunk * kDrawChunksPerGroup + ci;
-    if (cc >= C2) break;  // block-uniform
-    const long j0 = (long)cc * kResChunkElems + (long)threadIdx.x * kSegPerThread;
-    double ea[kSegPerThread], eb[kSegPerThread];
-    segment_terms<DT, NE, KIND>(prow, qrow, j0, V, resid, mp, mq, inv_t, tab, ea, eb);
-    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};  // sp, sq, w, dq, flag
-#pragma unroll
-    for (int e = 0; e < kSegPerThread; ++e) {
-      v[0] += ea[e];
-      v[1] += eb[e];
-      if (resid) {
-        const double d = ea[e] - rho32 * eb[e];
-        if (d > 0.0) {
-          v[2] += d;
-          v[3] -= eb[e];
-        }
-        if (KIND == 0 && fabs(d) <= kKinkBand * rho32 * eb[e] && eb[e] > 0.0) v[4] = 1.0;
-      } else {
-        v[2] += ea[e];
-      }
-    }
-    block_sum_d5(v);
-    if (threadIdx.x == 0) {
+  // ---- this work-group's chunks, one wave per chunk ----
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = 0; i < kDrawChunksPerWave; ++i) {
+    const int cc = grp * kDrawChunksPerGroup + wave * kDrawChunksPerWave + i;
+    if (cc >= C2) break;  // wave-uniform
+    double v[5];
+    wave_chunk_sums<DT, NE, KIND>(prow, qrow, V, cc, resid, c1, c0p, c0q, rho32, tab, v);
+    if (lane == 0) {
       DrawPart* p = &part[(long)b * C2 + cc];
       st_dev_d(&p->sp, v[0]);
       st_dev_d(&p->sq, v[1]);
@@ -404,6 +454,8 @@ __global__ __launch_bounds__(kThreads) void k_draw(
       st_dev_d(&p->flag, v[4]);
     }
   }
+  wait_stores();  // every wave's partials complete before the ticket below
+  __syncthreads();
   if (!block_arrive(&counters[(long)b * kCountersPerReq + 1], (unsigned)G2)) return;
 
   // ---- last work-group of request b: exact rho, chunk totals, draw ----
@@ -424,8 +476,8 @@ __global__ __launch_bounds__(kThreads) void k_draw(
   __syncthreads();
   const double rho = s_rho, sp_tot = s_sp;
   // Chunk totals at the exact rho: linear correction, or recomputation for
-  // the (rare) chunks with an element at the kink.  Written back in place.
-  // Chunks are handled 256 at a time, one per thread.
+  // the (rare) chunks with an element at the kink.  Written back in place,
+  // one chunk per thread.
   if (KIND == 0 && resid) {
     __shared__ int s_kink[kThreads];
     for (int base = 0; base < C2; base += kThreads) {
@@ -433,25 +485,27 @@ __global__ __launch_bounds__(kThreads) void k_draw(
       int kink = 0;
       if (cc < C2) {
         kink = ld_dev_d(&rp[cc].flag) > 0.0;
-        if (!kink) st_dev_d(&rp[cc].w, fmax(0.0, ld_dev_d(&rp[cc].w) + (rho - rho32) * ld_dev_d(&rp[cc].dq)));
+        if (!kink)
+          st_dev_d(&rp[cc].w,
+                   fmax(0.0, ld_dev_d(&rp[cc].w) + (rho - rho32) * ld_dev_d(&rp[cc].dq)));
       }
       s_kink[threadIdx.x] = kink;
       if (__syncthreads_count(kink) > 0) {
         for (int j = 0; j < kThreads && base + j < C2; ++j) {
           if (!s_kink[j]) continue;  // block-uniform
           const double wt =
-              chunk_total_exact<DT, NE, KIND>(prow, qrow, V, base + j, mp, mq, inv_t, rho, tab);
+              chunk_total_exact<DT, KIND>(prow, qrow, V, base + j, c1, c0p, c0q, rho, tab);
           if (threadIdx.x == 0) st_dev_d(&rp[base + j].w, fmax(0.0, wt));
         }
       }
       __syncthreads();
     }
   }
-  // Prefix of the chunk totals (residual weights, or the target weights when
-  // the residual is empty) by a tiled work-group scan; the same scan runs
-  // twice, first for the total and then to find the chunk holding u * total.
+  // Prefix of the chunk totals (residual weights, or the target terms when
+  // the residual is empty) by a tiled work-group scan: first the total, then
+  // the chunk holding u * total.
   const float u = get_uniform(uniforms, seed, ctr0, b, n, 1, k);
-  int mode = resid ? 0 : 1;  // 0: residual weights, 1: target weights
+  int mode = resid ? 0 : 1;  // 0: residual weights, 1: target terms
   double grand = 0.0;
   for (int pass = 0; pass < 2; ++pass) {
     double running = 0.0;
@@ -487,18 +541,16 @@ __global__ __launch_bounds__(kThreads) void k_draw(
     }
     __syncthreads();
   }
-  const double s_thr = thr, s_grand = grand;
-  const int s_mode = mode;
-  int t = search_chunk<DT, NE, KIND>(prow, qrow, V, s_cs, s_mode == 0, mp, mq, inv_t, rho, s_P,
-                                     s_thr, tab);
+  int t = search_chunk<DT, KIND>(prow, qrow, V, s_cs, mode == 0, c1, c0p, c0q, rho, s_P, thr,
+                                 tab);
   if (threadIdx.x == 0) {
-    if (!(s_grand > 0.0)) t = -1;  // rows without mass (invalid input)
+    if (!(grand > 0.0)) t = -1;  // rows without mass (invalid input)
     out_tokens[(long)b * (k + 1) + n] = t;
     if (probe) {
       // Mass of the distribution drawn from, in probability units.
       double mass;
-      if (KIND == 0) mass = resid ? (s_mode == 0 ? s_grand / sp_tot : 0.0) : 1.0;
-      else mass = s_mode == 0 ? s_grand : (resid ? 0.0 : s_grand);
+      if (KIND == 0) mass = resid ? (mode == 0 ? grand / sp_tot : 0.0) : 1.0;
+      else mass = mode == 0 ? grand : (resid ? 0.0 : grand);
       probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
   }
