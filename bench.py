@@ -33,6 +33,9 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0
 METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B=64 k=8 V=128256"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_b64_k8_v128256_traffic.json")
+# Algorithmic bytes of one row-statistics launch at this workload: every
+# logit of the 2k+1 = 17 rows of all 64 requests read once (bf16).
+ALGO_ROW_BYTES = 64 * 17 * 128256 * 2
 KERNEL_SOURCES = ["verify_accept_sampling_amd/csrc/sample.hip",
                   "verify_accept_sampling_amd/csrc/device_common.h",
                   "verify_accept_sampling_amd/csrc/internal.h"]
@@ -46,7 +49,7 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bytes_per_launch: float):
+def measured_traffic():
     """HBM bytes per launch of the row-statistics kernel from the committed
     rocprofv3 counter summary, or None if absent or taken on other sources."""
     try:
@@ -57,6 +60,57 @@ def measured_traffic(bytes_per_launch: float):
     if t.get("kernel_source_sha") != kernel_source_sha():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def _pmc_means(csv_path: str, counter: str):
+    """Mean per-dispatch value of `counter` for the row-statistics kernel
+    and for the calibration copy (torch's elementwise negation kernel), from
+    a rocprofv3 --pmc CSV."""
+    import csv
+
+    acc = {"row": [], "copy": []}
+    with open(csv_path, newline="") as f:
+        for rec in csv.DictReader(f):
+            if rec["Counter_Name"] != counter:
+                continue
+            name = rec["Kernel_Name"]
+            key = "row" if "k_row_stats" in name else "copy" if "neg_kernel" in name else None
+            if key:
+                acc[key].append(float(rec["Counter_Value"]))
+    if not acc["row"] or not acc["copy"]:
+        raise SystemExit(f"{csv_path}: no {counter} rows for k_row_stats and the copy kernel")
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str):
+    """Turn the FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch) into HBM
+    bytes per row-statistics launch.  Each counter is scaled by what it reads
+    for a plain elementwise copy of copy_mib MiB (which reads and writes
+    exactly that many bytes), and the result is written next to the
+    kernel-source hash it was taken on."""
+    nbytes = copy_mib * 1024 * 1024
+    fetch, nf = _pmc_means(fetch_csv, "FETCH_SIZE")
+    write, nw = _pmc_means(write_csv, "WRITE_SIZE")
+    f_scale = nbytes / (fetch["copy"] * 1024.0)
+    w_scale = nbytes / (write["copy"] * 1024.0)
+    rd = fetch["row"] * 1024.0 * f_scale
+    wr = write["row"] * 1024.0 * w_scale
+    out = {
+        "kernel": "k_row_stats", "workload": "B=64 k=8 V=128256 bf16",
+        "kernel_source_sha": kernel_source_sha(),
+        "fetch_kib_per_dispatch": fetch["row"], "write_kib_per_dispatch": write["row"],
+        "copy_bytes": nbytes, "copy_fetch_kib": fetch["copy"], "copy_write_kib": write["copy"],
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "dispatches": {"fetch_pass": nf, "write_pass": nw},
+        "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+        "hbm_bytes_per_launch": rd + wr,
+        "algorithmic_bytes_per_launch": ALGO_ROW_BYTES,
+        "command": command,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -88,12 +142,25 @@ def cpu_baseline(wl, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a plain elementwise copy (negation) of this many MiB of float32 "
+                         "three times before the warmup, as the reference kernel for HBM "
+                         "counter scaling")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) "
+                         "into the row-statistics traffic file")
+    ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        if args.copy_calibration_mib <= 0:
+            raise SystemExit("--summarize-pmc needs --copy-calibration-mib of the profiled runs")
+        summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.pmc_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the verifier is batch-parallel and this build "
@@ -126,6 +193,17 @@ def main():
         return S.spec_verify_sample(t, d, toks, wl.temperature, seed=wl.uniform_seed,
                                     counter0=i * n_u, workspace=ws)
 
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib * 1024 * 1024
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # one elementwise kernel: reads nb bytes, writes nb
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"bench: copy calibration, 3 x {args.copy_calibration_mib} MiB", file=sys.stderr,
+              flush=True)
+
     print(f"bench: warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
@@ -154,13 +232,14 @@ def main():
     acc_all = torch.stack(accs).cpu().numpy()
     row_bytes = V * 2
     pass1_bytes = B * (2 * k + 1) * row_bytes
+    assert pass1_bytes == ALGO_ROW_BYTES
     rejected = (acc_all < k).sum(axis=1)
     draw_bytes = (rejected * 2 + (B - rejected)) * row_bytes
     search_bytes = (rejected * 2 + (B - rejected)) * min(V, 4096) * 2
     step_bytes = float(np.mean(pass1_bytes + draw_bytes + search_bytes))
     avg_row_us = kern["row_pass"]["avg_us"]
     achieved = pass1_bytes / (avg_row_us * 1e-6) / 1e9
-    traffic = measured_traffic(pass1_bytes)
+    traffic = measured_traffic()
     positions = B * (k + 1)
     result = {
         "metric": METRIC,

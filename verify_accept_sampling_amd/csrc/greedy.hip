@@ -193,6 +193,22 @@ static bool rows_aligned(const void* p, int V, int dtype) {
   return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && (((long)V * eb) % 16 == 0);
 }
 
+// Kernel instantiation for the logit type and row alignment.
+template <template <int, int> class Pick>
+static auto pick_kernel(int dtype, bool vec) {
+  if (dtype == 1) return vec ? Pick<1, 8>::fn() : Pick<1, 1>::fn();
+  return vec ? Pick<0, 4>::fn() : Pick<0, 1>::fn();
+}
+
+template <int DT, int NE>
+struct ChainKernel {
+  static auto fn() { return &k_greedy_chain<DT, NE>; }
+};
+template <int DT, int NE>
+struct TreeKernel {
+  static auto fn() { return &k_tree_greedy<DT, NE>; }
+};
+
 hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int V,
                                const int32_t* draft_tokens, int32_t* accepted_len,
                                int32_t* out_tokens, void* ws, const WsLayout& L,
@@ -202,25 +218,9 @@ hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int 
   auto* part = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const dim3 grid((unsigned)((long)B * (k + 1) * C1)), block(kThreads);
-  const bool vec = rows_aligned(target, V, dtype);
-  prof_before(kProfRowPass, s);
-  if (dtype == 1) {
-    if (vec)
-      hipLaunchKernelGGL((k_greedy_chain<1, 8>), grid, block, 0, s, target, k, V, C1,
-                         draft_tokens, accepted_len, out_tokens, part, cnt);
-    else
-      hipLaunchKernelGGL((k_greedy_chain<1, 1>), grid, block, 0, s, target, k, V, C1,
-                         draft_tokens, accepted_len, out_tokens, part, cnt);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((k_greedy_chain<0, 4>), grid, block, 0, s, target, k, V, C1,
-                         draft_tokens, accepted_len, out_tokens, part, cnt);
-    else
-      hipLaunchKernelGGL((k_greedy_chain<0, 1>), grid, block, 0, s, target, k, V, C1,
-                         draft_tokens, accepted_len, out_tokens, part, cnt);
-  }
-  prof_after(kProfRowPass, s);
-  return hipGetLastError();
+  const auto kern = pick_kernel<ChainKernel>(dtype, rows_aligned(target, V, dtype));
+  return launch_timed(kProfRowPass, kern, grid, block, s, target, k, V, C1, draft_tokens,
+                      accepted_len, out_tokens, part, cnt);
 }
 
 hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes, int V,
@@ -232,29 +232,9 @@ hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
   auto* part = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const dim3 grid((unsigned)((long)B * n_nodes * C1)), block(kThreads);
-  const bool vec = rows_aligned(target, V, dtype);
-  prof_before(kProfRowPass, s);
-  if (dtype == 1) {
-    if (vec)
-      hipLaunchKernelGGL((k_tree_greedy<1, 8>), grid, block, 0, s, target, n_nodes, V, C1,
-                         tree, depth, node_tokens, accepted_len, out_tokens, out_path, part,
-                         cnt);
-    else
-      hipLaunchKernelGGL((k_tree_greedy<1, 1>), grid, block, 0, s, target, n_nodes, V, C1,
-                         tree, depth, node_tokens, accepted_len, out_tokens, out_path, part,
-                         cnt);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((k_tree_greedy<0, 4>), grid, block, 0, s, target, n_nodes, V, C1,
-                         tree, depth, node_tokens, accepted_len, out_tokens, out_path, part,
-                         cnt);
-    else
-      hipLaunchKernelGGL((k_tree_greedy<0, 1>), grid, block, 0, s, target, n_nodes, V, C1,
-                         tree, depth, node_tokens, accepted_len, out_tokens, out_path, part,
-                         cnt);
-  }
-  prof_after(kProfRowPass, s);
-  return hipGetLastError();
+  const auto kern = pick_kernel<TreeKernel>(dtype, rows_aligned(target, V, dtype));
+  return launch_timed(kProfRowPass, kern, grid, block, s, target, n_nodes, V, C1, tree, depth,
+                      node_tokens, accepted_len, out_tokens, out_path, part, cnt);
 }
 
 }  // namespace specv

@@ -2,6 +2,7 @@
 // kernel translation units.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -115,8 +116,27 @@ constexpr int kProfRowPass = 0;   // row statistics / argmax sweep + per-request
 constexpr int kProfDraw = 1;      // float64 residual / bonus pass + inverse-CDF draw
 constexpr int kProfUniforms = 2;  // spec_fill_uniforms
 constexpr int kProfKinds = 3;
-void prof_before(int kind, hipStream_t s);
-void prof_after(int kind, hipStream_t s);
+// While timing is enabled, prof_begin hands out a start/stop event pair that
+// the launch itself stamps (hipExtLaunchKernel records them from the
+// kernel's dispatch, so the interval is the kernel alone); otherwise both
+// events are null and the launch is an ordinary one.
+struct ProfEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int slot = -1;
+};
+ProfEvents prof_begin(int kind);
+void prof_end(const ProfEvents& ev, hipError_t launch_status);
+
+// Launch `kernel` (no dynamic shared memory) on stream s, timed as `kind`.
+template <typename... KArgs, typename... Args>
+hipError_t launch_timed(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                        hipStream_t s, Args... args) {
+  const ProfEvents ev = prof_begin(kind);
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  const hipError_t e = hipGetLastError();
+  prof_end(ev, e);
+  return e;
+}
 
 // Launch wrappers (defined in the .hip files).  Each returns a hipError_t.
 hipError_t launch_fill_uniforms(uint64_t seed, uint64_t counter0, int64_t n,

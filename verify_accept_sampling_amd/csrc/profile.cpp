@@ -1,8 +1,10 @@
 // Optional per-kernel timing with HIP events.  While enabled, every kernel a
-// spec_* call enqueues is bracketed by two events recorded on the same
-// stream; spec_profile_read synchronises the recorded events and reports, per
-// kernel kind, the launch count and the summed event time.  Disabled (the
-// default), the hooks cost one branch per launch.
+// spec_* call enqueues is launched with a start/stop event pair that the
+// runtime stamps from that kernel's own dispatch (hipExtLaunchKernel), so an
+// interval covers the kernel and not the queue gaps around it;
+// spec_profile_read synchronises the recorded events and reports, per kernel
+// kind, the launch count and the summed event time.  Disabled (the default),
+// the hooks cost one branch per launch.
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -23,7 +25,6 @@ std::mutex g_mu;
 std::atomic<bool> g_on{false};
 std::vector<Pair> g_pairs;
 size_t g_next = 0;
-int g_open = -1;  // index of the pair whose start has been recorded
 double g_ms[kProfKinds] = {0};
 long g_count[kProfKinds] = {0};
 
@@ -43,26 +44,28 @@ void drain_locked() {
 
 }  // namespace
 
-void prof_before(int kind, hipStream_t s) {
-  if (!g_on) return;
+ProfEvents prof_begin(int kind) {
+  ProfEvents ev;
+  if (!g_on) return ev;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return;
+  if (!g_on) return ev;
   if (g_next == g_pairs.size()) drain_locked();
   Pair& p = g_pairs[g_next];
   p.kind = kind;
-  if (hipEventRecord(p.a, s) != hipSuccess) return;
-  g_open = static_cast<int>(g_next);
+  ev.start = p.a;
+  ev.stop = p.b;
+  ev.slot = static_cast<int>(g_next);
+  return ev;
 }
 
-void prof_after(int kind, hipStream_t s) {
-  if (!g_on) return;
+void prof_end(const ProfEvents& ev, hipError_t launch_status) {
+  if (ev.slot < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on || g_open < 0 || g_pairs[g_open].kind != kind) return;
-  if (hipEventRecord(g_pairs[g_open].b, s) == hipSuccess) {
-    g_pairs[g_open].used = true;
+  if (!g_on || ev.slot != static_cast<int>(g_next)) return;
+  if (launch_status == hipSuccess) {
+    g_pairs[g_next].used = true;
     ++g_next;
   }
-  g_open = -1;
 }
 
 }  // namespace specv
@@ -87,7 +90,6 @@ int spec_profile_enable(int on) {
     }
     for (auto& p : g_pairs) p.used = false;
     g_next = 0;
-    g_open = -1;
     g_on = true;
   } else {
     g_on = false;

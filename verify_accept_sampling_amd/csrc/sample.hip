@@ -568,7 +568,7 @@ static bool rows_aligned(const void* p, int V, int dtype) {
 }
 
 template <int DT, int NE>
-static void launch_logits(const void* target, const void* draft, int B, int k, int V,
+static hipError_t launch_logits(const void* target, const void* draft, int B, int k, int V,
                           const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
                           uint64_t ctr0, float temperature, int32_t* accepted_len,
                           int32_t* out_tokens, float* probe, char* w, const WsLayout& L,
@@ -582,21 +582,19 @@ static void launch_logits(const void* target, const void* draft, int B, int k, i
   auto* p2 = reinterpret_cast<DrawPart*>(w + L.part2);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const long R = 2L * k + 1;
-  prof_before(kProfRowPass, s);
-  hipLaunchKernelGGL((k_row_stats<DT, NE>), dim3((unsigned)(B * R * C1)), dim3(kThreads), 0, s,
-                     target, draft, k, V, C1, c, draft_tokens, uniforms, seed, ctr0,
-                     accepted_len, out_tokens, probe, p1, st, cnt);
-  prof_after(kProfRowPass, s);
-  prof_before(kProfDraw, s);
+  hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>,
+                             dim3((unsigned)(B * R * C1)), dim3(kThreads), s, target, draft, k,
+                             V, C1, c, draft_tokens, uniforms, seed, ctr0, accepted_len,
+                             out_tokens, probe, p1, st, cnt);
+  if (e != hipSuccess) return e;
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  hipLaunchKernelGGL((k_draw<DT, NE, 0>), dim3((unsigned)(B * G2)), dim3(kThreads), 0, s, target,
-                     draft, k, V, C2, inv_t, draft_tokens, uniforms, seed, ctr0, accepted_len,
-                     out_tokens, probe, st, p2, cnt);
-  prof_after(kProfDraw, s);
+  return launch_timed(kProfDraw, &k_draw<DT, NE, 0>, dim3((unsigned)(B * G2)), dim3(kThreads), s,
+                      target, draft, k, V, C2, inv_t, draft_tokens, uniforms, seed, ctr0,
+                      accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);
 }
 
 template <int NE>
-static void launch_probs(const void* target, const void* draft, int B, int k, int V,
+static hipError_t launch_probs(const void* target, const void* draft, int B, int k, int V,
                          const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
                          uint64_t ctr0, int32_t* accepted_len, int32_t* out_tokens,
                          float* probe, char* w, const WsLayout& L, hipStream_t s) {
@@ -604,12 +602,10 @@ static void launch_probs(const void* target, const void* draft, int B, int k, in
   auto* st = reinterpret_cast<ReqState*>(w + L.state);
   auto* p2 = reinterpret_cast<DrawPart*>(w + L.part2);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
-  prof_before(kProfDraw, s);
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  hipLaunchKernelGGL((k_draw<0, NE, 1>), dim3((unsigned)(B * G2)), dim3(kThreads), 0, s, target,
-                     draft, k, V, C2, 1.0, draft_tokens, uniforms, seed, ctr0, accepted_len,
-                     out_tokens, probe, st, p2, cnt);
-  prof_after(kProfDraw, s);
+  return launch_timed(kProfDraw, &k_draw<0, NE, 1>, dim3((unsigned)(B * G2)), dim3(kThreads), s,
+                      target, draft, k, V, C2, 1.0, draft_tokens, uniforms, seed, ctr0,
+                      accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);
 }
 
 hipError_t launch_sample(const void* target, const void* draft, int dtype, int kind, int B,
@@ -621,27 +617,26 @@ hipError_t launch_sample(const void* target, const void* draft, int dtype, int k
   const bool vec = rows_aligned(target, V, dtype) && (k == 0 || rows_aligned(draft, V, dtype));
   if (kind == 1) {
     if (vec)
-      launch_probs<4>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+      return launch_probs<4>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
                       accepted_len, out_tokens, probe, w, L, s);
     else
-      launch_probs<1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+      return launch_probs<1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
                       accepted_len, out_tokens, probe, w, L, s);
   } else if (dtype == 1) {
     if (vec)
-      launch_logits<1, 8>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+      return launch_logits<1, 8>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
                           temperature, accepted_len, out_tokens, probe, w, L, s);
     else
-      launch_logits<1, 1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+      return launch_logits<1, 1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
                           temperature, accepted_len, out_tokens, probe, w, L, s);
   } else {
     if (vec)
-      launch_logits<0, 4>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+      return launch_logits<0, 4>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
                           temperature, accepted_len, out_tokens, probe, w, L, s);
     else
-      launch_logits<0, 1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+      return launch_logits<0, 1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
                           temperature, accepted_len, out_tokens, probe, w, L, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace specv
