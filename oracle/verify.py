@@ -260,6 +260,90 @@ def verify_sample(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarra
     return acc, out, results
 
 
+class FixedRowsSampler:
+    """Many verification calls over the same rows and draft tokens, each with
+    its own uniforms, for decision-rate runs.
+
+    Every decision is the one verify_sample_request takes: the acceptance
+    test u * q(x) < p(x) on the same float64 p(x), q(x), and inverse_cdf on
+    the same weight vector (max(0, p - q) after a rejection, falling back to
+    p when its total is zero; p at the bonus position).  The distributions
+    and cumulative sums of a request are computed once and reused; nothing
+    else differs.
+    """
+
+    def __init__(self, target, draft, draft_tokens, temperature, kind, dtype):
+        self.target, self.draft = target, draft
+        self.tokens = np.asarray(draft_tokens)
+        self.T, self.kind, self.dtype = temperature, kind, dtype
+        self.B, kp1, self.V = target.shape
+        self.k = kp1 - 1
+        self.px = np.zeros((self.B, self.k))
+        self.qx = np.zeros((self.B, self.k))
+        self.valid = np.zeros((self.B, self.k), dtype=bool)
+        for b in range(self.B):
+            for i in range(self.k):
+                x = int(self.tokens[b, i])
+                if 0 <= x < self.V:
+                    self.valid[b, i] = True
+                    self.px[b, i] = float(self._dist(target, b, i)[x])
+                    self.qx[b, i] = float(self._dist(draft, b, i)[x])
+        with np.errstate(divide="ignore"):
+            ratio = np.where(self.qx > 0.0, self.px / np.where(self.qx > 0.0, self.qx, 1.0),
+                             np.inf)
+        self.ratio = np.where(self.valid, ratio, np.nan)
+        self._cdf = {}
+
+    def _dist(self, rows, b, i):
+        row = decode(rows[b, i], self.dtype)
+        if self.kind == "logits":
+            return tempered_softmax(row, self.T)
+        return row
+
+    def cdf(self, b, n):
+        """Cumulative weights and their total for a request stopping at n."""
+        key = (b, n)
+        if key not in self._cdf:
+            p = self._dist(self.target, b, n)
+            if n < self.k:
+                C = np.cumsum(np.maximum(0.0, p - self._dist(self.draft, b, n)))
+                if not float(C[-1]) > 0.0:
+                    C = np.cumsum(p)
+            else:
+                C = np.cumsum(p)
+            self._cdf[key] = (C, float(C[-1]))
+        return self._cdf[key]
+
+    def run(self, u):
+        """u [N, B, k+1, 2] (float64).  Returns accepted [N, B], the drawn
+        token [N, B], the acceptance margins |u - p/q| [N, B, k] (inf for an
+        invalid token) and the draw margin [N, B]."""
+        N = u.shape[0]
+        k = self.k
+        ua = u[:, :, :k, 0]
+        accept = (ua * self.qx[None]) < self.px[None]
+        accept &= self.valid[None]
+        with np.errstate(invalid="ignore"):
+            amargin = np.where(self.valid[None], np.abs(ua - self.ratio[None]), np.inf)
+        rej = ~accept
+        first = np.where(rej.any(axis=2), rej.argmax(axis=2), k) if k > 0 else np.zeros(
+            (N, self.B), dtype=np.int64)
+        token = np.zeros((N, self.B), dtype=np.int64)
+        dmargin = np.zeros((N, self.B))
+        ures = np.take_along_axis(u[:, :, :, 1], first[:, :, None], axis=2)[:, :, 0]
+        for b in range(self.B):
+            for n in np.unique(first[:, b]):
+                sel = first[:, b] == n
+                C, total = self.cdf(b, int(n))
+                uu = ures[sel, b]
+                t = np.searchsorted(C, uu * total, side="right")
+                lo = np.where(t > 0, C[np.maximum(t - 1, 0)] / total, 0.0)
+                hi = C[t] / total
+                token[sel, b] = t
+                dmargin[sel, b] = np.minimum(uu - lo, hi - uu)
+        return first, token, amargin, dmargin
+
+
 def probe_values(target: np.ndarray, draft: np.ndarray, draft_tokens: np.ndarray,
                  temperature: float, kind: str, dtype: str, b: int):
     """p_i(x_i) and q_i(x_i) for every draft position i of request b (float64)."""

@@ -175,9 +175,9 @@ def test_sample_chain_v32000_full():
     _run_sample(W.sample_chain_v32000())
 
 
-def test_sample_chain_llama3_full():
+def test_sample_chain_llama3_full(llama3_full):
     _say("sample chain B=64 k=8 V=128256 bf16 T=0.7")
-    wl = W.sample_chain_llama3()
+    wl = llama3_full
     a1, o1 = _run_sample(wl, use_array=False)
     # the inline counter uniforms and an explicit uniform array agree exactly
     a2, o2 = _run_sample(wl, use_array=True)
@@ -231,12 +231,6 @@ def test_sample_probs_small_and_empty_residual():
     wl2 = W.ChainWorkload("empty_residual", p, q, toks, "probs", "f32", 1.0, 5)
     acc, out = _run_sample(wl2)
     assert (acc < k).any()
-
-
-@pytest.fixture(scope="module")
-def controlled_full():
-    _say("generating controlled-acceptance B=512 k=8 V=128256 f32 probs")
-    return W.controlled_acceptance()
 
 
 def test_sample_controlled_acceptance_full(controlled_full):

@@ -554,3 +554,55 @@ def test_planted_no_stop_at_first_reject_breaks_the_mean():
     em = [bad(wl.target[b], wl.draft[b], wl.draft_tokens[b], u[b], 1.0, "probs",
               "f32").accepted + 1 for b in range(N)]
     assert np.mean(em) > 2.47 + 1.0
+
+
+@pytest.mark.parametrize("kind,dtype,T", [("logits", "f32", 0.9), ("logits", "bf16", 1.4),
+                                          ("probs", "f32", 1.0)])
+def test_fixed_rows_sampler_takes_the_same_decisions(kind, dtype, T):
+    """The batched evaluator used for decision-rate runs reproduces
+    verify_sample_request decision for decision (tokens, stop positions and
+    margins identical), including an empty residual (probability rows with
+    q = 1.5 p) and out-of-range draft tokens."""
+    rng = np.random.default_rng(31)
+    B, k, V, N = 5, 3, 40, 150
+    if kind == "logits":
+        t = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+        d = (t[:, :k] + rng.standard_normal((B, k, V)).astype(np.float32)).astype(np.float32)
+        if dtype == "bf16":
+            t, d = W.f32_to_bf16_bits(t), W.f32_to_bf16_bits(d)
+    else:
+        t = rng.dirichlet(np.ones(V), size=(B, k + 1)).astype(np.float32)
+        d = rng.dirichlet(np.ones(V), size=(B, k)).astype(np.float32)
+        d[1] = (t[1, :k] * np.float32(1.5)).astype(np.float32)  # residual is empty
+    toks = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    toks[2, 1] = V      # out of range: a rejection
+    toks[3, 0] = -1
+    fr = O.FixedRowsSampler(t, d, toks, T, kind, dtype)
+    u = R.uniforms(77, 0, N * B * (k + 1) * 2).reshape(N, B, k + 1, 2)
+    first, token, am, dm = fr.run(u)
+    saw_fallback = False
+    for c in range(N):
+        for b in range(B):
+            r = O.verify_sample_request(t[b], d[b], toks[b], u[c, b], T, kind, dtype)
+            assert first[c, b] == r.accepted and token[c, b] == r.tokens[-1]
+            acc_m = [x.margin for x in r.decisions if x.kind == "accept"]
+            assert np.array_equal(am[c, b, :len(acc_m)], np.asarray(acc_m))
+            draw = [x for x in r.decisions if x.kind == "resample"]
+            assert dm[c, b] == draw[0].margin
+            saw_fallback |= any(x.kind == "empty_residual" for x in r.decisions)
+    assert saw_fallback == (kind == "probs")
+
+
+def test_fixed_rows_sampler_without_drafts():
+    rng = np.random.default_rng(5)
+    t = (rng.standard_normal((3, 1, 17))).astype(np.float32)
+    fr = O.FixedRowsSampler(t, np.zeros((3, 0, 17), np.float32), np.zeros((3, 0), np.int32),
+                            1.0, "logits", "f32")
+    u = R.uniforms(3, 0, 20 * 3 * 2).reshape(20, 3, 1, 2)
+    first, token, _, _ = fr.run(u)
+    assert np.all(first == 0)
+    for c in range(20):
+        for b in range(3):
+            r = O.verify_sample_request(t[b], None, np.zeros(0, np.int32), u[c, b], 1.0,
+                                        "logits", "f32")
+            assert token[c, b] == r.tokens[-1]
