@@ -48,6 +48,15 @@ __device__ __forceinline__ uint64_t pack2(float a, float b) {
 __device__ __forceinline__ float unpack_lo(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v)); }
 __device__ __forceinline__ float unpack_hi(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
 
+__device__ __forceinline__ void st_dev_f(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev_f(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // One thread per work-group calls this after its coherent stores.  Returns
 // true for the last of `total` arrivals; that caller also resets the counter
 // to zero for the next call.
@@ -69,6 +78,22 @@ __device__ __forceinline__ bool block_arrive(unsigned* counter, unsigned total) 
   return s_last != 0;
 }
 
+// Wave form (wave 0 of a work-group whose other waves have left): lane 0
+// arrives; the answer is broadcast across the wave.
+__device__ __forceinline__ bool wave_arrive(unsigned* counter, unsigned total) {
+  int last = 0;
+  if ((threadIdx.x & 63) == 0) last = arrive(counter, total) ? 1 : 0;
+  return __shfl(last, 0, 64) != 0;
+}
+
+// Orders this wave's shared-memory writes before its later reads (lanes
+// exchange values through shared memory without a work-group barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Elements per 16-byte vector for each input dtype (0 = f32, 1 = bf16).
@@ -80,6 +105,38 @@ struct Elems {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 16-byte non-temporal buffer loads from one row: the row's base address
+// and size sit in a buffer resource (SGPRs), each load takes a per-lane
+// 32-bit byte offset plus a uniform one, so the streaming loops need no
+// 64-bit address arithmetic per load.  Rows must be shorter than 2 GiB.
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+constexpr int kLoadNonTemporal = 2;       // cache policy: nt
+
+struct RowBuf {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ RowBuf(const void* base, uint32_t bytes)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                               kBufferWord3)) {}
+  __device__ __forceinline__ u32x4 load_nt(uint32_t lane_off, uint32_t uniform_off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)lane_off, (int)uniform_off,
+                                                 kLoadNonTemporal);
+  }
+};
+
+// The Elems<DT>::kVec elements of one 16-byte word as floats.
+template <int DT>
+__device__ __forceinline__ void unpack16(const u32x4& w, float* x) {
+  if constexpr (DT == 1) {
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+    x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+    x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  } else {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+  }
+}
 
 // One element of a row as float.
 template <int DT>
@@ -226,6 +283,32 @@ __device__ __forceinline__ double block_sum_d(double v) {
   return t;
 }
 
+// Sums of N doubles per thread over the work-group, in place (every thread
+// receives the totals).
+template <int N>
+__device__ __forceinline__ void block_sum_dn(double (&v)[N]) {
+  __shared__ double sd[kWaves][N];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) v[q] += shfl_xor_d(v[q], o);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) sd[wave][q] = v[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    double t = sd[0][q];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += sd[w][q];
+    v[q] = t;
+  }
+}
+
 // Sums of five doubles per thread over the work-group, in place (every
 // thread receives the totals).
 __device__ __forceinline__ void block_sum_d5(double (&v)[5]) {
@@ -271,6 +354,12 @@ __device__ __forceinline__ double block_exclusive_scan_d(double v) {
 }
 
 // Minimum of an int over the work-group, broadcast.
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 __device__ __forceinline__ int block_min_i(int v) {
   __shared__ int si[kWaves];
 #pragma unroll

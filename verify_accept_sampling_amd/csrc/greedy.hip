@@ -219,7 +219,7 @@ hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int 
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const dim3 grid((unsigned)((long)B * (k + 1) * C1)), block(kThreads);
   const auto kern = pick_kernel<ChainKernel>(dtype, rows_aligned(target, V, dtype));
-  return launch_timed(kProfRowPass, kern, grid, block, s, target, k, V, C1, draft_tokens,
+  return launch_timed(kProfRowPass, kern, grid, block, 0, s, target, k, V, C1, draft_tokens,
                       accepted_len, out_tokens, part, cnt);
 }
 
@@ -233,7 +233,7 @@ hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const dim3 grid((unsigned)((long)B * n_nodes * C1)), block(kThreads);
   const auto kern = pick_kernel<TreeKernel>(dtype, rows_aligned(target, V, dtype));
-  return launch_timed(kProfRowPass, kern, grid, block, s, target, n_nodes, V, C1, tree, depth,
+  return launch_timed(kProfRowPass, kern, grid, block, 0, s, target, n_nodes, V, C1, tree, depth,
                       node_tokens, accepted_len, out_tokens, out_path, part, cnt);
 }
 

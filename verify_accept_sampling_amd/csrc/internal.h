@@ -11,7 +11,8 @@ namespace specv {
 
 // Block shape of every kernel: 256 threads = 4 waves of 64 lanes.
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kWaveSize = 64;
+constexpr int kWaves = kThreads / kWaveSize;
 
 // Elements per work-group chunk of the pass over every row (tunable at
 // build time).
@@ -19,11 +20,18 @@ constexpr int kWaves = kThreads / 64;
 #define SPEC_ROW_CHUNK 65536
 #endif
 constexpr int kRowChunkElems = SPEC_ROW_CHUNK;
-// 16-byte loads in flight per thread in the row pass.
+// 16-byte loads in flight per thread in the argmax sweep.
 #ifndef SPEC_ROW_UNROLL
 #define SPEC_ROW_UNROLL 8
 #endif
 constexpr int kRowUnroll = SPEC_ROW_UNROLL;
+// 16-byte loads per thread per batch in the row-statistics sweep, which
+// keeps two batches in flight (the next one loads while the current one is
+// folded in).  4 keeps the kernel near 64 VGPRs, i.e. 7 waves per SIMD; 8
+// needs about 100 VGPRs (4 waves) and is slower.
+#ifndef SPEC_STATS_UNROLL
+#define SPEC_STATS_UNROLL 4
+#endif
 // Smallest chunk the workspace is sized for (leaves room to retune).
 constexpr int kRowChunkElemsMin = 2048;
 // Float64 residual / bonus pass: the row is cut into chunks of
@@ -77,6 +85,7 @@ constexpr int kCountersPerReq = 2;
 struct WsLayout {
   size_t count;  // uint32 [kMaxB * kCountersPerReq], always at offset 0
   size_t part1;  // uint64 [rows * row_chunks]: packed (max, sum) or (value, index)
+  size_t zrow;   // float [rows]: each row's logit at its draft token
   size_t state;  // ReqState [B]
   size_t part2;  // DrawPart [B * res_chunks]
   size_t total;
@@ -97,6 +106,8 @@ inline WsLayout ws_layout(int B, int n_pos, int V) {
   off = align_up(off + (size_t)kMaxB * kCountersPerReq * 4, 256);
   L.part1 = off;
   off = align_up(off + rows * (size_t)row_chunks_max(V) * 8, 256);
+  L.zrow = off;
+  off = align_up(off + rows * 4, 256);
   L.state = off;
   off = align_up(off + (size_t)B * sizeof(ReqState), 256);
   L.part2 = off;
@@ -127,12 +138,13 @@ struct ProfEvents {
 ProfEvents prof_begin(int kind);
 void prof_end(const ProfEvents& ev, hipError_t launch_status);
 
-// Launch `kernel` (no dynamic shared memory) on stream s, timed as `kind`.
+// Launch `kernel` with `shmem` bytes of dynamic shared memory on stream s,
+// timed as `kind`.
 template <typename... KArgs, typename... Args>
 hipError_t launch_timed(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 block,
-                        hipStream_t s, Args... args) {
+                        uint32_t shmem, hipStream_t s, Args... args) {
   const ProfEvents ev = prof_begin(kind);
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0, args...);
   const hipError_t e = hipGetLastError();
   prof_end(ev, e);
   return e;

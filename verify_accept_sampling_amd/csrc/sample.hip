@@ -31,7 +31,8 @@
 
 namespace specv {
 
-constexpr int kUnrollStats = kRowUnroll;
+constexpr int kUnrollStats = SPEC_STATS_UNROLL;
+
 
 // An element whose two terms differ by less than this fraction (relative to
 // rho32 e^{(y-mq)/T}) may change sides of max(0, .) between rho32 and the
@@ -53,52 +54,183 @@ __device__ __forceinline__ const void* stat_row(const void* target, const void* 
 // 1. Row statistics and acceptance
 // ---------------------------------------------------------------------------
 
-// Streaming softmax statistic of a chunk: running maximum m and
-// s = sum 2^(x c - mc) with mc = fl32(m c), the rounded product (each
-// element costs one fused multiply-add; merges recompute mc from m, so its
-// rounding cancels exactly).  Each group of NE terms is added in float32
-// and the group sums in float64: a float32 running sum near 1 would absorb
-// the many terms far below its last bit.
-template <int NE>
-__device__ __forceinline__ void ms_update(float& m, float& mc, double& s, const float (&x)[NE],
-                                          float c) {
-  float lm = x[0];
+// Streaming softmax statistic of a chunk: a reference value m (an element
+// of the chunk) and s = sum 2^(x c - mc) with mc = fl32(m c), the rounded
+// product; merges recompute mc from m, so its rounding cancels exactly.
+// Any reference gives the same statistic, since log p(x) = x c - mc -
+// log2 s; the reference only has to keep the terms finite.  So m is not
+// the running maximum: it is updated only when a batch's sum reaches
+// kBatchLimit (every term of the batch is then below 2^64) and on the first
+// batch that holds a finite value.  Each element costs one fused
+// multiply-add, one exp2 and one add.  Terms are added pairwise within a
+// batch in float32; batch sums are accumulated in float64, because a
+// float32 running sum would absorb the many terms far below its last bit.
+constexpr float kBatchLimit = 0x1p64f;
+
+template <int N>
+__device__ __forceinline__ float batch_sum(const float* x, float c, float mc) {
+  float t[N];
 #pragma unroll
-  for (int e = 1; e < NE; ++e) lm = fmaxf(lm, x[e]);
-  if (lm > m) {  // rare after the first groups
-    const float mcn = mul_rn(lm, c);
-    s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f(mc - mcn);
-    m = lm;
-    mc = mcn;
-  }
-  if (m == -INFINITY) return;  // only -inf so far
-  float g = 0.f;
+  for (int e = 0; e < N; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, -mc));
 #pragma unroll
-  for (int e = 0; e < NE; ++e) g += __builtin_amdgcn_exp2f(fmaf(x[e], c, -mc));
-  s += (double)g;
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int e = 0; e + w < N; e += 2 * w) t[e] += t[e + w];
+  return t[0];
 }
 
-// Merged maximum M and normaliser S = sum 2^(x c - fl32(M c)) (float64) of
-// one row from its chunk partials, by one thread: each partial is loaded
-// once and folded in.
-__device__ __forceinline__ void merge_row_thread(const uint64_t* part, long base_idx, int C1,
-                                                 float c, float& M, double& S) {
-  M = -INFINITY;
-  S = 0.0;
-  for (int cc = 0; cc < C1; ++cc) {
-    const uint64_t pp = ld_dev(&part[base_idx + cc]);
-    const float m2 = unpack_lo(pp);
-    const double s2 = (double)unpack_hi(pp);
-    if (m2 == -INFINITY) continue;
-    if (M == -INFINITY) {
-      M = m2;
-      S = s2;
-      continue;
+// Sum of one group's terms, moving the reference first when the group holds
+// a value far above it (or the first finite value).
+template <int N>
+__device__ __forceinline__ float group_sum(float& m, float& mc, double& s, const float* x,
+                                           float c) {
+  float g = batch_sum<N>(x, c, mc);
+  if (!(g < kBatchLimit)) {  // rare: no reference yet, or far above it
+    float lm = x[0];
+#pragma unroll
+    for (int e = 1; e < N; ++e) lm = fmaxf(lm, x[e]);
+    if (lm > m) {
+      const float mcn = mul_rn(lm, c);
+      s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f(mc - mcn);
+      m = lm;
+      mc = mcn;
     }
-    const float mn = fmaxf(M, m2);
-    const double mcn = (double)mul_rn(mn, c);
-    S = S * exp2((double)mul_rn(M, c) - mcn) + s2 * exp2((double)mul_rn(m2, c) - mcn);
-    M = mn;
+    g = (m == -INFINITY) ? 0.f : batch_sum<N>(x, c, mc);
+  }
+  return g;
+}
+
+// Fold kUnrollStats words (one per group) into (m, mc, s): group sums are
+// taken in order (a group may move the reference, which rescales s and
+// every later group), then added pairwise and once to s.
+template <int DT>
+__device__ __forceinline__ void stat_words(float& m, float& mc, double& s, const u32x4 (&w)[kUnrollStats],
+                                           float c) {
+  constexpr int NE = Elems<DT>::kVec;
+  float gs[kUnrollStats];
+  float mc0 = mc;
+#pragma unroll
+  for (int u = 0; u < kUnrollStats; ++u) {
+    float x[NE];
+    unpack16<DT>(w[u], x);
+    gs[u] = group_sum<NE>(m, mc, s, x, c);
+    if (mc != mc0) {  // rare: the reference moved; rescale the earlier groups
+      const float f = (mc0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc0 - mc);
+#pragma unroll
+      for (int v = 0; v < u; ++v) gs[v] *= f;
+      mc0 = mc;
+    }
+  }
+#pragma unroll
+  for (int w2 = 1; w2 < kUnrollStats; w2 *= 2)
+#pragma unroll
+    for (int e = 0; e + w2 < kUnrollStats; e += 2 * w2) gs[e] += gs[e + w2];
+  s += (double)gs[0];
+}
+
+// This thread's groups (16-byte words) [g0, g1) of one row.  Software
+// pipelined: the next iteration's kUnrollStats loads are issued before the
+// current words are folded in, so every wave keeps loads in flight while it
+// computes.
+template <int DT>
+__device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, long g0, long g1,
+                                            float c, float& m, float& mc, double& s) {
+  constexpr int NE = Elems<DT>::kVec;
+  constexpr uint32_t kStep = kThreads * kUnrollStats * 16u;
+  const RowBuf buf(rp, row_bytes);
+  long g = g0 + threadIdx.x;
+  uint32_t off = static_cast<uint32_t>(g) * 16u;
+  const long span = (long)(kUnrollStats - 1) * kThreads;
+  if (g + span < g1) {
+    // Two word buffers used in turn (no register copies, which would wait
+    // for the loads in flight).
+    u32x4 wa[kUnrollStats], wb[kUnrollStats];
+#pragma unroll
+    for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * kThreads * 16u);
+    for (;;) {
+      g += (long)kThreads * kUnrollStats;
+      off += kStep;
+      if (!(g + span < g1)) {
+        stat_words<DT>(m, mc, s, wa, c);
+        break;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnrollStats; ++u) wb[u] = buf.load_nt(off, u * kThreads * 16u);
+      __builtin_amdgcn_sched_barrier(0);
+      stat_words<DT>(m, mc, s, wa, c);
+      g += (long)kThreads * kUnrollStats;
+      off += kStep;
+      if (!(g + span < g1)) {
+        stat_words<DT>(m, mc, s, wb, c);
+        break;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * kThreads * 16u);
+      __builtin_amdgcn_sched_barrier(0);
+      stat_words<DT>(m, mc, s, wb, c);
+    }
+  }
+  for (; g < g1; g += kThreads, off += kThreads * 16u) {
+    float x[NE];
+    unpack16<DT>(buf.load_nt(off, 0), x);
+    const float gsum = group_sum<NE>(m, mc, s, x, c);  // may rescale s first
+    s += (double)gsum;
+  }
+}
+
+// Scalar form for rows that are not 16-byte aligned: elements [e0, e1).
+template <int DT>
+__device__ __forceinline__ void stats_sweep_scalar(const void* rp, long e0, long e1, float c,
+                                                   float& m, float& mc, double& s) {
+  for (long e = e0 + threadIdx.x; e < e1; e += kThreads) {
+    const float x = load_elem<DT>(rp, e);
+    const float gsum = group_sum<1>(m, mc, s, &x, c);  // may rescale s first
+    s += (double)gsum;
+  }
+}
+
+// Fold one chunk partial (reference m2, sum s2 relative to 2^fl32(m2 c))
+// into the row's running (M, S), S = sum 2^(x c - fl32(M c)) in float64.
+__device__ __forceinline__ void fold_partial(float& M, double& S, uint64_t pp, float c) {
+  const float m2 = unpack_lo(pp);
+  const double s2 = (double)unpack_hi(pp);
+  if (m2 == -INFINITY) return;
+  if (M == -INFINITY) {
+    M = m2;
+    S = s2;
+    return;
+  }
+  const float mn = fmaxf(M, m2);
+  const double mcn = (double)mul_rn(mn, c);
+  S = S * exp2((double)mul_rn(M, c) - mcn) + s2 * exp2((double)mul_rn(m2, c) - mcn);
+  M = mn;
+}
+
+// (M, S) of two rows of one request (the second only when has_b) from their
+// chunk partials, by one thread: up to four partials of each row are loaded
+// before any is folded in, so the loads of both rows are in flight together.
+__device__ __forceinline__ void merge_two_rows(const uint64_t* part, long base_a, long base_b,
+                                               bool has_b, int C1, float c, float& Ma,
+                                               double& Sa, float& Mb, double& Sb) {
+  Ma = Mb = -INFINITY;
+  Sa = Sb = 0.0;
+  for (int c0 = 0; c0 < C1; c0 += 4) {
+    uint64_t pa[4], pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pa[j] = pb[j] = 0;
+      if (c0 + j < C1) {
+        pa[j] = ld_dev(&part[base_a + c0 + j]);
+        if (has_b) pb[j] = ld_dev(&part[base_b + c0 + j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (c0 + j < C1) {
+        fold_partial(Ma, Sa, pa[j], c);
+        if (has_b) fold_partial(Mb, Sb, pb[j], c);
+      }
+    }
   }
 }
 
@@ -108,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     float c, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
     uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, float* __restrict__ probe, uint64_t* __restrict__ part,
-    ReqState* __restrict__ state, unsigned* __restrict__ counters) {
+    float* __restrict__ zrow, ReqState* __restrict__ state, unsigned* __restrict__ counters) {
   const int R = 2 * k + 1;
   const int chunk = blockIdx.x % C1;
   const long rowid = blockIdx.x / C1;
@@ -116,58 +248,69 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
   const int r = static_cast<int>(rowid % R);
   {
     const void* rp = stat_row<DT>(target, draft, b, r, k, V);
+    // The draft token this row is tested at (target row i and draft row i
+    // share x_i; the bonus row k has none), loaded now and used after the
+    // sweep.
+    const int tpos = r < k ? r : (r > k ? r - k - 1 : -1);
+    int x = -1;
+    if (threadIdx.x == 0 && tpos >= 0) x = draft_tokens[(long)b * k + tpos];
     const long n_groups = V / NE;
     const long gpc = (n_groups + C1 - 1) / C1;
     const long g0 = (long)chunk * gpc;
     const long g1 = min(g0 + gpc, n_groups);
     float m = -INFINITY, mc = -INFINITY;
     double s = 0.0;
-    long g = g0 + threadIdx.x;
-    // Main loop: kUnrollStats loads issued back to back, no bounds branch.
-    for (; g + (long)(kUnrollStats - 1) * kThreads < g1; g += (long)kThreads * kUnrollStats) {
-      float x[kUnrollStats][NE];
-#pragma unroll
-      for (int u = 0; u < kUnrollStats; ++u)
-        load_group<DT, NE, true>(rp, (g + (long)u * kThreads) * NE, x[u]);
-#pragma unroll
-      for (int u = 0; u < kUnrollStats; ++u) ms_update<NE>(m, mc, s, x[u], c);
-    }
-    for (; g < g1; g += kThreads) {
-      float x[NE];
-      load_group<DT, NE, true>(rp, g * NE, x);
-      ms_update<NE>(m, mc, s, x, c);
-    }
+    if constexpr (NE == 1)
+      stats_sweep_scalar<DT>(rp, g0, g1, c, m, mc, s);
+    else
+      stats_sweep<DT>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0, g1, c, m, mc,
+                      s);
+    // The chunk that holds the token also publishes the logit there.
+    const bool own = x >= 0 && x < V && (long)x >= g0 * NE && (long)x < g1 * NE;
+    float zx = 0.f;
+    if (own) zx = load_elem<DT>(rp, x);
     block_reduce_ms(m, s, c);
-    if (threadIdx.x == 0) st_dev(&part[rowid * C1 + chunk], pack2(m, (float)s));
+    if (threadIdx.x >= kWaveSize) return;  // wave 0 finishes the work-group
+    if (threadIdx.x == 0) {
+      st_dev(&part[rowid * C1 + chunk], pack2(m, (float)s));
+      if (own) st_dev_f(&zrow[rowid], zx);
+    }
   }
-  if (!block_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
+  if (!wave_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
 
-  // ---- last work-group of request b: acceptance tests ----
-  // Every row of the request is merged by its own thread (one round of
-  // coherent loads) while the logits at the draft tokens are gathered; then
-  // thread i tests draft i.
-  __shared__ float s_m[2 * kMaxK + 1];
-  __shared__ double s_s[2 * kMaxK + 1];
-  for (int rr = threadIdx.x; rr < R; rr += kThreads) {
-    float M;
-    double S;
-    merge_row_thread(part, ((long)b * R + rr) * C1, C1, c, M, S);
-    s_m[rr] = M;
-    s_s[rr] = S;
-  }
-  __syncthreads();
+  // ---- last work-group of request b, one wave: acceptance tests ----
+  // Lane i handles position i (and i + 64, ...): it loads the token, the two
+  // published token logits and the chunk partials of target row i and draft
+  // row i in one round, merges the rows and tests draft i.
+  extern __shared__ double dyn_lds[];
+  double* s_s = dyn_lds;                             // [R]
+  float* s_m = reinterpret_cast<float*>(dyn_lds + R);  // [R]
+  const int lane = threadIdx.x;
   int first = k;
-  for (int i = threadIdx.x; i < k; i += kThreads) {
-    const int x = draft_tokens[(long)b * k + i];
+  for (int i = lane; i <= k; i += kWaveSize) {
+    const bool draft_pos = i < k;
+    int x = -1;
+    float zp = 0.f, zq = 0.f;
+    if (draft_pos) {
+      x = draft_tokens[(long)b * k + i];
+      zp = ld_dev_f(&zrow[(long)b * R + i]);
+      zq = ld_dev_f(&zrow[(long)b * R + k + 1 + i]);
+    }
+    float Mp, Mq;
+    double Sp, Sq;
+    merge_two_rows(part, ((long)b * R + i) * C1, ((long)b * R + k + 1 + i) * C1, draft_pos, C1,
+                   c, Mp, Sp, Mq, Sq);
+    s_m[i] = Mp;
+    s_s[i] = Sp;
+    if (!draft_pos) continue;
+    s_m[k + 1 + i] = Mq;
+    s_s[k + 1 + i] = Sq;
     float pv = 0.f, qv = 0.f;
     bool accept = false;
     if (x >= 0 && x < V) {
-      const float zp = load_elem<DT>(stat_row<DT>(target, draft, b, i, k, V), x);
-      const float zq = load_elem<DT>(stat_row<DT>(target, draft, b, k + 1 + i, k, V), x);
       // log2 p_i(x) and log2 q_i(x) from the row statistics
-      const double lp = ((double)zp * c - (double)mul_rn(s_m[i], c)) - log2(s_s[i]);
-      const double lq =
-          ((double)zq * c - (double)mul_rn(s_m[k + 1 + i], c)) - log2(s_s[k + 1 + i]);
+      const double lp = ((double)zp * c - (double)mul_rn(Mp, c)) - log2(Sp);
+      const double lq = ((double)zq * c - (double)mul_rn(Mq, c)) - log2(Sq);
       const double ratio = exp2(lp - lq);
       const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
       accept = (double)u < ratio;
@@ -180,14 +323,15 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
       pr[0] = pv; pr[1] = qv; pr[2] = 0.f; pr[3] = 0.f;
     }
   }
-  const int n = block_min_i(first);
-  for (int i = threadIdx.x; i <= k; i += kThreads) {
+  const int n = wave_min_i(first);
+  wave_lds_sync();
+  for (int i = lane; i <= k; i += kWaveSize) {
     if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
     else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
   }
-  // State for the draw: maxima of target row n and (rejection) draft row n,
-  // and the float32-based normaliser ratio of that pair.
-  if (threadIdx.x == 0) {
+  // State for the draw: references of target row n and (rejection) draft
+  // row n, and the float32-based normaliser ratio of that pair.
+  if (lane == 0) {
     const float mp = s_m[n];
     const float mq = n < k ? s_m[k + 1 + n] : 0.f;
     // S relative to 2^(m c) instead of 2^fl32(m c): ratio of the pair.
@@ -351,20 +495,6 @@ __device__ __forceinline__ void search_terms(const void* prow, const void* qrow,
   }
 }
 
-// Exact chunk total with the float64 rho (for chunks flagged at the kink).
-template <int DT, int KIND>
-__device__ double chunk_total_exact(const void* prow, const void* qrow, int V, int chunk,
-                                    double c1, double c0p, double c0q, double rho,
-                                    const double* tab) {
-  double w[kSearchPerThread];
-  long j0;
-  search_terms<DT, KIND>(prow, qrow, V, chunk, true, c1, c0p, c0q, rho, tab, w, j0);
-  double t = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSearchPerThread; ++e) t += w[e];
-  return block_sum_d(t);
-}
-
 // Search one chunk with the exact weights.  Returns the first element whose
 // running sum, added to the prefix P of the earlier chunks, exceeds thr,
 // falling back to the chunk's last positive-weight element (reachable only
@@ -459,88 +589,95 @@ __global__ __launch_bounds__(kThreads) void k_draw(
   if (!block_arrive(&counters[(long)b * kCountersPerReq + 1], (unsigned)G2)) return;
 
   // ---- last work-group of request b: exact rho, chunk totals, draw ----
+  // Thread t owns chunk base + t of each tile of kThreads chunks.  With one
+  // tile (V up to 262144) the partials are loaded once and every step below
+  // works on registers; with more tiles the corrected totals are written back
+  // and reloaded by the same thread.
   DrawPart* rp = part + (long)b * C2;
-  __shared__ double s_rho, s_sp;
-  {
-    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-    for (int cc = threadIdx.x; cc < C2; cc += kThreads) {
-      v[0] += ld_dev_d(&rp[cc].sp);
-      v[1] += ld_dev_d(&rp[cc].sq);
+  const int n_tiles = (C2 + kThreads - 1) / kThreads;
+  double csp = 0.0, csq = 0.0, cw = 0.0, cdq = 0.0, cfl = 0.0;
+  auto load_chunk = [&](int cc) {
+    csp = csq = cw = cdq = cfl = 0.0;
+    if (cc < C2) {
+      csp = ld_dev_d(&rp[cc].sp);
+      csq = ld_dev_d(&rp[cc].sq);
+      cw = ld_dev_d(&rp[cc].w);
+      cdq = ld_dev_d(&rp[cc].dq);
+      cfl = ld_dev_d(&rp[cc].flag);
     }
-    block_sum_d5(v);
-    if (threadIdx.x == 0) {
-      s_sp = v[0];
-      s_rho = (KIND == 0 && resid) ? v[0] / v[1] : 1.0;
-    }
+  };
+  double sums[2] = {0.0, 0.0};  // S_p, S_q over the row(s)
+  for (int base = 0; base < C2; base += kThreads) {
+    load_chunk(base + threadIdx.x);
+    sums[0] += csp;
+    sums[1] += csq;
   }
-  __syncthreads();
-  const double rho = s_rho, sp_tot = s_sp;
-  // Chunk totals at the exact rho: linear correction, or recomputation for
-  // the (rare) chunks with an element at the kink.  Written back in place,
-  // one chunk per thread.
-  if (KIND == 0 && resid) {
-    __shared__ int s_kink[kThreads];
-    for (int base = 0; base < C2; base += kThreads) {
-      const int cc = base + threadIdx.x;
-      int kink = 0;
-      if (cc < C2) {
-        kink = ld_dev_d(&rp[cc].flag) > 0.0;
-        if (!kink)
-          st_dev_d(&rp[cc].w,
-                   fmax(0.0, ld_dev_d(&rp[cc].w) + (rho - rho32) * ld_dev_d(&rp[cc].dq)));
-      }
-      s_kink[threadIdx.x] = kink;
-      if (__syncthreads_count(kink) > 0) {
-        for (int j = 0; j < kThreads && base + j < C2; ++j) {
-          if (!s_kink[j]) continue;  // block-uniform
-          const double wt =
-              chunk_total_exact<DT, KIND>(prow, qrow, V, base + j, c1, c0p, c0q, rho, tab);
-          if (threadIdx.x == 0) st_dev_d(&rp[base + j].w, fmax(0.0, wt));
-        }
+  block_sum_dn<2>(sums);
+  const double sp_tot = sums[0];
+  const double rho = (KIND == 0 && resid) ? sums[0] / sums[1] : 1.0;
+  // Chunk totals of the draw weights at the exact rho: linear correction,
+  // or, for chunks with an element in the kink band, recomputation at rho,
+  // one wave per flagged chunk.
+  double grand_w = 0.0;
+  for (int base = 0; base < C2; base += kThreads) {
+    const int cc = base + threadIdx.x;
+    if (n_tiles > 1) load_chunk(cc);
+    const bool kink = KIND == 0 && resid && cfl > 0.0;
+    if (KIND == 0 && resid && !kink) cw = fmax(0.0, cw + (rho - rho32) * cdq);
+    if (__syncthreads_count(kink) > 0) {
+      __shared__ int s_list[kThreads];
+      __shared__ int s_nk;
+      __shared__ double s_wx[kThreads];
+      if (threadIdx.x == 0) s_nk = 0;
+      __syncthreads();
+      if (kink) s_list[atomicAdd(&s_nk, 1)] = threadIdx.x;
+      __syncthreads();
+      const int nk = s_nk;
+      for (int idx = wave; idx < nk; idx += kWaves) {  // wave-uniform
+        const int t2 = s_list[idx];
+        double v[5];
+        wave_chunk_sums<DT, NE, KIND>(prow, qrow, V, base + t2, true, c1, c0p, c0q, rho, tab, v);
+        if (lane == 0) s_wx[t2] = v[2];
       }
       __syncthreads();
+      if (kink) cw = fmax(0.0, s_wx[threadIdx.x]);
     }
+    if (n_tiles > 1) {
+      if (cc < C2) st_dev_d(&rp[cc].w, cw);
+      wait_stores();  // reloaded by this same thread below
+    }
+    grand_w += cw;
   }
-  // Prefix of the chunk totals (residual weights, or the target terms when
-  // the residual is empty) by a tiled work-group scan: first the total, then
-  // the chunk holding u * total.
+  grand_w = block_sum_d(grand_w);
+  // Weights drawn from: the residual, or the target terms when the
+  // residual is empty (or at the bonus position).
+  const bool use_w = resid && grand_w > 0.0;
+  const double grand = use_w ? grand_w : sp_tot;
   const float u = get_uniform(uniforms, seed, ctr0, b, n, 1, k);
-  int mode = resid ? 0 : 1;  // 0: residual weights, 1: target terms
-  double grand = 0.0;
-  for (int pass = 0; pass < 2; ++pass) {
-    double running = 0.0;
-    for (int base = 0; base < C2; base += kThreads) {
-      const int cc = base + threadIdx.x;
-      const double wc = cc < C2 ? (mode == 0 ? ld_dev_d(&rp[cc].w) : ld_dev_d(&rp[cc].sp)) : 0.0;
-      running += block_sum_d(wc);
-    }
-    grand = running;
-    if (!(grand > 0.0) && mode == 0) mode = 1;  // zero residual: draw from p_n
-    else break;
-  }
   const double thr = (double)u * grand;
+  // Locate the chunk holding thr: exclusive prefix over the chunk totals.
   __shared__ double s_P;
   __shared__ int s_cs;
   if (threadIdx.x == 0) { s_cs = C2 - 1; s_P = 0.0; }
   {
     double running = 0.0;
-    int found = 0;
-    for (int base = 0; base < C2 && !found; base += kThreads) {
+    for (int base = 0; base < C2; base += kThreads) {
       const int cc = base + threadIdx.x;
-      const double wc = cc < C2 ? (mode == 0 ? ld_dev_d(&rp[cc].w) : ld_dev_d(&rp[cc].sp)) : 0.0;
-      const double excl = running + block_exclusive_scan_d(wc);
-      const int hit = (cc < C2 && excl + wc > thr) ? cc : INT_MAX;
+      if (n_tiles > 1) load_chunk(cc);  // totals as written back above
+      const double val = cc < C2 ? (use_w ? cw : csp) : 0.0;
+      const double excl = running + block_exclusive_scan_d(val);
+      const int hit = (cc < C2 && excl + val > thr) ? cc : INT_MAX;
+      if (cc == C2 - 1 && hit == INT_MAX) s_P = excl;  // no hit: search the last chunk
       const int first_hit = block_min_i(hit);
       if (first_hit != INT_MAX) {
         if (cc == first_hit) { s_cs = cc; s_P = excl; }
-        found = 1;
-      } else if (cc == C2 - 1) {
-        s_P = excl;  // no hit (last-bit case): search the last chunk from its prefix
+        break;  // block-uniform
       }
-      running += block_sum_d(wc);
+      running += block_sum_d(val);
     }
     __syncthreads();
   }
+  const int mode = use_w ? 0 : 1;
   int t = search_chunk<DT, KIND>(prow, qrow, V, s_cs, mode == 0, c1, c0p, c0q, rho, s_P, thr,
                                  tab);
   if (threadIdx.x == 0) {
@@ -562,9 +699,12 @@ __global__ __launch_bounds__(kThreads) void k_draw(
 
 static int row_chunks(int V) { return (V + kRowChunkElems - 1) / kRowChunkElems; }
 
+// 16-byte loads need every row to start on a 16-byte boundary; the buffer
+// loads of the row-statistics sweep address rows below 2 GiB.
 static bool rows_aligned(const void* p, int V, int dtype) {
-  const int eb = dtype == 1 ? 2 : 4;
-  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && (((long)V * eb) % 16 == 0);
+  const long eb = dtype == 1 ? 2 : 4;
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && (((long)V * eb) % 16 == 0) &&
+         (long)V * eb < (1L << 31);
 }
 
 template <int DT, int NE>
@@ -582,13 +722,16 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   auto* p2 = reinterpret_cast<DrawPart*>(w + L.part2);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const long R = 2L * k + 1;
+  auto* zr = reinterpret_cast<float*>(w + L.zrow);
+  // finalize arrays: double [R] then float [R]
+  const uint32_t lds = static_cast<uint32_t>(R * (sizeof(double) + sizeof(float)));
   hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>,
-                             dim3((unsigned)(B * R * C1)), dim3(kThreads), s, target, draft, k,
-                             V, C1, c, draft_tokens, uniforms, seed, ctr0, accepted_len,
-                             out_tokens, probe, p1, st, cnt);
+                             dim3((unsigned)(B * R * C1)), dim3(kThreads), lds, s, target, draft,
+                             k, V, C1, c, draft_tokens, uniforms, seed, ctr0, accepted_len,
+                             out_tokens, probe, p1, zr, st, cnt);
   if (e != hipSuccess) return e;
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  return launch_timed(kProfDraw, &k_draw<DT, NE, 0>, dim3((unsigned)(B * G2)), dim3(kThreads), s,
+  return launch_timed(kProfDraw, &k_draw<DT, NE, 0>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
                       target, draft, k, V, C2, inv_t, draft_tokens, uniforms, seed, ctr0,
                       accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);
 }
@@ -603,7 +746,7 @@ static hipError_t launch_probs(const void* target, const void* draft, int B, int
   auto* p2 = reinterpret_cast<DrawPart*>(w + L.part2);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  return launch_timed(kProfDraw, &k_draw<0, NE, 1>, dim3((unsigned)(B * G2)), dim3(kThreads), s,
+  return launch_timed(kProfDraw, &k_draw<0, NE, 1>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
                       target, draft, k, V, C2, 1.0, draft_tokens, uniforms, seed, ctr0,
                       accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);
 }

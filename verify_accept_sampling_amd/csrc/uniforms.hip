@@ -17,7 +17,7 @@ hipError_t launch_fill_uniforms(uint64_t seed, uint64_t counter0, int64_t n, flo
                                 hipStream_t s) {
   int64_t blocks = (n + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;
-  return launch_timed(kProfUniforms, &k_fill_uniforms, dim3((unsigned)blocks), dim3(kThreads), s,
+  return launch_timed(kProfUniforms, &k_fill_uniforms, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                       seed, counter0, n, out);
 }
 
