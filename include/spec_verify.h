@@ -25,8 +25,10 @@
  *    outputs are valid once that stream has been synchronised.
  *  - `ws` is a caller-owned device workspace of at least
  *    spec_workspace_bytes(B, n_pos, V) bytes.  It must be zero-filled before
- *    its first use.  Its first 512 KiB hold per-request completion counters
- *    at fixed places, which every call leaves at zero again, so one
+ *    its first use.  Its first SPEC_WORKSPACE_COUNTER_BYTES bytes hold
+ *    per-request completion counters and markers and a call epoch at fixed
+ *    places, which the library keeps consistent from one call to the next
+ *    (the caller must not write to them after the initial zero fill), so one
  *    workspace serves calls of any shape without clearing it; the rest is
  *    scratch that each call writes before reading.  Calls that share a
  *    workspace must be ordered on one stream.
@@ -49,6 +51,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Bytes at the start of every workspace that must be zero before the first
+ * call and are the library's from then on. */
+#define SPEC_WORKSPACE_COUNTER_BYTES (1048576 + 256)
 
 /* Element type of logit / probability tensors. */
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
@@ -165,17 +171,33 @@ int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes,
  * error code if the array is malformed.  Host only. */
 int spec_tree_depth(const int32_t* parent_host, int n_nodes);
 
+/* Which kernels spec_verify_sample uses for raw logits.
+ * SPEC_PATH_AUTO (the default): one launch (SPEC_KERNEL_FUSED) whose row-pass
+ *   work-groups come first and whose draw work-groups each wait for their
+ *   request's acceptance result, so early requests' draws overlap the end of
+ *   the row pass.
+ * SPEC_PATH_TWO_LAUNCH: the row pass (SPEC_KERNEL_ROW_PASS), then the draw
+ *   (SPEC_KERNEL_DRAW).
+ * Both follow the same rule with the same arithmetic.  The setting is
+ * process-wide and applies to calls made after it.  Returns the previous
+ * setting, or SPEC_EINVAL for an unknown mode. */
+enum { SPEC_PATH_AUTO = 0, SPEC_PATH_TWO_LAUNCH = 1 };
+int spec_sample_path(int mode);
+
 /* Optional per-kernel timing for measurement tools (not part of the
  * verification itself).  spec_profile_enable(1) clears the totals and, from
- * then on, brackets every kernel the library enqueues with two HIP events on
- * the same stream; spec_profile_enable(0) stops recording.  spec_profile_read
+ * then on, times every kernel the library enqueues with a start/stop pair of
+ * HIP events on the same stream; spec_profile_enable(0) stops recording.  spec_profile_read
  * waits for the recorded events and returns, for one kernel kind, the number
- * of timed launches and their summed event time in milliseconds.  Kinds: */
+ * of timed launches and their summed event time in milliseconds.  The events
+ * are stamped by each kernel's own dispatch, so an interval covers that
+ * kernel alone.  Kinds: */
 enum {
   SPEC_KERNEL_ROW_PASS = 0, /* row pass over every logit row + per-request finish
                                (acceptance tests, greedy rule, tree walk) */
   SPEC_KERNEL_DRAW = 1,     /* float64 residual / bonus pass + inverse-CDF draw */
-  SPEC_KERNEL_UNIFORMS = 2  /* spec_fill_uniforms */
+  SPEC_KERNEL_UNIFORMS = 2, /* spec_fill_uniforms */
+  SPEC_KERNEL_FUSED = 3     /* one-launch sampling verification: row pass and draw */
 };
 int spec_profile_enable(int on);
 int spec_profile_read(int kind, long* launches, double* total_ms);

@@ -26,7 +26,7 @@ __all__ = [
     "SpecVerifyError", "Workspace", "library_path", "load_library", "declared_symbols",
     "spec_workspace_bytes", "spec_fill_uniforms", "spec_verify_greedy",
     "spec_verify_sample", "spec_verify_tree_greedy", "spec_tree_depth", "spec_strerror",
-    "spec_profile_enable", "spec_profile_read", "KERNEL_KINDS",
+    "spec_profile_enable", "spec_profile_read", "KERNEL_KINDS", "spec_sample_path",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -89,11 +89,24 @@ def load_library():
     lib.spec_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_long),
                                       ctypes.POINTER(ctypes.c_double)]
     lib.spec_profile_read.restype = c_int
+    lib.spec_sample_path.argtypes = [c_int]
+    lib.spec_sample_path.restype = c_int
     _lib = lib
     return lib
 
 
-KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2}
+KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2, "fused": 3}
+SAMPLE_PATHS = {"auto": 0, "two_launch": 1}
+
+
+def spec_sample_path(mode: str) -> str:
+    """Choose the kernels spec_verify_sample uses for raw logits ("auto": one
+    persistent launch where the shape allows it; "two_launch": always the
+    row pass then the draw).  Returns the previous mode."""
+    prev = load_library().spec_sample_path(SAMPLE_PATHS[mode])
+    if prev < 0:
+        _check(prev)
+    return {v: k for k, v in SAMPLE_PATHS.items()}[prev]
 
 
 def spec_profile_enable(on: bool = True) -> None:

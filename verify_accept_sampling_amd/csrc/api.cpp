@@ -3,6 +3,8 @@
 #include <cmath>
 #include <cstring>
 
+#include <atomic>
+
 #include "../../include/spec_verify.h"
 #include "internal.h"
 
@@ -44,7 +46,16 @@ int tree_depth_checked(const int32_t* parent, int n_nodes) {
 
 }  // namespace
 
+namespace specv {
+std::atomic<int> g_sample_path{SPEC_PATH_AUTO};
+}  // namespace specv
+
 extern "C" {
+
+int spec_sample_path(int mode) {
+  if (mode != SPEC_PATH_AUTO && mode != SPEC_PATH_TWO_LAUNCH) return SPEC_EINVAL;
+  return specv::g_sample_path.exchange(mode);
+}
 
 const char* spec_strerror(int code) {
   switch (code) {

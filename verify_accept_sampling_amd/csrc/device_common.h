@@ -214,6 +214,34 @@ __device__ __forceinline__ void ms_merge(float& m, double& s, float m2, double s
   m = mn;
 }
 
+// Wave reduction of (m, s); the result is valid in every lane.
+__device__ __forceinline__ void wave_reduce_ms(float& m, double& s, float c) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = shfl_xor_f(m, o);
+    const double s2 = shfl_xor_d(s, o);
+    ms_merge(m, s, m2, s2, c);
+  }
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += shfl_xor_d(v, o);
+  return v;
+}
+
+// Exclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ double wave_exclusive_scan_d(double v) {
+  const int lane = threadIdx.x & 63;
+  double inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = shfl_up_d(inc, d);
+    if (lane >= d) inc += o;
+  }
+  return inc - v;
+}
+
 // Work-group reduction of (m, s); result valid in thread 0.
 __device__ __forceinline__ void block_reduce_ms(float& m, double& s, float c) {
   __shared__ float sm[kWaves];

@@ -2,10 +2,14 @@
 // kernel translation units.  Not part of the public ABI.
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include "../../include/spec_verify.h"
 
 namespace specv {
 
@@ -75,15 +79,25 @@ struct DrawPart {
   double pad;
 };
 
-// Completion counters per request: [0] row pass, [1] draw pass.
-constexpr int kCountersPerReq = 2;
+// Per-request words of the counter region: [0] row-pass completion
+// ticket, [1] draw completion ticket, [2..3] the one-launch kernel's 64-bit
+// "state published" marker.  After them, the one-launch kernel's control
+// words: [0..1] 64-bit call epoch, [2] count of requests finished in this
+// call.
+constexpr int kCountersPerReq = 4;
+constexpr size_t kControlOffsetWords = (size_t)kMaxB * kCountersPerReq;
+constexpr size_t kCounterRegionBytes = kControlOffsetWords * 4 + 256;
+static_assert(kCounterRegionBytes == SPEC_WORKSPACE_COUNTER_BYTES, "counter region");
 
-// Workspace layout.  The completion counters sit at a fixed place (the
-// first kMaxB * kCountersPerReq words) whatever the call's shape; they must
-// be zero before the first call and every call leaves them at zero.  The
-// other regions are written before they are read within each call.
+// Workspace layout.  The counter region (kCounterRegionBytes) sits at a
+// fixed place whatever the call's shape; it must be zero before the first
+// call.  The completion tickets are left at zero by every call; the
+// one-launch kernel keeps a call epoch there and per-request markers that
+// hold the epoch of the call that wrote them, so stale markers are never
+// taken for new ones.  The other regions are written before they are read
+// within each call.
 struct WsLayout {
-  size_t count;  // uint32 [kMaxB * kCountersPerReq], always at offset 0
+  size_t count;  // counter region, always at offset 0
   size_t part1;  // uint64 [rows * row_chunks]: packed (max, sum) or (value, index)
   size_t zrow;   // float [rows]: each row's logit at its draft token
   size_t state;  // ReqState [B]
@@ -103,7 +117,7 @@ inline WsLayout ws_layout(int B, int n_pos, int V) {
   const size_t rows = (size_t)B * (size_t)n_pos * 2;
   size_t off = 0;
   L.count = off;
-  off = align_up(off + (size_t)kMaxB * kCountersPerReq * 4, 256);
+  off = align_up(off + kCounterRegionBytes, 256);
   L.part1 = off;
   off = align_up(off + rows * (size_t)row_chunks_max(V) * 8, 256);
   L.zrow = off;
@@ -126,7 +140,8 @@ struct TreeArgs {
 constexpr int kProfRowPass = 0;   // row statistics / argmax sweep + per-request finish
 constexpr int kProfDraw = 1;      // float64 residual / bonus pass + inverse-CDF draw
 constexpr int kProfUniforms = 2;  // spec_fill_uniforms
-constexpr int kProfKinds = 3;
+constexpr int kProfFused = 3;     // one-launch sampling verification (row pass + draw)
+constexpr int kProfKinds = 4;
 // While timing is enabled, prof_begin hands out a start/stop event pair that
 // the launch itself stamps (hipExtLaunchKernel records them from the
 // kernel's dispatch, so the interval is the kernel alone); otherwise both
@@ -153,6 +168,9 @@ hipError_t launch_timed(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 bloc
 // Launch wrappers (defined in the .hip files).  Each returns a hipError_t.
 hipError_t launch_fill_uniforms(uint64_t seed, uint64_t counter0, int64_t n,
                                 float* out, hipStream_t s);
+
+// Process-wide choice of the sampling path (spec_sample_path).
+extern std::atomic<int> g_sample_path;
 
 hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int V,
                                const int32_t* draft_tokens, int32_t* accepted_len,

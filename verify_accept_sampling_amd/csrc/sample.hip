@@ -5,15 +5,15 @@
 // rejection and drawing a bonus token when every draft passes (EAGLE-3
 // review "Speculative Decoding" step 3; serving chapter "how it works").
 //
-// Logits path, two launches on the caller's stream:
-//   1. k_row_stats: work-group (chunk, row) streams one chunk of one of the
+// Logits path.  Two kinds of work-group:
+//   1. row pass: work-group (chunk, row) streams one chunk of one of the
 //      request's 2k+1 rows (k+1 target, k draft) with 16-byte non-temporal
 //      loads and reduces it to (max, sum 2^((x - max) c)), c = log2(e)/T, in
 //      float32; it publishes the pair and takes the request's ticket.  The
 //      request's last work-group merges the pairs (float64), evaluates every
 //      acceptance ratio p_i(x_i)/q_i(x_i) from the gathered logits, finds the
 //      first rejection n and writes the accepted prefix and the request state.
-//   2. k_draw: work-group (request, chunk) over the row(s) the final token is
+//   2. draw: work-group (request, chunk group) over the row(s) the final token is
 //      drawn from -- target and draft row n after a rejection, target row k
 //      for the bonus -- in float64: the normaliser partials S_p, S_q and the
 //      draw weights, evaluated at the float32 estimate rho32 of S_p/S_q with
@@ -22,228 +22,31 @@
 //      element sits at the kink of max(0, .), in which case the chunk is
 //      recomputed), locates the chunk holding the inverse-CDF point and
 //      searches it with the exact weights.
+// By default both run in one launch (k_sample_one): the row-pass
+// work-groups first, then the draw work-groups, each of which waits for its
+// request's state, so the draws of early requests overlap the last row-pass
+// work-groups.  The two-launch form (k_row_stats, then k_draw) computes the
+// same thing.
 // Probabilities path (rows given as distributions): k_draw alone, each
 // work-group first repeating the (gather-only) acceptance tests.
-#include <climits>
-
-#include "device_common.h"
-#include "device_math.h"
+#include "sample_device.h"
 
 namespace specv {
 
-constexpr int kUnrollStats = SPEC_STATS_UNROLL;
-
-
-// An element whose two terms differ by less than this fraction (relative to
-// rho32 e^{(y-mq)/T}) may change sides of max(0, .) between rho32 and the
-// float64 rho; its chunk is then recomputed exactly.  rho32 is within about
-// 1e-6 of rho.
-constexpr double kKinkBand = 1e-5;
-
-// Row r of request b: r <= k is target row r, r > k is draft row r-k-1.
-template <int DT>
-__device__ __forceinline__ const void* stat_row(const void* target, const void* draft, int b,
-                                                int r, int k, int V) {
-  const long eb = Elems<DT>::kBytes;
-  if (r <= k)
-    return reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + r) * V * eb;
-  return reinterpret_cast<const char*>(draft) + ((long)b * k + (r - k - 1)) * V * eb;
-}
-
-// ---------------------------------------------------------------------------
-// 1. Row statistics and acceptance
-// ---------------------------------------------------------------------------
-
-// Streaming softmax statistic of a chunk: a reference value m (an element
-// of the chunk) and s = sum 2^(x c - mc) with mc = fl32(m c), the rounded
-// product; merges recompute mc from m, so its rounding cancels exactly.
-// Any reference gives the same statistic, since log p(x) = x c - mc -
-// log2 s; the reference only has to keep the terms finite.  So m is not
-// the running maximum: it is updated only when a batch's sum reaches
-// kBatchLimit (every term of the batch is then below 2^64) and on the first
-// batch that holds a finite value.  Each element costs one fused
-// multiply-add, one exp2 and one add.  Terms are added pairwise within a
-// batch in float32; batch sums are accumulated in float64, because a
-// float32 running sum would absorb the many terms far below its last bit.
-constexpr float kBatchLimit = 0x1p64f;
-
-template <int N>
-__device__ __forceinline__ float batch_sum(const float* x, float c, float mc) {
-  float t[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, -mc));
-#pragma unroll
-  for (int w = 1; w < N; w *= 2)
-#pragma unroll
-    for (int e = 0; e + w < N; e += 2 * w) t[e] += t[e + w];
-  return t[0];
-}
-
-// Sum of one group's terms, moving the reference first when the group holds
-// a value far above it (or the first finite value).
-template <int N>
-__device__ __forceinline__ float group_sum(float& m, float& mc, double& s, const float* x,
-                                           float c) {
-  float g = batch_sum<N>(x, c, mc);
-  if (!(g < kBatchLimit)) {  // rare: no reference yet, or far above it
-    float lm = x[0];
-#pragma unroll
-    for (int e = 1; e < N; ++e) lm = fmaxf(lm, x[e]);
-    if (lm > m) {
-      const float mcn = mul_rn(lm, c);
-      s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f(mc - mcn);
-      m = lm;
-      mc = mcn;
-    }
-    g = (m == -INFINITY) ? 0.f : batch_sum<N>(x, c, mc);
-  }
-  return g;
-}
-
-// Fold kUnrollStats words (one per group) into (m, mc, s): group sums are
-// taken in order (a group may move the reference, which rescales s and
-// every later group), then added pairwise and once to s.
-template <int DT>
-__device__ __forceinline__ void stat_words(float& m, float& mc, double& s, const u32x4 (&w)[kUnrollStats],
-                                           float c) {
-  constexpr int NE = Elems<DT>::kVec;
-  float gs[kUnrollStats];
-  float mc0 = mc;
-#pragma unroll
-  for (int u = 0; u < kUnrollStats; ++u) {
-    float x[NE];
-    unpack16<DT>(w[u], x);
-    gs[u] = group_sum<NE>(m, mc, s, x, c);
-    if (mc != mc0) {  // rare: the reference moved; rescale the earlier groups
-      const float f = (mc0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc0 - mc);
-#pragma unroll
-      for (int v = 0; v < u; ++v) gs[v] *= f;
-      mc0 = mc;
-    }
-  }
-#pragma unroll
-  for (int w2 = 1; w2 < kUnrollStats; w2 *= 2)
-#pragma unroll
-    for (int e = 0; e + w2 < kUnrollStats; e += 2 * w2) gs[e] += gs[e + w2];
-  s += (double)gs[0];
-}
-
-// This thread's groups (16-byte words) [g0, g1) of one row.  Software
-// pipelined: the next iteration's kUnrollStats loads are issued before the
-// current words are folded in, so every wave keeps loads in flight while it
-// computes.
-template <int DT>
-__device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, long g0, long g1,
-                                            float c, float& m, float& mc, double& s) {
-  constexpr int NE = Elems<DT>::kVec;
-  constexpr uint32_t kStep = kThreads * kUnrollStats * 16u;
-  const RowBuf buf(rp, row_bytes);
-  long g = g0 + threadIdx.x;
-  uint32_t off = static_cast<uint32_t>(g) * 16u;
-  const long span = (long)(kUnrollStats - 1) * kThreads;
-  if (g + span < g1) {
-    // Two word buffers used in turn (no register copies, which would wait
-    // for the loads in flight).
-    u32x4 wa[kUnrollStats], wb[kUnrollStats];
-#pragma unroll
-    for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * kThreads * 16u);
-    for (;;) {
-      g += (long)kThreads * kUnrollStats;
-      off += kStep;
-      if (!(g + span < g1)) {
-        stat_words<DT>(m, mc, s, wa, c);
-        break;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnrollStats; ++u) wb[u] = buf.load_nt(off, u * kThreads * 16u);
-      __builtin_amdgcn_sched_barrier(0);
-      stat_words<DT>(m, mc, s, wa, c);
-      g += (long)kThreads * kUnrollStats;
-      off += kStep;
-      if (!(g + span < g1)) {
-        stat_words<DT>(m, mc, s, wb, c);
-        break;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * kThreads * 16u);
-      __builtin_amdgcn_sched_barrier(0);
-      stat_words<DT>(m, mc, s, wb, c);
-    }
-  }
-  for (; g < g1; g += kThreads, off += kThreads * 16u) {
-    float x[NE];
-    unpack16<DT>(buf.load_nt(off, 0), x);
-    const float gsum = group_sum<NE>(m, mc, s, x, c);  // may rescale s first
-    s += (double)gsum;
-  }
-}
-
-// Scalar form for rows that are not 16-byte aligned: elements [e0, e1).
-template <int DT>
-__device__ __forceinline__ void stats_sweep_scalar(const void* rp, long e0, long e1, float c,
-                                                   float& m, float& mc, double& s) {
-  for (long e = e0 + threadIdx.x; e < e1; e += kThreads) {
-    const float x = load_elem<DT>(rp, e);
-    const float gsum = group_sum<1>(m, mc, s, &x, c);  // may rescale s first
-    s += (double)gsum;
-  }
-}
-
-// Fold one chunk partial (reference m2, sum s2 relative to 2^fl32(m2 c))
-// into the row's running (M, S), S = sum 2^(x c - fl32(M c)) in float64.
-__device__ __forceinline__ void fold_partial(float& M, double& S, uint64_t pp, float c) {
-  const float m2 = unpack_lo(pp);
-  const double s2 = (double)unpack_hi(pp);
-  if (m2 == -INFINITY) return;
-  if (M == -INFINITY) {
-    M = m2;
-    S = s2;
-    return;
-  }
-  const float mn = fmaxf(M, m2);
-  const double mcn = (double)mul_rn(mn, c);
-  S = S * exp2((double)mul_rn(M, c) - mcn) + s2 * exp2((double)mul_rn(m2, c) - mcn);
-  M = mn;
-}
-
-// (M, S) of two rows of one request (the second only when has_b) from their
-// chunk partials, by one thread: up to four partials of each row are loaded
-// before any is folded in, so the loads of both rows are in flight together.
-__device__ __forceinline__ void merge_two_rows(const uint64_t* part, long base_a, long base_b,
-                                               bool has_b, int C1, float c, float& Ma,
-                                               double& Sa, float& Mb, double& Sb) {
-  Ma = Mb = -INFINITY;
-  Sa = Sb = 0.0;
-  for (int c0 = 0; c0 < C1; c0 += 4) {
-    uint64_t pa[4], pb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pa[j] = pb[j] = 0;
-      if (c0 + j < C1) {
-        pa[j] = ld_dev(&part[base_a + c0 + j]);
-        if (has_b) pb[j] = ld_dev(&part[base_b + c0 + j]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (c0 + j < C1) {
-        fold_partial(Ma, Sa, pa[j], c);
-        if (has_b) fold_partial(Mb, Sb, pb[j], c);
-      }
-    }
-  }
-}
-
+// Row pass of one work-group: block `bid` of the row-pass grid.  epoch is 0
+// on the two-launch path; in the one-launch kernel it is the call's epoch,
+// and the request's state is followed by a marker holding it.
 template <int DT, int NE>
-__global__ __launch_bounds__(kThreads) void k_row_stats(
-    const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C1,
-    float c, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
-    uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ out_tokens, float* __restrict__ probe, uint64_t* __restrict__ part,
-    float* __restrict__ zrow, ReqState* __restrict__ state, unsigned* __restrict__ counters) {
+__device__ __forceinline__ void row_block(
+    long bid, uint64_t epoch, const void* __restrict__ target, const void* __restrict__ draft,
+    int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
+    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probe, uint64_t* __restrict__ part, float* __restrict__ zrow,
+    ReqState* __restrict__ state, unsigned* __restrict__ counters) {
   const int R = 2 * k + 1;
-  const int chunk = blockIdx.x % C1;
-  const long rowid = blockIdx.x / C1;
+  const int chunk = static_cast<int>(bid % C1);
+  const long rowid = bid / C1;
   const int b = static_cast<int>(rowid / R);
   const int r = static_cast<int>(rowid % R);
   {
@@ -263,8 +66,8 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     if constexpr (NE == 1)
       stats_sweep_scalar<DT>(rp, g0, g1, c, m, mc, s);
     else
-      stats_sweep<DT>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0, g1, c, m, mc,
-                      s);
+      stats_sweep<DT, kThreads>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0, g1,
+                                c, m, mc, s, threadIdx.x);
     // The chunk that holds the token also publishes the logit there.
     const bool own = x >= 0 && x < V && (long)x >= g0 * NE && (long)x < g1 * NE;
     float zx = 0.f;
@@ -320,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     if (!accept) first = min(first, i);
     if (probe) {
       float* pr = probe + ((long)b * (k + 1) + i) * 4;
-      pr[0] = pv; pr[1] = qv; pr[2] = 0.f; pr[3] = 0.f;
+      pr[0] = pv; pr[1] = qv; pr[3] = 0.f;
     }
   }
   const int n = wave_min_i(first);
@@ -328,6 +131,9 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
   for (int i = lane; i <= k; i += kWaveSize) {
     if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
     else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
+    // probe[b, n, 2] (the mass drawn from) belongs to the draw, which may
+    // run in another work-group of the same launch
+    if (probe && i != n) probe[((long)b * (k + 1) + i) * 4 + 2] = 0.f;
   }
   // State for the draw: references of target row n and (rejection) draft
   // row n, and the float32-based normaliser ratio of that pair.
@@ -339,10 +145,14 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     const double sq =
         n < k ? s_s[k + 1 + n] * exp2((double)mul_rn(mq, c) - (double)mq * c) : 1.0;
     accepted_len[b] = n;
-    state[b] = ReqState{n, n < k ? kModeResidual : kModeBonus, mp, mq, sp / sq};
+    st_dev_state(&state[b], ReqState{n, n < k ? kModeResidual : kModeBonus, mp, mq, sp / sq});
+    if (epoch != 0) {
+      wait_stores();  // the state is complete before its marker
+      st_dev(ready_marker(counters, b), epoch);
+    }
     if (probe) {
       float* pr = probe + ((long)b * (k + 1) + k) * 4;
-      pr[0] = 0.f; pr[1] = 0.f; pr[2] = 0.f; pr[3] = 0.f;
+      pr[0] = 0.f; pr[1] = 0.f; pr[3] = 0.f;
     }
   }
 }
@@ -395,162 +205,33 @@ __device__ int accept_scan_probs(const float* target, const float* draft, int b,
   return n;
 }
 
-// ---------------------------------------------------------------------------
-// 2. Float64 draw pass
-// ---------------------------------------------------------------------------
-
-// NN consecutive elements from j0 as floats (NN a multiple of NE); elements
-// at or beyond V read as `fill`.
-template <int DT, int NE, int NN>
-__device__ __forceinline__ void load_run(const void* row, long j0, int V, float fill,
-                                         float (&x)[NN]) {
-  static_assert(NN % NE == 0, "run length must be a multiple of the load width");
-#pragma unroll
-  for (int g = 0; g < NN / NE; ++g) {
-    const long e0 = j0 + (long)g * NE;
-    float t[NE];
-    if (e0 + NE <= V) {
-      load_group<DT, NE>(row, e0, t);
-    } else {
-#pragma unroll
-      for (int e = 0; e < NE; ++e) t[e] = (e0 + e < V) ? load_elem<DT>(row, e0 + e) : fill;
-    }
-#pragma unroll
-    for (int e = 0; e < NE; ++e) x[g * NE + e] = t[e];
-  }
-}
-
-// Float64 term of one element.  KIND 0 (logits): e^{(z - m)/T}, evaluated as
-// 2^(t/64) with t = z c1 + c0, c1 = 64/(T ln 2), c0 = -m c1; KIND 1
-// (probabilities): the value itself.
-template <int KIND>
-__device__ __forceinline__ double draw_term(float z, double c1, double c0, const double* tab) {
-  return KIND == 0 ? exp2_64(fma((double)z, c1, c0), tab) : (double)z;
-}
-
-// Sums of one chunk by one wave (lane l covers the 16 elements from
-// chunk * kDrawChunk + 16 l), reduced across the wave (valid in every lane):
-//   v[0] = sum a, v[1] = sum b (a, b the target and draft terms),
-//   v[2] = sum of the draw weights at rho32 (max(0, a - rho32 b), or a for
-//          the bonus), v[3] = their derivative in rho (minus the sum of b
-//          where the weight is positive), v[4] = 1 if an element lies within
-//          the kink band of max(0, .).
+// Draw of one work-group: block `bid` of the draw grid.  epoch as for
+// row_block: in the one-launch kernel the block first waits for the marker
+// of its request's state.
 template <int DT, int NE, int KIND>
-__device__ __forceinline__ void wave_chunk_sums(const void* prow, const void* qrow, int V,
-                                                int chunk, bool resid, double c1, double c0p,
-                                                double c0q, double rho32, const double* tab,
-                                                double (&v)[5]) {
-  const int lane = threadIdx.x & 63;
-  const long j0 = (long)chunk * kDrawChunk + (long)lane * kSegPerThread;
-  const float fill = KIND == 0 ? -INFINITY : 0.f;
-  float zp[kSegPerThread], zq[kSegPerThread];
-  load_run<DT, NE, kSegPerThread>(prow, j0, V, fill, zp);
-  if (resid) load_run<DT, NE, kSegPerThread>(qrow, j0, V, fill, zq);
-#pragma unroll
-  for (int q = 0; q < 5; ++q) v[q] = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSegPerThread; ++e) {
-    const double a = draw_term<KIND>(zp[e], c1, c0p, tab);
-    v[0] += a;
-    if (resid) {
-      const double bq = draw_term<KIND>(zq[e], c1, c0q, tab);
-      v[1] += bq;
-      const double d = a - rho32 * bq;
-      if (d > 0.0) {
-        v[2] += d;
-        v[3] -= bq;
-      }
-      if (KIND == 0 && bq > 0.0 && fabs(d) <= kKinkBand * rho32 * bq) v[4] = 1.0;
-    } else {
-      v[2] += a;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-#pragma unroll
-    for (int q = 0; q < 5; ++q) v[q] += shfl_xor_d(v[q], o);
-  }
-}
-
-// kSearchPerThread consecutive elements of a chunk for this thread of a
-// whole work-group: [chunk * kDrawChunk + kSearchPerThread t, ...).
-template <int DT, int KIND>
-__device__ __forceinline__ void search_terms(const void* prow, const void* qrow, int V, int chunk,
-                                             bool resid, double c1, double c0p, double c0q,
-                                             double rho, const double* tab,
-                                             double (&w)[kSearchPerThread], long& j0) {
-  j0 = (long)chunk * kDrawChunk + (long)threadIdx.x * kSearchPerThread;
-  const float fill = KIND == 0 ? -INFINITY : 0.f;
-  float zp[kSearchPerThread], zq[kSearchPerThread];
-#pragma unroll
-  for (int e = 0; e < kSearchPerThread; ++e) {
-    zp[e] = (j0 + e < V) ? load_elem<DT>(prow, j0 + e) : fill;
-    zq[e] = (resid && j0 + e < V) ? load_elem<DT>(qrow, j0 + e) : fill;
-  }
-  // Runs once per request on a cold instruction cache: rolled.
-#pragma unroll 1
-  for (int e = 0; e < kSearchPerThread; ++e) {
-    const double a = draw_term<KIND>(zp[e], c1, c0p, tab);
-    w[e] = resid ? fmax(0.0, a - rho * draw_term<KIND>(zq[e], c1, c0q, tab)) : a;
-  }
-}
-
-// Search one chunk with the exact weights.  Returns the first element whose
-// running sum, added to the prefix P of the earlier chunks, exceeds thr,
-// falling back to the chunk's last positive-weight element (reachable only
-// through a last-bit difference between the chunk total used to locate it
-// and the sums here).
-template <int DT, int KIND>
-__device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk, bool resid,
-                            double c1, double c0p, double c0q, double rho, double P, double thr,
-                            const double* tab) {
-  double w[kSearchPerThread];
-  long j0;
-  search_terms<DT, KIND>(prow, qrow, V, chunk, resid, c1, c0p, c0q, rho, tab, w, j0);
-  double tsum = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSearchPerThread; ++e) tsum += w[e];
-  const double excl = block_exclusive_scan_d(tsum);
-  int tok = INT_MAX, lastpos = -1;
-  double run = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSearchPerThread; ++e) {
-    run += w[e];
-    if (j0 + e < V) {
-      if (w[e] > 0.0) lastpos = static_cast<int>(j0 + e);
-      if (tok == INT_MAX && P + (excl + run) > thr) tok = static_cast<int>(j0 + e);
-    }
-  }
-  tok = block_min_i(tok);
-  lastpos = -block_min_i(-lastpos);
-  return tok == INT_MAX ? lastpos : tok;
-}
-
-// Wait until this wave's earlier stores have completed.
-__device__ __forceinline__ void wait_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-template <int DT, int NE, int KIND>
-__global__ __launch_bounds__(kThreads) void k_draw(
-    const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C2,
-    double inv_t, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
-    uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ out_tokens, float* __restrict__ probe,
-    const ReqState* __restrict__ state, DrawPart* __restrict__ part,
-    unsigned* __restrict__ counters) {
+__device__ __forceinline__ void draw_block(
+    long bid, uint64_t epoch, const void* __restrict__ target, const void* __restrict__ draft,
+    int k, int V, int C2, double inv_t, const int32_t* __restrict__ draft_tokens,
+    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probe, const ReqState* __restrict__ state, DrawPart* __restrict__ part,
+    unsigned* __restrict__ counters, unsigned* __restrict__ control, int B) {
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  const int b = blockIdx.x / G2;
-  const int grp = blockIdx.x % G2;
+  const int b = static_cast<int>(bid / G2);
+  const int grp = static_cast<int>(bid % G2);
   __shared__ double tab[64];
   if (KIND == 0 && threadIdx.x < 64) tab[threadIdx.x] = kExp2Frac64[threadIdx.x];
   int n;
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
-    const ReqState st = state[b];
-    n = st.n;
+    if (epoch != 0) {
+      __shared__ int s_ok;
+      if (threadIdx.x == 0) s_ok = wait_marker(ready_marker(counters, b), epoch) ? 1 : 0;
+      __syncthreads();
+      if (!s_ok) return;  // never expected: the request's state did not appear
+    }
+    const ReqState st = ld_dev_state(&state[b]);
+    n = min(max(st.n, 0), k);  // always a valid row index
     mp = st.mp;
     mq = st.mq;
     rho32 = st.rho32;
@@ -690,7 +371,67 @@ __global__ __launch_bounds__(kThreads) void k_draw(
       else mass = mode == 0 ? grand : (resid ? 0.0 : grand);
       probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
+    if (epoch != 0) {
+      // The request that finishes last advances the epoch for the next call.
+      const unsigned done =
+          __hip_atomic_fetch_add(&control[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == (unsigned)B - 1u) {
+        __hip_atomic_store(&control[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_dev(reinterpret_cast<uint64_t*>(control), epoch);
+      }
+    }
   }
+}
+
+// Two-launch path: the row pass, then the draw.
+template <int DT, int NE>
+__global__ __launch_bounds__(kThreads) void k_row_stats(
+    const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C1,
+    float c, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
+    uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ out_tokens, float* __restrict__ probe, uint64_t* __restrict__ part,
+    float* __restrict__ zrow, ReqState* __restrict__ state, unsigned* __restrict__ counters) {
+  row_block<DT, NE>(blockIdx.x, 0, target, draft, k, V, C1, c, draft_tokens, uniforms, seed, ctr0,
+                    accepted_len, out_tokens, probe, part, zrow, state, counters);
+}
+
+template <int DT, int NE, int KIND>
+__global__ __launch_bounds__(kThreads) void k_draw(
+    const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C2,
+    double inv_t, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
+    uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ out_tokens, float* __restrict__ probe,
+    const ReqState* __restrict__ state, DrawPart* __restrict__ part,
+    unsigned* __restrict__ counters) {
+  draw_block<DT, NE, KIND>(blockIdx.x, 0, target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
+                           seed, ctr0, accepted_len, out_tokens, probe, state, part, counters,
+                           nullptr, 0);
+}
+
+// One-launch path: the row-pass work-groups, then the draw work-groups
+// (request by request).  Work-groups are dispatched in index order, so
+// every row-pass work-group has been dispatched before a draw work-group
+// takes a slot, and a draw work-group only waits for row-pass work of its
+// own request: the wait ends.  Early requests' draws run while the last
+// row-pass work-groups stream.
+template <int DT, int NE>
+__global__ __launch_bounds__(kThreads) void k_sample_one(
+    const void* __restrict__ target, const void* __restrict__ draft, int B, int k, int V, int C1,
+    int C2, float c, double inv_t, const int32_t* __restrict__ draft_tokens,
+    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probe, uint64_t* __restrict__ part1, float* __restrict__ zrow,
+    ReqState* __restrict__ state, DrawPart* __restrict__ part2, unsigned* __restrict__ counters,
+    unsigned* __restrict__ control, long n_row_blocks) {
+  // This call's markers carry the epoch after the stored one.
+  const uint64_t epoch = ld_dev(reinterpret_cast<const uint64_t*>(control)) + 1;
+  if ((long)blockIdx.x < n_row_blocks)
+    row_block<DT, NE>(blockIdx.x, epoch, target, draft, k, V, C1, c, draft_tokens, uniforms, seed,
+                      ctr0, accepted_len, out_tokens, probe, part1, zrow, state, counters);
+  else
+    draw_block<DT, NE, 0>((long)blockIdx.x - n_row_blocks, epoch, target, draft, k, V, C2, inv_t,
+                          draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe,
+                          state, part2, counters, control, B);
 }
 
 // ---------------------------------------------------------------------------
@@ -725,12 +466,20 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   auto* zr = reinterpret_cast<float*>(w + L.zrow);
   // finalize arrays: double [R] then float [R]
   const uint32_t lds = static_cast<uint32_t>(R * (sizeof(double) + sizeof(float)));
-  hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>,
-                             dim3((unsigned)(B * R * C1)), dim3(kThreads), lds, s, target, draft,
-                             k, V, C1, c, draft_tokens, uniforms, seed, ctr0, accepted_len,
-                             out_tokens, probe, p1, zr, st, cnt);
-  if (e != hipSuccess) return e;
+  const long n_row = (long)B * R * C1;
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  if (g_sample_path.load(std::memory_order_relaxed) == SPEC_PATH_AUTO) {
+    unsigned* control = cnt + kControlOffsetWords;
+    return launch_timed(kProfFused, &k_sample_one<DT, NE>, dim3((unsigned)(n_row + (long)B * G2)),
+                        dim3(kThreads), lds, s, target, draft, B, k, V, C1, C2, c, inv_t,
+                        draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1,
+                        zr, st, p2, cnt, control, n_row);
+  }
+  hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>, dim3((unsigned)n_row),
+                             dim3(kThreads), lds, s, target, draft, k, V, C1, c, draft_tokens,
+                             uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1, zr, st,
+                             cnt);
+  if (e != hipSuccess) return e;
   return launch_timed(kProfDraw, &k_draw<DT, NE, 0>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
                       target, draft, k, V, C2, inv_t, draft_tokens, uniforms, seed, ctr0,
                       accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);

@@ -1,0 +1,393 @@
+// Device routines of the sampling verification kernels: the float32 row
+// statistic and its sweep, the float64 draw terms and chunk sums, the chunk
+// search of the inverse-CDF draw, and the coherent state and markers the
+// one-launch kernel passes between work-groups.
+#pragma once
+
+#include <climits>
+
+#include "device_common.h"
+#include "device_math.h"
+
+namespace specv {
+
+constexpr int kUnrollStats = SPEC_STATS_UNROLL;
+
+
+// An element whose two terms differ by less than this fraction (relative to
+// rho32 e^{(y-mq)/T}) may change sides of max(0, .) between rho32 and the
+// float64 rho; its chunk is then recomputed exactly.  rho32 is within about
+// 1e-6 of rho.
+constexpr double kKinkBand = 1e-5;
+
+// Row r of request b: r <= k is target row r, r > k is draft row r-k-1.
+template <int DT>
+__device__ __forceinline__ const void* stat_row(const void* target, const void* draft, int b,
+                                                int r, int k, int V) {
+  const long eb = Elems<DT>::kBytes;
+  if (r <= k)
+    return reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + r) * V * eb;
+  return reinterpret_cast<const char*>(draft) + ((long)b * k + (r - k - 1)) * V * eb;
+}
+
+// ---------------------------------------------------------------------------
+// 1. Row statistics and acceptance
+// ---------------------------------------------------------------------------
+
+// Streaming softmax statistic of a chunk: a reference value m (an element
+// of the chunk) and s = sum 2^(x c - mc) with mc = fl32(m c), the rounded
+// product; merges recompute mc from m, so its rounding cancels exactly.
+// Any reference gives the same statistic, since log p(x) = x c - mc -
+// log2 s; the reference only has to keep the terms finite.  So m is not
+// the running maximum: it is updated only when a batch's sum reaches
+// kBatchLimit (every term of the batch is then below 2^64) and on the first
+// batch that holds a finite value.  Each element costs one fused
+// multiply-add, one exp2 and one add.  Terms are added pairwise within a
+// batch in float32; batch sums are accumulated in float64, because a
+// float32 running sum would absorb the many terms far below its last bit.
+constexpr float kBatchLimit = 0x1p64f;
+
+template <int N>
+__device__ __forceinline__ float batch_sum(const float* x, float c, float mc) {
+  float t[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) t[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, -mc));
+#pragma unroll
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int e = 0; e + w < N; e += 2 * w) t[e] += t[e + w];
+  return t[0];
+}
+
+// Sum of one group's terms, moving the reference first when the group holds
+// a value far above it (or the first finite value).
+template <int N>
+__device__ __forceinline__ float group_sum(float& m, float& mc, double& s, const float* x,
+                                           float c) {
+  float g = batch_sum<N>(x, c, mc);
+  if (!(g < kBatchLimit)) {  // rare: no reference yet, or far above it
+    float lm = x[0];
+#pragma unroll
+    for (int e = 1; e < N; ++e) lm = fmaxf(lm, x[e]);
+    if (lm > m) {
+      const float mcn = mul_rn(lm, c);
+      s = (m == -INFINITY) ? 0.0 : s * (double)__builtin_amdgcn_exp2f(mc - mcn);
+      m = lm;
+      mc = mcn;
+    }
+    g = (m == -INFINITY) ? 0.f : batch_sum<N>(x, c, mc);
+  }
+  return g;
+}
+
+// Fold kUnrollStats words (one per group) into (m, mc, s): group sums are
+// taken in order (a group may move the reference, which rescales s and
+// every later group), then added pairwise and once to s.
+template <int DT>
+__device__ __forceinline__ void stat_words(float& m, float& mc, double& s, const u32x4 (&w)[kUnrollStats],
+                                           float c) {
+  constexpr int NE = Elems<DT>::kVec;
+  float gs[kUnrollStats];
+  float mc0 = mc;
+#pragma unroll
+  for (int u = 0; u < kUnrollStats; ++u) {
+    float x[NE];
+    unpack16<DT>(w[u], x);
+    gs[u] = group_sum<NE>(m, mc, s, x, c);
+    if (mc != mc0) {  // rare: the reference moved; rescale the earlier groups
+      const float f = (mc0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc0 - mc);
+#pragma unroll
+      for (int v = 0; v < u; ++v) gs[v] *= f;
+      mc0 = mc;
+    }
+  }
+#pragma unroll
+  for (int w2 = 1; w2 < kUnrollStats; w2 *= 2)
+#pragma unroll
+    for (int e = 0; e + w2 < kUnrollStats; e += 2 * w2) gs[e] += gs[e + w2];
+  s += (double)gs[0];
+}
+
+// Groups (16-byte words) [g0, g1) of one row shared by NT threads; this
+// thread (index tid) takes every NT-th word.  Software pipelined: the next
+// iteration's kUnrollStats loads are issued before the current words are
+// folded in, so every wave keeps loads in flight while it computes.
+template <int DT, int NT>
+__device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, long g0, long g1,
+                                            float c, float& m, float& mc, double& s, int tid) {
+  constexpr int NE = Elems<DT>::kVec;
+  constexpr uint32_t kStep = NT * kUnrollStats * 16u;
+  const RowBuf buf(rp, row_bytes);
+  long g = g0 + tid;
+  uint32_t off = static_cast<uint32_t>(g) * 16u;
+  const long span = (long)(kUnrollStats - 1) * NT;
+  if (g + span < g1) {
+    // Two word buffers used in turn (no register copies, which would wait
+    // for the loads in flight).
+    u32x4 wa[kUnrollStats], wb[kUnrollStats];
+#pragma unroll
+    for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
+    for (;;) {
+      g += (long)NT * kUnrollStats;
+      off += kStep;
+      if (!(g + span < g1)) {
+        stat_words<DT>(m, mc, s, wa, c);
+        break;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnrollStats; ++u) wb[u] = buf.load_nt(off, u * NT * 16u);
+      __builtin_amdgcn_sched_barrier(0);
+      stat_words<DT>(m, mc, s, wa, c);
+      g += (long)NT * kUnrollStats;
+      off += kStep;
+      if (!(g + span < g1)) {
+        stat_words<DT>(m, mc, s, wb, c);
+        break;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
+      __builtin_amdgcn_sched_barrier(0);
+      stat_words<DT>(m, mc, s, wb, c);
+    }
+  }
+  for (; g < g1; g += NT, off += NT * 16u) {
+    float x[NE];
+    unpack16<DT>(buf.load_nt(off, 0), x);
+    const float gsum = group_sum<NE>(m, mc, s, x, c);  // may rescale s first
+    s += (double)gsum;
+  }
+}
+
+// Scalar form for rows that are not 16-byte aligned: elements [e0, e1).
+template <int DT>
+__device__ __forceinline__ void stats_sweep_scalar(const void* rp, long e0, long e1, float c,
+                                                   float& m, float& mc, double& s) {
+  for (long e = e0 + threadIdx.x; e < e1; e += kThreads) {
+    const float x = load_elem<DT>(rp, e);
+    const float gsum = group_sum<1>(m, mc, s, &x, c);  // may rescale s first
+    s += (double)gsum;
+  }
+}
+
+// Fold one chunk partial (reference m2, sum s2 relative to 2^fl32(m2 c))
+// into the row's running (M, S), S = sum 2^(x c - fl32(M c)) in float64.
+__device__ __forceinline__ void fold_partial(float& M, double& S, uint64_t pp, float c) {
+  const float m2 = unpack_lo(pp);
+  const double s2 = (double)unpack_hi(pp);
+  if (m2 == -INFINITY) return;
+  if (M == -INFINITY) {
+    M = m2;
+    S = s2;
+    return;
+  }
+  const float mn = fmaxf(M, m2);
+  const double mcn = (double)mul_rn(mn, c);
+  S = S * exp2((double)mul_rn(M, c) - mcn) + s2 * exp2((double)mul_rn(m2, c) - mcn);
+  M = mn;
+}
+
+// (M, S) of two rows of one request (the second only when has_b) from their
+// chunk partials, by one thread: up to four partials of each row are loaded
+// before any is folded in, so the loads of both rows are in flight together.
+__device__ __forceinline__ void merge_two_rows(const uint64_t* part, long base_a, long base_b,
+                                               bool has_b, int C1, float c, float& Ma,
+                                               double& Sa, float& Mb, double& Sb) {
+  Ma = Mb = -INFINITY;
+  Sa = Sb = 0.0;
+  for (int c0 = 0; c0 < C1; c0 += 4) {
+    uint64_t pa[4], pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pa[j] = pb[j] = 0;
+      if (c0 + j < C1) {
+        pa[j] = ld_dev(&part[base_a + c0 + j]);
+        if (has_b) pb[j] = ld_dev(&part[base_b + c0 + j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (c0 + j < C1) {
+        fold_partial(Ma, Sa, pa[j], c);
+        if (has_b) fold_partial(Mb, Sb, pb[j], c);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. Float64 draw pass
+// ---------------------------------------------------------------------------
+
+// NN consecutive elements from j0 as floats (NN a multiple of NE); elements
+// at or beyond V read as `fill`.
+template <int DT, int NE, int NN>
+__device__ __forceinline__ void load_run(const void* row, long j0, int V, float fill,
+                                         float (&x)[NN]) {
+  static_assert(NN % NE == 0, "run length must be a multiple of the load width");
+#pragma unroll
+  for (int g = 0; g < NN / NE; ++g) {
+    const long e0 = j0 + (long)g * NE;
+    float t[NE];
+    if (e0 + NE <= V) {
+      load_group<DT, NE>(row, e0, t);
+    } else {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) t[e] = (e0 + e < V) ? load_elem<DT>(row, e0 + e) : fill;
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) x[g * NE + e] = t[e];
+  }
+}
+
+// Float64 term of one element.  KIND 0 (logits): e^{(z - m)/T}, evaluated as
+// 2^(t/64) with t = z c1 + c0, c1 = 64/(T ln 2), c0 = -m c1; KIND 1
+// (probabilities): the value itself.
+template <int KIND>
+__device__ __forceinline__ double draw_term(float z, double c1, double c0, const double* tab) {
+  return KIND == 0 ? exp2_64(fma((double)z, c1, c0), tab) : (double)z;
+}
+
+// Sums of one chunk by one wave (lane l covers the 16 elements from
+// chunk * kDrawChunk + 16 l), reduced across the wave (valid in every lane):
+//   v[0] = sum a, v[1] = sum b (a, b the target and draft terms),
+//   v[2] = sum of the draw weights at rho32 (max(0, a - rho32 b), or a for
+//          the bonus), v[3] = their derivative in rho (minus the sum of b
+//          where the weight is positive), v[4] = 1 if an element lies within
+//          the kink band of max(0, .).
+template <int DT, int NE, int KIND>
+__device__ __forceinline__ void wave_chunk_sums(const void* prow, const void* qrow, int V,
+                                                int chunk, bool resid, double c1, double c0p,
+                                                double c0q, double rho32, const double* tab,
+                                                double (&v)[5]) {
+  const int lane = threadIdx.x & 63;
+  const long j0 = (long)chunk * kDrawChunk + (long)lane * kSegPerThread;
+  const float fill = KIND == 0 ? -INFINITY : 0.f;
+  float zp[kSegPerThread], zq[kSegPerThread];
+  load_run<DT, NE, kSegPerThread>(prow, j0, V, fill, zp);
+  if (resid) load_run<DT, NE, kSegPerThread>(qrow, j0, V, fill, zq);
+#pragma unroll
+  for (int q = 0; q < 5; ++q) v[q] = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSegPerThread; ++e) {
+    const double a = draw_term<KIND>(zp[e], c1, c0p, tab);
+    v[0] += a;
+    if (resid) {
+      const double bq = draw_term<KIND>(zq[e], c1, c0q, tab);
+      v[1] += bq;
+      const double d = a - rho32 * bq;
+      if (d > 0.0) {
+        v[2] += d;
+        v[3] -= bq;
+      }
+      if (KIND == 0 && bq > 0.0 && fabs(d) <= kKinkBand * rho32 * bq) v[4] = 1.0;
+    } else {
+      v[2] += a;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int q = 0; q < 5; ++q) v[q] += shfl_xor_d(v[q], o);
+  }
+}
+
+// kSearchPerThread consecutive elements of a chunk for this thread of a
+// whole work-group: [chunk * kDrawChunk + kSearchPerThread t, ...).
+template <int DT, int KIND>
+__device__ __forceinline__ void search_terms(const void* prow, const void* qrow, int V, int chunk,
+                                             bool resid, double c1, double c0p, double c0q,
+                                             double rho, const double* tab,
+                                             double (&w)[kSearchPerThread], long& j0) {
+  j0 = (long)chunk * kDrawChunk + (long)threadIdx.x * kSearchPerThread;
+  const float fill = KIND == 0 ? -INFINITY : 0.f;
+  float zp[kSearchPerThread], zq[kSearchPerThread];
+#pragma unroll
+  for (int e = 0; e < kSearchPerThread; ++e) {
+    zp[e] = (j0 + e < V) ? load_elem<DT>(prow, j0 + e) : fill;
+    zq[e] = (resid && j0 + e < V) ? load_elem<DT>(qrow, j0 + e) : fill;
+  }
+  // Runs once per request on a cold instruction cache: rolled.
+#pragma unroll 1
+  for (int e = 0; e < kSearchPerThread; ++e) {
+    const double a = draw_term<KIND>(zp[e], c1, c0p, tab);
+    w[e] = resid ? fmax(0.0, a - rho * draw_term<KIND>(zq[e], c1, c0q, tab)) : a;
+  }
+}
+
+// Search one chunk with the exact weights.  Returns the first element whose
+// running sum, added to the prefix P of the earlier chunks, exceeds thr,
+// falling back to the chunk's last positive-weight element (reachable only
+// through a last-bit difference between the chunk total used to locate it
+// and the sums here).
+template <int DT, int KIND>
+__device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk, bool resid,
+                            double c1, double c0p, double c0q, double rho, double P, double thr,
+                            const double* tab) {
+  double w[kSearchPerThread];
+  long j0;
+  search_terms<DT, KIND>(prow, qrow, V, chunk, resid, c1, c0p, c0q, rho, tab, w, j0);
+  double tsum = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSearchPerThread; ++e) tsum += w[e];
+  const double excl = block_exclusive_scan_d(tsum);
+  int tok = INT_MAX, lastpos = -1;
+  double run = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSearchPerThread; ++e) {
+    run += w[e];
+    if (j0 + e < V) {
+      if (w[e] > 0.0) lastpos = static_cast<int>(j0 + e);
+      if (tok == INT_MAX && P + (excl + run) > thr) tok = static_cast<int>(j0 + e);
+    }
+  }
+  tok = block_min_i(tok);
+  lastpos = -block_min_i(-lastpos);
+  return tok == INT_MAX ? lastpos : tok;
+}
+
+// Per-request marker of the one-launch kernel: set to the call's epoch once
+// the request's state (acceptance result) is published.
+__device__ __forceinline__ uint64_t* ready_marker(unsigned* counters, int b) {
+  return reinterpret_cast<uint64_t*>(&counters[(long)b * kCountersPerReq + 2]);
+}
+
+// ReqState through coherent 64-bit words (read by other work-groups).
+__device__ __forceinline__ void st_dev_state(ReqState* p, const ReqState& v) {
+  static_assert(sizeof(ReqState) == 24, "ReqState layout");
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(&v);
+  uint64_t* d = reinterpret_cast<uint64_t*>(p);
+  st_dev(&d[0], w[0]);
+  st_dev(&d[1], w[1]);
+  st_dev(&d[2], w[2]);
+}
+__device__ __forceinline__ ReqState ld_dev_state(const ReqState* p) {
+  ReqState v;
+  uint64_t* w = reinterpret_cast<uint64_t*>(&v);
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(p);
+  w[0] = ld_dev(&s[0]);
+  w[1] = ld_dev(&s[1]);
+  w[2] = ld_dev(&s[2]);
+  return v;
+}
+
+// Polls of a marker before a wait gives up (about a second; a legitimate
+// wait lasts microseconds).
+constexpr long kSpinLimit = 1L << 20;
+
+// One thread waits until *marker == epoch.  False if the bound is reached.
+__device__ __forceinline__ bool wait_marker(const uint64_t* marker, uint64_t epoch) {
+  for (long spin = 0; spin < kSpinLimit; ++spin) {
+    if (ld_dev(marker) == epoch) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
+// Wait until this wave's earlier stores have completed.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+}  // namespace specv
