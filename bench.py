@@ -8,14 +8,17 @@ distribution, uniforms from the SplitMix64 counter (fresh per step).
 
 One step = one spec_verify_sample call: the float32 row-statistics pass over
 all 17 rows per request, the float64 min(1, p/q) tests, and the float64
-residual / bonus draw.  Inputs are resident in HBM; `--copies` input copies
-are rotated so the 256 MB Infinity Cache cannot serve a step from the
-previous one.
+residual / bonus draw -- by default in one launch (k_sample_one), with
+--path two_launch as the row pass then the draw.  Inputs are resident in
+HBM; `--copies` input copies are rotated so the 256 MB Infinity Cache cannot
+serve a step from the previous one.
 
 Prints one JSON line: verified positions per second (B * (k+1) target
-positions per step) and, for the dominant kernel (the row-statistics pass),
-algorithmic HBM bytes per launch over its average event-timed duration
-against the 8 TB/s peak; plus the float64 oracle timed on the host.
+positions per step) and, for the dominant kernel, algorithmic HBM bytes per
+launch (every logit row once, plus the rows each request draws from and the
+searched chunk) over its average duration, timed with events that each
+launch stamps from its own dispatch, against the 8 TB/s peak; plus the
+float64 oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -32,12 +35,24 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B=64 k=8 V=128256"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_b64_k8_v128256_traffic.json")
-# Algorithmic bytes of one row-statistics launch at this workload: every
-# logit of the 2k+1 = 17 rows of all 64 requests read once (bf16).
+# Dominant kernel of each path, and the committed rocprofv3 counter summary of
+# its HBM traffic at this workload.
+KERNELS = {"auto": "k_sample_one", "two_launch": "k_row_stats"}
+
+
+def traffic_file(kernel: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_b64_k8_v128256_traffic.json")
+
+
+# Algorithmic bytes of the row pass at this workload: every logit of the
+# 2k+1 = 17 rows of all 64 requests read once (bf16).
 ALGO_ROW_BYTES = 64 * 17 * 128256 * 2
+# Elements of the chunk the inverse-CDF search reads again.
+DRAW_CHUNK = 1024
 KERNEL_SOURCES = ["verify_accept_sampling_amd/csrc/sample.hip",
+                  "verify_accept_sampling_amd/csrc/sample_device.h",
                   "verify_accept_sampling_amd/csrc/device_common.h",
+                  "verify_accept_sampling_amd/csrc/device_math.h",
                   "verify_accept_sampling_amd/csrc/internal.h"]
 
 
@@ -49,11 +64,11 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the row-statistics kernel from the committed
-    rocprofv3 counter summary, or None if absent or taken on other sources."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if absent or taken on other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -62,10 +77,10 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def _pmc_means(csv_path: str, counter: str):
-    """Mean per-dispatch value of `counter` for the row-statistics kernel
-    and for the calibration copy (torch's elementwise negation kernel), from
-    a rocprofv3 --pmc CSV."""
+def _pmc_means(csv_path: str, counter: str, kernel: str):
+    """Mean per-dispatch value of `counter` for `kernel` and for the
+    calibration copy (torch's elementwise negation kernel), from a rocprofv3
+    --pmc CSV."""
     import csv
 
     acc = {"row": [], "copy": []}
@@ -74,29 +89,29 @@ def _pmc_means(csv_path: str, counter: str):
             if rec["Counter_Name"] != counter:
                 continue
             name = rec["Kernel_Name"]
-            key = "row" if "k_row_stats" in name else "copy" if "neg_kernel" in name else None
+            key = "row" if kernel in name else "copy" if "neg_kernel" in name else None
             if key:
                 acc[key].append(float(rec["Counter_Value"]))
     if not acc["row"] or not acc["copy"]:
-        raise SystemExit(f"{csv_path}: no {counter} rows for k_row_stats and the copy kernel")
+        raise SystemExit(f"{csv_path}: no {counter} rows for {kernel} and the copy kernel")
     return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str):
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, kernel: str):
     """Turn the FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch) into HBM
-    bytes per row-statistics launch.  Each counter is scaled by what it reads
+    bytes per launch of `kernel`.  Each counter is scaled by what it reads
     for a plain elementwise copy of copy_mib MiB (which reads and writes
     exactly that many bytes), and the result is written next to the
     kernel-source hash it was taken on."""
     nbytes = copy_mib * 1024 * 1024
-    fetch, nf = _pmc_means(fetch_csv, "FETCH_SIZE")
-    write, nw = _pmc_means(write_csv, "WRITE_SIZE")
+    fetch, nf = _pmc_means(fetch_csv, "FETCH_SIZE", kernel)
+    write, nw = _pmc_means(write_csv, "WRITE_SIZE", kernel)
     f_scale = nbytes / (fetch["copy"] * 1024.0)
     w_scale = nbytes / (write["copy"] * 1024.0)
     rd = fetch["row"] * 1024.0 * f_scale
     wr = write["row"] * 1024.0 * w_scale
     out = {
-        "kernel": "k_row_stats", "workload": "B=64 k=8 V=128256 bf16",
+        "kernel": kernel, "workload": "B=64 k=8 V=128256 bf16",
         "kernel_source_sha": kernel_source_sha(),
         "fetch_kib_per_dispatch": fetch["row"], "write_kib_per_dispatch": write["row"],
         "copy_bytes": nbytes, "copy_fetch_kib": fetch["copy"], "copy_write_kib": write["copy"],
@@ -104,10 +119,9 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str):
         "dispatches": {"fetch_pass": nf, "write_pass": nw},
         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
         "hbm_bytes_per_launch": rd + wr,
-        "algorithmic_bytes_per_launch": ALGO_ROW_BYTES,
         "command": command,
     }
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(kernel), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -155,11 +169,14 @@ def main():
                     help="host only: turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) "
                          "into the row-statistics traffic file")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
+    ap.add_argument("--path", choices=sorted(KERNELS), default="auto",
+                    help="auto: the one-launch kernel; two_launch: row pass, then draw")
     args = ap.parse_args()
     if args.summarize_pmc:
         if args.copy_calibration_mib <= 0:
             raise SystemExit("--summarize-pmc needs --copy-calibration-mib of the profiled runs")
-        summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.pmc_command)
+        summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.pmc_command,
+                      KERNELS[args.path])
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -175,6 +192,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    S.spec_sample_path(args.path)
     print("bench: generating B=64 k=8 V=128256 bf16 workload", file=sys.stderr, flush=True)
     wl = W.sample_chain_llama3()
     B, k, V = wl.B, wl.k, wl.V
@@ -223,9 +241,10 @@ def main():
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
     kern = {}
-    for name in ("row_pass", "draw"):
+    for name in ("fused", "row_pass", "draw"):
         n, ms = S.spec_profile_read(name)
-        kern[name] = {"launches": n, "avg_us": (ms / n * 1e3) if n else None}
+        if n:
+            kern[name] = {"launches": n, "avg_us": ms / n * 1e3}
     print(f"bench: timed {args.steps} steps, {ms_step * 1e3:.1f} us/step", file=sys.stderr,
           flush=True)
 
@@ -233,13 +252,19 @@ def main():
     row_bytes = V * 2
     pass1_bytes = B * (2 * k + 1) * row_bytes
     assert pass1_bytes == ALGO_ROW_BYTES
-    rejected = (acc_all < k).sum(axis=1)
-    draw_bytes = (rejected * 2 + (B - rejected)) * row_bytes
-    search_bytes = (rejected * 2 + (B - rejected)) * min(V, 4096) * 2
-    step_bytes = float(np.mean(pass1_bytes + draw_bytes + search_bytes))
-    avg_row_us = kern["row_pass"]["avg_us"]
-    achieved = pass1_bytes / (avg_row_us * 1e-6) / 1e9
-    traffic = measured_traffic()
+    # rows the final token is drawn from: target and draft row n after a
+    # rejection, target row k for the bonus; each read once more, plus the
+    # searched chunk of each
+    drawn_rows = (acc_all < k).sum(axis=1) + B
+    draw_bytes = drawn_rows * row_bytes + drawn_rows * min(V, DRAW_CHUNK) * 2
+    step_bytes = float(np.mean(pass1_bytes + draw_bytes))
+    kernel = KERNELS[args.path]
+    if args.path == "auto":
+        dom, dom_bytes = kern["fused"]["avg_us"], step_bytes
+    else:
+        dom, dom_bytes = kern["row_pass"]["avg_us"], float(pass1_bytes)
+    achieved = dom_bytes / (dom * 1e-6) / 1e9
+    traffic = measured_traffic(kernel)
     positions = B * (k + 1)
     result = {
         "metric": METRIC,
@@ -256,10 +281,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": "sample_chain_b64_k8_v128256_bf16_t0.7", "B": B, "k": k, "V": V,
                    "logits": "bf16", "temperature": wl.temperature, "input_copies": len(copies),
-                   "draw_arithmetic": "f64"},
-        "roofline": {"bound": "hbm", "kernel": "k_row_stats", "achieved": achieved,
+                   "draw_arithmetic": "f64", "path": args.path},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": pass1_bytes},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes},
         "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_algorithmic_bytes": step_bytes,
         "kernels_avg_us": {n: v["avg_us"] for n, v in kern.items()},
