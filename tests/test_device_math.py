@@ -1,6 +1,8 @@
 """Accuracy of the float64 exponential used by the draw pass (CPU build of
-the same header): Tang's table-driven method, 2^(t/64) for t <= 0, against
-the C library's long double exp2l, over the whole range it serves."""
+the same header): Tang's table-driven method, 2^(t/256), against the C
+library's long double exp2l, over the whole range it serves (every table
+entry, arguments down to the underflow clamp, and the positive arguments a
+reference below the row maximum produces)."""
 import os
 import shutil
 import subprocess
@@ -19,13 +21,18 @@ DRIVER = r"""
 #include "device_math.h"
 int main() {
   std::mt19937_64 g(12345);
-  const double tmin = -745.0 * 0x1.71547652b82fep+6;
-  std::uniform_real_distribution<double> wide(tmin, 0.0), narrow(-4000.0, 0.0);
+  const double tmin = -745.0 * 256.0 / 0.6931471805599453;
+  std::uniform_real_distribution<double> wide(tmin, 0.0), narrow(-16000.0, 0.0),
+      above(0.0, 64.0 * 256.0);
   double worst = 0.0, worst_t = 0.0;
   long n = 0;
+  for (int j = 0; j < 256; ++j) {  // table entries, correctly rounded
+    const long double ref = exp2l((long double)j / 256.0L);
+    if (specv::kExp2Frac256[j] != (double)ref) std::printf("BAD table %d\n", j);
+  }
   auto check = [&](double t) {
-    const double got = specv::exp2_64(t, specv::kExp2Frac64);
-    const long double ref = exp2l((long double)t / 64.0L);
+    const double got = specv::exp2_256(t, specv::kExp2Frac256);
+    const long double ref = exp2l((long double)t / 256.0L);
     if (ref < 2.2250738585072014e-308L) {  // subnormal results: absolute bound
       const long double err = fabsl((long double)got - ref) / 4.9406564584124654e-324L;
       if (err > 2.0) { std::printf("BAD subnormal t=%a got=%a\n", t, got); }
@@ -38,14 +45,16 @@ int main() {
   };
   for (int i = 0; i < 2000000; ++i) check(wide(g));
   for (int i = 0; i < 2000000; ++i) check(narrow(g));
+  for (int i = 0; i < 500000; ++i) check(above(g));
   for (int i = 0; i < 100000; ++i) check(-std::ldexp((double)i, -14));
-  const double specials[] = {0.0, -0.0, -1e-300, -1e-17, -0.5, -1.0, -64.0, -65.5, tmin, tmin + 1};
+  const double specials[] = {0.0, -0.0, -1e-300, -1e-17, -0.5, -1.0, -256.0, -257.5, tmin, tmin + 1,
+                             -1074.0 * 256.0, -1075.5 * 256.0};
   for (double t : specials) check(t);
   std::printf("checked %ld worst_ulp %.3f at %a\n", n, worst, worst_t);
   std::printf("minus_inf %a below_range %a zero %a\n",
-              specv::exp2_64(-INFINITY, specv::kExp2Frac64),
-              specv::exp2_64(-800.0 * 0x1.71547652b82fep+6, specv::kExp2Frac64),
-              specv::exp2_64(0.0, specv::kExp2Frac64));
+              specv::exp2_256(-INFINITY, specv::kExp2Frac256),
+              specv::exp2_256(-1200.0 * 256.0, specv::kExp2Frac256),
+              specv::exp2_256(0.0, specv::kExp2Frac256));
   return 0;
 }
 """

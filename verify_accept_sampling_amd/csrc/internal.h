@@ -39,10 +39,13 @@ constexpr int kRowUnroll = SPEC_ROW_UNROLL;
 // Smallest chunk the workspace is sized for (leaves room to retune).
 constexpr int kRowChunkElemsMin = 2048;
 // Float64 residual / bonus pass: the row is cut into chunks of
-// kDrawChunk elements, one wave per chunk (64 lanes x 16 consecutive
-// elements); a work-group of kThreads/64 waves handles kDrawChunksPerWave
+// kDrawChunk elements, one wave per chunk (64 lanes x kSegPerThread
+// consecutive elements); a work-group of kThreads/64 waves handles kDrawChunksPerWave
 // consecutive chunks per wave.
-constexpr int kSegPerThread = 16;
+#ifndef SPEC_DRAW_SEG
+#define SPEC_DRAW_SEG 8
+#endif
+constexpr int kSegPerThread = SPEC_DRAW_SEG;
 constexpr int kDrawChunk = 64 * kSegPerThread;
 #ifndef SPEC_DRAW_CHUNKS_PER_WAVE
 #define SPEC_DRAW_CHUNKS_PER_WAVE 2
@@ -69,15 +72,21 @@ constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
 
 // Chunk partial of the float64 draw pass.
+// Elements in the kink band of max(0, a - rho b) are kept out of w and dq
+// (their sign may differ between rho32 and the exact rho) and recorded, up
+// to kKinkSlots of them, as (a, b) pairs; a chunk with more is recomputed.
+constexpr int kKinkSlots = 2;
 struct DrawPart {
   double sp;    // sum of e^{(z - mp)/T} (probabilities: sum of p) over the chunk
   double sq;    // sum of e^{(y - mq)/T} over the chunk (residual mode)
-  double w;     // sum of the draw weights at rho32
+  double w;     // sum of the draw weights at rho32, kink-band elements excluded
   double dq;    // d w / d rho at rho32: minus the sum of e^{(y-mq)/T} where the weight is positive
-  double flag;  // 1 if an element lies so close to the rho32 kink that the
-                // linear correction to the exact rho may not hold
+  double nk;    // number of kink-band elements (more than kKinkSlots: recompute)
+  double ka[kKinkSlots];  // their target terms a
+  double kb[kKinkSlots];  // and draft terms b
   double pad;
 };
+static_assert(sizeof(DrawPart) == 80, "DrawPart layout");
 
 // Per-request words of the counter region: [0] row-pass completion
 // ticket, [1] draw completion ticket, [2..3] the one-launch kernel's 64-bit

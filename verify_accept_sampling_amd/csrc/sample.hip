@@ -219,8 +219,9 @@ __device__ __forceinline__ void draw_block(
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
   const int b = static_cast<int>(bid / G2);
   const int grp = static_cast<int>(bid % G2);
-  __shared__ double tab[64];
-  if (KIND == 0 && threadIdx.x < 64) tab[threadIdx.x] = kExp2Frac64[threadIdx.x];
+  __shared__ double tab[256];
+  static_assert(kThreads == 256, "one table entry per thread");
+  if (KIND == 0) tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
   int n;
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
@@ -242,7 +243,7 @@ __device__ __forceinline__ void draw_block(
   }
   __syncthreads();
   const bool resid = n < k;
-  const double c1 = inv_t * kInvLn2x64, c0p = -mp * c1, c0q = -mq * c1;
+  const double c1 = inv_t * kInvLn2x256, c0p = -mp * c1, c0q = -mq * c1;
   const long eb_bytes = Elems<DT>::kBytes;
   const void* prow =
       reinterpret_cast<const char*>(target) + ((long)b * (k + 1) + n) * V * eb_bytes;
@@ -254,15 +255,19 @@ __device__ __forceinline__ void draw_block(
   for (int i = 0; i < kDrawChunksPerWave; ++i) {
     const int cc = grp * kDrawChunksPerGroup + wave * kDrawChunksPerWave + i;
     if (cc >= C2) break;  // wave-uniform
-    double v[5];
-    wave_chunk_sums<DT, NE, KIND>(prow, qrow, V, cc, resid, c1, c0p, c0q, rho32, tab, v);
+    double v[5], ka[kKinkSlots], kb[kKinkSlots];
+    wave_chunk_sums<DT, NE, KIND>(prow, qrow, V, cc, resid, c1, c0p, c0q, rho32, tab, v, ka, kb);
     if (lane == 0) {
       DrawPart* p = &part[(long)b * C2 + cc];
       st_dev_d(&p->sp, v[0]);
       st_dev_d(&p->sq, v[1]);
       st_dev_d(&p->w, v[2]);
       st_dev_d(&p->dq, v[3]);
-      st_dev_d(&p->flag, v[4]);
+      st_dev_d(&p->nk, v[4]);
+      for (int j = 0; j < kKinkSlots; ++j) {
+        st_dev_d(&p->ka[j], ka[j]);
+        st_dev_d(&p->kb[j], kb[j]);
+      }
     }
   }
   wait_stores();  // every wave's partials complete before the ticket below
@@ -276,15 +281,21 @@ __device__ __forceinline__ void draw_block(
   // and reloaded by the same thread.
   DrawPart* rp = part + (long)b * C2;
   const int n_tiles = (C2 + kThreads - 1) / kThreads;
-  double csp = 0.0, csq = 0.0, cw = 0.0, cdq = 0.0, cfl = 0.0;
+  double csp = 0.0, csq = 0.0, cw = 0.0, cdq = 0.0, cnk = 0.0;
+  double cka[kKinkSlots], ckb[kKinkSlots];
   auto load_chunk = [&](int cc) {
-    csp = csq = cw = cdq = cfl = 0.0;
+    csp = csq = cw = cdq = cnk = 0.0;
+    for (int j = 0; j < kKinkSlots; ++j) cka[j] = ckb[j] = 0.0;
     if (cc < C2) {
       csp = ld_dev_d(&rp[cc].sp);
       csq = ld_dev_d(&rp[cc].sq);
       cw = ld_dev_d(&rp[cc].w);
       cdq = ld_dev_d(&rp[cc].dq);
-      cfl = ld_dev_d(&rp[cc].flag);
+      cnk = ld_dev_d(&rp[cc].nk);
+      for (int j = 0; j < kKinkSlots; ++j) {
+        cka[j] = ld_dev_d(&rp[cc].ka[j]);
+        ckb[j] = ld_dev_d(&rp[cc].kb[j]);
+      }
     }
   };
   double sums[2] = {0.0, 0.0};  // S_p, S_q over the row(s)
@@ -296,32 +307,36 @@ __device__ __forceinline__ void draw_block(
   block_sum_dn<2>(sums);
   const double sp_tot = sums[0];
   const double rho = (KIND == 0 && resid) ? sums[0] / sums[1] : 1.0;
-  // Chunk totals of the draw weights at the exact rho: linear correction,
-  // or, for chunks with an element in the kink band, recomputation at rho,
-  // one wave per flagged chunk.
+  // Chunk totals of the draw weights at the exact rho: the linear part moved
+  // to rho, plus the exact weights of the recorded kink-band elements; a
+  // chunk with more of them than recorded is recomputed (one wave each).
   double grand_w = 0.0;
   for (int base = 0; base < C2; base += kThreads) {
     const int cc = base + threadIdx.x;
     if (n_tiles > 1) load_chunk(cc);
-    const bool kink = KIND == 0 && resid && cfl > 0.0;
-    if (KIND == 0 && resid && !kink) cw = fmax(0.0, cw + (rho - rho32) * cdq);
-    if (__syncthreads_count(kink) > 0) {
+    const bool redo = KIND == 0 && resid && cnk > (double)kKinkSlots;
+    if (KIND == 0 && resid && !redo) {
+      cw = fmax(0.0, cw + (rho - rho32) * cdq);
+      for (int j = 0; j < kKinkSlots; ++j)
+        if ((double)j < cnk) cw += fmax(0.0, cka[j] - rho * ckb[j]);
+    }
+    if (__syncthreads_count(redo) > 0) {
       __shared__ int s_list[kThreads];
-      __shared__ int s_nk;
+      __shared__ int s_nr;
       __shared__ double s_wx[kThreads];
-      if (threadIdx.x == 0) s_nk = 0;
+      if (threadIdx.x == 0) s_nr = 0;
       __syncthreads();
-      if (kink) s_list[atomicAdd(&s_nk, 1)] = threadIdx.x;
+      if (redo) s_list[atomicAdd(&s_nr, 1)] = threadIdx.x;
       __syncthreads();
-      const int nk = s_nk;
-      for (int idx = wave; idx < nk; idx += kWaves) {  // wave-uniform
+      const int nr = s_nr;
+      for (int idx = wave; idx < nr; idx += kWaves) {  // wave-uniform
         const int t2 = s_list[idx];
-        double v[5];
-        wave_chunk_sums<DT, NE, KIND>(prow, qrow, V, base + t2, true, c1, c0p, c0q, rho, tab, v);
-        if (lane == 0) s_wx[t2] = v[2];
+        const double wx =
+            wave_chunk_w_exact<DT, KIND>(prow, qrow, V, base + t2, c1, c0p, c0q, rho, tab);
+        if (lane == 0) s_wx[t2] = wx;
       }
       __syncthreads();
-      if (kink) cw = fmax(0.0, s_wx[threadIdx.x]);
+      if (redo) cw = fmax(0.0, s_wx[threadIdx.x]);
     }
     if (n_tiles > 1) {
       if (cc < C2) st_dev_d(&rp[cc].w, cw);
@@ -413,7 +428,9 @@ __global__ __launch_bounds__(kThreads) void k_draw(
 // every row-pass work-group has been dispatched before a draw work-group
 // takes a slot, and a draw work-group only waits for row-pass work of its
 // own request: the wait ends.  Early requests' draws run while the last
-// row-pass work-groups stream.
+// row-pass work-groups stream.  (Interleaving draw work-groups earlier in
+// the grid was slower: waiting draw work-groups hold slots that streaming
+// work-groups need.)
 template <int DT, int NE>
 __global__ __launch_bounds__(kThreads) void k_sample_one(
     const void* __restrict__ target, const void* __restrict__ draft, int B, int k, int V, int C1,

@@ -240,25 +240,29 @@ __device__ __forceinline__ void load_run(const void* row, long j0, int V, float 
 }
 
 // Float64 term of one element.  KIND 0 (logits): e^{(z - m)/T}, evaluated as
-// 2^(t/64) with t = z c1 + c0, c1 = 64/(T ln 2), c0 = -m c1; KIND 1
+// 2^(t/256) with t = z c1 + c0, c1 = 256/(T ln 2), c0 = -m c1; KIND 1
 // (probabilities): the value itself.
 template <int KIND>
 __device__ __forceinline__ double draw_term(float z, double c1, double c0, const double* tab) {
-  return KIND == 0 ? exp2_64(fma((double)z, c1, c0), tab) : (double)z;
+  return KIND == 0 ? exp2_256(fma((double)z, c1, c0), tab) : (double)z;
 }
 
-// Sums of one chunk by one wave (lane l covers the 16 elements from
-// chunk * kDrawChunk + 16 l), reduced across the wave (valid in every lane):
+// Sums of one chunk by one wave (lane l covers the kSegPerThread elements
+// from chunk * kDrawChunk + kSegPerThread l), reduced across the wave
+// (valid in every lane):
 //   v[0] = sum a, v[1] = sum b (a, b the target and draft terms),
 //   v[2] = sum of the draw weights at rho32 (max(0, a - rho32 b), or a for
 //          the bonus), v[3] = their derivative in rho (minus the sum of b
-//          where the weight is positive), v[4] = 1 if an element lies within
-//          the kink band of max(0, .).
+//          where the weight is positive), v[4] = the number of elements in
+//          the kink band of max(0, .), which are left out of v[2] and v[3];
+//   ka, kb = (a, b) of the first kKinkSlots of them (valid when v[4] is at
+//          most kKinkSlots and no lane holds two).
 template <int DT, int NE, int KIND>
 __device__ __forceinline__ void wave_chunk_sums(const void* prow, const void* qrow, int V,
                                                 int chunk, bool resid, double c1, double c0p,
                                                 double c0q, double rho32, const double* tab,
-                                                double (&v)[5]) {
+                                                double (&v)[5], double (&ka)[kKinkSlots],
+                                                double (&kb)[kKinkSlots]) {
   const int lane = threadIdx.x & 63;
   const long j0 = (long)chunk * kDrawChunk + (long)lane * kSegPerThread;
   const float fill = KIND == 0 ? -INFINITY : 0.f;
@@ -267,6 +271,8 @@ __device__ __forceinline__ void wave_chunk_sums(const void* prow, const void* qr
   if (resid) load_run<DT, NE, kSegPerThread>(qrow, j0, V, fill, zq);
 #pragma unroll
   for (int q = 0; q < 5; ++q) v[q] = 0.0;
+  double la = 0.0, lb = 0.0;  // this lane's first kink-band element
+  int lk = 0;
 #pragma unroll
   for (int e = 0; e < kSegPerThread; ++e) {
     const double a = draw_term<KIND>(zp[e], c1, c0p, tab);
@@ -275,20 +281,59 @@ __device__ __forceinline__ void wave_chunk_sums(const void* prow, const void* qr
       const double bq = draw_term<KIND>(zq[e], c1, c0q, tab);
       v[1] += bq;
       const double d = a - rho32 * bq;
-      if (d > 0.0) {
+      if (KIND == 0 && bq > 0.0 && fabs(d) <= kKinkBand * rho32 * bq) {
+        if (lk == 0) {
+          la = a;
+          lb = bq;
+        }
+        ++lk;
+      } else if (d > 0.0) {
         v[2] += d;
         v[3] -= bq;
       }
-      if (KIND == 0 && bq > 0.0 && fabs(d) <= kKinkBand * rho32 * bq) v[4] = 1.0;
     } else {
       v[2] += a;
     }
   }
+  v[4] = (double)lk;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
 #pragma unroll
     for (int q = 0; q < 5; ++q) v[q] += shfl_xor_d(v[q], o);
   }
+  // the kink-band elements of the first lanes that hold one
+  uint64_t holders = __ballot(lk > 0);
+  if (__ballot(lk > 1) != 0) v[4] = (double)(kKinkSlots + 1);  // cannot list them all
+#pragma unroll
+  for (int j = 0; j < kKinkSlots; ++j) {
+    ka[j] = kb[j] = 0.0;
+    if (holders) {
+      const int src = __builtin_ctzll(holders);
+      holders &= holders - 1;
+      ka[j] = __shfl(la, src, 64);
+      kb[j] = __shfl(lb, src, 64);
+    }
+  }
+}
+
+// Draw-weight total of one chunk at the exact rho, by one wave, one element
+// at a time per lane (rolled: few registers; for chunks with too many
+// kink-band elements, which are rare).
+template <int DT, int KIND>
+__device__ double wave_chunk_w_exact(const void* prow, const void* qrow, int V, int chunk,
+                                     double c1, double c0p, double c0q, double rho,
+                                     const double* tab) {
+  const int lane = threadIdx.x & 63;
+  const long j0 = (long)chunk * kDrawChunk + (long)lane * kSegPerThread;
+  double w = 0.0;
+#pragma unroll 1
+  for (int e = 0; e < kSegPerThread; ++e) {
+    if (j0 + e >= V) break;
+    const double a = draw_term<KIND>(load_elem<DT>(prow, j0 + e), c1, c0p, tab);
+    const double bq = draw_term<KIND>(load_elem<DT>(qrow, j0 + e), c1, c0q, tab);
+    w += fmax(0.0, a - rho * bq);
+  }
+  return wave_sum_d(w);
 }
 
 // kSearchPerThread consecutive elements of a chunk for this thread of a
