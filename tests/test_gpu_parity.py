@@ -195,7 +195,10 @@ def test_sample_chain_llama3_full(llama3_full, sample_path):
 
 @pytest.mark.parametrize("B,k,V,dtype,T", [(50, 3, 1001, "f32", 1.0), (40, 5, 4000, "bf16", 0.3),
                                            (30, 4, 32000, "f32", 2.5), (16, 0, 5000, "bf16", 1.0),
-                                           (20, 1, 17, "bf16", 0.8), (8, 12, 65536, "bf16", 1.0)])
+                                           (20, 1, 17, "bf16", 0.8), (8, 12, 65536, "bf16", 1.0),
+                                           # more draw chunks than threads of a work-group:
+                                           # the draw's tiled tail
+                                           (4, 3, 152064, "bf16", 1.0), (3, 2, 262400, "f32", 0.6)])
 def test_sample_chain_shapes(B, k, V, dtype, T, sample_path):
     _say(f"sample chain B={B} k={k} V={V} {dtype} T={T} path={sample_path}")
     wl = W.sample_chain(B, k, V, seed=B + k + V, uniform_seed=77 + V, target_std=2.0,
@@ -240,6 +243,12 @@ def test_sample_probs_small_and_empty_residual():
     wl2 = W.ChainWorkload("empty_residual", p, q, toks, "probs", "f32", 1.0, 5)
     acc, out = _run_sample(wl2)
     assert (acc < k).any()
+
+
+def test_sample_probs_wide_vocabulary():
+    # probability rows wider than one tile of draw chunks
+    wl = W.controlled_acceptance(B=6, k=3, V=200003, seed=31, uniform_seed=32, logit_std=1.0)
+    _run_sample(wl)
 
 
 def test_sample_controlled_acceptance_full(controlled_full):

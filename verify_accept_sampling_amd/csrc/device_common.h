@@ -381,6 +381,44 @@ __device__ __forceinline__ double block_exclusive_scan_d(double v) {
   return base + (inc - v);
 }
 
+// Exclusive prefix sums of N values over the work-group, and their
+// work-group totals (every thread receives them).
+template <int N>
+__device__ __forceinline__ void block_exclusive_scan_total_dn(const double (&v)[N],
+                                                              double (&excl)[N],
+                                                              double (&total)[N]) {
+  __shared__ double wsum[N][kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double inc[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) inc[j] = v[j];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const double o = shfl_up_d(inc[j], d);
+      if (lane >= d) inc[j] += o;
+    }
+  }
+  __syncthreads();
+  if (lane == 63) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) wsum[j][wave] = inc[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    double base = 0.0, all = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) base += wsum[j][w];
+      all += wsum[j][w];
+    }
+    excl[j] = base + (inc[j] - v[j]);
+    total[j] = all;
+  }
+}
+
 // Minimum of an int over the work-group, broadcast.
 __device__ __forceinline__ int wave_min_i(int v) {
 #pragma unroll

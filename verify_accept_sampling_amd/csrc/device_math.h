@@ -4,7 +4,7 @@
 // a 256-entry table:
 //   t = x * 256/ln2 = 256 m + j + f,  |f| <= 1/2,
 //   exp(x) = 2^m * 2^(j/256) * exp(f ln2/256),
-// with exp(r), |r| <= ln2/512, from its degree-4 Taylor polynomial
+// with exp(f ln2/256), |f| <= 1/2, from its degree-4 Taylor polynomial
 // (truncation below 4e-17 relative) and 2^(j/256) from the table.
 // Callers pass the scaled argument t directly (one fused multiply-add on the
 // input).  Arguments are clamped from below at a point where the final
@@ -86,21 +86,27 @@ constexpr double kExp2Frac256[256] = {
 };
 
 constexpr double kInvLn2x256 = 0x1.71547652b82fep+8;  // 256 / ln 2
-constexpr double kLn2d256 = 0x1.62e42fefa39efp-9;     // ln 2 / 256
+// Taylor coefficients of exp(f ln2/256) in f: (ln2/256)^i / i!, i = 1..4.
+constexpr double kExpF1 = 0x1.62e42fefa39efp-9;
+constexpr double kExpF2 = 0x1.ebfbdff82c58fp-19;
+constexpr double kExpF3 = 0x1.c6b08d704a0c0p-29;
+constexpr double kExpF4 = 0x1.3b2ab6fba4e77p-39;
 // Below this scaled argument the result is 0: 2^(t/256) < 2^-1100.
 constexpr double kTClamp = -1100.0 * 256.0;
 
 // exp(t ln2/256); `tab` points at the 256-entry table (a shared-memory
-// copy on the device, kExp2Frac256 on the host).
+// copy on the device, kExp2Frac256 on the host).  The polynomial is taken
+// in f = t - n itself (|f| <= 1/2, exact), its coefficients carrying the
+// ln2/256 factor.
 __host__ __device__ inline double exp2_256(double t, const double* tab) {
   const double tc = fmax(t, kTClamp);  // also maps -inf
   const double n = rint(tc);
-  const double r = (tc - n) * kLn2d256;  // tc - n is exact
-  double p = 1.0 / 24.0;
-  p = fma(p, r, 1.0 / 6.0);
-  p = fma(p, r, 0.5);
-  p = fma(p, r, 1.0);
-  p = fma(p, r, 1.0);
+  const double f = tc - n;  // exact
+  double p = kExpF4;
+  p = fma(p, f, kExpF3);
+  p = fma(p, f, kExpF2);
+  p = fma(p, f, kExpF1);
+  p = fma(p, f, 1.0);
   const int ni = static_cast<int>(n);
   return ldexp(tab[ni & 255] * p, ni >> 8);
 }

@@ -250,24 +250,18 @@ __device__ __forceinline__ void draw_block(
   const void* qrow =
       resid ? reinterpret_cast<const char*>(draft) + ((long)b * k + n) * V * eb_bytes : nullptr;
 
-  // ---- this work-group's chunks, one wave per chunk ----
+  // ---- this work-group's chunks, kDrawChunksPerWave per wave ----
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = 0; i < kDrawChunksPerWave; ++i) {
-    const int cc = grp * kDrawChunksPerGroup + wave * kDrawChunksPerWave + i;
-    if (cc >= C2) break;  // wave-uniform
-    double v[5], ka[kKinkSlots], kb[kKinkSlots];
-    wave_chunk_sums<DT, NE, KIND>(prow, qrow, V, cc, resid, c1, c0p, c0q, rho32, tab, v, ka, kb);
-    if (lane == 0) {
-      DrawPart* p = &part[(long)b * C2 + cc];
-      st_dev_d(&p->sp, v[0]);
-      st_dev_d(&p->sq, v[1]);
-      st_dev_d(&p->w, v[2]);
-      st_dev_d(&p->dq, v[3]);
-      st_dev_d(&p->nk, v[4]);
-      for (int j = 0; j < kKinkSlots; ++j) {
-        st_dev_d(&p->ka[j], ka[j]);
-        st_dev_d(&p->kb[j], kb[j]);
-      }
+  {
+    const int first = grp * kDrawChunksPerGroup + wave * kDrawChunksPerWave;
+    DrawPart* pb = part + (long)b * C2;
+    if (first < C2) {  // wave-uniform
+      if (resid)
+        wave_draw_chunks<DT, NE, KIND, true>(prow, qrow, V, C2, first, c1, c0p, c0q, rho32, tab,
+                                             pb);
+      else
+        wave_draw_chunks<DT, NE, KIND, false>(prow, qrow, V, C2, first, c1, c0p, c0q, rho32, tab,
+                                              pb);
     }
   }
   wait_stores();  // every wave's partials complete before the ticket below
@@ -275,10 +269,13 @@ __device__ __forceinline__ void draw_block(
   if (!block_arrive(&counters[(long)b * kCountersPerReq + 1], (unsigned)G2)) return;
 
   // ---- last work-group of request b: exact rho, chunk totals, draw ----
+  // Every other wave on this compute unit is bulk work of other requests,
+  // while this one decides when its request ends: it issues first.
+  __builtin_amdgcn_s_setprio(3);
   // Thread t owns chunk base + t of each tile of kThreads chunks.  With one
-  // tile (V up to 262144) the partials are loaded once and every step below
-  // works on registers; with more tiles the corrected totals are written back
-  // and reloaded by the same thread.
+  // tile (V up to kThreads * kDrawChunk) the partials are loaded once and
+  // every step below works on registers; with more tiles the corrected
+  // totals are written back and reloaded by the same thread.
   DrawPart* rp = part + (long)b * C2;
   const int n_tiles = (C2 + kThreads - 1) / kThreads;
   double csp = 0.0, csq = 0.0, cw = 0.0, cdq = 0.0, cnk = 0.0;
@@ -298,29 +295,37 @@ __device__ __forceinline__ void draw_block(
       }
     }
   };
-  double sums[2] = {0.0, 0.0};  // S_p, S_q over the row(s)
+  const bool resid_w = KIND == 0 && resid;  // weights move with rho
+  __shared__ int s_cs;      // chunk holding the threshold
+  __shared__ double s_P;    // weight of the chunks before it
+  if (threadIdx.x == 0) s_cs = INT_MAX;  // ordered by the reduction's barriers
+  // S_p, S_q and the number of chunks with more kink-band elements than
+  // recorded, in one reduction.
+  double sums[3] = {0.0, 0.0, 0.0};
   for (int base = 0; base < C2; base += kThreads) {
     load_chunk(base + threadIdx.x);
     sums[0] += csp;
     sums[1] += csq;
+    sums[2] += cnk > (double)kKinkSlots ? 1.0 : 0.0;
   }
-  block_sum_dn<2>(sums);
+  block_sum_dn<3>(sums);
   const double sp_tot = sums[0];
-  const double rho = (KIND == 0 && resid) ? sums[0] / sums[1] : 1.0;
+  const double rho = resid_w ? sums[0] / sums[1] : 1.0;
+  const bool any_redo = resid_w && sums[2] > 0.0;  // block-uniform
   // Chunk totals of the draw weights at the exact rho: the linear part moved
   // to rho, plus the exact weights of the recorded kink-band elements; a
   // chunk with more of them than recorded is recomputed (one wave each).
-  double grand_w = 0.0;
+  double acc_w = 0.0, acc_p = 0.0;  // this thread's share of the totals
   for (int base = 0; base < C2; base += kThreads) {
     const int cc = base + threadIdx.x;
     if (n_tiles > 1) load_chunk(cc);
-    const bool redo = KIND == 0 && resid && cnk > (double)kKinkSlots;
-    if (KIND == 0 && resid && !redo) {
+    const bool redo = resid_w && cnk > (double)kKinkSlots;
+    if (resid_w && !redo) {
       cw = fmax(0.0, cw + (rho - rho32) * cdq);
       for (int j = 0; j < kKinkSlots; ++j)
         if ((double)j < cnk) cw += fmax(0.0, cka[j] - rho * ckb[j]);
     }
-    if (__syncthreads_count(redo) > 0) {
+    if (any_redo) {
       __shared__ int s_list[kThreads];
       __shared__ int s_nr;
       __shared__ double s_wx[kThreads];
@@ -342,40 +347,60 @@ __device__ __forceinline__ void draw_block(
       if (cc < C2) st_dev_d(&rp[cc].w, cw);
       wait_stores();  // reloaded by this same thread below
     }
-    grand_w += cw;
+    acc_w += cw;
+    acc_p += csp;
   }
-  grand_w = block_sum_d(grand_w);
   // Weights drawn from: the residual, or the target terms when the
-  // residual is empty (or at the bonus position).
-  const bool use_w = resid && grand_w > 0.0;
-  const double grand = use_w ? grand_w : sp_tot;
+  // residual is empty (or at the bonus position).  Locate the chunk where
+  // the running total first exceeds u times the grand total; past the end
+  // (a last-bit difference) the last chunk is searched.
   const float u = get_uniform(uniforms, seed, ctr0, b, n, 1, k);
-  const double thr = (double)u * grand;
-  // Locate the chunk holding thr: exclusive prefix over the chunk totals.
-  __shared__ double s_P;
-  __shared__ int s_cs;
-  if (threadIdx.x == 0) { s_cs = C2 - 1; s_P = 0.0; }
-  {
+  bool use_w;
+  double grand;
+  if (n_tiles == 1) {
+    // One scan gives every chunk's prefix and both totals.
+    const double v2[2] = {cw, csp};
+    double ex[2], tot[2];
+    block_exclusive_scan_total_dn<2>(v2, ex, tot);
+    use_w = resid && tot[0] > 0.0;
+    grand = use_w ? tot[0] : tot[1];
+    const double thr = (double)u * grand;
+    const int cc = threadIdx.x;
+    const double val = use_w ? cw : csp, excl = use_w ? ex[0] : ex[1];
+    const uint64_t mh = __ballot(cc < C2 && excl + val > thr);
+    if (mh != 0 && lane == __builtin_ctzll(mh)) atomicMin(&s_cs, cc);  // the wave's first
+    __syncthreads();
+    if (cc == (s_cs == INT_MAX ? C2 - 1 : s_cs)) s_P = excl;
+  } else {
+    double tot[2] = {acc_w, acc_p};
+    block_sum_dn<2>(tot);
+    use_w = resid && tot[0] > 0.0;
+    grand = use_w ? tot[0] : tot[1];
+    const double thr = (double)u * grand;
     double running = 0.0;
     for (int base = 0; base < C2; base += kThreads) {
       const int cc = base + threadIdx.x;
-      if (n_tiles > 1) load_chunk(cc);  // totals as written back above
-      const double val = cc < C2 ? (use_w ? cw : csp) : 0.0;
-      const double excl = running + block_exclusive_scan_d(val);
-      const int hit = (cc < C2 && excl + val > thr) ? cc : INT_MAX;
-      if (cc == C2 - 1 && hit == INT_MAX) s_P = excl;  // no hit: search the last chunk
-      const int first_hit = block_min_i(hit);
-      if (first_hit != INT_MAX) {
-        if (cc == first_hit) { s_cs = cc; s_P = excl; }
-        break;  // block-uniform
+      load_chunk(cc);  // totals as written back above
+      const double v1[1] = {use_w ? cw : csp};
+      double ex[1], ts[1];
+      block_exclusive_scan_total_dn<1>(v1, ex, ts);
+      const double excl = running + ex[0];
+      const uint64_t mh = __ballot(cc < C2 && excl + v1[0] > thr);
+      if (mh != 0 && lane == __builtin_ctzll(mh)) atomicMin(&s_cs, cc);
+      __syncthreads();
+      const int hit = s_cs;
+      if (hit != INT_MAX || base + kThreads >= C2) {  // block-uniform
+        if (cc == (hit == INT_MAX ? C2 - 1 : hit)) s_P = excl;
+        break;
       }
-      running += block_sum_d(val);
+      running += ts[0];
     }
-    __syncthreads();
   }
+  const double thr = (double)u * grand;
+  const int cs = s_cs == INT_MAX ? C2 - 1 : s_cs;
   const int mode = use_w ? 0 : 1;
-  int t = search_chunk<DT, KIND>(prow, qrow, V, s_cs, mode == 0, c1, c0p, c0q, rho, s_P, thr,
-                                 tab);
+  // s_P is stored by one thread above; the search reads it after a barrier.
+  int t = search_chunk<DT, KIND>(prow, qrow, V, cs, mode == 0, c1, c0p, c0q, rho, s_P, thr, tab);
   if (threadIdx.x == 0) {
     if (!(grand > 0.0)) t = -1;  // rows without mass (invalid input)
     out_tokens[(long)b * (k + 1) + n] = t;

@@ -218,27 +218,6 @@ __device__ __forceinline__ void merge_two_rows(const uint64_t* part, long base_a
 // 2. Float64 draw pass
 // ---------------------------------------------------------------------------
 
-// NN consecutive elements from j0 as floats (NN a multiple of NE); elements
-// at or beyond V read as `fill`.
-template <int DT, int NE, int NN>
-__device__ __forceinline__ void load_run(const void* row, long j0, int V, float fill,
-                                         float (&x)[NN]) {
-  static_assert(NN % NE == 0, "run length must be a multiple of the load width");
-#pragma unroll
-  for (int g = 0; g < NN / NE; ++g) {
-    const long e0 = j0 + (long)g * NE;
-    float t[NE];
-    if (e0 + NE <= V) {
-      load_group<DT, NE>(row, e0, t);
-    } else {
-#pragma unroll
-      for (int e = 0; e < NE; ++e) t[e] = (e0 + e < V) ? load_elem<DT>(row, e0 + e) : fill;
-    }
-#pragma unroll
-    for (int e = 0; e < NE; ++e) x[g * NE + e] = t[e];
-  }
-}
-
 // Float64 term of one element.  KIND 0 (logits): e^{(z - m)/T}, evaluated as
 // 2^(t/256) with t = z c1 + c0, c1 = 256/(T ln 2), c0 = -m c1; KIND 1
 // (probabilities): the value itself.
@@ -247,71 +226,191 @@ __device__ __forceinline__ double draw_term(float z, double c1, double c0, const
   return KIND == 0 ? exp2_256(fma((double)z, c1, c0), tab) : (double)z;
 }
 
+// One lane's run of kSegPerThread consecutive elements of one row, kept as
+// the raw words loaded (two bfloat16 or one float32 per word) until used.
+template <int DT>
+struct RunWords {
+  static constexpr int kWords = kSegPerThread * Elems<DT>::kBytes / 4;
+  uint32_t w[kWords];
+};
+
+// Loads the run at element j0; elements at or beyond V read as `fill`
+// (raw bits of the element type).  With 16-byte groups (NE > 1) the row
+// length is a multiple of NE, so each group is wholly inside or wholly past
+// the end; a group past the end loads the row's first group instead and
+// keeps the fill, so the loads are unconditional.
+template <int DT, int NE>
+__device__ __forceinline__ void load_run_words(const void* row, long j0, int V, uint32_t fill,
+                                               RunWords<DT>& r) {
+  constexpr int kPerWord = 4 / Elems<DT>::kBytes;
+  if constexpr (NE > 1) {
+    static_assert(NE == Elems<DT>::kVec, "vector group must be 16 bytes");
+    static_assert(kSegPerThread % NE == 0, "run length must be a multiple of the load width");
+    const uint32_t fw = DT == 1 ? (fill | (fill << 16)) : fill;
+#pragma unroll
+    for (int g = 0; g < kSegPerThread / NE; ++g) {
+      const long e0 = j0 + (long)g * NE;
+      const bool ok = e0 < V;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(row) +
+                                                      (ok ? e0 : 0) * Elems<DT>::kBytes);
+      r.w[g * 4 + 0] = ok ? w.x : fw;
+      r.w[g * 4 + 1] = ok ? w.y : fw;
+      r.w[g * 4 + 2] = ok ? w.z : fw;
+      r.w[g * 4 + 3] = ok ? w.w : fw;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < RunWords<DT>::kWords; ++q) r.w[q] = 0;
+#pragma unroll
+    for (int e = 0; e < kSegPerThread; ++e) {
+      uint32_t bits = fill;
+      if (j0 + e < V) {
+        if constexpr (DT == 1) bits = reinterpret_cast<const uint16_t*>(row)[j0 + e];
+        else bits = reinterpret_cast<const uint32_t*>(row)[j0 + e];
+      }
+      r.w[e / kPerWord] |= bits << (32 / kPerWord * (e % kPerWord));
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float run_elem(const RunWords<DT>& r, int e) {
+  if constexpr (DT == 1) return (e & 1) ? bf16_hi(r.w[e >> 1]) : bf16_lo(r.w[e >> 1]);
+  else return __uint_as_float(r.w[e]);
+}
+
+// Raw bits read for elements past the end of a row: -inf logits (weight 0)
+// or probability 0.
+template <int DT, int KIND>
+__host__ __device__ constexpr uint32_t run_fill() {
+  if constexpr (KIND == 1) return 0u;
+  else return DT == 1 ? 0xff80u : 0xff800000u;
+}
+
 // Sums of one chunk by one wave (lane l covers the kSegPerThread elements
-// from chunk * kDrawChunk + kSegPerThread l), reduced across the wave
-// (valid in every lane):
+// from chunk * kDrawChunk + kSegPerThread l, given as runs rp, rq of the
+// target and draft rows), reduced across the wave (valid in every lane):
 //   v[0] = sum a, v[1] = sum b (a, b the target and draft terms),
 //   v[2] = sum of the draw weights at rho32 (max(0, a - rho32 b), or a for
 //          the bonus), v[3] = their derivative in rho (minus the sum of b
 //          where the weight is positive), v[4] = the number of elements in
 //          the kink band of max(0, .), which are left out of v[2] and v[3];
-//   ka, kb = (a, b) of the first kKinkSlots of them (valid when v[4] is at
-//          most kKinkSlots and no lane holds two).
-template <int DT, int NE, int KIND>
-__device__ __forceinline__ void wave_chunk_sums(const void* prow, const void* qrow, int V,
-                                                int chunk, bool resid, double c1, double c0p,
-                                                double c0q, double rho32, const double* tab,
-                                                double (&v)[5], double (&ka)[kKinkSlots],
+//   ka, kb = (a, b) of the first kKinkSlots of them, in element order
+//          within each lane position (valid when v[4] is at most
+//          kKinkSlots; then they are uniform across the wave).
+// RESID: the residual draw (false: the bonus draw, from the target terms).
+// The loop has no branches: kink-band membership is kept as one wave mask
+// per element position, and the rare kink elements are reloaded and
+// evaluated after it.
+template <int DT, int KIND, bool RESID>
+__device__ __forceinline__ void wave_chunk_sums(const RunWords<DT>& rp, const RunWords<DT>& rq,
+                                                const void* prow, const void* qrow, int chunk,
+                                                double c1, double c0p, double c0q, double rho32,
+                                                const double* tab, double (&v)[5],
+                                                double (&ka)[kKinkSlots],
                                                 double (&kb)[kKinkSlots]) {
-  const int lane = threadIdx.x & 63;
-  const long j0 = (long)chunk * kDrawChunk + (long)lane * kSegPerThread;
-  const float fill = KIND == 0 ? -INFINITY : 0.f;
-  float zp[kSegPerThread], zq[kSegPerThread];
-  load_run<DT, NE, kSegPerThread>(prow, j0, V, fill, zp);
-  if (resid) load_run<DT, NE, kSegPerThread>(qrow, j0, V, fill, zq);
-#pragma unroll
-  for (int q = 0; q < 5; ++q) v[q] = 0.0;
-  double la = 0.0, lb = 0.0;  // this lane's first kink-band element
-  int lk = 0;
+  double sa = 0.0, sb = 0.0, sw = 0.0, sq = 0.0;
+  uint64_t km[kSegPerThread];
+  const double bandr = kKinkBand * rho32;
 #pragma unroll
   for (int e = 0; e < kSegPerThread; ++e) {
-    const double a = draw_term<KIND>(zp[e], c1, c0p, tab);
-    v[0] += a;
-    if (resid) {
-      const double bq = draw_term<KIND>(zq[e], c1, c0q, tab);
-      v[1] += bq;
-      const double d = a - rho32 * bq;
-      if (KIND == 0 && bq > 0.0 && fabs(d) <= kKinkBand * rho32 * bq) {
-        if (lk == 0) {
-          la = a;
-          lb = bq;
-        }
-        ++lk;
-      } else if (d > 0.0) {
-        v[2] += d;
-        v[3] -= bq;
+    const double a = draw_term<KIND>(run_elem<DT>(rp, e), c1, c0p, tab);
+    sa += a;
+    km[e] = 0;
+    if constexpr (RESID) {
+      const double bq = draw_term<KIND>(run_elem<DT>(rq, e), c1, c0q, tab);
+      sb += bq;
+      const double d = fma(-rho32, bq, a);
+      bool kink = false;
+      if constexpr (KIND == 0) {
+        kink = fabs(d) < bandr * bq;  // false when bq = 0
+        km[e] = __ballot(kink);
       }
-    } else {
-      v[2] += a;
+      const bool pos = d > 0.0 && !kink;
+      sw += pos ? d : 0.0;
+      sq += pos ? bq : 0.0;
     }
   }
-  v[4] = (double)lk;
+  v[0] = sa;
+  v[1] = sb;
+  v[2] = RESID ? sw : sa;
+  v[3] = -sq;
+  v[4] = 0.0;
+  constexpr int kSums = RESID ? 4 : 1;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
 #pragma unroll
-    for (int q = 0; q < 5; ++q) v[q] += shfl_xor_d(v[q], o);
+    for (int q = 0; q < kSums; ++q) v[q] += shfl_xor_d(v[q], o);
   }
-  // the kink-band elements of the first lanes that hold one
-  uint64_t holders = __ballot(lk > 0);
-  if (__ballot(lk > 1) != 0) v[4] = (double)(kKinkSlots + 1);  // cannot list them all
+  if constexpr (!RESID) v[2] = v[0];
 #pragma unroll
-  for (int j = 0; j < kKinkSlots; ++j) {
-    ka[j] = kb[j] = 0.0;
-    if (holders) {
-      const int src = __builtin_ctzll(holders);
-      holders &= holders - 1;
-      ka[j] = __shfl(la, src, 64);
-      kb[j] = __shfl(lb, src, 64);
+  for (int j = 0; j < kKinkSlots; ++j) ka[j] = kb[j] = 0.0;
+  if constexpr (KIND == 0 && RESID) {
+    static_assert(kKinkSlots == 2, "two recorded kink elements");
+    int nk = 0;
+#pragma unroll
+    for (int e = 0; e < kSegPerThread; ++e) nk += __popcll(km[e]);
+    v[4] = (double)nk;
+    if (nk > 0 && nk <= kKinkSlots) {  // wave-uniform, rare
+      int kj0 = -1, kj1 = -1;          // element offsets within the chunk
+#pragma unroll
+      for (int e = 0; e < kSegPerThread; ++e) {
+        uint64_t m = km[e];
+        while (m) {
+          const int off = __builtin_ctzll(m) * kSegPerThread + e;
+          m &= m - 1;
+          if (kj0 < 0) kj0 = off;
+          else if (kj1 < 0) kj1 = off;
+        }
+      }
+      const long base = (long)chunk * kDrawChunk;
+      ka[0] = draw_term<KIND>(load_elem<DT>(prow, base + kj0), c1, c0p, tab);
+      kb[0] = draw_term<KIND>(load_elem<DT>(qrow, base + kj0), c1, c0q, tab);
+      if (kj1 >= 0) {
+        ka[1] = draw_term<KIND>(load_elem<DT>(prow, base + kj1), c1, c0p, tab);
+        kb[1] = draw_term<KIND>(load_elem<DT>(qrow, base + kj1), c1, c0q, tab);
+      }
+    }
+  }
+}
+
+// This wave's chunks first .. first + kDrawChunksPerWave - 1 of the draw
+// (those below C2): every run is loaded before the first is summed, then
+// lane 0 publishes each chunk's partial (coherent stores).  A chunk index
+// past the end loads the last chunk again, so the loads are unconditional
+// and the first chunk's sums wait only for its own loads.
+template <int DT, int NE, int KIND, bool RESID>
+__device__ __forceinline__ void wave_draw_chunks(const void* prow, const void* qrow, int V, int C2,
+                                                 int first, double c1, double c0p, double c0q,
+                                                 double rho32, const double* tab,
+                                                 DrawPart* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  constexpr uint32_t fill = run_fill<DT, KIND>();
+  RunWords<DT> rp[kDrawChunksPerWave], rq[kDrawChunksPerWave];
+#pragma unroll
+  for (int i = 0; i < kDrawChunksPerWave; ++i) {
+    const long j0 = (long)min(first + i, C2 - 1) * kDrawChunk + (long)lane * kSegPerThread;
+    load_run_words<DT, NE>(prow, j0, V, fill, rp[i]);
+    if constexpr (RESID) load_run_words<DT, NE>(qrow, j0, V, fill, rq[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < kDrawChunksPerWave; ++i) {
+    const int cc = first + i;
+    if (cc >= C2) break;  // wave-uniform
+    double v[5], ka[kKinkSlots], kb[kKinkSlots];
+    wave_chunk_sums<DT, KIND, RESID>(rp[i], rq[i], prow, qrow, cc, c1, c0p, c0q, rho32, tab, v,
+                                     ka, kb);
+    if (lane == 0) {
+      DrawPart* p = &part[cc];
+      st_dev_d(&p->sp, v[0]);
+      st_dev_d(&p->sq, v[1]);
+      st_dev_d(&p->w, v[2]);
+      st_dev_d(&p->dq, v[3]);
+      st_dev_d(&p->nk, v[4]);
+      for (int j = 0; j < kKinkSlots; ++j) {
+        st_dev_d(&p->ka[j], ka[j]);
+        st_dev_d(&p->kb[j], kb[j]);
+      }
     }
   }
 }
@@ -366,15 +465,23 @@ __device__ __forceinline__ void search_terms(const void* prow, const void* qrow,
 // and the sums here).
 template <int DT, int KIND>
 __device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk, bool resid,
-                            double c1, double c0p, double c0q, double rho, double P, double thr,
-                            const double* tab) {
+                            double c1, double c0p, double c0q, double rho, const double& P,
+                            double thr, const double* tab) {
+  __shared__ int s_tok, s_last;
+  if (threadIdx.x == 0) {
+    s_tok = INT_MAX;
+    s_last = -1;
+  }
   double w[kSearchPerThread];
   long j0;
   search_terms<DT, KIND>(prow, qrow, V, chunk, resid, c1, c0p, c0q, rho, tab, w, j0);
   double tsum = 0.0;
 #pragma unroll
   for (int e = 0; e < kSearchPerThread; ++e) tsum += w[e];
+  // The scan's barriers order the initialisation above and the caller's
+  // store of P before the reads below.
   const double excl = block_exclusive_scan_d(tsum);
+  const double P0 = P;
   int tok = INT_MAX, lastpos = -1;
   double run = 0.0;
 #pragma unroll
@@ -382,12 +489,17 @@ __device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk
     run += w[e];
     if (j0 + e < V) {
       if (w[e] > 0.0) lastpos = static_cast<int>(j0 + e);
-      if (tok == INT_MAX && P + (excl + run) > thr) tok = static_cast<int>(j0 + e);
+      if (tok == INT_MAX && P0 + (excl + run) > thr) tok = static_cast<int>(j0 + e);
     }
   }
-  tok = block_min_i(tok);
-  lastpos = -block_min_i(-lastpos);
-  return tok == INT_MAX ? lastpos : tok;
+  // Element indices grow with the lane: the wave's first hit is in its
+  // lowest hitting lane, its last positive weight in its highest lane.
+  const int lane = threadIdx.x & 63;
+  const uint64_t mt = __ballot(tok != INT_MAX), ml = __ballot(lastpos >= 0);
+  if (mt != 0 && lane == __builtin_ctzll(mt)) atomicMin(&s_tok, tok);
+  if (ml != 0 && lane == 63 - __builtin_clzll(ml)) atomicMax(&s_last, lastpos);
+  __syncthreads();
+  return s_tok == INT_MAX ? s_last : s_tok;
 }
 
 // Per-request marker of the one-launch kernel: set to the call's epoch once
