@@ -26,12 +26,11 @@
  *  - `ws` is a caller-owned device workspace of at least
  *    spec_workspace_bytes(B, n_pos, V) bytes.  It must be zero-filled before
  *    its first use.  Its first SPEC_WORKSPACE_COUNTER_BYTES bytes hold
- *    per-request completion counters and markers and a call epoch at fixed
- *    places, which the library keeps consistent from one call to the next
- *    (the caller must not write to them after the initial zero fill), so one
- *    workspace serves calls of any shape without clearing it; the rest is
- *    scratch that each call writes before reading.  Calls that share a
- *    workspace must be ordered on one stream.
+ *    per-request completion counters and ready markers at fixed places;
+ *    every call leaves them zero again when it completes, so one workspace
+ *    serves calls of any shape without clearing it (the caller must not
+ *    write to them); the rest is scratch that each call writes before
+ *    reading.  Calls that share a workspace must be ordered on one stream.
  *  - Return value: SPEC_OK, or a negative code.  Any code other than
  *    SPEC_EHIP means the arguments were rejected on the host and nothing was
  *    enqueued.  SPEC_EHIP reports a failed HIP launch.
@@ -53,7 +52,7 @@ extern "C" {
 #endif
 
 /* Bytes at the start of every workspace that must be zero before the first
- * call and are the library's from then on. */
+ * call; each completed call leaves them zero. */
 #define SPEC_WORKSPACE_COUNTER_BYTES (1048576 + 256)
 
 /* Element type of logit / probability tensors. */

@@ -262,7 +262,7 @@ COUNTER_BYTES = (1 << 20) + 256  # SPEC_WORKSPACE_COUNTER_BYTES: fixed region at
 def test_workspace_reuse_with_stale_partials(sample_path):
     """A workspace whose scratch holds garbage (as left by calls of other
     shapes) gives the same results: only the counter region must start at
-    zero, and the library keeps it consistent from call to call."""
+    zero, and every completed call leaves it zero again."""
     ws = S.Workspace(DEV)
     buf = ws.get(S.spec_workspace_bytes(64, 9, 128256))
     buf[COUNTER_BYTES:].fill_(0xA5)
@@ -279,4 +279,6 @@ def test_workspace_reuse_with_stale_partials(sample_path):
         ggot = S.spec_verify_greedy(to_device(g.target, "f32"), ints_to_device(g.draft_tokens),
                                     workspace=ws)
         assert all(torch.equal(a, b) for a, b in zip(gref, ggot))
+        torch.cuda.synchronize()
+        assert int(buf[:COUNTER_BYTES].count_nonzero()) == 0
         buf[COUNTER_BYTES:].fill_(0x5A)

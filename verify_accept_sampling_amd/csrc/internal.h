@@ -90,12 +90,10 @@ static_assert(sizeof(DrawPart) == 80, "DrawPart layout");
 
 // Per-request words of the counter region: [0] row-pass completion
 // ticket, [1] draw completion ticket, [2..3] the one-launch kernel's 64-bit
-// "state published" marker.  After them, the one-launch kernel's control
-// words: [0..1] 64-bit call epoch, [2] count of requests finished in this
-// call.
+// ready marker.  Every word is back to 0 when a call completes.  The last
+// 256 bytes are reserved.
 constexpr int kCountersPerReq = 4;
-constexpr size_t kControlOffsetWords = (size_t)kMaxB * kCountersPerReq;
-constexpr size_t kCounterRegionBytes = kControlOffsetWords * 4 + 256;
+constexpr size_t kCounterRegionBytes = (size_t)kMaxB * kCountersPerReq * 4 + 256;
 static_assert(kCounterRegionBytes == SPEC_WORKSPACE_COUNTER_BYTES, "counter region");
 
 // Workspace layout.  The counter region (kCounterRegionBytes) sits at a

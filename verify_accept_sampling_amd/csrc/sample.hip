@@ -29,16 +29,18 @@
 // same thing.
 // Probabilities path (rows given as distributions): k_draw alone, each
 // work-group first repeating the (gather-only) acceptance tests.
+#include <atomic>
+
 #include "sample_device.h"
 
 namespace specv {
 
-// Row pass of one work-group: block `bid` of the row-pass grid.  epoch is 0
-// on the two-launch path; in the one-launch kernel it is the call's epoch,
-// and the request's state is followed by a marker holding it.
+// Row pass of one work-group: block `bid` of the row-pass grid.  In the
+// one-launch kernel (one_launch) the request's state is followed by its
+// ready marker, set to 1.
 template <int DT, int NE>
 __device__ __forceinline__ void row_block(
-    long bid, uint64_t epoch, const void* __restrict__ target, const void* __restrict__ draft,
+    long bid, bool one_launch, const void* __restrict__ target, const void* __restrict__ draft,
     int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
@@ -146,9 +148,9 @@ __device__ __forceinline__ void row_block(
         n < k ? s_s[k + 1 + n] * exp2((double)mul_rn(mq, c) - (double)mq * c) : 1.0;
     accepted_len[b] = n;
     st_dev_state(&state[b], ReqState{n, n < k ? kModeResidual : kModeBonus, mp, mq, sp / sq});
-    if (epoch != 0) {
+    if (one_launch) {
       wait_stores();  // the state is complete before its marker
-      st_dev(ready_marker(counters, b), epoch);
+      st_dev(ready_marker(counters, b), (uint64_t)1);
     }
     if (probe) {
       float* pr = probe + ((long)b * (k + 1) + k) * 4;
@@ -205,17 +207,17 @@ __device__ int accept_scan_probs(const float* target, const float* draft, int b,
   return n;
 }
 
-// Draw of one work-group: block `bid` of the draw grid.  epoch as for
-// row_block: in the one-launch kernel the block first waits for the marker
-// of its request's state.
+// Draw of one work-group: block `bid` of the draw grid.  In the one-launch
+// kernel (one_launch) the block first waits for the ready marker of its
+// request's state, and the request's last work-group clears it.
 template <int DT, int NE, int KIND>
 __device__ __forceinline__ void draw_block(
-    long bid, uint64_t epoch, const void* __restrict__ target, const void* __restrict__ draft,
+    long bid, bool one_launch, const void* __restrict__ target, const void* __restrict__ draft,
     int k, int V, int C2, double inv_t, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe, const ReqState* __restrict__ state, DrawPart* __restrict__ part,
-    unsigned* __restrict__ counters, unsigned* __restrict__ control, int B) {
+    unsigned* __restrict__ counters) {
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
   const int b = static_cast<int>(bid / G2);
   const int grp = static_cast<int>(bid % G2);
@@ -225,9 +227,9 @@ __device__ __forceinline__ void draw_block(
   int n;
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
-    if (epoch != 0) {
+    if (one_launch) {
       __shared__ int s_ok;
-      if (threadIdx.x == 0) s_ok = wait_marker(ready_marker(counters, b), epoch) ? 1 : 0;
+      if (threadIdx.x == 0) s_ok = wait_marker(ready_marker(counters, b)) ? 1 : 0;
       __syncthreads();
       if (!s_ok) return;  // never expected: the request's state did not appear
     }
@@ -411,15 +413,9 @@ __device__ __forceinline__ void draw_block(
       else mass = mode == 0 ? grand : (resid ? 0.0 : grand);
       probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
-    if (epoch != 0) {
-      // The request that finishes last advances the epoch for the next call.
-      const unsigned done =
-          __hip_atomic_fetch_add(&control[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (done == (unsigned)B - 1u) {
-        __hip_atomic_store(&control[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        st_dev(reinterpret_cast<uint64_t*>(control), epoch);
-      }
-    }
+    // Every draw work-group of the request has passed its wait (each took
+    // the ticket after it): the marker goes back to 0 for the next call.
+    if (one_launch) st_dev(ready_marker(counters, b), (uint64_t)0);
   }
 }
 
@@ -431,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, float* __restrict__ probe, uint64_t* __restrict__ part,
     float* __restrict__ zrow, ReqState* __restrict__ state, unsigned* __restrict__ counters) {
-  row_block<DT, NE>(blockIdx.x, 0, target, draft, k, V, C1, c, draft_tokens, uniforms, seed, ctr0,
+  row_block<DT, NE>(blockIdx.x, false, target, draft, k, V, C1, c, draft_tokens, uniforms, seed, ctr0,
                     accepted_len, out_tokens, probe, part, zrow, state, counters);
 }
 
@@ -443,9 +439,9 @@ __global__ __launch_bounds__(kThreads) void k_draw(
     int32_t* __restrict__ out_tokens, float* __restrict__ probe,
     const ReqState* __restrict__ state, DrawPart* __restrict__ part,
     unsigned* __restrict__ counters) {
-  draw_block<DT, NE, KIND>(blockIdx.x, 0, target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
-                           seed, ctr0, accepted_len, out_tokens, probe, state, part, counters,
-                           nullptr, 0);
+  draw_block<DT, NE, KIND>(blockIdx.x, false, target, draft, k, V, C2, inv_t, draft_tokens,
+                           uniforms, seed, ctr0, accepted_len, out_tokens, probe, state, part,
+                           counters);
 }
 
 // One-launch path: the row-pass work-groups, then the draw work-groups
@@ -464,16 +460,14 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe, uint64_t* __restrict__ part1, float* __restrict__ zrow,
     ReqState* __restrict__ state, DrawPart* __restrict__ part2, unsigned* __restrict__ counters,
-    unsigned* __restrict__ control, long n_row_blocks) {
-  // This call's markers carry the epoch after the stored one.
-  const uint64_t epoch = ld_dev(reinterpret_cast<const uint64_t*>(control)) + 1;
+    long n_row_blocks) {
   if ((long)blockIdx.x < n_row_blocks)
-    row_block<DT, NE>(blockIdx.x, epoch, target, draft, k, V, C1, c, draft_tokens, uniforms, seed,
+    row_block<DT, NE>(blockIdx.x, true, target, draft, k, V, C1, c, draft_tokens, uniforms, seed,
                       ctr0, accepted_len, out_tokens, probe, part1, zrow, state, counters);
   else
-    draw_block<DT, NE, 0>((long)blockIdx.x - n_row_blocks, epoch, target, draft, k, V, C2, inv_t,
+    draw_block<DT, NE, 0>((long)blockIdx.x - n_row_blocks, true, target, draft, k, V, C2, inv_t,
                           draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe,
-                          state, part2, counters, control, B);
+                          state, part2, counters);
 }
 
 // ---------------------------------------------------------------------------
@@ -481,6 +475,49 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
 // ---------------------------------------------------------------------------
 
 static int row_chunks(int V) { return (V + kRowChunkElems - 1) / kRowChunkElems; }
+
+// Work-groups of the one-launch kernel resident per compute unit.  The row
+// pass runs in rounds of (compute units x this) work-groups, and the early
+// requests' draws share the second round.  Measured at B = 64, k = 8,
+// V = 128256 bf16: 4 per unit +2 us per call, 5 best, 6 +9 us.
+constexpr int kOneLaunchGroupsPerCU = 5;
+
+// Shared memory per compute unit of the current device.
+static int device_lds_per_cu() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+        hipSuccess)
+      return 0;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Dynamic shared memory for the one-launch kernel: at least `need`, and
+// with the kernel's static shared memory more than 1/(groups + 1) of a
+// compute unit's (plus allocation granularity), so that at most
+// kOneLaunchGroupsPerCU work-groups are resident per unit.
+template <int DT, int NE>
+static uint32_t one_launch_lds(uint32_t need) {
+  static std::atomic<int> static_lds{-1};
+  int sl = static_lds.load(std::memory_order_relaxed);
+  if (sl < 0) {
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&k_sample_one<DT, NE>)) !=
+        hipSuccess)
+      return need;
+    sl = static_cast<int>(fa.sharedSizeBytes);
+    static_lds.store(sl, std::memory_order_relaxed);
+  }
+  const int lds_cu = device_lds_per_cu();
+  if (lds_cu <= 0) return need;
+  const long pad = (long)lds_cu / (kOneLaunchGroupsPerCU + 1) + 1024 - sl;
+  return pad > (long)need ? static_cast<uint32_t>(pad) : need;
+}
 
 // 16-byte loads need every row to start on a 16-byte boundary; the buffer
 // loads of the row-statistics sweep address rows below 2 GiB.
@@ -511,11 +548,10 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   const long n_row = (long)B * R * C1;
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
   if (g_sample_path.load(std::memory_order_relaxed) == SPEC_PATH_AUTO) {
-    unsigned* control = cnt + kControlOffsetWords;
     return launch_timed(kProfFused, &k_sample_one<DT, NE>, dim3((unsigned)(n_row + (long)B * G2)),
-                        dim3(kThreads), lds, s, target, draft, B, k, V, C1, C2, c, inv_t,
+                        dim3(kThreads), one_launch_lds<DT, NE>(lds), s, target, draft, B, k, V, C1, C2, c, inv_t,
                         draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1,
-                        zr, st, p2, cnt, control, n_row);
+                        zr, st, p2, cnt, n_row);
   }
   hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>, dim3((unsigned)n_row),
                              dim3(kThreads), lds, s, target, draft, k, V, C1, c, draft_tokens,

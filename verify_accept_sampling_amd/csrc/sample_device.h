@@ -502,8 +502,8 @@ __device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk
   return s_tok == INT_MAX ? s_last : s_tok;
 }
 
-// Per-request marker of the one-launch kernel: set to the call's epoch once
-// the request's state (acceptance result) is published.
+// Per-request ready marker of the one-launch kernel: 1 once the request's
+// state (acceptance result) is published, 0 again when its draw is done.
 __device__ __forceinline__ uint64_t* ready_marker(unsigned* counters, int b) {
   return reinterpret_cast<uint64_t*>(&counters[(long)b * kCountersPerReq + 2]);
 }
@@ -531,10 +531,10 @@ __device__ __forceinline__ ReqState ld_dev_state(const ReqState* p) {
 // wait lasts microseconds).
 constexpr long kSpinLimit = 1L << 20;
 
-// One thread waits until *marker == epoch.  False if the bound is reached.
-__device__ __forceinline__ bool wait_marker(const uint64_t* marker, uint64_t epoch) {
+// One thread waits until the marker is set.  False if the bound is reached.
+__device__ __forceinline__ bool wait_marker(const uint64_t* marker) {
   for (long spin = 0; spin < kSpinLimit; ++spin) {
-    if (ld_dev(marker) == epoch) return true;
+    if (ld_dev(marker) != 0) return true;
     __builtin_amdgcn_s_sleep(2);
   }
   return false;
