@@ -48,7 +48,7 @@ def traffic_file(kernel: str) -> str:
 # 2k+1 = 17 rows of all 64 requests read once (bf16).
 ALGO_ROW_BYTES = 64 * 17 * 128256 * 2
 # Elements of the chunk the inverse-CDF search reads again.
-DRAW_CHUNK = 1024
+DRAW_CHUNK = 512
 KERNEL_SOURCES = ["verify_accept_sampling_amd/csrc/sample.hip",
                   "verify_accept_sampling_amd/csrc/sample_device.h",
                   "verify_accept_sampling_amd/csrc/device_common.h",

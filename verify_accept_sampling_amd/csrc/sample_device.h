@@ -400,18 +400,18 @@ __device__ __forceinline__ void wave_draw_chunks(const void* prow, const void* q
     double v[5], ka[kKinkSlots], kb[kKinkSlots];
     wave_chunk_sums<DT, KIND, RESID>(rp[i], rq[i], prow, qrow, cc, c1, c0p, c0q, rho32, tab, v,
                                      ka, kb);
-    if (lane == 0) {
-      DrawPart* p = &part[cc];
-      st_dev_d(&p->sp, v[0]);
-      st_dev_d(&p->sq, v[1]);
-      st_dev_d(&p->w, v[2]);
-      st_dev_d(&p->dq, v[3]);
-      st_dev_d(&p->nk, v[4]);
-      for (int j = 0; j < kKinkSlots; ++j) {
-        st_dev_d(&p->ka[j], ka[j]);
-        st_dev_d(&p->kb[j], kb[j]);
-      }
-    }
+    // Lane f stores field f of the record: one coalesced store.
+    static_assert(sizeof(DrawPart) == 10 * sizeof(double) && kKinkSlots == 2, "DrawPart fields");
+    double f = v[0];
+    f = lane == 1 ? v[1] : f;
+    f = lane == 2 ? v[2] : f;
+    f = lane == 3 ? v[3] : f;
+    f = lane == 4 ? v[4] : f;
+    f = lane == 5 ? ka[0] : f;
+    f = lane == 6 ? ka[1] : f;
+    f = lane == 7 ? kb[0] : f;
+    f = lane == 8 ? kb[1] : f;
+    if (lane < 9) st_dev_d(reinterpret_cast<double*>(&part[cc]) + lane, f);
   }
 }
 
