@@ -89,8 +89,9 @@ struct DrawPart {
 static_assert(sizeof(DrawPart) == 80, "DrawPart layout");
 
 // Per-request words of the counter region: [0] row-pass completion
-// ticket, [1] draw completion ticket, [2..3] the one-launch kernel's 64-bit
-// ready marker.  Every word is back to 0 when a call completes.  The last
+// ticket, [1] draw completion ticket, [2..3] a 64-bit ready marker slot of
+// the one-launch kernel (slot j holds the marker of request j with its two
+// bytes swapped).  Every word is back to 0 when a call completes.  The last
 // 256 bytes are reserved.
 constexpr int kCountersPerReq = 4;
 constexpr size_t kCounterRegionBytes = (size_t)kMaxB * kCountersPerReq * 4 + 256;

@@ -35,62 +35,68 @@
 
 namespace specv {
 
-// Row pass of one work-group: block `bid` of the row-pass grid.  In the
-// one-launch kernel (one_launch) the request's state is followed by its
-// ready marker, set to 1.
+// Statistic of chunk `chunk` (of C1) of row r of request b: the sweep, the
+// block reduction, and thread 0's coherent stores of the (reference, sum)
+// pair and, in the chunk holding the row's draft token, of the logit there.
+// Every thread returns.
 template <int DT, int NE>
-__device__ __forceinline__ void row_block(
-    long bid, bool one_launch, const void* __restrict__ target, const void* __restrict__ draft,
-    int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
-    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
-    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probe, uint64_t* __restrict__ part, float* __restrict__ zrow,
-    ReqState* __restrict__ state, unsigned* __restrict__ counters) {
+__device__ __forceinline__ void row_chunk_stat(int b, int r, int chunk,
+                                               const void* __restrict__ target,
+                                               const void* __restrict__ draft, int k, int V,
+                                               int C1, float c,
+                                               const int32_t* __restrict__ draft_tokens,
+                                               uint64_t* __restrict__ part,
+                                               float* __restrict__ zrow) {
   const int R = 2 * k + 1;
-  const int chunk = static_cast<int>(bid % C1);
-  const long rowid = bid / C1;
-  const int b = static_cast<int>(rowid / R);
-  const int r = static_cast<int>(rowid % R);
-  {
-    const void* rp = stat_row<DT>(target, draft, b, r, k, V);
-    // The draft token this row is tested at (target row i and draft row i
-    // share x_i; the bonus row k has none), loaded now and used after the
-    // sweep.
-    const int tpos = r < k ? r : (r > k ? r - k - 1 : -1);
-    int x = -1;
-    if (threadIdx.x == 0 && tpos >= 0) x = draft_tokens[(long)b * k + tpos];
-    const long n_groups = V / NE;
-    const long gpc = (n_groups + C1 - 1) / C1;
-    const long g0 = (long)chunk * gpc;
-    const long g1 = min(g0 + gpc, n_groups);
-    float m = -INFINITY, mc = -INFINITY;
-    double s = 0.0;
-    if constexpr (NE == 1)
-      stats_sweep_scalar<DT>(rp, g0, g1, c, m, mc, s);
-    else
-      stats_sweep<DT, kThreads>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0, g1,
-                                c, m, mc, s, threadIdx.x);
-    // The chunk that holds the token also publishes the logit there.
-    const bool own = x >= 0 && x < V && (long)x >= g0 * NE && (long)x < g1 * NE;
-    float zx = 0.f;
-    if (own) zx = load_elem<DT>(rp, x);
-    block_reduce_ms(m, s, c);
-    if (threadIdx.x >= kWaveSize) return;  // wave 0 finishes the work-group
-    if (threadIdx.x == 0) {
-      st_dev(&part[rowid * C1 + chunk], pack2(m, (float)s));
-      if (own) st_dev_f(&zrow[rowid], zx);
-    }
+  const long rowid = (long)b * R + r;
+  const void* rp = stat_row<DT>(target, draft, b, r, k, V);
+  // The draft token this row is tested at (target row i and draft row i
+  // share x_i; the bonus row k has none), loaded now and used after the
+  // sweep.
+  const int tpos = r < k ? r : (r > k ? r - k - 1 : -1);
+  int x = -1;
+  if (threadIdx.x == 0 && tpos >= 0) x = draft_tokens[(long)b * k + tpos];
+  const long n_groups = V / NE;
+  const long gpc = (n_groups + C1 - 1) / C1;
+  const long g0 = (long)chunk * gpc;
+  const long g1 = min(g0 + gpc, n_groups);
+  float m = -INFINITY, mc = -INFINITY;
+  double s = 0.0;
+  if constexpr (NE == 1)
+    stats_sweep_scalar<DT>(rp, g0, g1, c, m, mc, s);
+  else
+    stats_sweep<DT, kThreads>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0, g1, c,
+                              m, mc, s, threadIdx.x);
+  // The chunk that holds the token also publishes the logit there.
+  const bool own = x >= 0 && x < V && (long)x >= g0 * NE && (long)x < g1 * NE;
+  float zx = 0.f;
+  if (own) zx = load_elem<DT>(rp, x);
+  block_reduce_ms(m, s, c);
+  if (threadIdx.x == 0) {
+    st_dev(&part[rowid * C1 + chunk], pack2(m, (float)s));
+    if (own) st_dev_f(&zrow[rowid], zx);
   }
-  if (!wave_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
+}
 
-  // ---- last work-group of request b, one wave: acceptance tests ----
-  // Lane i handles position i (and i + 64, ...): it loads the token, the two
-  // published token logits and the chunk partials of target row i and draft
-  // row i in one round, merges the rows and tests draft i.
+// Acceptance tests of request b by one wave, from its published row
+// statistics.  Lane i handles position i (and i + 64, ...): it loads the
+// token, the two published token logits and the chunk partials of target
+// row i and draft row i in one round, merges the rows and tests draft i.
+// Returns the draw state (n valid in every lane, the rest in lane 0).  With
+// `write` it also stores accepted_len[b], the accepted prefix, the -1
+// padding and the probe values other than probe[b, n, 2], which belongs to
+// the draw.  Uses R doubles and R floats of dynamic shared memory.
+__device__ __forceinline__ ReqState finalize_request(
+    int b, int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
+    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    const uint64_t* __restrict__ part, const float* __restrict__ zrow, bool write,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probe) {
+  const int R = 2 * k + 1;
   extern __shared__ double dyn_lds[];
-  double* s_s = dyn_lds;                             // [R]
+  double* s_s = dyn_lds;                               // [R]
   float* s_m = reinterpret_cast<float*>(dyn_lds + R);  // [R]
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   int first = k;
   for (int i = lane; i <= k; i += kWaveSize) {
     const bool draft_pos = i < k;
@@ -123,22 +129,25 @@ __device__ __forceinline__ void row_block(
       qv = (float)exp2(lq);
     }
     if (!accept) first = min(first, i);
-    if (probe) {
+    if (write && probe) {
       float* pr = probe + ((long)b * (k + 1) + i) * 4;
       pr[0] = pv; pr[1] = qv; pr[3] = 0.f;
     }
   }
   const int n = wave_min_i(first);
   wave_lds_sync();
-  for (int i = lane; i <= k; i += kWaveSize) {
-    if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
-    else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
-    // probe[b, n, 2] (the mass drawn from) belongs to the draw, which may
-    // run in another work-group of the same launch
-    if (probe && i != n) probe[((long)b * (k + 1) + i) * 4 + 2] = 0.f;
+  if (write) {
+    for (int i = lane; i <= k; i += kWaveSize) {
+      if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
+      else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
+      // probe[b, n, 2] (the mass drawn from) belongs to the draw, which may
+      // run in another work-group of the same launch
+      if (probe && i != n) probe[((long)b * (k + 1) + i) * 4 + 2] = 0.f;
+    }
   }
   // State for the draw: references of target row n and (rejection) draft
   // row n, and the float32-based normaliser ratio of that pair.
+  ReqState st{n, n < k ? kModeResidual : kModeBonus, 0.f, 0.f, 1.0};
   if (lane == 0) {
     const float mp = s_m[n];
     const float mq = n < k ? s_m[k + 1 + n] : 0.f;
@@ -146,15 +155,48 @@ __device__ __forceinline__ void row_block(
     const double sp = s_s[n] * exp2((double)mul_rn(mp, c) - (double)mp * c);
     const double sq =
         n < k ? s_s[k + 1 + n] * exp2((double)mul_rn(mq, c) - (double)mq * c) : 1.0;
-    accepted_len[b] = n;
-    st_dev_state(&state[b], ReqState{n, n < k ? kModeResidual : kModeBonus, mp, mq, sp / sq});
+    st.mp = mp;
+    st.mq = mq;
+    st.rho32 = sp / sq;
+    if (write) {
+      accepted_len[b] = n;
+      if (probe) {
+        float* pr = probe + ((long)b * (k + 1) + k) * 4;
+        pr[0] = 0.f; pr[1] = 0.f; pr[3] = 0.f;
+      }
+    }
+  }
+  return st;
+}
+
+// Row pass of one work-group: block `bid` of the row-pass grid.  The
+// request's last work-group (by ticket) runs the acceptance tests on one
+// wave and stores the draw state.  In the grid-ordered one-launch kernel
+// (one_launch) the state is followed by its ready marker, set to 1.
+template <int DT, int NE>
+__device__ __forceinline__ void row_block(
+    long bid, bool one_launch, const void* __restrict__ target, const void* __restrict__ draft,
+    int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
+    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probe, uint64_t* __restrict__ part, float* __restrict__ zrow,
+    ReqState* __restrict__ state, unsigned* __restrict__ counters) {
+  const int R = 2 * k + 1;
+  const int chunk = static_cast<int>(bid % C1);
+  const long rowid = bid / C1;
+  const int b = static_cast<int>(rowid / R);
+  const int r = static_cast<int>(rowid % R);
+  row_chunk_stat<DT, NE>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens, part, zrow);
+  if (threadIdx.x >= kWaveSize) return;  // wave 0 finishes the work-group
+  if (!wave_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
+  // ---- last work-group of request b, one wave: acceptance tests ----
+  const ReqState st = finalize_request(b, k, V, C1, c, draft_tokens, uniforms, seed, ctr0, part,
+                                       zrow, true, accepted_len, out_tokens, probe);
+  if ((threadIdx.x & 63) == 0) {
+    st_dev_state(&state[b], st);
     if (one_launch) {
       wait_stores();  // the state is complete before its marker
       st_dev(ready_marker(counters, b), (uint64_t)1);
-    }
-    if (probe) {
-      float* pr = probe + ((long)b * (k + 1) + k) * 4;
-      pr[0] = 0.f; pr[1] = 0.f; pr[3] = 0.f;
     }
   }
 }
@@ -207,27 +249,31 @@ __device__ int accept_scan_probs(const float* target, const float* draft, int b,
   return n;
 }
 
-// Draw of one work-group: block `bid` of the draw grid.  In the one-launch
-// kernel (one_launch) the block first waits for the ready marker of its
-// request's state, and the request's last work-group clears it.
+// How a draw work-group learns its request's state.
+enum {
+  kStateStored = 0,  // from the state array, written by an earlier launch
+  kStateMarker = 1,  // from the state array once the request's ready marker is set
+};
+
+// Draw of one work-group: chunk group grp of request b.  With kStateMarker
+// the work-group first waits for the request's ready marker, and the
+// request's last draw work-group clears it.
 template <int DT, int NE, int KIND>
 __device__ __forceinline__ void draw_block(
-    long bid, bool one_launch, const void* __restrict__ target, const void* __restrict__ draft,
+    int b, int grp, int how, const void* __restrict__ target, const void* __restrict__ draft,
     int k, int V, int C2, double inv_t, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe, const ReqState* __restrict__ state, DrawPart* __restrict__ part,
     unsigned* __restrict__ counters) {
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  const int b = static_cast<int>(bid / G2);
-  const int grp = static_cast<int>(bid % G2);
   __shared__ double tab[256];
   static_assert(kThreads == 256, "one table entry per thread");
   if (KIND == 0) tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
   int n;
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
-    if (one_launch) {
+    if (how == kStateMarker) {
       __shared__ int s_ok;
       if (threadIdx.x == 0) s_ok = wait_marker(ready_marker(counters, b)) ? 1 : 0;
       __syncthreads();
@@ -414,8 +460,9 @@ __device__ __forceinline__ void draw_block(
       probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
     // Every draw work-group of the request has passed its wait (each took
-    // the ticket after it): the marker goes back to 0 for the next call.
-    if (one_launch) st_dev(ready_marker(counters, b), (uint64_t)0);
+    // the ticket after it): the marker or row-pass count goes back to 0 for
+    // the next call.
+    if (how == kStateMarker) st_dev(ready_marker(counters, b), (uint64_t)0);
   }
 }
 
@@ -439,9 +486,10 @@ __global__ __launch_bounds__(kThreads) void k_draw(
     int32_t* __restrict__ out_tokens, float* __restrict__ probe,
     const ReqState* __restrict__ state, DrawPart* __restrict__ part,
     unsigned* __restrict__ counters) {
-  draw_block<DT, NE, KIND>(blockIdx.x, false, target, draft, k, V, C2, inv_t, draft_tokens,
-                           uniforms, seed, ctr0, accepted_len, out_tokens, probe, state, part,
-                           counters);
+  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  draw_block<DT, NE, KIND>(static_cast<int>(blockIdx.x / G2), static_cast<int>(blockIdx.x % G2),
+                           kStateStored, target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
+                           seed, ctr0, accepted_len, out_tokens, probe, state, part, counters);
 }
 
 // One-launch path: the row-pass work-groups, then the draw work-groups
@@ -464,10 +512,13 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
   if ((long)blockIdx.x < n_row_blocks)
     row_block<DT, NE>(blockIdx.x, true, target, draft, k, V, C1, c, draft_tokens, uniforms, seed,
                       ctr0, accepted_len, out_tokens, probe, part1, zrow, state, counters);
-  else
-    draw_block<DT, NE, 0>((long)blockIdx.x - n_row_blocks, true, target, draft, k, V, C2, inv_t,
-                          draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe,
-                          state, part2, counters);
+  else {
+    const long db = (long)blockIdx.x - n_row_blocks;
+    const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+    draw_block<DT, NE, 0>(static_cast<int>(db / G2), static_cast<int>(db % G2), kStateMarker,
+                          target, draft, k, V, C2, inv_t, draft_tokens, uniforms, seed, ctr0,
+                          accepted_len, out_tokens, probe, state, part2, counters);
+  }
 }
 
 // ---------------------------------------------------------------------------

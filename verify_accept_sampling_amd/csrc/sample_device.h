@@ -504,8 +504,14 @@ __device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk
 
 // Per-request ready marker of the one-launch kernel: 1 once the request's
 // state (acceptance result) is published, 0 again when its draw is done.
+// Request b's marker sits in the marker slot of request j, j = b with its
+// two bytes swapped, so the markers of up to 256 consecutive requests are
+// 4 KB apart: many work-groups waiting on neighbouring requests then poll
+// different memory channels instead of one.
 __device__ __forceinline__ uint64_t* ready_marker(unsigned* counters, int b) {
-  return reinterpret_cast<uint64_t*>(&counters[(long)b * kCountersPerReq + 2]);
+  static_assert(kMaxB == 65536, "two-byte request index");
+  const long j = (long)((b & 255) << 8 | (b >> 8 & 255));
+  return reinterpret_cast<uint64_t*>(&counters[j * kCountersPerReq + 2]);
 }
 
 // ReqState through coherent 64-bit words (read by other work-groups).
@@ -527,7 +533,7 @@ __device__ __forceinline__ ReqState ld_dev_state(const ReqState* p) {
   return v;
 }
 
-// Polls of a marker before a wait gives up (about a second; a legitimate
+// Polls of a marker before a wait gives up (a few seconds; a legitimate
 // wait lasts microseconds).
 constexpr long kSpinLimit = 1L << 20;
 
@@ -535,7 +541,9 @@ constexpr long kSpinLimit = 1L << 20;
 __device__ __forceinline__ bool wait_marker(const uint64_t* marker) {
   for (long spin = 0; spin < kSpinLimit; ++spin) {
     if (ld_dev(marker) != 0) return true;
-    __builtin_amdgcn_s_sleep(2);
+    // A few quick polls, then about 2000 cycles between polls.
+    if (spin < 4) __builtin_amdgcn_s_sleep(2);
+    else __builtin_amdgcn_s_sleep(32);
   }
   return false;
 }
