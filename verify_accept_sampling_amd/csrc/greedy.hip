@@ -19,8 +19,9 @@
 
 namespace specv {
 
-// Groups in flight per thread in the streaming loop.
-constexpr int kUnrollArgmax = kRowUnroll;
+// Smallest row chunk the greedy kernels split rows into.
+constexpr int kMinChunkElems = 16384;
+static_assert(kMinChunkElems >= kRowChunkElemsMin, "partials are sized for chunks of at least this");
 
 // Fold one group of NE elements (group index gi) into the running argmax;
 // a strict '>' keeps the lowest index because groups arrive in ascending
@@ -41,25 +42,80 @@ __device__ __forceinline__ void argmax_update(float& bv, int& bi, const float (&
 }
 
 // Argmax of this thread's groups in [g0, g1) (ascending, so a strict '>'
-// keeps the lowest index).  NE = elements per load.
+// keeps the lowest index).  NE = elements per load.  Scalar loads (NE = 1,
+// rows that are not 16-byte aligned).
 template <int DT, int NE>
 __device__ __forceinline__ void argmax_sweep(const void* row, long g0, long g1, float& bv,
                                              int& bi) {
   bv = -INFINITY;
   bi = INT_MAX;
-  long g = g0 + threadIdx.x;
-  // Main loop: kUnrollArgmax loads issued back to back, no bounds branch.
-  for (; g + (long)(kUnrollArgmax - 1) * kThreads < g1; g += (long)kThreads * kUnrollArgmax) {
-    float x[kUnrollArgmax][NE];
-#pragma unroll
-    for (int u = 0; u < kUnrollArgmax; ++u)
-      load_group<DT, NE, true>(row, (g + (long)u * kThreads) * NE, x[u]);
-#pragma unroll
-    for (int u = 0; u < kUnrollArgmax; ++u) argmax_update<NE>(bv, bi, x[u], g + (long)u * kThreads);
-  }
-  for (; g < g1; g += kThreads) {
+  for (long g = g0 + threadIdx.x; g < g1; g += kThreads) {
     float x[NE];
     load_group<DT, NE, true>(row, g * NE, x);
+    argmax_update<NE>(bv, bi, x, g);
+  }
+}
+
+// Fold kArgmaxBatch words (groups g, g + NT, ...) into the running argmax.
+constexpr int kArgmaxBatch = 4;
+template <int DT, int NT>
+__device__ __forceinline__ void argmax_words(float& bv, int& bi, const u32x4 (&w)[kArgmaxBatch],
+                                             long g) {
+  constexpr int NE = Elems<DT>::kVec;
+#pragma unroll
+  for (int u = 0; u < kArgmaxBatch; ++u) {
+    float x[NE];
+    unpack16<DT>(w[u], x);
+    argmax_update<NE>(bv, bi, x, g + (long)u * NT);
+  }
+}
+
+// 16-byte form over a row of row_bytes bytes: buffer loads (base and size
+// in SGPRs, one 32-bit lane offset) in two word buffers used in turn, so the
+// next batch is in flight while the current one is folded in.
+template <int DT, int NT>
+__device__ __forceinline__ void argmax_sweep_buf(const void* row, uint32_t row_bytes, long g0,
+                                                 long g1, float& bv, int& bi) {
+  constexpr int NE = Elems<DT>::kVec;
+  constexpr uint32_t kStep = NT * kArgmaxBatch * 16u;
+  bv = -INFINITY;
+  bi = INT_MAX;
+  const RowBuf buf(row, row_bytes);
+  long g = g0 + threadIdx.x;
+  uint32_t off = static_cast<uint32_t>(g) * 16u;
+  const long span = (long)(kArgmaxBatch - 1) * NT;
+  if (g + span < g1) {
+    u32x4 wa[kArgmaxBatch], wb[kArgmaxBatch];
+#pragma unroll
+    for (int u = 0; u < kArgmaxBatch; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
+    for (;;) {
+      const long ga = g;
+      g += (long)NT * kArgmaxBatch;
+      off += kStep;
+      if (!(g + span < g1)) {
+        argmax_words<DT, NT>(bv, bi, wa, ga);
+        break;
+      }
+#pragma unroll
+      for (int u = 0; u < kArgmaxBatch; ++u) wb[u] = buf.load_nt(off, u * NT * 16u);
+      __builtin_amdgcn_sched_barrier(0);
+      argmax_words<DT, NT>(bv, bi, wa, ga);
+      const long gb = g;
+      g += (long)NT * kArgmaxBatch;
+      off += kStep;
+      if (!(g + span < g1)) {
+        argmax_words<DT, NT>(bv, bi, wb, gb);
+        break;
+      }
+#pragma unroll
+      for (int u = 0; u < kArgmaxBatch; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
+      __builtin_amdgcn_sched_barrier(0);
+      argmax_words<DT, NT>(bv, bi, wb, gb);
+    }
+  }
+  for (; g < g1; g += NT, off += NT * 16u) {
+    float x[NE];
+    unpack16<DT>(buf.load_nt(off, 0), x);
     argmax_update<NE>(bv, bi, x, g);
   }
 }
@@ -80,7 +136,11 @@ __device__ __forceinline__ bool argmax_chunk(const void* target, int n_pos, int 
   const void* rp = reinterpret_cast<const char*>(target) + row * (long)V * Elems<DT>::kBytes;
   float bv;
   int bi;
-  argmax_sweep<DT, NE>(rp, g0, g1, bv, bi);
+  if constexpr (NE == 1)
+    argmax_sweep<DT, NE>(rp, g0, g1, bv, bi);
+  else
+    argmax_sweep_buf<DT, kThreads>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0,
+                                   g1, bv, bi);
   block_reduce_am(bv, bi);
   if (threadIdx.x == 0) st_dev(&part[row * C1 + chunk], pack2(bv, __int_as_float(bi)));
   return block_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(n_pos * C1));
@@ -185,12 +245,39 @@ __global__ __launch_bounds__(kThreads) void k_tree_greedy(
 // Host launchers
 // ---------------------------------------------------------------------------
 
-static int row_chunks(int V) { return (V + kRowChunkElems - 1) / kRowChunkElems; }
+// Chunks per row: at most as many as keep every (row, chunk) work-group
+// within one round of resident work-groups (a second, partial round streams
+// at low concurrency while the rest of the chip idles) divided by `share`,
+// with chunks of at least 16K elements.  Measured on MI355X at B=64, 9 rows,
+// V=128256 (three chunks: 27.0 us, two: 27.6, four: 28.4; share 1) and at
+// B=16, 61 tree rows (one chunk: 51.5 us, two: 53.7; share 2).
+static int row_chunks(int per_cu, long rows, int V, int share) {
+  int dev = 0, cus = 1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 1;
+  const long by_slots = (long)max(per_cu, 1) * cus / max(rows * share, 1L);
+  const long by_size = ((long)V + kMinChunkElems - 1) / kMinChunkElems;
+  return (int)max(1L, min(by_slots, by_size));
+}
 
-// 16-byte loads need every row to start on a 16-byte boundary.
+// Resident work-groups per compute unit of a kernel (queried once).
+template <typename K>
+static int groups_per_cu(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel),
+                                                   kThreads, 0) != hipSuccess || n <= 0)
+    n = 1;
+  return n;
+}
+
+// 16-byte loads need every row to start on a 16-byte boundary; the buffer
+// loads of the sweep address rows below 2 GiB.
 static bool rows_aligned(const void* p, int V, int dtype) {
-  const int eb = dtype == 1 ? 2 : 4;
-  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && (((long)V * eb) % 16 == 0);
+  const long eb = dtype == 1 ? 2 : 4;
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && (((long)V * eb) % 16 == 0) &&
+         (long)V * eb < (1L << 31);
 }
 
 // Kernel instantiation for the logit type and row alignment.
@@ -199,26 +286,40 @@ static auto pick_kernel(int dtype, bool vec) {
   if (dtype == 1) return vec ? Pick<1, 8>::fn() : Pick<1, 1>::fn();
   return vec ? Pick<0, 4>::fn() : Pick<0, 1>::fn();
 }
+template <template <int, int> class Pick>
+static int pick_per_cu(int dtype, bool vec) {
+  if (dtype == 1) return vec ? Pick<1, 8>::per_cu() : Pick<1, 1>::per_cu();
+  return vec ? Pick<0, 4>::per_cu() : Pick<0, 1>::per_cu();
+}
 
 template <int DT, int NE>
 struct ChainKernel {
   static auto fn() { return &k_greedy_chain<DT, NE>; }
+  static int per_cu() {
+    static const int n = groups_per_cu(fn());
+    return n;
+  }
 };
 template <int DT, int NE>
 struct TreeKernel {
   static auto fn() { return &k_tree_greedy<DT, NE>; }
+  static int per_cu() {
+    static const int n = groups_per_cu(fn());
+    return n;
+  }
 };
 
 hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int V,
                                const int32_t* draft_tokens, int32_t* accepted_len,
                                int32_t* out_tokens, void* ws, const WsLayout& L,
                                hipStream_t s) {
-  const int C1 = row_chunks(V);
+  const bool vec = rows_aligned(target, V, dtype);
+  const auto kern = pick_kernel<ChainKernel>(dtype, vec);
+  const int C1 = row_chunks(pick_per_cu<ChainKernel>(dtype, vec), (long)B * (k + 1), V, 1);
   char* w = static_cast<char*>(ws);
   auto* part = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const dim3 grid((unsigned)((long)B * (k + 1) * C1)), block(kThreads);
-  const auto kern = pick_kernel<ChainKernel>(dtype, rows_aligned(target, V, dtype));
   return launch_timed(kProfRowPass, kern, grid, block, 0, s, target, k, V, C1, draft_tokens,
                       accepted_len, out_tokens, part, cnt);
 }
@@ -227,12 +328,13 @@ hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
                               const TreeArgs& tree, int depth, const int32_t* node_tokens,
                               int32_t* accepted_len, int32_t* out_tokens, int32_t* out_path,
                               void* ws, const WsLayout& L, hipStream_t s) {
-  const int C1 = row_chunks(V);
+  const bool vec = rows_aligned(target, V, dtype);
+  const auto kern = pick_kernel<TreeKernel>(dtype, vec);
+  const int C1 = row_chunks(pick_per_cu<TreeKernel>(dtype, vec), (long)B * n_nodes, V, 2);
   char* w = static_cast<char*>(ws);
   auto* part = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const dim3 grid((unsigned)((long)B * n_nodes * C1)), block(kThreads);
-  const auto kern = pick_kernel<TreeKernel>(dtype, rows_aligned(target, V, dtype));
   return launch_timed(kProfRowPass, kern, grid, block, 0, s, target, n_nodes, V, C1, tree, depth,
                       node_tokens, accepted_len, out_tokens, out_path, part, cnt);
 }
