@@ -153,6 +153,113 @@ def cpu_baseline(wl, budget_s: float):
                       f"(batch repeated with fresh uniforms), {dt:.1f} s on 1 host thread"}
 
 
+# Extra workloads (not the headline line): greedy chain and tree greedy.
+GREEDY_WORKLOADS = {
+    "tree": "tree greedy, B=16, 61 nodes (1 root + 60, depth 5), V=128256, bf16",
+    "greedy_b64": "greedy chain, B=64, k=8, V=128256, bf16",
+    "greedy_b1": "greedy chain, B=1, k=4, V=1000, fp32 (latency)",
+}
+GREEDY_KERNELS = {"tree": "k_tree_greedy", "greedy_b64": "k_greedy_chain",
+                  "greedy_b1": "k_greedy_chain"}
+
+
+def timed_steps(step, first, steps, profile, keep=None):
+    """Run `steps` steps between two events and return ms per step.  With
+    profile, every launch also carries dispatch-stamped start/stop events
+    (read afterwards with spec_profile_read); those add host work per launch,
+    so the step rate comes from an uninstrumented pass."""
+    import torch
+
+    import verify_accept_sampling_amd as S
+
+    S.spec_profile_enable(profile)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        out = step(first + i)
+        if keep is not None:
+            keep.append(out[0])
+    end.record()
+    torch.cuda.synchronize()
+    if profile:
+        S.spec_profile_enable(False)
+    return start.elapsed_time(end) / steps
+
+
+def bench_greedy(args):
+    """One JSON line for a greedy workload: the kernel reads every logit row
+    once (B * rows * V * elem bytes), so its roofline is HBM at that size."""
+    import numpy as np
+    import torch
+
+    import verify_accept_sampling_amd as S
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    print(f"bench: generating {GREEDY_WORKLOADS[name]}", file=sys.stderr, flush=True)
+    if name == "tree":
+        wl = W.tree_greedy()
+        rows, dtype = len(wl.parent), wl.dtype
+        parent = wl.parent.tolist()
+        toks = torch.from_numpy(wl.node_tokens).to(dev)
+    elif name == "greedy_b64":
+        wl = W.greedy_chain(B=64, k=8, V=128256, seed=1003, dtype="bf16")
+        rows, dtype = wl.k + 1, wl.dtype
+        toks = torch.from_numpy(wl.draft_tokens).to(dev)
+    else:
+        wl = W.greedy_chain()
+        rows, dtype = wl.k + 1, wl.dtype
+        toks = torch.from_numpy(wl.draft_tokens).to(dev)
+    B, V = wl.target.shape[0], wl.target.shape[-1]
+
+    def to_dev(a):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t0 = to_dev(wl.target)
+    copies = [t0] + [t0.clone() for _ in range(args.copies - 1)]
+    ws = S.Workspace(dev)
+
+    def step(i):
+        t = copies[i % len(copies)]
+        if name == "tree":
+            return S.spec_verify_tree_greedy(t, parent, toks, want_path=False, workspace=ws)
+        return S.spec_verify_greedy(t, toks, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = timed_steps(step, args.warmup, args.steps, profile=False)
+    timed_steps(step, args.warmup + args.steps, args.steps, profile=True)
+    n, ms = S.spec_profile_read("row_pass")
+    kern_us = ms / n * 1e3
+    elem = 2 if dtype == "bf16" else 4
+    nbytes = float(B * rows * V * elem)
+    achieved = nbytes / (kern_us * 1e-6) / 1e9
+    positions = B * rows
+    result = {
+        "metric": f"verified positions/s ({GREEDY_WORKLOADS[name]})",
+        "value": positions / (ms_step * 1e-3),
+        "unit": "verified positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "B": B, "rows_per_request": rows, "V": V, "logits": dtype,
+                   "input_copies": len(copies)},
+        "roofline": {"bound": "hbm", "kernel": GREEDY_KERNELS[name], "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+        "kernels_avg_us": {GREEDY_KERNELS[name]: kern_us},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +276,9 @@ def main():
                     help="host only: turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) "
                          "into the row-statistics traffic file")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
+    ap.add_argument("--workload", choices=["sample"] + sorted(GREEDY_WORKLOADS), default="sample",
+                    help="sample (default): the headline sampling workload; the others print "
+                         "a line for a greedy kernel")
     ap.add_argument("--path", choices=sorted(KERNELS), default="auto",
                     help="auto: the one-launch kernel; two_launch: row pass, then draw")
     args = ap.parse_args()
@@ -183,6 +293,9 @@ def main():
         print("bench.py measures one GPU only: the verifier is batch-parallel and this build "
               "runs on a single MI355X (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "sample":
+        bench_greedy(args)
+        return
 
     import numpy as np
     import torch
@@ -227,19 +340,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    S.spec_profile_enable(True)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     accs = []
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        acc, _ = step(args.warmup + i)
-        accs.append(acc)
-    end.record()
-    torch.cuda.synchronize()
-    S.spec_profile_enable(False)
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
+    ms_step = timed_steps(step, args.warmup, args.steps, profile=False, keep=accs)
+    timed_steps(step, args.warmup + args.steps, args.steps, profile=True)
     kern = {}
     for name in ("fused", "row_pass", "draw"):
         n, ms = S.spec_profile_read(name)

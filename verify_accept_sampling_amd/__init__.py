@@ -16,6 +16,7 @@ is missing or a call fails, an exception is raised.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import re
 from typing import Optional, Sequence
@@ -135,7 +136,14 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device) -> ctypes.c_void_p:
+    # The raw handle of the current stream, without building a Stream object.
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(idx))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -154,6 +162,7 @@ def _need_cuda(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+@functools.lru_cache(maxsize=256)
 def spec_workspace_bytes(B: int, n_pos: int, V: int) -> int:
     return int(load_library().spec_workspace_bytes(int(B), int(n_pos), int(V)))
 
@@ -292,7 +301,9 @@ def spec_verify_tree_greedy(target: torch.Tensor, parent: Sequence[int],
     arr, n = _parent_array(parent)
     if n != N:
         raise ValueError("parent must have one entry per node")
-    D = spec_tree_depth(parent)
+    D = int(load_library().spec_tree_depth(ctypes.cast(arr, ctypes.c_void_p), n))
+    if D < 0:
+        _check(D)
     dev = target.device
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     out = torch.empty(B, D + 1, dtype=torch.int32, device=dev)

@@ -29,6 +29,9 @@ int check_grid(long blocks) {
 
 long row_chunks_for(int V) { return (V + kRowChunkElems - 1) / kRowChunkElems; }
 
+// Most chunks per row the greedy kernels use.
+long greedy_chunks_max(int V) { return (V + kMinChunkElems - 1) / kMinChunkElems; }
+
 int tree_depth_checked(const int32_t* parent, int n_nodes) {
   if (parent == nullptr || n_nodes < 1 || n_nodes > kMaxNodes) return SPEC_EINVAL;
   if (parent[0] != -1) return SPEC_ETREE;
@@ -96,7 +99,7 @@ int spec_verify_greedy(const void* target, int dtype, int B, int k, int V,
   if (B == 0) return SPEC_OK;
   if (target == nullptr || accepted_len == nullptr || out_tokens == nullptr) return SPEC_EINVAL;
   if (k > 0 && draft_tokens == nullptr) return SPEC_EINVAL;
-  if (check_grid((long)B * (k + 1) * row_chunks_for(V)) != SPEC_OK) return SPEC_EINVAL;
+  if (check_grid((long)B * (k + 1) * greedy_chunks_max(V)) != SPEC_OK) return SPEC_EINVAL;
   WsLayout L;
   if (int rc = check_workspace(ws, ws_bytes, B, k + 1, V, &L)) return rc;
   if (launch_greedy_chain(target, dtype, B, k, V, draft_tokens, accepted_len, out_tokens, ws, L,
@@ -124,7 +127,9 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
   if (target == nullptr || accepted_len == nullptr || out_tokens == nullptr) return SPEC_EINVAL;
   if (k > 0 && (draft == nullptr || draft_tokens == nullptr)) return SPEC_EINVAL;
   const long C2 = (V + kDrawChunk - 1) / kDrawChunk;
-  if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V)) != SPEC_OK) return SPEC_EINVAL;
+  const long draw_groups = (long)B * ((res_chunks(V) + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup);
+  if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V) + draw_groups) != SPEC_OK)
+    return SPEC_EINVAL;
   if (check_grid((long)B * C2) != SPEC_OK) return SPEC_EINVAL;
   WsLayout L;
   if (int rc = check_workspace(ws, ws_bytes, B, k + 1, V, &L)) return rc;
@@ -148,7 +153,7 @@ int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes, i
   if (target == nullptr || node_tokens == nullptr || accepted_len == nullptr ||
       out_tokens == nullptr)
     return SPEC_EINVAL;
-  if (check_grid((long)B * n_nodes * row_chunks_for(V)) != SPEC_OK) return SPEC_EINVAL;
+  if (check_grid((long)B * n_nodes * greedy_chunks_max(V)) != SPEC_OK) return SPEC_EINVAL;
   WsLayout L;
   if (int rc = check_workspace(ws, ws_bytes, B, n_nodes, V, &L)) return rc;
   TreeArgs tree;

@@ -19,9 +19,6 @@
 
 namespace specv {
 
-// Smallest row chunk the greedy kernels split rows into.
-constexpr int kMinChunkElems = 16384;
-static_assert(kMinChunkElems >= kRowChunkElemsMin, "partials are sized for chunks of at least this");
 
 // Fold one group of NE elements (group index gi) into the running argmax;
 // a strict '>' keeps the lowest index because groups arrive in ascending
@@ -187,18 +184,18 @@ __global__ __launch_bounds__(kThreads) void k_greedy_chain(
   if (threadIdx.x == 0) accepted_len[b] = n;
 }
 
-template <int DT, int NE>
+template <int DT, int NE, int NMAX>
 __global__ __launch_bounds__(kThreads) void k_tree_greedy(
-    const void* __restrict__ target, int n_nodes, int V, int C1, TreeArgs tree, int D,
+    const void* __restrict__ target, int n_nodes, int V, int C1, TreeArgsN<NMAX> tree, int D,
     const int32_t* __restrict__ node_tokens, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_path,
     uint64_t* __restrict__ part, unsigned* __restrict__ counters) {
   int b;
   if (!argmax_chunk<DT, NE>(target, n_nodes, V, C1, part, counters, b)) return;
-  __shared__ int amax[kMaxNodes];
-  __shared__ int tok[kMaxNodes];
-  __shared__ int path[kMaxNodes];
-  __shared__ int16_t dep[kMaxNodes];
+  __shared__ int amax[NMAX];
+  __shared__ int tok[NMAX];
+  __shared__ int path[NMAX];
+  __shared__ int16_t dep[NMAX];
   __shared__ int s_best;
   for (int j = threadIdx.x; j < n_nodes; j += kThreads) tok[j] = node_tokens[(long)b * n_nodes + j];
   merge_argmax_rows(part, b, n_nodes, C1, amax);
@@ -301,8 +298,16 @@ struct ChainKernel {
   }
 };
 template <int DT, int NE>
+struct SmallTreeKernel {
+  static auto fn() { return &k_tree_greedy<DT, NE, kSmallTree>; }
+  static int per_cu() {
+    static const int n = groups_per_cu(fn());
+    return n;
+  }
+};
+template <int DT, int NE>
 struct TreeKernel {
-  static auto fn() { return &k_tree_greedy<DT, NE>; }
+  static auto fn() { return &k_tree_greedy<DT, NE, kMaxNodes>; }
   static int per_cu() {
     static const int n = groups_per_cu(fn());
     return n;
@@ -329,11 +334,23 @@ hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
                               int32_t* accepted_len, int32_t* out_tokens, int32_t* out_path,
                               void* ws, const WsLayout& L, hipStream_t s) {
   const bool vec = rows_aligned(target, V, dtype);
-  const auto kern = pick_kernel<TreeKernel>(dtype, vec);
-  const int C1 = row_chunks(pick_per_cu<TreeKernel>(dtype, vec), (long)B * n_nodes, V, 2);
   char* w = static_cast<char*>(ws);
   auto* part = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
+  if (n_nodes <= kSmallTree) {
+    // A 2 KiB argument block made each launch ~20 us slower on the device
+    // at 61 nodes than this 256-byte one.
+    TreeArgsN<kSmallTree> small;
+    for (int j = 0; j < kSmallTree; ++j) small.parent[j] = j < n_nodes ? tree.parent[j] : 0;
+    const auto kern = pick_kernel<SmallTreeKernel>(dtype, vec);
+    const int C1 =
+        row_chunks(pick_per_cu<SmallTreeKernel>(dtype, vec), (long)B * n_nodes, V, 2);
+    const dim3 grid((unsigned)((long)B * n_nodes * C1)), block(kThreads);
+    return launch_timed(kProfRowPass, kern, grid, block, 0, s, target, n_nodes, V, C1, small,
+                        depth, node_tokens, accepted_len, out_tokens, out_path, part, cnt);
+  }
+  const auto kern = pick_kernel<TreeKernel>(dtype, vec);
+  const int C1 = row_chunks(pick_per_cu<TreeKernel>(dtype, vec), (long)B * n_nodes, V, 2);
   const dim3 grid((unsigned)((long)B * n_nodes * C1)), block(kThreads);
   return launch_timed(kProfRowPass, kern, grid, block, 0, s, target, n_nodes, V, C1, tree, depth,
                       node_tokens, accepted_len, out_tokens, out_path, part, cnt);

@@ -38,6 +38,9 @@ constexpr int kRowUnroll = SPEC_ROW_UNROLL;
 #endif
 // Smallest chunk the workspace is sized for (leaves room to retune).
 constexpr int kRowChunkElemsMin = 2048;
+// Smallest row chunk the greedy kernels split rows into.
+constexpr int kMinChunkElems = 16384;
+static_assert(kMinChunkElems >= kRowChunkElemsMin, "partials are sized for chunks of at least this");
 // Float64 residual / bonus pass: the row is cut into chunks of
 // kDrawChunk elements, one wave per chunk (64 lanes x kSegPerThread
 // consecutive elements); a work-group of kThreads/64 waves handles kDrawChunksPerWave
@@ -138,10 +141,15 @@ inline WsLayout ws_layout(int B, int n_pos, int V) {
   return L;
 }
 
-// Tree description passed by value in the kernel arguments (2 KiB).
-struct TreeArgs {
-  int16_t parent[kMaxNodes];
+// Tree description passed by value in the kernel arguments: a small form
+// for trees of up to kSmallTree nodes (the kernel-argument block stays
+// small), and the full one.
+constexpr int kSmallTree = 128;
+template <int N>
+struct TreeArgsN {
+  int16_t parent[N];
 };
+using TreeArgs = TreeArgsN<kMaxNodes>;
 
 // Kernel kinds for the optional event timing (same values as the public
 // SPEC_KERNEL_* constants).
