@@ -102,11 +102,9 @@ static_assert(kCounterRegionBytes == SPEC_WORKSPACE_COUNTER_BYTES, "counter regi
 
 // Workspace layout.  The counter region (kCounterRegionBytes) sits at a
 // fixed place whatever the call's shape; it must be zero before the first
-// call.  The completion tickets are left at zero by every call; the
-// one-launch kernel keeps a call epoch there and per-request markers that
-// hold the epoch of the call that wrote them, so stale markers are never
-// taken for new ones.  The other regions are written before they are read
-// within each call.
+// call, and every call leaves it zero (tickets reset by their last taker,
+// ready markers cleared by the request's draw).  The other regions are
+// written before they are read within each call.
 struct WsLayout {
   size_t count;  // counter region, always at offset 0
   size_t part1;  // uint64 [rows * row_chunks]: packed (max, sum) or (value, index)

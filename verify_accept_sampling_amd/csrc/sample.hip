@@ -82,10 +82,14 @@ __device__ __forceinline__ void row_chunk_stat(int b, int r, int chunk,
 // statistics.  Lane i handles position i (and i + 64, ...): it loads the
 // token, the two published token logits and the chunk partials of target
 // row i and draft row i in one round, merges the rows and tests draft i.
-// Returns the draw state (n valid in every lane, the rest in lane 0).  With
-// `write` it also stores accepted_len[b], the accepted prefix, the -1
-// padding and the probe values other than probe[b, n, 2], which belongs to
-// the draw.  Uses R doubles and R floats of dynamic shared memory.
+// With e_p = z c - fl(M_p c) (z the target logit at x_i) and e_q likewise,
+// p_i(x_i) / q_i(x_i) = 2^(e_p - e_q) S_q / S_p, one exp2 per position.
+// Each lane also prepares the draw state of the row it would hand over (its
+// first rejected position, or the bonus row), and after the wave minimum
+// the owner of the first rejection supplies it.  Returns the state in every
+// lane.  With `write` it also stores accepted_len[b], the accepted prefix,
+// the -1 padding and the probe values other than probe[b, n, 2], which
+// belongs to the draw.
 __device__ __forceinline__ ReqState finalize_request(
     int b, int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
@@ -93,11 +97,10 @@ __device__ __forceinline__ ReqState finalize_request(
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe) {
   const int R = 2 * k + 1;
-  extern __shared__ double dyn_lds[];
-  double* s_s = dyn_lds;                               // [R]
-  float* s_m = reinterpret_cast<float*>(dyn_lds + R);  // [R]
   const int lane = threadIdx.x & 63;
   int first = k;
+  float cand_mp = 0.f, cand_mq = 0.f;  // draw state of this lane's hand-over row
+  double cand_rho = 1.0;
   for (int i = lane; i <= k; i += kWaveSize) {
     const bool draft_pos = i < k;
     int x = -1;
@@ -111,31 +114,47 @@ __device__ __forceinline__ ReqState finalize_request(
     double Sp, Sq;
     merge_two_rows(part, ((long)b * R + i) * C1, ((long)b * R + k + 1 + i) * C1, draft_pos, C1,
                    c, Mp, Sp, Mq, Sq);
-    s_m[i] = Mp;
-    s_s[i] = Sp;
-    if (!draft_pos) continue;
-    s_m[k + 1 + i] = Mq;
-    s_s[k + 1 + i] = Sq;
+    if (!draft_pos) {
+      // bonus row k: handed over only if nothing was rejected
+      if (first == k) cand_mp = Mp;
+      continue;
+    }
     float pv = 0.f, qv = 0.f;
     bool accept = false;
     if (x >= 0 && x < V) {
-      // log2 p_i(x) and log2 q_i(x) from the row statistics
-      const double lp = ((double)zp * c - (double)mul_rn(Mp, c)) - log2(Sp);
-      const double lq = ((double)zq * c - (double)mul_rn(Mq, c)) - log2(Sq);
-      const double ratio = exp2(lp - lq);
+      const double ep = (double)zp * c - (double)mul_rn(Mp, c);
+      const double eq = (double)zq * c - (double)mul_rn(Mq, c);
+      const double ratio = exp2(ep - eq) * (Sq / Sp);
       const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
       accept = (double)u < ratio;
-      pv = (float)exp2(lp);
-      qv = (float)exp2(lq);
+      if (probe != nullptr) {
+        pv = (float)(exp2(ep) / Sp);
+        qv = (float)(exp2(eq) / Sq);
+      }
     }
-    if (!accept) first = min(first, i);
+    if (!accept && first == k) {
+      first = i;
+      // S_p / S_q with both sums taken relative to 2^(M c) instead of
+      // 2^fl32(M c).
+      cand_mp = Mp;
+      cand_mq = Mq;
+      cand_rho = Sp / Sq *
+                 exp2(((double)mul_rn(Mp, c) - (double)Mp * c) -
+                      ((double)mul_rn(Mq, c) - (double)Mq * c));
+    }
     if (write && probe) {
       float* pr = probe + ((long)b * (k + 1) + i) * 4;
       pr[0] = pv; pr[1] = qv; pr[3] = 0.f;
     }
   }
   const int n = wave_min_i(first);
-  wave_lds_sync();
+  const int owner = n & (kWaveSize - 1);  // the lane that handled position n
+  ReqState st;
+  st.n = n;
+  st.mode = n < k ? kModeResidual : kModeBonus;
+  st.mp = __shfl(cand_mp, owner, 64);
+  st.mq = __shfl(cand_mq, owner, 64);
+  st.rho32 = __shfl(cand_rho, owner, 64);
   if (write) {
     for (int i = lane; i <= k; i += kWaveSize) {
       if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
@@ -144,21 +163,7 @@ __device__ __forceinline__ ReqState finalize_request(
       // run in another work-group of the same launch
       if (probe && i != n) probe[((long)b * (k + 1) + i) * 4 + 2] = 0.f;
     }
-  }
-  // State for the draw: references of target row n and (rejection) draft
-  // row n, and the float32-based normaliser ratio of that pair.
-  ReqState st{n, n < k ? kModeResidual : kModeBonus, 0.f, 0.f, 1.0};
-  if (lane == 0) {
-    const float mp = s_m[n];
-    const float mq = n < k ? s_m[k + 1 + n] : 0.f;
-    // S relative to 2^(m c) instead of 2^fl32(m c): ratio of the pair.
-    const double sp = s_s[n] * exp2((double)mul_rn(mp, c) - (double)mp * c);
-    const double sq =
-        n < k ? s_s[k + 1 + n] * exp2((double)mul_rn(mq, c) - (double)mq * c) : 1.0;
-    st.mp = mp;
-    st.mq = mq;
-    st.rho32 = sp / sq;
-    if (write) {
+    if (lane == 0) {
       accepted_len[b] = n;
       if (probe) {
         float* pr = probe + ((long)b * (k + 1) + k) * 4;
@@ -190,6 +195,9 @@ __device__ __forceinline__ void row_block(
   if (threadIdx.x >= kWaveSize) return;  // wave 0 finishes the work-group
   if (!wave_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
   // ---- last work-group of request b, one wave: acceptance tests ----
+  // The other waves of this compute unit stream rows; this one decides when
+  // the request's draw can start: it issues first.
+  __builtin_amdgcn_s_setprio(3);
   const ReqState st = finalize_request(b, k, V, C1, c, draft_tokens, uniforms, seed, ctr0, part,
                                        zrow, true, accepted_len, out_tokens, probe);
   if ((threadIdx.x & 63) == 0) {
@@ -594,18 +602,16 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
   const long R = 2L * k + 1;
   auto* zr = reinterpret_cast<float*>(w + L.zrow);
-  // finalize arrays: double [R] then float [R]
-  const uint32_t lds = static_cast<uint32_t>(R * (sizeof(double) + sizeof(float)));
   const long n_row = (long)B * R * C1;
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
   if (g_sample_path.load(std::memory_order_relaxed) == SPEC_PATH_AUTO) {
     return launch_timed(kProfFused, &k_sample_one<DT, NE>, dim3((unsigned)(n_row + (long)B * G2)),
-                        dim3(kThreads), one_launch_lds<DT, NE>(lds), s, target, draft, B, k, V, C1, C2, c, inv_t,
+                        dim3(kThreads), one_launch_lds<DT, NE>(0), s, target, draft, B, k, V, C1, C2, c, inv_t,
                         draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1,
                         zr, st, p2, cnt, n_row);
   }
   hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>, dim3((unsigned)n_row),
-                             dim3(kThreads), lds, s, target, draft, k, V, C1, c, draft_tokens,
+                             dim3(kThreads), 0, s, target, draft, k, V, C1, c, draft_tokens,
                              uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1, zr, st,
                              cnt);
   if (e != hipSuccess) return e;

@@ -180,9 +180,12 @@ __device__ __forceinline__ void fold_partial(float& M, double& S, uint64_t pp, f
     S = s2;
     return;
   }
-  const float mn = fmaxf(M, m2);
-  const double mcn = (double)mul_rn(mn, c);
-  S = S * exp2((double)mul_rn(M, c) - mcn) + s2 * exp2((double)mul_rn(m2, c) - mcn);
+  // One scale factor: the side with the smaller reference moves to the
+  // larger one (the other factor is 2^0 = 1).
+  const bool up = m2 > M;
+  const float mn = up ? m2 : M, mo = up ? M : m2;
+  const double e = exp2((double)mul_rn(mo, c) - (double)mul_rn(mn, c));
+  S = up ? S * e + s2 : S + s2 * e;
   M = mn;
 }
 
