@@ -26,7 +26,7 @@
  *  - `ws` is a caller-owned device workspace of at least
  *    spec_workspace_bytes(B, n_pos, V) bytes.  It must be zero-filled before
  *    its first use.  Its first SPEC_WORKSPACE_COUNTER_BYTES bytes hold
- *    per-request completion counters and ready markers at fixed places;
+ *    per-request completion counters and ready slots at fixed places;
  *    every call leaves them zero again when it completes, so one workspace
  *    serves calls of any shape without clearing it (the caller must not
  *    write to them); the rest is scratch that each call writes before
@@ -53,7 +53,7 @@ extern "C" {
 
 /* Bytes at the start of every workspace that must be zero before the first
  * call; each completed call leaves them zero. */
-#define SPEC_WORKSPACE_COUNTER_BYTES (1048576 + 256)
+#define SPEC_WORKSPACE_COUNTER_BYTES (2097152 + 256)
 
 /* Element type of logit / probability tensors. */
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };

@@ -36,7 +36,7 @@ def test_workspace_bytes(lib):
     a = S.spec_workspace_bytes(64, 9, 128256)
     assert a > 0 and a % 256 == 0
     assert S.spec_workspace_bytes(128, 9, 128256) > a
-    assert S.spec_workspace_bytes(0, 9, 128256) >= (1 << 20) + 256  # fixed counter region
+    assert S.spec_workspace_bytes(0, 9, 128256) >= (2 << 20) + 256  # fixed counter region
     for bad in ((-1, 9, 10), (65537, 9, 10), (1, 0, 10), (1, 9, 0), (1, 2000, 10), (1, 9, 2 ** 30 + 1)):
         assert S.spec_workspace_bytes(*bad) == 0
 

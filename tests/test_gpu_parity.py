@@ -256,7 +256,7 @@ def test_sample_controlled_acceptance_full(controlled_full):
     _run_sample(controlled_full)
 
 
-COUNTER_BYTES = (1 << 20) + 256  # SPEC_WORKSPACE_COUNTER_BYTES: fixed region at the start
+COUNTER_BYTES = (2 << 20) + 256  # SPEC_WORKSPACE_COUNTER_BYTES: fixed region at the start
 
 
 def test_workspace_reuse_with_stale_partials(sample_path):

@@ -111,7 +111,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // 32-bit byte offset plus a uniform one, so the streaming loops need no
 // 64-bit address arithmetic per load.  Rows must be shorter than 2 GiB.
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
-constexpr int kLoadNonTemporal = 2;       // cache policy: nt
+// Cache policy of the row sweeps' loads (tunable at build time): nt, i.e.
+// streamed data that is read once.
+#ifndef SPEC_ROW_LOAD_POLICY
+#define SPEC_ROW_LOAD_POLICY 2
+#endif
+constexpr int kLoadNonTemporal = SPEC_ROW_LOAD_POLICY;
 
 struct RowBuf {
   __amdgpu_buffer_rsrc_t rsrc;

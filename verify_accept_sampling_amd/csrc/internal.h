@@ -91,19 +91,23 @@ struct DrawPart {
 };
 static_assert(sizeof(DrawPart) == 80, "DrawPart layout");
 
-// Per-request words of the counter region: [0] row-pass completion
-// ticket, [1] draw completion ticket, [2..3] a 64-bit ready marker slot of
-// the one-launch kernel (slot j holds the marker of request j with its two
-// bytes swapped).  Every word is back to 0 when a call completes.  The last
-// 256 bytes are reserved.
-constexpr int kCountersPerReq = 4;
+// Per-request 32-bit words of the counter region: [0] row-pass completion
+// ticket, [1] draw completion ticket, [2] the row count of the one-launch
+// kernel, [3] unused, [4..7] the ready slot of the one-launch kernel, two
+// 64-bit words that carry a request's packed draw state.  The one-launch
+// words of position j belong to request j with its two bytes swapped.
+// Every word is back to 0 when a call completes.  The last 256 bytes are
+// reserved.
+constexpr int kCountersPerReq = 8;
+constexpr int kRowCountWord = 2;
+constexpr int kReadySlotWord = 4;
 constexpr size_t kCounterRegionBytes = (size_t)kMaxB * kCountersPerReq * 4 + 256;
 static_assert(kCounterRegionBytes == SPEC_WORKSPACE_COUNTER_BYTES, "counter region");
 
 // Workspace layout.  The counter region (kCounterRegionBytes) sits at a
 // fixed place whatever the call's shape; it must be zero before the first
 // call, and every call leaves it zero (tickets reset by their last taker,
-// ready markers cleared by the request's draw).  The other regions are
+// ready slots cleared by the request's draw).  The other regions are
 // written before they are read within each call.
 struct WsLayout {
   size_t count;  // counter region, always at offset 0

@@ -23,10 +23,14 @@
 //      recomputed), locates the chunk holding the inverse-CDF point and
 //      searches it with the exact weights.
 // By default both run in one launch (k_sample_one): the row-pass
-// work-groups first, then the draw work-groups, each of which waits for its
-// request's state, so the draws of early requests overlap the last row-pass
-// work-groups.  The two-launch form (k_row_stats, then k_draw) computes the
-// same thing.
+// work-groups first, then the draw work-groups, so the draws of early
+// requests overlap the last row-pass work-groups.  There a row-pass
+// work-group counts itself in without awaiting a reply; the request's first
+// draw work-group waits for the count, runs the acceptance tests and
+// publishes the draw state, for which the request's other draw work-groups
+// wait.  The two-launch form (k_row_stats, then k_draw) computes the same
+// thing, with the acceptance tests in the request's last row-pass
+// work-group.
 // Probabilities path (rows given as distributions): k_draw alone, each
 // work-group first repeating the (gather-only) acceptance tests.
 #include <atomic>
@@ -154,7 +158,9 @@ __device__ __forceinline__ ReqState finalize_request(
   st.mode = n < k ? kModeResidual : kModeBonus;
   st.mp = __shfl(cand_mp, owner, 64);
   st.mq = __shfl(cand_mq, owner, 64);
-  st.rho32 = __shfl(cand_rho, owner, 64);
+  // rounded to float: it travels packed in the one-launch kernel's ready
+  // slot, and both forms use the same value
+  st.rho32 = (double)(float)__shfl(cand_rho, owner, 64);
   if (write) {
     for (int i = lane; i <= k; i += kWaveSize) {
       if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
@@ -174,10 +180,11 @@ __device__ __forceinline__ ReqState finalize_request(
   return st;
 }
 
-// Row pass of one work-group: block `bid` of the row-pass grid.  The
-// request's last work-group (by ticket) runs the acceptance tests on one
-// wave and stores the draw state.  In the grid-ordered one-launch kernel
-// (one_launch) the state is followed by its ready marker, set to 1.
+// Row pass of one work-group: block `bid` of the row-pass grid.  In the
+// two-launch form the request's last work-group (by ticket) runs the
+// acceptance tests on one wave and stores the draw state.  In the
+// grid-ordered one-launch kernel (one_launch) the work-group only counts
+// itself in, and the request's first draw work-group takes over.
 template <int DT, int NE>
 __device__ __forceinline__ void row_block(
     long bid, bool one_launch, const void* __restrict__ target, const void* __restrict__ draft,
@@ -192,6 +199,16 @@ __device__ __forceinline__ void row_block(
   const int b = static_cast<int>(rowid / R);
   const int r = static_cast<int>(rowid % R);
   row_chunk_stat<DT, NE>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens, part, zrow);
+  if (one_launch) {
+    // Count this work-group in once its pair (and logit) are complete; no
+    // reply is awaited, so the work-group ends one round trip earlier.
+    if (threadIdx.x == 0) {  // the thread that stored them
+      wait_stores();
+      __hip_atomic_fetch_add(row_count(counters, b), 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
   if (threadIdx.x >= kWaveSize) return;  // wave 0 finishes the work-group
   if (!wave_arrive(&counters[(long)b * kCountersPerReq + 0], (unsigned)(R * C1))) return;
   // ---- last work-group of request b, one wave: acceptance tests ----
@@ -200,13 +217,7 @@ __device__ __forceinline__ void row_block(
   __builtin_amdgcn_s_setprio(3);
   const ReqState st = finalize_request(b, k, V, C1, c, draft_tokens, uniforms, seed, ctr0, part,
                                        zrow, true, accepted_len, out_tokens, probe);
-  if ((threadIdx.x & 63) == 0) {
-    st_dev_state(&state[b], st);
-    if (one_launch) {
-      wait_stores();  // the state is complete before its marker
-      st_dev(ready_marker(counters, b), (uint64_t)1);
-    }
-  }
+  if ((threadIdx.x & 63) == 0) st_dev_state(&state[b], st);
 }
 
 // Acceptance tests on probability rows: u * q(x) < p(x), exact in float64
@@ -260,20 +271,31 @@ __device__ int accept_scan_probs(const float* target, const float* draft, int b,
 // How a draw work-group learns its request's state.
 enum {
   kStateStored = 0,  // from the state array, written by an earlier launch
-  kStateMarker = 1,  // from the state array once the request's ready marker is set
+  kStateSlot = 1,    // one-launch hand-over through the row count and ready slot
 };
 
-// Draw of one work-group: chunk group grp of request b.  With kStateMarker
-// the work-group first waits for the request's ready marker, and the
-// request's last draw work-group clears it.
-template <int DT, int NE, int KIND>
+// Row-pass outputs the finishing draw work-group reads.
+struct RowPass {
+  const uint64_t* part;  // (reference, sum) pairs, C1 per row
+  const float* zrow;     // each row's logit at its draft token
+  int C1;                // chunks per row
+  float c;               // log2(e) / T
+};
+
+// Draw of one work-group: chunk group grp of request b.  With kStateSlot,
+// work-group 0 of the request waits until every row-pass work-group of the
+// request has counted itself in, runs the acceptance tests on one wave
+// (writing their outputs), publishes the packed state in the request's ready
+// slot and resets the count; the request's other draw work-groups wait for
+// the ready slot, and the request's last draw work-group clears it.
+template <int DT, int NE, int KIND, int HOW>
 __device__ __forceinline__ void draw_block(
-    int b, int grp, int how, const void* __restrict__ target, const void* __restrict__ draft,
+    int b, int grp, const void* __restrict__ target, const void* __restrict__ draft,
     int k, int V, int C2, double inv_t, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probe, const ReqState* __restrict__ state, DrawPart* __restrict__ part,
-    unsigned* __restrict__ counters) {
+    float* __restrict__ probe, const ReqState* __restrict__ state, const RowPass& rows,
+    DrawPart* __restrict__ part, unsigned* __restrict__ counters) {
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
   __shared__ double tab[256];
   static_assert(kThreads == 256, "one table entry per thread");
@@ -281,13 +303,50 @@ __device__ __forceinline__ void draw_block(
   int n;
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
-    if (how == kStateMarker) {
+    ReqState st;
+    if constexpr (HOW == kStateSlot) {
       __shared__ int s_ok;
-      if (threadIdx.x == 0) s_ok = wait_marker(ready_marker(counters, b)) ? 1 : 0;
+      __shared__ uint64_t s_w[2];
+      if (grp == 0) {  // work-group-uniform
+        if (threadIdx.x < kWaveSize) {
+          unsigned* cnt = row_count(counters, b);
+          int ok = 0;
+          if (threadIdx.x == 0) ok = wait_count(cnt, (unsigned)((2 * k + 1) * rows.C1)) ? 1 : 0;
+          ok = __shfl(ok, 0, 64);
+          if (ok) {
+            // The other waves of this compute unit stream rows or draw; this
+            // one decides when the request's draw can start: it issues first.
+            __builtin_amdgcn_s_setprio(3);
+            const ReqState mine =
+                finalize_request(b, k, V, rows.C1, rows.c, draft_tokens, uniforms, seed, ctr0,
+                                 rows.part, rows.zrow, true, accepted_len, out_tokens, probe);
+            __builtin_amdgcn_s_setprio(0);
+            if (threadIdx.x == 0) {
+              uint64_t w0, w1;
+              pack_state(mine, w0, w1);
+              uint64_t* slot = ready_slot(counters, b);
+              st_dev(&slot[0], w0);
+              st_dev(&slot[1], w1);
+              // every row-pass work-group of the request has counted itself in
+              __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              s_w[0] = w0;
+              s_w[1] = w1;
+            }
+          }
+          if (threadIdx.x == 0) s_ok = ok;
+        }
+      } else if (threadIdx.x == 0) {
+        uint64_t w0 = 0, w1 = 0;
+        s_ok = wait_slot(ready_slot(counters, b), w0, w1) ? 1 : 0;
+        s_w[0] = w0;
+        s_w[1] = w1;
+      }
       __syncthreads();
-      if (!s_ok) return;  // never expected: the request's state did not appear
+      if (!s_ok) return;  // never expected: the request's rows or state did not appear
+      st = unpack_state(s_w[0], s_w[1], k);
+    } else {
+      st = ld_dev_state(&state[b]);
     }
-    const ReqState st = ld_dev_state(&state[b]);
     n = min(max(st.n, 0), k);  // always a valid row index
     mp = st.mp;
     mq = st.mq;
@@ -468,9 +527,13 @@ __device__ __forceinline__ void draw_block(
       probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
     // Every draw work-group of the request has passed its wait (each took
-    // the ticket after it): the marker or row-pass count goes back to 0 for
-    // the next call.
-    if (how == kStateMarker) st_dev(ready_marker(counters, b), (uint64_t)0);
+    // the ticket after it): the ready slot goes back to 0 for the next
+    // call.
+    if constexpr (HOW == kStateSlot) {
+      uint64_t* slot = ready_slot(counters, b);
+      st_dev(&slot[0], (uint64_t)0);
+      st_dev(&slot[1], (uint64_t)0);
+    }
   }
 }
 
@@ -495,9 +558,12 @@ __global__ __launch_bounds__(kThreads) void k_draw(
     const ReqState* __restrict__ state, DrawPart* __restrict__ part,
     unsigned* __restrict__ counters) {
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  draw_block<DT, NE, KIND>(static_cast<int>(blockIdx.x / G2), static_cast<int>(blockIdx.x % G2),
-                           kStateStored, target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
-                           seed, ctr0, accepted_len, out_tokens, probe, state, part, counters);
+  const RowPass none{nullptr, nullptr, 0, 0.f};
+  draw_block<DT, NE, KIND, kStateStored>(static_cast<int>(blockIdx.x / G2),
+                                         static_cast<int>(blockIdx.x % G2), target, draft, k, V,
+                                         C2, inv_t, draft_tokens, uniforms, seed, ctr0,
+                                         accepted_len, out_tokens, probe, state, none, part,
+                                         counters);
 }
 
 // One-launch path: the row-pass work-groups, then the draw work-groups
@@ -523,9 +589,11 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
   else {
     const long db = (long)blockIdx.x - n_row_blocks;
     const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-    draw_block<DT, NE, 0>(static_cast<int>(db / G2), static_cast<int>(db % G2), kStateMarker,
-                          target, draft, k, V, C2, inv_t, draft_tokens, uniforms, seed, ctr0,
-                          accepted_len, out_tokens, probe, state, part2, counters);
+    const RowPass rows{part1, zrow, C1, c};
+    draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(db / G2), static_cast<int>(db % G2),
+                                      target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
+                                      seed, ctr0, accepted_len, out_tokens, probe, state, rows,
+                                      part2, counters);
   }
 }
 

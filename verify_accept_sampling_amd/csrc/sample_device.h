@@ -1,7 +1,7 @@
 // Device routines of the sampling verification kernels: the float32 row
 // statistic and its sweep, the float64 draw terms and chunk sums, the chunk
-// search of the inverse-CDF draw, and the coherent state and markers the
-// one-launch kernel passes between work-groups.
+// search of the inverse-CDF draw, and the coherent state and ready slots
+// the one-launch kernel passes between work-groups.
 #pragma once
 
 #include <climits>
@@ -505,16 +505,46 @@ __device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk
   return s_tok == INT_MAX ? s_last : s_tok;
 }
 
-// Per-request ready marker of the one-launch kernel: 1 once the request's
-// state (acceptance result) is published, 0 again when its draw is done.
-// Request b's marker sits in the marker slot of request j, j = b with its
-// two bytes swapped, so the markers of up to 256 consecutive requests are
-// 4 KB apart: many work-groups waiting on neighbouring requests then poll
-// different memory channels instead of one.
-__device__ __forceinline__ uint64_t* ready_marker(unsigned* counters, int b) {
+// Words of the one-launch kernel's hand-over.  Request b's words sit at the
+// counter-region position of request j, j = b with its two bytes swapped, so
+// those of up to 256 consecutive requests are 8 KB apart: many work-groups
+// waiting on neighbouring requests then poll different memory channels
+// instead of one.
+__device__ __forceinline__ long handover_pos(int b) {
   static_assert(kMaxB == 65536, "two-byte request index");
-  const long j = (long)((b & 255) << 8 | (b >> 8 & 255));
-  return reinterpret_cast<uint64_t*>(&counters[j * kCountersPerReq + 2]);
+  return (long)((b & 255) << 8 | (b >> 8 & 255)) * kCountersPerReq;
+}
+// Row count: every row-pass work-group of request b adds 1 once its pair is
+// published; complete at (2k + 1) x chunks; set back to 0 by the work-group
+// that saw it complete.
+__device__ __forceinline__ unsigned* row_count(unsigned* counters, int b) {
+  return &counters[handover_pos(b) + kRowCountWord];
+}
+// Ready slot: two 64-bit words that hold the request's packed draw state
+// once its acceptance tests are done, both zero otherwise (the request's
+// draw clears them).
+__device__ __forceinline__ uint64_t* ready_slot(unsigned* counters, int b) {
+  return reinterpret_cast<uint64_t*>(&counters[handover_pos(b) + kReadySlotWord]);
+}
+
+// Packed draw state: word 0 = (n + 1, mp), word 1 = (mq, rho32 as float with
+// the sign bit set).  Neither word of a published state is zero, so a reader
+// that sees both nonzero has the whole state whatever order the two stores
+// arrive in.  rho32 only places the kink band (relative width 1e-5) and the
+// linear correction's base point, so float precision suffices.
+__device__ __forceinline__ void pack_state(const ReqState& st, uint64_t& w0, uint64_t& w1) {
+  w0 = (uint64_t)(uint32_t)(st.n + 1) | ((uint64_t)__float_as_uint(st.mp) << 32);
+  w1 = (uint64_t)__float_as_uint(st.mq) |
+       ((uint64_t)(__float_as_uint((float)st.rho32) | 0x80000000u) << 32);
+}
+__device__ __forceinline__ ReqState unpack_state(uint64_t w0, uint64_t w1, int k) {
+  ReqState st;
+  st.n = (int)(uint32_t)w0 - 1;
+  st.mode = st.n < k ? kModeResidual : kModeBonus;
+  st.mp = __uint_as_float((uint32_t)(w0 >> 32));
+  st.mq = __uint_as_float((uint32_t)w1);
+  st.rho32 = (double)__uint_as_float((uint32_t)(w1 >> 32) & 0x7fffffffu);
+  return st;
 }
 
 // ReqState through coherent 64-bit words (read by other work-groups).
@@ -536,14 +566,30 @@ __device__ __forceinline__ ReqState ld_dev_state(const ReqState* p) {
   return v;
 }
 
-// Polls of a marker before a wait gives up (a few seconds; a legitimate
+// Polls of a ready slot before a wait gives up (a few seconds; a legitimate
 // wait lasts microseconds).
 constexpr long kSpinLimit = 1L << 20;
 
-// One thread waits until the marker is set.  False if the bound is reached.
-__device__ __forceinline__ bool wait_marker(const uint64_t* marker) {
+// One thread waits until the count reaches `target`.  False if the bound is
+// reached.
+__device__ __forceinline__ bool wait_count(const unsigned* count, unsigned target) {
   for (long spin = 0; spin < kSpinLimit; ++spin) {
-    if (ld_dev(marker) != 0) return true;
+    if (__hip_atomic_load(const_cast<unsigned*>(count), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT) >= target)
+      return true;
+    if (spin < 4) __builtin_amdgcn_s_sleep(2);
+    else __builtin_amdgcn_s_sleep(32);
+  }
+  return false;
+}
+
+// One thread waits until both words of a ready slot are set and returns
+// them.  False if the bound is reached.
+__device__ __forceinline__ bool wait_slot(const uint64_t* slot, uint64_t& w0, uint64_t& w1) {
+  for (long spin = 0; spin < kSpinLimit; ++spin) {
+    w0 = ld_dev(&slot[0]);
+    w1 = ld_dev(&slot[1]);
+    if (w0 != 0 && w1 != 0) return true;
     // A few quick polls, then about 2000 cycles between polls.
     if (spin < 4) __builtin_amdgcn_s_sleep(2);
     else __builtin_amdgcn_s_sleep(32);
