@@ -299,7 +299,9 @@ __device__ __forceinline__ void draw_block(
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
   __shared__ double tab[256];
   static_assert(kThreads == 256, "one table entry per thread");
-  if (KIND == 0) tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
+  // The exp table's load is issued now and stored to shared memory after
+  // the wait below, so the load and the first poll share one round trip.
+  const double tv = KIND == 0 ? kExp2Frac256[threadIdx.x] : 0.0;
   int n;
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
@@ -356,6 +358,7 @@ __device__ __forceinline__ void draw_block(
                           k, V, draft_tokens, uniforms, seed, ctr0, grp == 0, accepted_len,
                           out_tokens, probe);
   }
+  if (KIND == 0) tab[threadIdx.x] = tv;
   __syncthreads();
   const bool resid = n < k;
   const double c1 = inv_t * kInvLn2x256, c0p = -mp * c1, c0q = -mq * c1;
