@@ -37,11 +37,12 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B=64 k=8 V=128256"
 # Dominant kernel of each path, and the committed rocprofv3 counter summary of
 # its HBM traffic at this workload.
-KERNELS = {"auto": "k_sample_one", "two_launch": "k_row_stats"}
+KERNELS = {"auto": "k_sample_one", "two_launch": "k_row_stats", "early_exit": "k_sample_one"}
 
 
-def traffic_file(kernel: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{kernel}_b64_k8_v128256_traffic.json")
+def traffic_file(path: str) -> str:
+    suffix = "_early_exit" if path == "early_exit" else ""
+    return os.path.join(ROOT, "profiles", f"{KERNELS[path]}_b64_k8_v128256{suffix}_traffic.json")
 
 
 # Algorithmic bytes of the row pass at this workload: every logit of the
@@ -64,11 +65,12 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if absent or taken on other kernel sources."""
+def measured_traffic(path: str):
+    """HBM bytes per launch of the dominant kernel of sampling path `path`
+    from the committed rocprofv3 counter summary, or None if absent or taken
+    on other kernel sources."""
     try:
-        with open(traffic_file(kernel)) as f:
+        with open(traffic_file(path)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -97,13 +99,14 @@ def _pmc_means(csv_path: str, counter: str, kernel: str):
     return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, kernel: str):
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, path: str):
     """Turn the FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch) into HBM
     bytes per launch of `kernel`.  Each counter is scaled by what it reads
     for a plain elementwise copy of copy_mib MiB (which reads and writes
     exactly that many bytes), and the result is written next to the
     kernel-source hash it was taken on."""
     nbytes = copy_mib * 1024 * 1024
+    kernel = KERNELS[path]
     fetch, nf = _pmc_means(fetch_csv, "FETCH_SIZE", kernel)
     write, nw = _pmc_means(write_csv, "WRITE_SIZE", kernel)
     f_scale = nbytes / (fetch["copy"] * 1024.0)
@@ -111,7 +114,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, k
     rd = fetch["row"] * 1024.0 * f_scale
     wr = write["row"] * 1024.0 * w_scale
     out = {
-        "kernel": kernel, "workload": "B=64 k=8 V=128256 bf16",
+        "kernel": kernel, "path": path, "workload": "B=64 k=8 V=128256 bf16",
         "kernel_source_sha": kernel_source_sha(),
         "fetch_kib_per_dispatch": fetch["row"], "write_kib_per_dispatch": write["row"],
         "copy_bytes": nbytes, "copy_fetch_kib": fetch["copy"], "copy_write_kib": write["copy"],
@@ -121,7 +124,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, k
         "hbm_bytes_per_launch": rd + wr,
         "command": command,
     }
-    with open(traffic_file(kernel), "w") as f:
+    with open(traffic_file(path), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -280,13 +283,16 @@ def main():
                     help="sample (default): the headline sampling workload; the others print "
                          "a line for a greedy kernel")
     ap.add_argument("--path", choices=sorted(KERNELS), default="auto",
-                    help="auto: the one-launch kernel; two_launch: row pass, then draw")
+                    help="auto: the one-launch kernel; two_launch: row pass, then draw; "
+                         "early_exit: the one-launch kernel that stops reading rows past each "
+                         "request's first rejection (bandwidth over the bytes each call must "
+                         "read)")
     args = ap.parse_args()
     if args.summarize_pmc:
         if args.copy_calibration_mib <= 0:
             raise SystemExit("--summarize-pmc needs --copy-calibration-mib of the profiled runs")
         summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.pmc_command,
-                      KERNELS[args.path])
+                      args.path)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -360,14 +366,21 @@ def main():
     # searched chunk of each
     drawn_rows = (acc_all < k).sum(axis=1) + B
     draw_bytes = drawn_rows * row_bytes + drawn_rows * min(V, DRAW_CHUNK) * 2
-    step_bytes = float(np.mean(pass1_bytes + draw_bytes))
+    if args.path == "early_exit":
+        # Bytes each call must read: per request the target rows 0..n and
+        # the draft rows 0..min(n, k-1) (a request's outputs depend on
+        # nothing else), plus the draw's re-read.
+        need_rows = (np.minimum(acc_all + 1, k + 1) + np.minimum(acc_all + 1, k)).sum(axis=1)
+        step_bytes = float(np.mean(need_rows * row_bytes + draw_bytes))
+    else:
+        step_bytes = float(np.mean(pass1_bytes + draw_bytes))
     kernel = KERNELS[args.path]
-    if args.path == "auto":
+    if args.path in ("auto", "early_exit"):
         dom, dom_bytes = kern["fused"]["avg_us"], step_bytes
     else:
         dom, dom_bytes = kern["row_pass"]["avg_us"], float(pass1_bytes)
     achieved = dom_bytes / (dom * 1e-6) / 1e9
-    traffic = measured_traffic(kernel)
+    traffic = measured_traffic(args.path)
     positions = B * (k + 1)
     result = {
         "metric": METRIC,
@@ -389,6 +402,8 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes},
         "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "bytes_basis": ("must-read rows up to each request's first rejection + draw re-read"
+                        if args.path == "early_exit" else "every logit row once + draw re-read"),
         "step_algorithmic_bytes": step_bytes,
         "kernels_avg_us": {n: v["avg_us"] for n, v in kern.items()},
         "mean_accepted": float(acc_all.mean()),

@@ -171,16 +171,22 @@ int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes,
 int spec_tree_depth(const int32_t* parent_host, int n_nodes);
 
 /* Which kernels spec_verify_sample uses for raw logits.
- * SPEC_PATH_AUTO (the default): one launch (SPEC_KERNEL_FUSED) whose row-pass
- *   work-groups come first and whose draw work-groups each wait for their
- *   request's acceptance result, so early requests' draws overlap the end of
- *   the row pass.
+ * SPEC_PATH_AUTO (the default): one launch (SPEC_KERNEL_FUSED) that reads
+ *   every row once.  The rows of each request's early positions come first;
+ *   most requests stop at one of them (stop at the first rejection: EAGLE-3
+ *   review "Speculative Decoding" step 3), so their draws run while the rows
+ *   of later positions stream.
  * SPEC_PATH_TWO_LAUNCH: the row pass (SPEC_KERNEL_ROW_PASS), then the draw
  *   (SPEC_KERNEL_DRAW).
- * Both follow the same rule with the same arithmetic.  The setting is
- * process-wide and applies to calls made after it.  Returns the previous
- * setting, or SPEC_EINVAL for an unknown mode. */
-enum { SPEC_PATH_AUTO = 0, SPEC_PATH_TWO_LAUNCH = 1 };
+ * SPEC_PATH_EARLY_EXIT: as SPEC_PATH_AUTO, except that the row pass stops
+ *   reading a row once its request is known to stop before that row's
+ *   position (such rows cannot change any output), so fewer bytes are read.
+ *   When probe values are asked for, every row is read as with
+ *   SPEC_PATH_AUTO.
+ * All follow the same rule with the same arithmetic and give identical
+ * outputs.  The setting is process-wide and applies to calls made after it.
+ * Returns the previous setting, or SPEC_EINVAL for an unknown mode. */
+enum { SPEC_PATH_AUTO = 0, SPEC_PATH_TWO_LAUNCH = 1, SPEC_PATH_EARLY_EXIT = 2 };
 int spec_sample_path(int mode);
 
 /* Optional per-kernel timing for measurement tools (not part of the

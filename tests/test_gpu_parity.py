@@ -24,12 +24,20 @@ def _say(msg):
     print(msg, flush=True)
 
 
-@pytest.fixture(params=["auto", "two_launch"])
+# Whether _run_sample asks for probe values (set per sampling path).
+_WANT_PROBE = {"value": True}
+
+
+@pytest.fixture(params=["auto", "two_launch", "early_exit"])
 def sample_path(request):
-    """Run a sampling test through the one-launch kernel (where the shape
-    allows it) and through the two-launch kernels."""
+    """Run a sampling test through the one-launch kernel, the two-launch
+    kernels and the early-exit kernel.  Early exit reads every row when probe
+    values are asked for, so there the probe is left out and the outputs
+    alone are compared."""
     prev = S.spec_sample_path(request.param)
+    _WANT_PROBE["value"] = request.param != "early_exit"
     yield request.param
+    _WANT_PROBE["value"] = True
     S.spec_sample_path(prev)
 
 
@@ -150,7 +158,9 @@ def test_tree_shapes_chain_single_and_deep():
 # ---------------------------------------------------------------------------
 
 
-def _run_sample(wl, seed=None, counter0=0, requests=None, use_array=True, max_mismatch=0):
+def _run_sample(wl, seed=None, counter0=0, requests=None, use_array=True, max_mismatch=0,
+                probe=None):
+    probe = _WANT_PROBE["value"] if probe is None else probe
     seed = wl.uniform_seed if seed is None else seed
     u = R.chain_uniforms(seed, wl.B, wl.k, counter0)
     tgt = to_device(wl.target, wl.dtype)
@@ -158,24 +168,28 @@ def _run_sample(wl, seed=None, counter0=0, requests=None, use_array=True, max_mi
     toks = ints_to_device(wl.draft_tokens)
     if use_array:
         ug = S.spec_fill_uniforms(seed, counter0, wl.B * (wl.k + 1) * 2).view(wl.B, wl.k + 1, 2)
-        acc_g, out_g, pr_g = S.spec_verify_sample(tgt, dft, toks, wl.temperature, uniforms=ug,
-                                                  kind=wl.kind, probe=True)
+        res_g = S.spec_verify_sample(tgt, dft, toks, wl.temperature, uniforms=ug, kind=wl.kind,
+                                     probe=probe)
     else:
-        acc_g, out_g, pr_g = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=seed,
-                                                  counter0=counter0, kind=wl.kind, probe=True)
+        res_g = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=seed,
+                                     counter0=counter0, kind=wl.kind, probe=probe)
     torch.cuda.synchronize()
-    acc_g, out_g, pr_g = acc_g.cpu().numpy(), out_g.cpu().numpy(), pr_g.cpu().numpy()
+    acc_g, out_g = res_g[0].cpu().numpy(), res_g[1].cpu().numpy()
     check_chain_structure(acc_g, out_g, wl.draft_tokens, wl.V)
     reqs = list(range(wl.B)) if requests is None else list(requests)
     acc_o, out_o, res = O.verify_sample(wl.target, wl.draft, wl.draft_tokens, u,
                                         wl.temperature, wl.kind, wl.dtype, requests=reqs)
     st = compare_sample(acc_g, out_g, acc_o, out_o, res, reqs)
-    where = []
-    worst = check_probe(pr_g, wl, acc_g, acc_o, res, reqs, where)
-    _say(f"  {wl.name}: {st} probe_max_abs_err={worst:.3g} at (b, i, field, gpu, oracle)={where[0]}")
+    if probe:
+        where = []
+        worst = check_probe(res_g[2].cpu().numpy(), wl, acc_g, acc_o, res, reqs, where)
+        _say(f"  {wl.name}: {st} probe_max_abs_err={worst:.3g} at "
+             f"(b, i, field, gpu, oracle)={where[0]}")
+        assert worst <= PROB_TOL
+    else:
+        _say(f"  {wl.name}: {st} (no probe)")
     assert st["unflagged"] == 0, st["unflagged_requests"]
     assert st["mismatches"] <= max_mismatch, st
-    assert worst <= PROB_TOL
     return acc_g, out_g
 
 
@@ -214,6 +228,29 @@ def test_sample_identical_draft_accepts_everything(sample_path):
     assert np.all(acc == wl.k)
 
 
+def test_sample_requests_decided_after_early_positions(sample_path):
+    """Rows of only the first few positions precede the one-launch kernel's
+    early acceptance tests when B x row chunks is large (here 48 requests x 3
+    chunks of V = 140000).  A request that accepts all of them is finished
+    by its first draw work-group from the later rows: every draft accepted
+    (identical draft rows), and drafts that match for four positions, then
+    differ."""
+    wl = W.sample_chain(48, 5, 140000, seed=5, uniform_seed=6, target_std=2.0, noise_std=1.0,
+                        temperature=1.0, dtype="bf16")
+    same = wl.draft.copy()
+    same[:] = wl.target[:, : wl.k]
+    wl_all = W.ChainWorkload("identical_draft_wide", wl.target, same, wl.draft_tokens, "logits",
+                             wl.dtype, wl.temperature, wl.uniform_seed)
+    acc, _ = _run_sample(wl_all)
+    assert np.all(acc == wl.k)
+    part = wl.draft.copy()
+    part[:, :4] = wl.target[:, :4]
+    wl_part = W.ChainWorkload("late_rejections", wl.target, part, wl.draft_tokens, "logits",
+                              wl.dtype, wl.temperature, wl.uniform_seed)
+    acc, _ = _run_sample(wl_part)
+    assert np.all(acc >= 4) and (acc < wl.k).any()
+
+
 def test_sample_masks_and_bad_tokens(sample_path):
     rng = np.random.default_rng(11)
     wl = W.sample_chain(32, 4, 2048, seed=9, uniform_seed=10, target_std=2.0, noise_std=1.0,
@@ -229,6 +266,30 @@ def test_sample_masks_and_bad_tokens(sample_path):
     toks[2, 3] = 2 ** 31 - 1
     wl.draft_tokens = toks
     _run_sample(wl)
+
+
+def test_sample_early_exit_matches_full_sweep(llama3_full):
+    """Early exit stops reading rows past each request's first rejection;
+    with and without probe values its outputs equal the full sweep's, bit
+    for bit, over several uniform draws."""
+    wl = llama3_full
+    tgt, dft = to_device(wl.target, wl.dtype), to_device(wl.draft, wl.dtype)
+    toks = ints_to_device(wl.draft_tokens)
+    prev = S.spec_sample_path("auto")
+    try:
+        for c in range(4):
+            ctr = c * wl.B * (wl.k + 1) * 2
+            outs = []
+            for path, probe in (("auto", False), ("early_exit", False), ("early_exit", True)):
+                S.spec_sample_path(path)
+                r = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=wl.uniform_seed,
+                                         counter0=ctr, probe=probe)
+                torch.cuda.synchronize()
+                outs.append((r[0].cpu().numpy(), r[1].cpu().numpy()))
+            for a, o in outs[1:]:
+                assert np.array_equal(a, outs[0][0]) and np.array_equal(o, outs[0][1])
+    finally:
+        S.spec_sample_path(prev)
 
 
 def test_sample_probs_small_and_empty_residual():

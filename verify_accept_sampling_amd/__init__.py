@@ -97,13 +97,15 @@ def load_library():
 
 
 KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2, "fused": 3}
-SAMPLE_PATHS = {"auto": 0, "two_launch": 1}
+SAMPLE_PATHS = {"auto": 0, "two_launch": 1, "early_exit": 2}
 
 
 def spec_sample_path(mode: str) -> str:
     """Choose the kernels spec_verify_sample uses for raw logits ("auto": one
-    persistent launch where the shape allows it; "two_launch": always the
-    row pass then the draw).  Returns the previous mode."""
+    launch that reads every row; "two_launch": the row pass, then the draw;
+    "early_exit": one launch that stops reading rows past each request's
+    first rejection, unless probe values are asked for).  All give identical
+    outputs.  Returns the previous mode."""
     prev = load_library().spec_sample_path(SAMPLE_PATHS[mode])
     if prev < 0:
         _check(prev)

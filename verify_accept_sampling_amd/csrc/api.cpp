@@ -56,7 +56,8 @@ std::atomic<int> g_sample_path{SPEC_PATH_AUTO};
 extern "C" {
 
 int spec_sample_path(int mode) {
-  if (mode != SPEC_PATH_AUTO && mode != SPEC_PATH_TWO_LAUNCH) return SPEC_EINVAL;
+  if (mode != SPEC_PATH_AUTO && mode != SPEC_PATH_TWO_LAUNCH && mode != SPEC_PATH_EARLY_EXIT)
+    return SPEC_EINVAL;
   return specv::g_sample_path.exchange(mode);
 }
 
@@ -128,7 +129,8 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
   if (k > 0 && (draft == nullptr || draft_tokens == nullptr)) return SPEC_EINVAL;
   const long C2 = (V + kDrawChunk - 1) / kDrawChunk;
   const long draw_groups = (long)B * ((res_chunks(V) + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup);
-  if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V) + draw_groups) != SPEC_OK)
+  const long finalizers = ((long)B + kWaves - 1) / kWaves;
+  if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V) + finalizers + draw_groups) != SPEC_OK)
     return SPEC_EINVAL;
   if (check_grid((long)B * C2) != SPEC_OK) return SPEC_EINVAL;
   WsLayout L;

@@ -51,7 +51,7 @@ static_assert(kMinChunkElems >= kRowChunkElemsMin, "partials are sized for chunk
 constexpr int kSegPerThread = SPEC_DRAW_SEG;
 constexpr int kDrawChunk = 64 * kSegPerThread;
 #ifndef SPEC_DRAW_CHUNKS_PER_WAVE
-#define SPEC_DRAW_CHUNKS_PER_WAVE 2
+#define SPEC_DRAW_CHUNKS_PER_WAVE 3
 #endif
 constexpr int kDrawChunksPerWave = SPEC_DRAW_CHUNKS_PER_WAVE;
 constexpr int kDrawChunksPerGroup = kWaves * kDrawChunksPerWave;
@@ -92,14 +92,14 @@ struct DrawPart {
 static_assert(sizeof(DrawPart) == 80, "DrawPart layout");
 
 // Per-request 32-bit words of the counter region: [0] row-pass completion
-// ticket, [1] draw completion ticket, [2] the row count of the one-launch
-// kernel, [3] unused, [4..7] the ready slot of the one-launch kernel, two
+// ticket, [1] draw completion ticket, [2] the verdict word of the one-launch
+// kernel's early acceptance tests, [3] unused, [4..7] its ready slot, two
 // 64-bit words that carry a request's packed draw state.  The one-launch
 // words of position j belong to request j with its two bytes swapped.
 // Every word is back to 0 when a call completes.  The last 256 bytes are
 // reserved.
 constexpr int kCountersPerReq = 8;
-constexpr int kRowCountWord = 2;
+constexpr int kVerdictWord = 2;
 constexpr int kReadySlotWord = 4;
 constexpr size_t kCounterRegionBytes = (size_t)kMaxB * kCountersPerReq * 4 + 256;
 static_assert(kCounterRegionBytes == SPEC_WORKSPACE_COUNTER_BYTES, "counter region");
@@ -107,11 +107,15 @@ static_assert(kCounterRegionBytes == SPEC_WORKSPACE_COUNTER_BYTES, "counter regi
 // Workspace layout.  The counter region (kCounterRegionBytes) sits at a
 // fixed place whatever the call's shape; it must be zero before the first
 // call, and every call leaves it zero (tickets reset by their last taker,
-// ready slots cleared by the request's draw).  The other regions are
-// written before they are read within each call.
+// ready slots cleared by the request's draw).  The completion tags of the
+// one-launch row pass hold the tag of the call that wrote them; every call
+// has a tag of its own, so a tag left by an earlier call (or any other
+// content) is never taken for a current one.  The other regions are written
+// before they are read within each call.
 struct WsLayout {
   size_t count;  // counter region, always at offset 0
   size_t part1;  // uint64 [rows * row_chunks]: packed (max, sum) or (value, index)
+  size_t flag;   // uint64 [rows * row_chunks]: completion tags of the one-launch row pass
   size_t zrow;   // float [rows]: each row's logit at its draft token
   size_t state;  // ReqState [B]
   size_t part2;  // DrawPart [B * res_chunks]
@@ -132,6 +136,8 @@ inline WsLayout ws_layout(int B, int n_pos, int V) {
   L.count = off;
   off = align_up(off + kCounterRegionBytes, 256);
   L.part1 = off;
+  off = align_up(off + rows * (size_t)row_chunks_max(V) * 8, 256);
+  L.flag = off;
   off = align_up(off + rows * (size_t)row_chunks_max(V) * 8, 256);
   L.zrow = off;
   off = align_up(off + rows * 4, 256);

@@ -33,7 +33,9 @@
 // work-group.
 // Probabilities path (rows given as distributions): k_draw alone, each
 // work-group first repeating the (gather-only) acceptance tests.
+#include <algorithm>
 #include <atomic>
+#include <random>
 
 #include "sample_device.h"
 
@@ -42,15 +44,18 @@ namespace specv {
 // Statistic of chunk `chunk` (of C1) of row r of request b: the sweep, the
 // block reduction, and thread 0's coherent stores of the (reference, sum)
 // pair and, in the chunk holding the row's draft token, of the logit there.
-// Every thread returns.
-template <int DT, int NE>
-__device__ __forceinline__ void row_chunk_stat(int b, int r, int chunk,
+// Every thread returns.  WATCH: the sweep stops early once the request's
+// ready slot (`watch`) shows it stopped before this row's position; then
+// nothing is stored.  Returns, in thread 0, whether the pair was stored.
+template <int DT, int NE, bool WATCH = false>
+__device__ __forceinline__ bool row_chunk_stat(int b, int r, int chunk,
                                                const void* __restrict__ target,
                                                const void* __restrict__ draft, int k, int V,
                                                int C1, float c,
                                                const int32_t* __restrict__ draft_tokens,
                                                uint64_t* __restrict__ part,
-                                               float* __restrict__ zrow) {
+                                               float* __restrict__ zrow,
+                                               const uint64_t* watch = nullptr) {
   const int R = 2 * k + 1;
   const long rowid = (long)b * R + r;
   const void* rp = stat_row<DT>(target, draft, b, r, k, V);
@@ -69,87 +74,141 @@ __device__ __forceinline__ void row_chunk_stat(int b, int r, int chunk,
   if constexpr (NE == 1)
     stats_sweep_scalar<DT>(rp, g0, g1, c, m, mc, s);
   else
-    stats_sweep<DT, kThreads>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0, g1, c,
-                              m, mc, s, threadIdx.x);
+    stats_sweep<DT, kThreads, WATCH>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0,
+                                     g1, c, m, mc, s, threadIdx.x, watch,
+                                     r <= k ? r : r - k - 1);
   // The chunk that holds the token also publishes the logit there.
   const bool own = x >= 0 && x < V && (long)x >= g0 * NE && (long)x < g1 * NE;
   float zx = 0.f;
   if (own) zx = load_elem<DT>(rp, x);
   block_reduce_ms(m, s, c);
-  if (threadIdx.x == 0) {
+  // m = +inf: a wave stopped early (inputs are finite or -inf)
+  const bool store = !WATCH || m != INFINITY;
+  if (threadIdx.x == 0 && store) {
     st_dev(&part[rowid * C1 + chunk], pack2(m, (float)s));
     if (own) st_dev_f(&zrow[rowid], zx);
   }
+  return store;
 }
 
-// Acceptance tests of request b by one wave, from its published row
-// statistics.  Lane i handles position i (and i + 64, ...): it loads the
-// token, the two published token logits and the chunk partials of target
-// row i and draft row i in one round, merges the rows and tests draft i.
-// With e_p = z c - fl(M_p c) (z the target logit at x_i) and e_q likewise,
-// p_i(x_i) / q_i(x_i) = 2^(e_p - e_q) S_q / S_p, one exp2 per position.
-// Each lane also prepares the draw state of the row it would hand over (its
-// first rejected position, or the bonus row), and after the wave minimum
-// the owner of the first rejection supplies it.  Returns the state in every
-// lane.  With `write` it also stores accepted_len[b], the accepted prefix,
-// the -1 padding and the probe values other than probe[b, n, 2], which
-// belongs to the draw.
+// Position i of request b, by one lane, from the published row statistics:
+// the token, the two token logits and the chunk partials of target row i
+// and draft row i are loaded in one round and the rows merged.  With
+// e_p = z c - fl(M_p c) (z the target logit at x_i) and e_q likewise,
+// p_i(x_i) / q_i(x_i) = 2^(e_p - e_q) S_q / S_p, one exp2.  Position k, the
+// bonus row, has no test: it reports acceptance.  mp, mq and rho are the
+// draw state if the request stops here (target row k for the bonus).
+struct PosResult {
+  bool accept;
+  float pv, qv;  // p_i(x_i), q_i(x_i) when asked for, else 0
+  float mp, mq;  // references of the rows drawn from
+  double rho;    // S_p / S_q of those rows from the float32 statistics
+};
+__device__ __forceinline__ PosResult test_position(
+    int b, int i, int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
+    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    const uint64_t* __restrict__ part, const float* __restrict__ zrow, bool want_probe) {
+  const int R = 2 * k + 1;
+  const bool draft_pos = i < k;
+  int x = -1;
+  float zp = 0.f, zq = 0.f;
+  if (draft_pos) {
+    x = draft_tokens[(long)b * k + i];
+    zp = ld_dev_f(&zrow[(long)b * R + i]);
+    zq = ld_dev_f(&zrow[(long)b * R + k + 1 + i]);
+  }
+  float Mp, Mq;
+  double Sp, Sq;
+  merge_two_rows(part, ((long)b * R + i) * C1, ((long)b * R + k + 1 + i) * C1, draft_pos, C1, c,
+                 Mp, Sp, Mq, Sq);
+  PosResult res{true, 0.f, 0.f, Mp, 0.f, 1.0};
+  if (!draft_pos) return res;
+  res.accept = false;
+  if (x >= 0 && x < V) {
+    const double ep = (double)zp * c - (double)mul_rn(Mp, c);
+    const double eq = (double)zq * c - (double)mul_rn(Mq, c);
+    const double ratio = exp2(ep - eq) * (Sq / Sp);
+    const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
+    res.accept = (double)u < ratio;
+    if (want_probe) {
+      res.pv = (float)(exp2(ep) / Sp);
+      res.qv = (float)(exp2(eq) / Sq);
+    }
+  }
+  if (!res.accept) {
+    // S_p / S_q with both sums taken relative to 2^(M c) instead of
+    // 2^fl32(M c), rounded to float: it travels packed in the one-launch
+    // kernel's ready slot, and both forms use the same value.
+    res.mq = Mq;
+    res.rho = (double)(float)(Sp / Sq *
+                              exp2(((double)mul_rn(Mp, c) - (double)Mp * c) -
+                                   ((double)mul_rn(Mq, c) - (double)Mq * c)));
+  }
+  return res;
+}
+
+// probe[b, i, 0, 1, 3] of a tested position (i < k): p, q and 0.
+__device__ __forceinline__ void write_probe_position(float* probe, int b, int i, int k,
+                                                     const PosResult& r) {
+  float* pr = probe + ((long)b * (k + 1) + i) * 4;
+  pr[0] = r.pv;
+  pr[1] = r.qv;
+  pr[3] = 0.f;
+}
+
+// Outputs of the acceptance tests once n is known, by one wave:
+// accepted_len[b], the accepted prefix, the -1 padding, probe[b, i, 2] = 0
+// for i != n (probe[b, n, 2] belongs to the draw) and the other probe
+// entries of the bonus row k.
+__device__ __forceinline__ void write_accept_outputs(int b, int k, int n,
+                                                     const int32_t* __restrict__ draft_tokens,
+                                                     int32_t* __restrict__ accepted_len,
+                                                     int32_t* __restrict__ out_tokens,
+                                                     float* __restrict__ probe) {
+  const int lane = threadIdx.x & 63;
+  for (int i = lane; i <= k; i += kWaveSize) {
+    if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
+    else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
+    if (probe && i != n) probe[((long)b * (k + 1) + i) * 4 + 2] = 0.f;
+  }
+  if (lane == 0) {
+    accepted_len[b] = n;
+    if (probe) {
+      float* pr = probe + ((long)b * (k + 1) + k) * 4;
+      pr[0] = 0.f;
+      pr[1] = 0.f;
+      pr[3] = 0.f;
+    }
+  }
+}
+
+// Acceptance tests of request b by one wave once every row is complete.
+// Lane i handles position i (and i + 64, ...); each lane keeps the draw
+// state of its first rejected position (or of the bonus row), and after the
+// wave minimum the owner of the first rejection supplies it.  Returns the
+// state in every lane, and with `write` stores the outputs and every probe
+// value other than probe[b, n, 2].
 __device__ __forceinline__ ReqState finalize_request(
     int b, int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     const uint64_t* __restrict__ part, const float* __restrict__ zrow, bool write,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe) {
-  const int R = 2 * k + 1;
   const int lane = threadIdx.x & 63;
+  const bool want_probe = write && probe != nullptr;
   int first = k;
   float cand_mp = 0.f, cand_mq = 0.f;  // draw state of this lane's hand-over row
   double cand_rho = 1.0;
   for (int i = lane; i <= k; i += kWaveSize) {
-    const bool draft_pos = i < k;
-    int x = -1;
-    float zp = 0.f, zq = 0.f;
-    if (draft_pos) {
-      x = draft_tokens[(long)b * k + i];
-      zp = ld_dev_f(&zrow[(long)b * R + i]);
-      zq = ld_dev_f(&zrow[(long)b * R + k + 1 + i]);
+    const PosResult r = test_position(b, i, k, V, C1, c, draft_tokens, uniforms, seed, ctr0, part,
+                                      zrow, want_probe);
+    if (first == k && (!r.accept || i == k)) {
+      if (!r.accept) first = i;
+      cand_mp = r.mp;
+      cand_mq = r.mq;
+      cand_rho = r.rho;
     }
-    float Mp, Mq;
-    double Sp, Sq;
-    merge_two_rows(part, ((long)b * R + i) * C1, ((long)b * R + k + 1 + i) * C1, draft_pos, C1,
-                   c, Mp, Sp, Mq, Sq);
-    if (!draft_pos) {
-      // bonus row k: handed over only if nothing was rejected
-      if (first == k) cand_mp = Mp;
-      continue;
-    }
-    float pv = 0.f, qv = 0.f;
-    bool accept = false;
-    if (x >= 0 && x < V) {
-      const double ep = (double)zp * c - (double)mul_rn(Mp, c);
-      const double eq = (double)zq * c - (double)mul_rn(Mq, c);
-      const double ratio = exp2(ep - eq) * (Sq / Sp);
-      const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
-      accept = (double)u < ratio;
-      if (probe != nullptr) {
-        pv = (float)(exp2(ep) / Sp);
-        qv = (float)(exp2(eq) / Sq);
-      }
-    }
-    if (!accept && first == k) {
-      first = i;
-      // S_p / S_q with both sums taken relative to 2^(M c) instead of
-      // 2^fl32(M c).
-      cand_mp = Mp;
-      cand_mq = Mq;
-      cand_rho = Sp / Sq *
-                 exp2(((double)mul_rn(Mp, c) - (double)Mp * c) -
-                      ((double)mul_rn(Mq, c) - (double)Mq * c));
-    }
-    if (write && probe) {
-      float* pr = probe + ((long)b * (k + 1) + i) * 4;
-      pr[0] = pv; pr[1] = qv; pr[3] = 0.f;
-    }
+    if (want_probe && i < k) write_probe_position(probe, b, i, k, r);
   }
   const int n = wave_min_i(first);
   const int owner = n & (kWaveSize - 1);  // the lane that handled position n
@@ -158,54 +217,228 @@ __device__ __forceinline__ ReqState finalize_request(
   st.mode = n < k ? kModeResidual : kModeBonus;
   st.mp = __shfl(cand_mp, owner, 64);
   st.mq = __shfl(cand_mq, owner, 64);
-  // rounded to float: it travels packed in the one-launch kernel's ready
-  // slot, and both forms use the same value
-  st.rho32 = (double)(float)__shfl(cand_rho, owner, 64);
-  if (write) {
-    for (int i = lane; i <= k; i += kWaveSize) {
-      if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
-      else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
-      // probe[b, n, 2] (the mass drawn from) belongs to the draw, which may
-      // run in another work-group of the same launch
-      if (probe && i != n) probe[((long)b * (k + 1) + i) * 4 + 2] = 0.f;
-    }
-    if (lane == 0) {
-      accepted_len[b] = n;
-      if (probe) {
-        float* pr = probe + ((long)b * (k + 1) + k) * 4;
-        pr[0] = 0.f; pr[1] = 0.f; pr[3] = 0.f;
-      }
-    }
-  }
+  st.rho32 = __shfl(cand_rho, owner, 64);
+  if (write) write_accept_outputs(b, k, n, draft_tokens, accepted_len, out_tokens, probe);
   return st;
 }
 
-// Row pass of one work-group: block `bid` of the row-pass grid.  In the
-// two-launch form the request's last work-group (by ticket) runs the
-// acceptance tests on one wave and stores the draw state.  In the
-// grid-ordered one-launch kernel (one_launch) the work-group only counts
-// itself in, and the request's first draw work-group takes over.
-template <int DT, int NE>
-__device__ __forceinline__ void row_block(
-    long bid, bool one_launch, const void* __restrict__ target, const void* __restrict__ draft,
-    int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
+// Whether every chunk of the rows of position i of request b (target row i,
+// and draft row i for i < k) carries this call's completion tag.
+__device__ __forceinline__ bool position_complete(const uint64_t* __restrict__ flags, int b, int i,
+                                                  int k, int C1, uint64_t tag) {
+  const long R = 2L * k + 1;
+  const long tr = ((long)b * R + i) * C1;
+  const long dr = ((long)b * R + k + 1 + i) * C1;
+  bool have = true;
+  for (int ch = 0; ch < C1; ++ch) {
+    have &= ld_dev(&flags[tr + ch]) == tag;
+    if (i < k) have &= ld_dev(&flags[dr + ch]) == tag;
+  }
+  return have;
+}
+
+// Acceptance tests of request b by one wave while the rows still stream
+// (one-launch kernel, rows in position order), from position `base` (every
+// earlier one tested and accepted) up to, not including, `limit`.  Each round
+// takes the positions whose rows are complete, tests that prefix, and stops
+// at the first rejection, or after the bonus row k; rows past that point are
+// never waited for.  kDecided: `st` holds the state.  kDeferred: every
+// position below `limit` was accepted and position k lies beyond it.
+// kTimedOut: the wait bound was reached.  `tested` is the number of
+// positions tested (whose probe values were written, with a probe).
+enum { kDecided = 0, kDeferred = 1, kTimedOut = 2 };
+__device__ __forceinline__ int finalize_progressive(
+    int b, int k, int V, int C1, float c, int base, int limit,
+    const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms, uint64_t seed,
+    uint64_t ctr0, const uint64_t* __restrict__ part, const float* __restrict__ zrow,
+    const uint64_t* __restrict__ flags, uint64_t tag, float* __restrict__ probe, ReqState& st,
+    int& tested) {
+  const int lane = threadIdx.x & 63;
+  const bool want_probe = probe != nullptr;
+  const int end = min(limit, k + 1);
+  tested = base;
+  for (long spin = 0; spin < kSpinLimit; ++spin) {
+    if (base >= end) return kDeferred;
+    const int i = base + lane;
+    const bool have = i < end && position_complete(flags, b, i, k, C1, tag);
+    const uint64_t hm = __ballot(have);
+    const int m = ~hm == 0 ? kWaveSize : __builtin_ctzll(~hm);  // complete prefix
+    if (m == 0) {
+      if (spin < 4) __builtin_amdgcn_s_sleep(2);
+      else __builtin_amdgcn_s_sleep(32);
+      continue;
+    }
+    PosResult r{true, 0.f, 0.f, 0.f, 0.f, 1.0};
+    if (lane < m)
+      r = test_position(b, i, k, V, C1, c, draft_tokens, uniforms, seed, ctr0, part, zrow,
+                        want_probe);
+    if (want_probe && lane < m && i < k) write_probe_position(probe, b, i, k, r);
+    tested = base + m;
+    const uint64_t rm = __ballot(lane < m && !r.accept);
+    if (rm != 0 || base + m > k) {
+      const int owner = rm != 0 ? __builtin_ctzll(rm) : k - base;
+      const int n = base + owner;
+      st.n = n;
+      st.mode = n < k ? kModeResidual : kModeBonus;
+      st.mp = __shfl(r.mp, owner, 64);
+      st.mq = __shfl(r.mq, owner, 64);
+      st.rho32 = __shfl(r.rho, owner, 64);
+      return kDecided;
+    }
+    base += m;
+  }
+  return kTimedOut;
+}
+
+// Publishes a decided state in request b's ready slot (lane 0 of the
+// deciding wave).
+__device__ __forceinline__ void publish_state(unsigned* counters, int b, const ReqState& st) {
+  uint64_t w0, w1;
+  pack_state(st, w0, w1);
+  uint64_t* slot = ready_slot(counters, b);
+  st_dev(&slot[0], w0);
+  st_dev(&slot[1], w1);
+}
+
+// Verdict word of request b's early acceptance tests (one-launch kernel):
+// 0 until they end; then kVerdictDecided | tested << 2 (the state is in the
+// ready slot, `tested` positions have probe values) or kVerdictDeferred |
+// next << 2 (positions from `next` on remain to be tested).  The request's
+// first draw work-group reads it and resets it.
+constexpr unsigned kVerdictDecided = 1, kVerdictDeferred = 2;
+__device__ __forceinline__ unsigned* verdict_word(unsigned* counters, int b) {
+  return &counters[handover_pos(b) + kVerdictWord];
+}
+
+// Early acceptance tests of request b, by one wave of a finalizer
+// work-group, over the positions whose rows precede the finalizers in the
+// grid (`limit` of them).
+__device__ __forceinline__ void early_finalize(
+    int b, int k, int V, int C1, float c, int limit, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
-    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    const uint64_t* __restrict__ part, const float* __restrict__ zrow,
+    const uint64_t* __restrict__ flags, uint64_t tag, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ out_tokens, float* __restrict__ probe, unsigned* __restrict__ counters) {
+  // This wave decides when the request's draw can start: it issues first.
+  __builtin_amdgcn_s_setprio(3);
+  ReqState st;
+  int tested = 0;
+  const int res = finalize_progressive(b, k, V, C1, c, 0, limit, draft_tokens, uniforms, seed,
+                                       ctr0, part, zrow, flags, tag, probe, st, tested);
+  if (res == kTimedOut) return;  // never expected
+  unsigned verdict;
+  if (res == kDecided) {
+    if ((threadIdx.x & 63) == 0) publish_state(counters, b, st);
+    write_accept_outputs(b, k, st.n, draft_tokens, accepted_len, out_tokens, probe);
+    verdict = kVerdictDecided | (unsigned)tested << 2;
+  } else {
+    verdict = kVerdictDeferred | (unsigned)tested << 2;
+  }
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_store(verdict_word(counters, b), verdict, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One thread waits until the verdict word is set, returns it and resets it.
+// 0 if the bound is reached.
+__device__ __forceinline__ unsigned take_verdict(unsigned* word) {
+  for (long spin = 0; spin < kSpinLimit; ++spin) {
+    const unsigned v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v != 0) {
+      __hip_atomic_store(word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return v;
+    }
+    if (spin < 4) __builtin_amdgcn_s_sleep(2);
+    else __builtin_amdgcn_s_sleep(32);
+  }
+  return 0;
+}
+
+// Probe values of the positions from `from` on that the progressive tests
+// did not reach (they follow the first rejection), by one wave, each once
+// its rows are complete.
+__device__ __forceinline__ void probe_remaining(
+    int b, int k, int V, int C1, float c, int from, const int32_t* __restrict__ draft_tokens,
+    const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    const uint64_t* __restrict__ part, const float* __restrict__ zrow,
+    const uint64_t* __restrict__ flags, uint64_t tag, float* __restrict__ probe) {
+  const int lane = threadIdx.x & 63;
+  for (int base = from; base < k; base += kWaveSize) {
+    const int i = base + lane;
+    bool done = i >= k;
+    for (long spin = 0; spin < kSpinLimit; ++spin) {
+      if (!done && position_complete(flags, b, i, k, C1, tag)) {
+        const PosResult r = test_position(b, i, k, V, C1, c, draft_tokens, uniforms, seed, ctr0,
+                                          part, zrow, true);
+        write_probe_position(probe, b, i, k, r);
+        done = true;
+      }
+      if (__ballot(!done) == 0) break;
+      __builtin_amdgcn_s_sleep(32);
+    }
+  }
+}
+
+// Row-pass grid of the one-launch kernel, in position order: for each
+// position i = 0..k-1 every request's target row i and draft row i (C1
+// chunks each), then every request's bonus row k.  Requests are decided by
+// the rows of the positions up to their first rejection, so most are
+// decided early in the pass and their draws overlap the rest of it.
+__device__ __forceinline__ void position_major_row(long bid, int B, int k, int C1, int& b,
+                                                   int& r, int& chunk) {
+  const long per_pos = (long)B * 2 * C1;
+  if (bid < (long)k * per_pos) {
+    const int pos = static_cast<int>(bid / per_pos);
+    const long rem = bid % per_pos;
+    b = static_cast<int>(rem / (2 * C1));
+    const int rem2 = static_cast<int>(rem % (2 * C1));
+    r = rem2 < C1 ? pos : k + 1 + pos;
+    chunk = rem2 % C1;
+  } else {
+    const long rem = bid - (long)k * per_pos;
+    b = static_cast<int>(rem / C1);
+    r = k;
+    chunk = static_cast<int>(rem % C1);
+  }
+}
+
+// Row pass of one work-group: block `bid` of the row-pass grid.
+// Two-launch form (rows in request order): the request's last work-group
+// (by ticket) runs the acceptance tests on one wave and stores the draw
+// state.  One-launch kernel (rows in position order): the work-group tags
+// its chunk complete once its pair is published, and the request's first
+// draw work-group takes it from there.
+template <int DT, int NE, bool EXIT = false>
+__device__ __forceinline__ void row_block(
+    long bid, bool one_launch, int B, const void* __restrict__ target,
+    const void* __restrict__ draft, int k, int V, int C1, float c,
+    const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms, uint64_t seed,
+    uint64_t ctr0, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe, uint64_t* __restrict__ part, float* __restrict__ zrow,
-    ReqState* __restrict__ state, unsigned* __restrict__ counters) {
+    uint64_t* __restrict__ flags, uint64_t tag, ReqState* __restrict__ state,
+    unsigned* __restrict__ counters) {
   const int R = 2 * k + 1;
-  const int chunk = static_cast<int>(bid % C1);
-  const long rowid = bid / C1;
-  const int b = static_cast<int>(rowid / R);
-  const int r = static_cast<int>(rowid % R);
-  row_chunk_stat<DT, NE>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens, part, zrow);
+  int b, r, chunk;
   if (one_launch) {
-    // Count this work-group in once its pair (and logit) are complete; no
-    // reply is awaited, so the work-group ends one round trip earlier.
-    if (threadIdx.x == 0) {  // the thread that stored them
+    position_major_row(bid, B, k, C1, b, r, chunk);
+  } else {
+    chunk = static_cast<int>(bid % C1);
+    b = static_cast<int>(bid / C1 / R);
+    r = static_cast<int>(bid / C1 % R);
+  }
+  // Early exit: rows after position 0 stop once the request is decided
+  // before their position (no probe values are asked for then).
+  const bool stored =
+      EXIT && (r <= k ? r : r - k - 1) > 0
+          ? row_chunk_stat<DT, NE, true>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens,
+                                         part, zrow, ready_slot(counters, b))
+          : row_chunk_stat<DT, NE>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens, part,
+                                   zrow);
+  if (one_launch) {
+    // The tag follows the pair (and logit) once they are complete.
+    if (threadIdx.x == 0 && stored) {  // the thread that stored them
       wait_stores();
-      __hip_atomic_fetch_add(row_count(counters, b), 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+      st_dev(&flags[((long)b * R + r) * C1 + chunk], tag);
     }
     return;
   }
@@ -274,20 +507,23 @@ enum {
   kStateSlot = 1,    // one-launch hand-over through the row count and ready slot
 };
 
-// Row-pass outputs the finishing draw work-group reads.
+// Row-pass outputs the request's first draw work-group reads.
 struct RowPass {
-  const uint64_t* part;  // (reference, sum) pairs, C1 per row
-  const float* zrow;     // each row's logit at its draft token
-  int C1;                // chunks per row
-  float c;               // log2(e) / T
+  const uint64_t* part;   // (reference, sum) pairs, C1 per row
+  const float* zrow;      // each row's logit at its draft token
+  const uint64_t* flags;  // completion tag of each row chunk
+  uint64_t tag;           // this call's completion tag
+  int C1;                 // chunks per row
+  float c;                // log2(e) / T
 };
 
 // Draw of one work-group: chunk group grp of request b.  With kStateSlot,
-// work-group 0 of the request waits until every row-pass work-group of the
-// request has counted itself in, runs the acceptance tests on one wave
-// (writing their outputs), publishes the packed state in the request's ready
-// slot and resets the count; the request's other draw work-groups wait for
-// the ready slot, and the request's last draw work-group clears it.
+// work-group 0 of the request takes the verdict of the request's early
+// acceptance tests; if they left positions untested it tests those on one
+// wave as their rows complete, publishes the packed state in the request's
+// ready slot and writes the tests' outputs.  The request's other draw
+// work-groups wait for the ready slot, and the request's last draw
+// work-group clears it.
 template <int DT, int NE, int KIND, int HOW>
 __device__ __forceinline__ void draw_block(
     int b, int grp, const void* __restrict__ target, const void* __restrict__ draft,
@@ -310,32 +546,40 @@ __device__ __forceinline__ void draw_block(
       __shared__ int s_ok;
       __shared__ uint64_t s_w[2];
       if (grp == 0) {  // work-group-uniform
+        // The request's early acceptance tests either decided it or left
+        // the positions from some point on to this work-group.
         if (threadIdx.x < kWaveSize) {
-          unsigned* cnt = row_count(counters, b);
-          int ok = 0;
-          if (threadIdx.x == 0) ok = wait_count(cnt, (unsigned)((2 * k + 1) * rows.C1)) ? 1 : 0;
-          ok = __shfl(ok, 0, 64);
-          if (ok) {
-            // The other waves of this compute unit stream rows or draw; this
-            // one decides when the request's draw can start: it issues first.
+          unsigned v = 0;
+          if (threadIdx.x == 0) v = take_verdict(verdict_word(counters, b));
+          v = __shfl(v, 0, 64);
+          int tested = (int)(v >> 2);
+          int ok = (v & 3) == kVerdictDecided ? 1 : 0;
+          bool mine_ready = false;
+          ReqState mine;
+          if ((v & 3) == kVerdictDeferred) {
             __builtin_amdgcn_s_setprio(3);
-            const ReqState mine =
-                finalize_request(b, k, V, rows.C1, rows.c, draft_tokens, uniforms, seed, ctr0,
-                                 rows.part, rows.zrow, true, accepted_len, out_tokens, probe);
+            const int res = finalize_progressive(
+                b, k, V, rows.C1, rows.c, tested, INT_MAX, draft_tokens, uniforms, seed, ctr0,
+                rows.part, rows.zrow, rows.flags, rows.tag, probe, mine, tested);
             __builtin_amdgcn_s_setprio(0);
-            if (threadIdx.x == 0) {
-              uint64_t w0, w1;
-              pack_state(mine, w0, w1);
-              uint64_t* slot = ready_slot(counters, b);
-              st_dev(&slot[0], w0);
-              st_dev(&slot[1], w1);
-              // every row-pass work-group of the request has counted itself in
-              __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              s_w[0] = w0;
-              s_w[1] = w1;
+            if (res == kDecided) {
+              if (threadIdx.x == 0) publish_state(counters, b, mine);
+              write_accept_outputs(b, k, mine.n, draft_tokens, accepted_len, out_tokens, probe);
+              ok = 1;
+              mine_ready = true;
             }
           }
-          if (threadIdx.x == 0) s_ok = ok;
+          if (ok && probe)  // positions after the first rejection, as their rows complete
+            probe_remaining(b, k, V, rows.C1, rows.c, tested, draft_tokens, uniforms, seed, ctr0,
+                            rows.part, rows.zrow, rows.flags, rows.tag, probe);
+          if (threadIdx.x == 0) {
+            uint64_t w0 = 0, w1 = 0;
+            if (mine_ready) pack_state(mine, w0, w1);
+            else if (ok) ok = wait_slot(ready_slot(counters, b), w0, w1) ? 1 : 0;
+            s_w[0] = w0;
+            s_w[1] = w1;
+            s_ok = ok;
+          }
         }
       } else if (threadIdx.x == 0) {
         uint64_t w0 = 0, w1 = 0;
@@ -548,8 +792,9 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, float* __restrict__ probe, uint64_t* __restrict__ part,
     float* __restrict__ zrow, ReqState* __restrict__ state, unsigned* __restrict__ counters) {
-  row_block<DT, NE>(blockIdx.x, false, target, draft, k, V, C1, c, draft_tokens, uniforms, seed, ctr0,
-                    accepted_len, out_tokens, probe, part, zrow, state, counters);
+  row_block<DT, NE>(blockIdx.x, false, 0, target, draft, k, V, C1, c, draft_tokens, uniforms, seed,
+                    ctr0, accepted_len, out_tokens, probe, part, zrow, nullptr, 0, state,
+                    counters);
 }
 
 template <int DT, int NE, int KIND>
@@ -561,7 +806,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(
     const ReqState* __restrict__ state, DrawPart* __restrict__ part,
     unsigned* __restrict__ counters) {
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  const RowPass none{nullptr, nullptr, 0, 0.f};
+  const RowPass none{nullptr, nullptr, nullptr, 0, 0, 0.f};
   draw_block<DT, NE, KIND, kStateStored>(static_cast<int>(blockIdx.x / G2),
                                          static_cast<int>(blockIdx.x % G2), target, draft, k, V,
                                          C2, inv_t, draft_tokens, uniforms, seed, ctr0,
@@ -569,31 +814,70 @@ __global__ __launch_bounds__(kThreads) void k_draw(
                                          counters);
 }
 
-// One-launch path: the row-pass work-groups, then the draw work-groups
-// (request by request).  Work-groups are dispatched in index order, so
-// every row-pass work-group has been dispatched before a draw work-group
-// takes a slot, and a draw work-group only waits for row-pass work of its
-// own request: the wait ends.  Early requests' draws run while the last
-// row-pass work-groups stream.  (Interleaving draw work-groups earlier in
-// the grid was slower: waiting draw work-groups hold slots that streaming
-// work-groups need.)
-template <int DT, int NE>
+// One-launch path.  Grid, in dispatch order:
+//   1. the row-pass work-groups of positions 0 .. E-1 of every request, in
+//      position order (E: as many positions as the first round of resident
+//      work-groups streams);
+//   2. the finalizer work-groups, one request per wave, which test each
+//      request's early positions as their rows complete;
+//   3. for each request b in turn: the row-pass work-groups of b's positions
+//      E .. k, then b's draw work-groups.
+// Most requests stop at one of their early positions, so their states are
+// ready about when the first round of row-pass work-groups ends, and their
+// draws run while the rows of later positions and requests stream.  A
+// request the finalizers leave undecided is finished by its first draw
+// work-group, whose remaining rows precede it.  Work-groups are dispatched
+// in index order and every wait is for work earlier in the grid (a
+// finalizer for early rows, a first draw work-group for its finalizer and
+// its request's rows, the other draw work-groups for the request's state),
+// so every wait ends.  EXIT: row-pass work-groups after position 0 stop
+// once their request is decided before their position.
+template <int DT, int NE, bool EXIT>
 __global__ __launch_bounds__(kThreads) void k_sample_one(
     const void* __restrict__ target, const void* __restrict__ draft, int B, int k, int V, int C1,
     int C2, float c, double inv_t, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe, uint64_t* __restrict__ part1, float* __restrict__ zrow,
-    ReqState* __restrict__ state, DrawPart* __restrict__ part2, unsigned* __restrict__ counters,
-    long n_row_blocks) {
-  if ((long)blockIdx.x < n_row_blocks)
-    row_block<DT, NE>(blockIdx.x, true, target, draft, k, V, C1, c, draft_tokens, uniforms, seed,
-                      ctr0, accepted_len, out_tokens, probe, part1, zrow, state, counters);
-  else {
-    const long db = (long)blockIdx.x - n_row_blocks;
-    const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-    const RowPass rows{part1, zrow, C1, c};
-    draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(db / G2), static_cast<int>(db % G2),
+    uint64_t* __restrict__ flags, uint64_t tag, ReqState* __restrict__ state,
+    DrawPart* __restrict__ part2, unsigned* __restrict__ counters, int E, long n_early_rows,
+    int n_fin) {
+  const long bid = blockIdx.x;
+  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  long row = -1;  // row-pass index in position order
+  long draw = -1;
+  if (bid < n_early_rows) {
+    row = bid;
+  } else if (bid < n_early_rows + n_fin) {
+    const int b = static_cast<int>((bid - n_early_rows) * kWaves + (threadIdx.x >> 6));
+    if (b < B)
+      early_finalize(b, k, V, C1, c, E, draft_tokens, uniforms, seed, ctr0, part1, zrow, flags,
+                     tag, accepted_len, out_tokens, probe, counters);
+    return;
+  } else {
+    // Request b's rows of positions E .. k (target and draft row of each
+    // position, then the bonus row), then its draw work-groups.
+    const long L = E > k ? 0 : (2L * (k - E) + 1) * C1;
+    const long j = bid - n_early_rows - n_fin;
+    const int b = static_cast<int>(j / (L + G2));
+    const long o = j % (L + G2);
+    if (o >= L) {
+      draw = (long)b * G2 + (o - L);
+    } else {
+      const long per_pos = (long)B * 2 * C1;
+      const int pos = E + static_cast<int>(o / (2 * C1));
+      const long w = o % (2 * C1);
+      row = pos < k ? (long)pos * per_pos + (long)b * 2 * C1 + w
+                    : (long)k * per_pos + (long)b * C1 + w;
+    }
+  }
+  if (row >= 0) {
+    row_block<DT, NE, EXIT>(row, true, B, target, draft, k, V, C1, c, draft_tokens, uniforms,
+                            seed, ctr0, accepted_len, out_tokens, probe, part1, zrow, flags, tag,
+                            state, counters);
+  } else {
+    const RowPass rows{part1, zrow, flags, tag, C1, c};
+    draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2),
                                       target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
                                       seed, ctr0, accepted_len, out_tokens, probe, state, rows,
                                       part2, counters);
@@ -606,11 +890,40 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
 
 static int row_chunks(int V) { return (V + kRowChunkElems - 1) / kRowChunkElems; }
 
+// Completion tag of one one-launch call: a marker byte, 16 bits drawn once
+// per process and a 40-bit call counter, so no two calls of a process share
+// a tag, and neither zero-filled memory nor any value the workspace holds
+// otherwise (floats, doubles, counts) looks like one.
+static uint64_t call_tag() {
+  static const uint64_t process_bits = [] {
+    std::random_device rd;
+    return (uint64_t)(rd() & 0xffffu);
+  }();
+  static std::atomic<uint64_t> calls{0};
+  const uint64_t n = calls.fetch_add(1, std::memory_order_relaxed) + 1;
+  return (0xC3ull << 56) | (process_bits << 40) | (n & ((1ull << 40) - 1));
+}
+
 // Work-groups of the one-launch kernel resident per compute unit.  The row
 // pass runs in rounds of (compute units x this) work-groups, and the early
 // requests' draws share the second round.  Measured at B = 64, k = 8,
 // V = 128256 bf16: 4 per unit +2 us per call, 5 best, 6 +9 us.
 constexpr int kOneLaunchGroupsPerCU = 5;
+
+// Compute units of the current device.
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      return 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 // Shared memory per compute unit of the current device.
 static int device_lds_per_cu() {
@@ -637,7 +950,7 @@ static uint32_t one_launch_lds(uint32_t need) {
   int sl = static_lds.load(std::memory_order_relaxed);
   if (sl < 0) {
     hipFuncAttributes fa;
-    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&k_sample_one<DT, NE>)) !=
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&k_sample_one<DT, NE, false>)) !=
         hipSuccess)
       return need;
     sl = static_cast<int>(fa.sharedSizeBytes);
@@ -675,11 +988,24 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   auto* zr = reinterpret_cast<float*>(w + L.zrow);
   const long n_row = (long)B * R * C1;
   const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
-  if (g_sample_path.load(std::memory_order_relaxed) == SPEC_PATH_AUTO) {
-    return launch_timed(kProfFused, &k_sample_one<DT, NE>, dim3((unsigned)(n_row + (long)B * G2)),
-                        dim3(kThreads), one_launch_lds<DT, NE>(0), s, target, draft, B, k, V, C1, C2, c, inv_t,
+  const int path = g_sample_path.load(std::memory_order_relaxed);
+  if (path != SPEC_PATH_TWO_LAUNCH) {
+    auto* fl = reinterpret_cast<uint64_t*>(w + L.flag);
+    // Early positions: as many as the first round of resident work-groups
+    // streams (at least one).
+    const long per_pos = (long)B * 2 * C1;
+    const long slots = (long)device_cus() * kOneLaunchGroupsPerCU;
+    const int E = (int)std::max(1L, std::min((long)k + 1, slots / per_pos));
+    const long n_early_rows = E > k ? n_row : (long)E * per_pos;
+    const int n_fin = (B + kWaves - 1) / kWaves;
+    // Early exit needs no probe values beyond each request's stop.
+    const bool exit_early = path == SPEC_PATH_EARLY_EXIT && probe == nullptr;
+    return launch_timed(kProfFused,
+                        exit_early ? &k_sample_one<DT, NE, true> : &k_sample_one<DT, NE, false>,
+                        dim3((unsigned)(n_row + n_fin + (long)B * G2)), dim3(kThreads),
+                        one_launch_lds<DT, NE>(0), s, target, draft, B, k, V, C1, C2, c, inv_t,
                         draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1,
-                        zr, st, p2, cnt, n_row);
+                        zr, fl, call_tag(), st, p2, cnt, E, n_early_rows, n_fin);
   }
   hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>, dim3((unsigned)n_row),
                              dim3(kThreads), 0, s, target, draft, k, V, C1, c, draft_tokens,

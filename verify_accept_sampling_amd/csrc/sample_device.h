@@ -112,15 +112,22 @@ __device__ __forceinline__ void stat_words(float& m, float& mc, double& s, const
 // thread (index tid) takes every NT-th word.  Software pipelined: the next
 // iteration's kUnrollStats loads are issued before the current words are
 // folded in, so every wave keeps loads in flight while it computes.
-template <int DT, int NT>
+template <int DT, int NT, bool WATCH = false>
 __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, long g0, long g1,
-                                            float c, float& m, float& mc, double& s, int tid) {
+                                            float c, float& m, float& mc, double& s, int tid,
+                                            const uint64_t* watch = nullptr, int pos = 0) {
   constexpr int NE = Elems<DT>::kVec;
   constexpr uint32_t kStep = NT * kUnrollStats * 16u;
   const RowBuf buf(rp, row_bytes);
   long g = g0 + tid;
   uint32_t off = static_cast<uint32_t>(g) * 16u;
   const long span = (long)(kUnrollStats - 1) * NT;
+  // WATCH: the request's ready slot is read once per pair of batches (the
+  // value is used one pair later, so the read never stalls the stream); once
+  // it shows the request stopped before position `pos`, this row decides
+  // nothing and the wave stops, marking its partial with m = +inf.
+  uint64_t wv = 0;
+  if constexpr (WATCH) wv = ld_dev(watch);
   if (g + span < g1) {
     // Two word buffers used in turn (no register copies, which would wait
     // for the loads in flight).
@@ -148,6 +155,14 @@ __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, 
       for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
       __builtin_amdgcn_sched_barrier(0);
       stat_words<DT>(m, mc, s, wb, c);
+      if constexpr (WATCH) {
+        if (wv != 0 && (int)(uint32_t)wv - 1 < pos) {  // wave-uniform: one address
+          m = INFINITY;
+          s = 0.0;
+          return;
+        }
+        wv = ld_dev(watch);
+      }
     }
   }
   for (; g < g1; g += NT, off += NT * 16u) {
@@ -505,20 +520,13 @@ __device__ int search_chunk(const void* prow, const void* qrow, int V, int chunk
   return s_tok == INT_MAX ? s_last : s_tok;
 }
 
-// Words of the one-launch kernel's hand-over.  Request b's words sit at the
-// counter-region position of request j, j = b with its two bytes swapped, so
-// those of up to 256 consecutive requests are 8 KB apart: many work-groups
-// waiting on neighbouring requests then poll different memory channels
-// instead of one.
+// Counter-region position of request b's ready slot: that of request j,
+// j = b with its two bytes swapped, so the slots of up to 256 consecutive
+// requests are 8 KB apart: many work-groups waiting on neighbouring
+// requests then poll different memory channels instead of one.
 __device__ __forceinline__ long handover_pos(int b) {
   static_assert(kMaxB == 65536, "two-byte request index");
   return (long)((b & 255) << 8 | (b >> 8 & 255)) * kCountersPerReq;
-}
-// Row count: every row-pass work-group of request b adds 1 once its pair is
-// published; complete at (2k + 1) x chunks; set back to 0 by the work-group
-// that saw it complete.
-__device__ __forceinline__ unsigned* row_count(unsigned* counters, int b) {
-  return &counters[handover_pos(b) + kRowCountWord];
 }
 // Ready slot: two 64-bit words that hold the request's packed draw state
 // once its acceptance tests are done, both zero otherwise (the request's
@@ -569,19 +577,6 @@ __device__ __forceinline__ ReqState ld_dev_state(const ReqState* p) {
 // Polls of a ready slot before a wait gives up (a few seconds; a legitimate
 // wait lasts microseconds).
 constexpr long kSpinLimit = 1L << 20;
-
-// One thread waits until the count reaches `target`.  False if the bound is
-// reached.
-__device__ __forceinline__ bool wait_count(const unsigned* count, unsigned target) {
-  for (long spin = 0; spin < kSpinLimit; ++spin) {
-    if (__hip_atomic_load(const_cast<unsigned*>(count), __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_AGENT) >= target)
-      return true;
-    if (spin < 4) __builtin_amdgcn_s_sleep(2);
-    else __builtin_amdgcn_s_sleep(32);
-  }
-  return false;
-}
 
 // One thread waits until both words of a ready slot are set and returns
 // them.  False if the bound is reached.
