@@ -194,39 +194,46 @@ __global__ __launch_bounds__(kThreads) void k_tree_greedy(
   if (!argmax_chunk<DT, NE>(target, n_nodes, V, C1, part, counters, b)) return;
   __shared__ int amax[NMAX];
   __shared__ int tok[NMAX];
+  __shared__ int16_t par[NMAX];
   __shared__ int path[NMAX];
-  __shared__ int16_t dep[NMAX];
-  __shared__ int s_best;
-  for (int j = threadIdx.x; j < n_nodes; j += kThreads) tok[j] = node_tokens[(long)b * n_nodes + j];
-  merge_argmax_rows(part, b, n_nodes, C1, amax);
-  if (threadIdx.x == 0) {
-    // parent[j] < j, so one ascending pass settles every node's depth and
-    // acceptance.  The accepted flags use path[] as scratch before the path
-    // is written.
-    path[0] = 1;
-    dep[0] = 0;
-    int best = 0;
-    for (int j = 1; j < n_nodes; ++j) {
-      const int pa = tree.parent[j];
-      dep[j] = static_cast<int16_t>(dep[pa] + 1);
-      const int ok = path[pa] && (tok[j] == amax[pa]);
-      path[j] = ok;
-      if (ok && dep[j] > dep[best]) best = j;
-    }
-    s_best = best;
+  __shared__ int s_len, s_best;
+  for (int j = threadIdx.x; j < n_nodes; j += kThreads) {
+    tok[j] = node_tokens[(long)b * n_nodes + j];
+    par[j] = tree.parent[j];
   }
-  __syncthreads();
-  const int best = s_best;
-  const int len = dep[best];
-  __syncthreads();
+  merge_argmax_rows(part, b, n_nodes, C1, amax);  // ends with a barrier
+  // Node j is accepted when every node on its path below the root matches
+  // its parent's argmax.  Each thread walks up from its own nodes (stopping
+  // at the first mismatch), so the whole tree is settled in about its depth
+  // of steps; the deepest accepted node wins, the lowest index among equals
+  // (key: depth, then -index; the root alone is depth 0).
+  int key = 0xFFFF;  // the root: depth 0, index 0
+  for (int j = threadIdx.x + 1; j < n_nodes; j += kThreads) {
+    int x = j, d = 0;
+    bool ok = true;
+    while (x != 0 && ok) {
+      const int pa = par[x];
+      ok = tok[x] == amax[pa];
+      x = pa;
+      ++d;
+    }
+    if (ok) key = max(key, d << 16 | (0xFFFF - j));
+  }
+  key = -block_min_i(-key);  // the largest key, in every thread
   if (threadIdx.x == 0) {
+    const int best = 0xFFFF - (key & 0xFFFF);
+    const int len = key >> 16;
     int node = best;
     for (int d = len; d >= 0; --d) {
       path[d] = node;
-      node = tree.parent[node];
+      node = par[node];
     }
+    s_best = best;
+    s_len = len;
   }
   __syncthreads();
+  const int best = s_best;
+  const int len = s_len;
   for (int d = threadIdx.x; d <= D; d += kThreads) {
     int t = -1, p = -1;
     if (d < len) t = tok[path[d + 1]];
