@@ -5,32 +5,31 @@
 // rejection and drawing a bonus token when every draft passes (EAGLE-3
 // review "Speculative Decoding" step 3; serving chapter "how it works").
 //
-// Logits path.  Two kinds of work-group:
+// Logits path.  Three kinds of work-group:
 //   1. row pass: work-group (chunk, row) streams one chunk of one of the
 //      request's 2k+1 rows (k+1 target, k draft) with 16-byte non-temporal
 //      loads and reduces it to (max, sum 2^((x - max) c)), c = log2(e)/T, in
-//      float32; it publishes the pair and takes the request's ticket.  The
-//      request's last work-group merges the pairs (float64), evaluates every
-//      acceptance ratio p_i(x_i)/q_i(x_i) from the gathered logits, finds the
-//      first rejection n and writes the accepted prefix and the request state.
-//   2. draw: work-group (request, chunk group) over the row(s) the final token is
-//      drawn from -- target and draft row n after a rejection, target row k
-//      for the bonus -- in float64: the normaliser partials S_p, S_q and the
-//      draw weights, evaluated at the float32 estimate rho32 of S_p/S_q with
-//      their derivative in rho.  The request's last work-group forms the
-//      float64 rho, moves every chunk total to it (linear in rho unless an
-//      element sits at the kink of max(0, .), in which case the chunk is
-//      recomputed), locates the chunk holding the inverse-CDF point and
-//      searches it with the exact weights.
-// By default both run in one launch (k_sample_one): the row-pass
-// work-groups first, then the draw work-groups, so the draws of early
-// requests overlap the last row-pass work-groups.  There a row-pass
-// work-group counts itself in without awaiting a reply; the request's first
-// draw work-group waits for the count, runs the acceptance tests and
-// publishes the draw state, for which the request's other draw work-groups
-// wait.  The two-launch form (k_row_stats, then k_draw) computes the same
-// thing, with the acceptance tests in the request's last row-pass
-// work-group.
+//      float32, publishing the pair (and, in the chunk holding the row's
+//      draft token, the logit there).
+//   2. acceptance tests, one wave per request: merge the pairs (float64),
+//      evaluate each acceptance ratio p_i(x_i)/q_i(x_i) from the gathered
+//      logits, find the first rejection n, write the accepted prefix and the
+//      draw state.
+//   3. draw: work-group (request, chunk group) over the row(s) the final
+//      token is drawn from -- target and draft row n after a rejection,
+//      target row k for the bonus -- in float64: the normaliser partials
+//      S_p, S_q and the draw weights, evaluated at the float32 estimate rho32
+//      of S_p/S_q with their derivative in rho.  The request's last
+//      work-group forms the float64 rho, moves every chunk total to it
+//      (linear in rho unless an element sits at the kink of max(0, .), in
+//      which case the chunk is recomputed), locates the chunk holding the
+//      inverse-CDF point and searches it with the exact weights.
+// By default all run in one launch (k_sample_one): rows in position order,
+// so that most requests are decided by their early positions while the
+// rows of later ones stream (the grid order and its waits are described at
+// the kernel).  The two-launch form (k_row_stats, then k_draw) computes the
+// same thing, with the acceptance tests in the request's last row-pass
+// work-group (by ticket).
 // Probabilities path (rows given as distributions): k_draw alone, each
 // work-group first repeating the (gather-only) acceptance tests.
 #include <algorithm>
@@ -904,10 +903,10 @@ static uint64_t call_tag() {
   return (0xC3ull << 56) | (process_bits << 40) | (n & ((1ull << 40) - 1));
 }
 
-// Work-groups of the one-launch kernel resident per compute unit.  The row
-// pass runs in rounds of (compute units x this) work-groups, and the early
-// requests' draws share the second round.  Measured at B = 64, k = 8,
-// V = 128256 bf16: 4 per unit +2 us per call, 5 best, 6 +9 us.
+// Work-groups of the one-launch kernel resident per compute unit; the
+// first round of row-pass work-groups (compute units x this) sets how many
+// positions are early.  Measured at B = 64, k = 8, V = 128256 bf16: six per
+// unit needs the kernel held to 80 VGPRs, which spills, and is slower.
 constexpr int kOneLaunchGroupsPerCU = 5;
 
 // Compute units of the current device.
