@@ -251,6 +251,24 @@ def test_sample_requests_decided_after_early_positions(sample_path):
     assert np.all(acc >= 4) and (acc < wl.k).any()
 
 
+def test_sample_long_chain(sample_path):
+    """k = 130 draft positions: the acceptance tests run in rounds of 64
+    positions per wave (and the probe values of the positions after a stop
+    in batches of 64)."""
+    # drafts close to the target: the oracle stops these four at 130, 101,
+    # 130 and 99 (the second and third rounds of 64)
+    wl = W.sample_chain(4, 130, 512, seed=23, uniform_seed=24, target_std=1.0, noise_std=0.01,
+                        temperature=1.0, dtype="f32")
+    acc, _ = _run_sample(wl)
+    assert acc.min() >= 64
+    same = wl.draft.copy()
+    same[:] = wl.target[:, : wl.k]
+    wl_all = W.ChainWorkload("long_identical", wl.target, same, wl.draft_tokens, "logits",
+                             wl.dtype, wl.temperature, wl.uniform_seed)
+    acc_all, _ = _run_sample(wl_all)
+    assert np.all(acc_all == wl.k)
+
+
 def test_sample_masks_and_bad_tokens(sample_path):
     rng = np.random.default_rng(11)
     wl = W.sample_chain(32, 4, 2048, seed=9, uniform_seed=10, target_std=2.0, noise_std=1.0,
