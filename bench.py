@@ -263,6 +263,72 @@ def bench_greedy(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_probs(args):
+    """One JSON line for the probability-row workload: B=512, k=8, V=128256
+    float32 rows with a prescribed overlap alpha in {0.6, 0.8, 0.9}.  The
+    acceptance tests gather p(x) and q(x); the draw reads each request's
+    rows drawn from (target and draft row n after a rejection, target row k
+    for the bonus) once, so those rows are the algorithmic bytes."""
+    import numpy as np
+    import torch
+
+    import verify_accept_sampling_amd as S
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating B=512 k=8 V=128256 fp32 probability rows", file=sys.stderr,
+          flush=True)
+    wl = W.controlled_acceptance()
+    B, k, V = wl.B, wl.k, wl.V
+    t0 = torch.from_numpy(wl.target).to(dev)
+    d0 = torch.from_numpy(wl.draft).to(dev)
+    n_copies = max(1, min(args.copies, 2))  # 4.5 GB per copy, far beyond the caches
+    copies = [(t0, d0)] + [(t0.clone(), d0.clone()) for _ in range(n_copies - 1)]
+    toks = torch.from_numpy(wl.draft_tokens).to(dev)
+    ws = S.Workspace(dev)
+    n_u = B * (k + 1) * 2
+
+    def step(i):
+        t, d = copies[i % len(copies)]
+        return S.spec_verify_sample(t, d, toks, 1.0, seed=wl.uniform_seed, counter0=i * n_u,
+                                    kind="probs", workspace=ws)
+
+    print(f"bench: warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    accs = []
+    ms_step = timed_steps(step, args.warmup, args.steps, profile=False, keep=accs)
+    timed_steps(step, args.warmup + args.steps, args.steps, profile=True)
+    n, ms = S.spec_profile_read("draw")
+    kern_us = ms / n * 1e3
+    acc_all = torch.stack(accs).cpu().numpy()
+    row_bytes = V * 4
+    drawn_rows = (acc_all < k).sum(axis=1) + B
+    gathers = np.minimum(acc_all + 1, k).sum(axis=1) * 2 * 4
+    nbytes = float(np.mean(drawn_rows * row_bytes + drawn_rows * min(V, DRAW_CHUNK) * 4
+                           + gathers))
+    achieved = nbytes / (kern_us * 1e-6) / 1e9
+    result = {
+        "metric": "verified positions/s (sampling, probability rows, B=512, k=8, V=128256, fp32)",
+        "value": B * (k + 1) / (ms_step * 1e-3),
+        "unit": "verified positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "probs_b512_k8_v128256_f32", "B": B, "k": k, "V": V,
+                   "alphas": [0.6, 0.8, 0.9], "input_copies": len(copies)},
+        "roofline": {"bound": "hbm", "kernel": "k_draw", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+        "kernels_avg_us": {"k_draw": kern_us},
+        "mean_accepted": float(acc_all.mean()),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,9 +345,11 @@ def main():
                     help="host only: turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) "
                          "into the row-statistics traffic file")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
-    ap.add_argument("--workload", choices=["sample"] + sorted(GREEDY_WORKLOADS), default="sample",
-                    help="sample (default): the headline sampling workload; the others print "
-                         "a line for a greedy kernel")
+    ap.add_argument("--workload", choices=["sample", "probs"] + sorted(GREEDY_WORKLOADS),
+                    default="sample",
+                    help="sample (default): the headline sampling workload; probs: sampling on "
+                         "probability rows (B=512); the others print a line for a greedy "
+                         "kernel")
     ap.add_argument("--path", choices=sorted(KERNELS), default="auto",
                     help="auto: the one-launch kernel; two_launch: row pass, then draw; "
                          "early_exit: the one-launch kernel that stops reading rows past each "
@@ -299,6 +367,9 @@ def main():
         print("bench.py measures one GPU only: the verifier is batch-parallel and this build "
               "runs on a single MI355X (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "probs":
+        bench_probs(args)
+        return
     if args.workload != "sample":
         bench_greedy(args)
         return

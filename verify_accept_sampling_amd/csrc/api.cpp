@@ -128,9 +128,9 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
   if (target == nullptr || accepted_len == nullptr || out_tokens == nullptr) return SPEC_EINVAL;
   if (k > 0 && (draft == nullptr || draft_tokens == nullptr)) return SPEC_EINVAL;
   const long C2 = (V + kDrawChunk - 1) / kDrawChunk;
-  const long draw_groups = (long)B * ((res_chunks(V) + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup);
+  const long draws = (long)B * specv::draw_groups(res_chunks(V), 1);
   const long finalizers = ((long)B + kWaves - 1) / kWaves;
-  if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V) + finalizers + draw_groups) != SPEC_OK)
+  if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V) + finalizers + draws) != SPEC_OK)
     return SPEC_EINVAL;
   if (check_grid((long)B * C2) != SPEC_OK) return SPEC_EINVAL;
   WsLayout L;

@@ -55,6 +55,12 @@ constexpr int kDrawChunk = 64 * kSegPerThread;
 #endif
 constexpr int kDrawChunksPerWave = SPEC_DRAW_CHUNKS_PER_WAVE;
 constexpr int kDrawChunksPerGroup = kWaves * kDrawChunksPerWave;
+// Draw work-groups per request when each takes nb batches of
+// kDrawChunksPerGroup chunks.
+__host__ __device__ inline int draw_groups(int C2, int nb) {
+  const int per = kDrawChunksPerGroup * nb;
+  return (C2 + per - 1) / per;
+}
 // Elements per thread when a whole work-group searches one chunk.
 constexpr int kSearchPerThread = kDrawChunk / kThreads;
 

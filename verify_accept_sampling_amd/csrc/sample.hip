@@ -525,13 +525,13 @@ struct RowPass {
 // work-group clears it.
 template <int DT, int NE, int KIND, int HOW>
 __device__ __forceinline__ void draw_block(
-    int b, int grp, const void* __restrict__ target, const void* __restrict__ draft,
+    int b, int grp, int nb, const void* __restrict__ target, const void* __restrict__ draft,
     int k, int V, int C2, double inv_t, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe, const ReqState* __restrict__ state, const RowPass& rows,
     DrawPart* __restrict__ part, unsigned* __restrict__ counters) {
-  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  const int G2 = draw_groups(C2, nb);
   __shared__ double tab[256];
   static_assert(kThreads == 256, "one table entry per thread");
   // The exp table's load is issued now and stored to shared memory after
@@ -611,10 +611,11 @@ __device__ __forceinline__ void draw_block(
   const void* qrow =
       resid ? reinterpret_cast<const char*>(draft) + ((long)b * k + n) * V * eb_bytes : nullptr;
 
-  // ---- this work-group's chunks, kDrawChunksPerWave per wave ----
+  // ---- this work-group's chunks: nb batches, kDrawChunksPerWave per wave
+  // in each ----
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  {
-    const int first = grp * kDrawChunksPerGroup + wave * kDrawChunksPerWave;
+  for (int bt = 0; bt < nb; ++bt) {
+    const int first = (grp * nb + bt) * kDrawChunksPerGroup + wave * kDrawChunksPerWave;
     DrawPart* pb = part + (long)b * C2;
     if (first < C2) {  // wave-uniform
       if (resid)
@@ -798,16 +799,16 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
 
 template <int DT, int NE, int KIND>
 __global__ __launch_bounds__(kThreads) void k_draw(
-    const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C2,
+    const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C2, int nb,
     double inv_t, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
     uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, float* __restrict__ probe,
     const ReqState* __restrict__ state, DrawPart* __restrict__ part,
     unsigned* __restrict__ counters) {
-  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  const int G2 = draw_groups(C2, nb);
   const RowPass none{nullptr, nullptr, nullptr, 0, 0, 0.f};
   draw_block<DT, NE, KIND, kStateStored>(static_cast<int>(blockIdx.x / G2),
-                                         static_cast<int>(blockIdx.x % G2), target, draft, k, V,
+                                         static_cast<int>(blockIdx.x % G2), nb, target, draft, k, V,
                                          C2, inv_t, draft_tokens, uniforms, seed, ctr0,
                                          accepted_len, out_tokens, probe, state, none, part,
                                          counters);
@@ -842,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
     DrawPart* __restrict__ part2, unsigned* __restrict__ counters, int E, long n_early_rows,
     int n_fin) {
   const long bid = blockIdx.x;
-  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  const int G2 = draw_groups(C2, 1);
   long row = -1;  // row-pass index in position order
   long draw = -1;
   if (bid < n_early_rows) {
@@ -876,7 +877,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
                             state, counters);
   } else {
     const RowPass rows{part1, zrow, flags, tag, C1, c};
-    draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2),
+    draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2), 1,
                                       target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
                                       seed, ctr0, accepted_len, out_tokens, probe, state, rows,
                                       part2, counters);
@@ -986,7 +987,7 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   const long R = 2L * k + 1;
   auto* zr = reinterpret_cast<float*>(w + L.zrow);
   const long n_row = (long)B * R * C1;
-  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  const int G2 = draw_groups(C2, 1);
   const int path = g_sample_path.load(std::memory_order_relaxed);
   if (path != SPEC_PATH_TWO_LAUNCH) {
     auto* fl = reinterpret_cast<uint64_t*>(w + L.flag);
@@ -1012,7 +1013,7 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
                              cnt);
   if (e != hipSuccess) return e;
   return launch_timed(kProfDraw, &k_draw<DT, NE, 0>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
-                      target, draft, k, V, C2, inv_t, draft_tokens, uniforms, seed, ctr0,
+                      target, draft, k, V, C2, 1, inv_t, draft_tokens, uniforms, seed, ctr0,
                       accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);
 }
 
@@ -1025,9 +1026,29 @@ static hipError_t launch_probs(const void* target, const void* draft, int B, int
   auto* st = reinterpret_cast<ReqState*>(w + L.state);
   auto* p2 = reinterpret_cast<DrawPart*>(w + L.part2);
   auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
-  const int G2 = (C2 + kDrawChunksPerGroup - 1) / kDrawChunksPerGroup;
+  // Probability rows need little float64 work per element, so a draw
+  // work-group takes several batches of chunks: about two and a half rounds
+  // of resident work-groups in all (fewer acceptance scans, stores and
+  // tickets per byte, while later rounds still cover the load latency).
+  // Measured at B = 512, V = 128256: 1 batch 140.5 us, 2 118.8, 3 117.7
+  // (this rule), 7 (one round) 123.1.
+  static std::atomic<int> per_cu_cached{0};
+  int per_cu = per_cu_cached.load(std::memory_order_relaxed);
+  if (per_cu <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&k_draw<0, NE, 1>), kThreads, 0) !=
+            hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    per_cu_cached.store(per_cu, std::memory_order_relaxed);
+  }
+  const long slots = (long)device_cus() * per_cu;
+  const int g1 = draw_groups(C2, 1);
+  const int want = (int)std::max(1L, std::min((long)g1, (5 * slots + 2L * B - 1) / (2L * B)));
+  const int nb = (g1 + want - 1) / want;
+  const int G2 = draw_groups(C2, nb);
   return launch_timed(kProfDraw, &k_draw<0, NE, 1>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
-                      target, draft, k, V, C2, 1.0, draft_tokens, uniforms, seed, ctr0,
+                      target, draft, k, V, C2, nb, 1.0, draft_tokens, uniforms, seed, ctr0,
                       accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);
 }
 
