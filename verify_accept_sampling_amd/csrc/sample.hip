@@ -611,19 +611,20 @@ __device__ __forceinline__ void draw_block(
   const void* qrow =
       resid ? reinterpret_cast<const char*>(draft) + ((long)b * k + n) * V * eb_bytes : nullptr;
 
-  // ---- this work-group's chunks: nb batches, kDrawChunksPerWave per wave
-  // in each ----
+  // ---- this work-group's chunks: nb * kDrawChunksPerWave consecutive
+  // chunks per wave ----
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int bt = 0; bt < nb; ++bt) {
-    const int first = (grp * nb + bt) * kDrawChunksPerGroup + wave * kDrawChunksPerWave;
+  {
+    const int per_wave = nb * kDrawChunksPerWave;
+    const int first = grp * nb * kDrawChunksPerGroup + wave * per_wave;
     DrawPart* pb = part + (long)b * C2;
     if (first < C2) {  // wave-uniform
       if (resid)
-        wave_draw_chunks<DT, NE, KIND, true>(prow, qrow, V, C2, first, c1, c0p, c0q, rho32, tab,
-                                             pb);
+        wave_draw_chunks<DT, NE, KIND, true>(prow, qrow, V, C2, first, per_wave, c1, c0p, c0q,
+                                             rho32, tab, pb);
       else
-        wave_draw_chunks<DT, NE, KIND, false>(prow, qrow, V, C2, first, c1, c0p, c0q, rho32, tab,
-                                              pb);
+        wave_draw_chunks<DT, NE, KIND, false>(prow, qrow, V, C2, first, per_wave, c1, c0p, c0q,
+                                              rho32, tab, pb);
     }
   }
   wait_stores();  // every wave's partials complete before the ticket below

@@ -324,7 +324,7 @@ template <int DT, int KIND, bool RESID>
 __device__ __forceinline__ void wave_chunk_sums(const RunWords<DT>& rp, const RunWords<DT>& rq,
                                                 const void* prow, const void* qrow, int chunk,
                                                 double c1, double c0p, double c0q, double rho32,
-                                                const double* tab, double (&v)[5],
+                                                const double* tab, double& red, double& nkd,
                                                 double (&ka)[kKinkSlots],
                                                 double (&kb)[kKinkSlots]) {
   double sa = 0.0, sb = 0.0, sw = 0.0, sq = 0.0;
@@ -349,18 +349,29 @@ __device__ __forceinline__ void wave_chunk_sums(const RunWords<DT>& rp, const Ru
       sq += pos ? bq : 0.0;
     }
   }
-  v[0] = sa;
-  v[1] = sb;
-  v[2] = RESID ? sw : sa;
-  v[3] = -sq;
-  v[4] = 0.0;
-  constexpr int kSums = RESID ? 4 : 1;
+  // Record fields 0-3 (S_p, S_q, w, dw/drho) summed over the wave; lane
+  // group q (lanes 16q .. 16q+15) ends with field q in `red`.
+  const int lane = threadIdx.x & 63;
+  if constexpr (RESID) {
+    // Transposed reduction: each exchange also halves the values a lane
+    // carries (4 -> 2 -> 1), then one value per lane group finishes: 7
+    // exchanges instead of 24.
+    const bool h = (lane & 32) != 0, g = (lane & 16) != 0;
+    double k0 = h ? sw : sa, k1 = h ? -sq : sb;
+    k0 += shfl_xor_d(h ? sa : sw, 32);
+    k1 += shfl_xor_d(h ? sb : -sq, 32);
+    red = g ? k1 : k0;
+    red += shfl_xor_d(g ? k0 : k1, 16);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
+    for (int o = 8; o >= 1; o >>= 1) red += shfl_xor_d(red, o);
+  } else {
+    // bonus: S_p alone (S_q = 0, w = S_p, dw/drho = -0)
 #pragma unroll
-    for (int q = 0; q < kSums; ++q) v[q] += shfl_xor_d(v[q], o);
+    for (int o = 32; o >= 1; o >>= 1) sa += shfl_xor_d(sa, o);
+    const int q = lane >> 4;
+    red = (q & 1) ? (q == 1 ? 0.0 : -0.0) : sa;
   }
-  if constexpr (!RESID) v[2] = v[0];
+  nkd = 0.0;
 #pragma unroll
   for (int j = 0; j < kKinkSlots; ++j) ka[j] = kb[j] = 0.0;
   if constexpr (KIND == 0 && RESID) {
@@ -368,7 +379,7 @@ __device__ __forceinline__ void wave_chunk_sums(const RunWords<DT>& rp, const Ru
     int nk = 0;
 #pragma unroll
     for (int e = 0; e < kSegPerThread; ++e) nk += __popcll(km[e]);
-    v[4] = (double)nk;
+    nkd = (double)nk;
     if (nk > 0 && nk <= kKinkSlots) {  // wave-uniform, rare
       int kj0 = -1, kj1 = -1;          // element offsets within the chunk
 #pragma unroll
@@ -392,44 +403,64 @@ __device__ __forceinline__ void wave_chunk_sums(const RunWords<DT>& rp, const Ru
   }
 }
 
-// This wave's chunks first .. first + kDrawChunksPerWave - 1 of the draw
-// (those below C2): every run is loaded before the first is summed, then
-// lane 0 publishes each chunk's partial (coherent stores).  A chunk index
-// past the end loads the last chunk again, so the loads are unconditional
-// and the first chunk's sums wait only for its own loads.
+// This wave's chunks first .. first + count - 1 of the draw (those below
+// C2; count is a multiple of kDrawChunksPerWave), with a ring of
+// kDrawChunksPerWave run buffers: the first kDrawChunksPerWave chunks' runs
+// are loaded up front, and once a chunk is summed its buffer is refilled
+// with the chunk kDrawChunksPerWave ahead, so every chunk's sums wait only
+// for its own loads and a wave with many chunks keeps its loads in flight
+// while it sums.  Every block of the ring but the last refills
+// unconditionally (a chunk index past the end loads the last chunk again),
+// so the number of loads in flight, and each wait, is fixed.  Lanes 0-8
+// publish each chunk's record (one coalesced coherent store).
 template <int DT, int NE, int KIND, bool RESID>
 __device__ __forceinline__ void wave_draw_chunks(const void* prow, const void* qrow, int V, int C2,
-                                                 int first, double c1, double c0p, double c0q,
-                                                 double rho32, const double* tab,
+                                                 int first, int count, double c1, double c0p,
+                                                 double c0q, double rho32, const double* tab,
                                                  DrawPart* __restrict__ part) {
+  constexpr int P = kDrawChunksPerWave;
   const int lane = threadIdx.x & 63;
   constexpr uint32_t fill = run_fill<DT, KIND>();
-  RunWords<DT> rp[kDrawChunksPerWave], rq[kDrawChunksPerWave];
-#pragma unroll
-  for (int i = 0; i < kDrawChunksPerWave; ++i) {
-    const long j0 = (long)min(first + i, C2 - 1) * kDrawChunk + (long)lane * kSegPerThread;
+  RunWords<DT> rp[P], rq[P];
+  auto load = [&](int i, int cc) {
+    const long j0 = (long)min(cc, C2 - 1) * kDrawChunk + (long)lane * kSegPerThread;
     load_run_words<DT, NE>(prow, j0, V, fill, rp[i]);
     if constexpr (RESID) load_run_words<DT, NE>(qrow, j0, V, fill, rq[i]);
+  };
+  auto sum_store = [&](int i, int cc) {
+    double red, nkd, ka[kKinkSlots], kb[kKinkSlots];
+    wave_chunk_sums<DT, KIND, RESID>(rp[i], rq[i], prow, qrow, cc, c1, c0p, c0q, rho32, tab,
+                                     red, nkd, ka, kb);
+    // One coalesced store of the record: fields 0-3 from lanes 0, 16, 32
+    // and 48 (their groups' sums), fields 4-8 (kink count and recorded kink
+    // terms, the same in every lane) from lanes 4-8.
+    static_assert(sizeof(DrawPart) == 10 * sizeof(double) && kKinkSlots == 2,
+                  "DrawPart fields");
+    int field = -1;
+    double f = red;
+    if ((lane & 15) == 0) {
+      field = lane >> 4;
+    } else if (lane >= 4 && lane <= 8) {
+      field = lane;
+      f = lane == 4 ? nkd : lane == 5 ? ka[0] : lane == 6 ? ka[1] : lane == 7 ? kb[0] : kb[1];
+    }
+    if (field >= 0) st_dev_d(reinterpret_cast<double*>(&part[cc]) + field, f);
+  };
+  const int blocks = count / P;
+#pragma unroll
+  for (int i = 0; i < P; ++i) load(i, first + i);
+  for (int blk = 0; blk + 1 < blocks; ++blk) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int cc = first + blk * P + i;
+      if (cc < C2) sum_store(i, cc);  // wave-uniform
+      load(i, cc + P);
+    }
   }
 #pragma unroll
-  for (int i = 0; i < kDrawChunksPerWave; ++i) {
-    const int cc = first + i;
-    if (cc >= C2) break;  // wave-uniform
-    double v[5], ka[kKinkSlots], kb[kKinkSlots];
-    wave_chunk_sums<DT, KIND, RESID>(rp[i], rq[i], prow, qrow, cc, c1, c0p, c0q, rho32, tab, v,
-                                     ka, kb);
-    // Lane f stores field f of the record: one coalesced store.
-    static_assert(sizeof(DrawPart) == 10 * sizeof(double) && kKinkSlots == 2, "DrawPart fields");
-    double f = v[0];
-    f = lane == 1 ? v[1] : f;
-    f = lane == 2 ? v[2] : f;
-    f = lane == 3 ? v[3] : f;
-    f = lane == 4 ? v[4] : f;
-    f = lane == 5 ? ka[0] : f;
-    f = lane == 6 ? ka[1] : f;
-    f = lane == 7 ? kb[0] : f;
-    f = lane == 8 ? kb[1] : f;
-    if (lane < 9) st_dev_d(reinterpret_cast<double*>(&part[cc]) + lane, f);
+  for (int i = 0; i < P; ++i) {
+    const int cc = first + (blocks - 1) * P + i;
+    if (cc < C2) sum_store(i, cc);  // wave-uniform
   }
 }
 
