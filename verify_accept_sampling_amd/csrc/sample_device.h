@@ -337,7 +337,6 @@ __device__ __forceinline__ void wave_chunk_sums(const RunWords<DT>& rp, const Ru
     km[e] = 0;
     if constexpr (RESID) {
       const double bq = draw_term<KIND>(run_elem<DT>(rq, e), c1, c0q, tab);
-      sb += bq;
       const double d = fma(-rho32, bq, a);
       bool kink = false;
       if constexpr (KIND == 0) {
@@ -346,13 +345,27 @@ __device__ __forceinline__ void wave_chunk_sums(const RunWords<DT>& rp, const Ru
       }
       const bool pos = d > 0.0 && !kink;
       sw += pos ? d : 0.0;
-      sq += pos ? bq : 0.0;
+      // S_q and dw/drho only move the weights to the exact rho of logits;
+      // probability rows are drawn from as given (rho = 1).
+      if constexpr (KIND == 0) {
+        sb += bq;
+        sq += pos ? bq : 0.0;
+      }
     }
   }
   // Record fields 0-3 (S_p, S_q, w, dw/drho) summed over the wave; lane
   // group q (lanes 16q .. 16q+15) ends with field q in `red`.
   const int lane = threadIdx.x & 63;
-  if constexpr (RESID) {
+  if constexpr (RESID && KIND == 1) {
+    // S_p and w only (S_q and dw/drho stay 0): lanes 0-31 end with S_p,
+    // lanes 32-63 with w.
+    const bool h = (lane & 32) != 0;
+    double r = h ? sw : sa;
+    r += shfl_xor_d(h ? sa : sw, 32);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) r += shfl_xor_d(r, o);
+    red = (lane & 16) ? 0.0 : r;
+  } else if constexpr (RESID) {
     // Transposed reduction: each exchange also halves the values a lane
     // carries (4 -> 2 -> 1), then one value per lane group finishes: 7
     // exchanges instead of 24.
