@@ -4,6 +4,7 @@
 #include <cstring>
 
 #include <atomic>
+#include <random>
 
 #include "../../include/spec_verify.h"
 #include "internal.h"
@@ -51,6 +52,16 @@ int tree_depth_checked(const int32_t* parent, int n_nodes) {
 
 namespace specv {
 std::atomic<int> g_sample_path{SPEC_PATH_AUTO};
+
+uint64_t next_call_tag() {
+  static const uint64_t process_bits = [] {
+    std::random_device rd;
+    return (uint64_t)(rd() & 0xffffu);
+  }();
+  static std::atomic<uint64_t> calls{0};
+  const uint64_t n = calls.fetch_add(1, std::memory_order_relaxed) + 1;
+  return (0xC3ull << 56) | (process_bits << 40) | (n & ((1ull << 40) - 1));
+}
 }  // namespace specv
 
 extern "C" {

@@ -57,6 +57,17 @@ __device__ __forceinline__ float ld_dev_f(const float* p) {
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
+// Polls of a bounded wait before it gives up (a few seconds; a legitimate
+// wait lasts microseconds).
+constexpr long kSpinLimit = 1L << 20;
+
+// Wait until this wave's earlier stores have completed.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // One thread per work-group calls this after its coherent stores.  Returns
 // true for the last of `total` arrivals; that caller also resets the counter
 // to zero for the next call.

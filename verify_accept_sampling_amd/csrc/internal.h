@@ -195,6 +195,13 @@ hipError_t launch_timed(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 bloc
   return e;
 }
 
+// Completion tag of one call (tags that work-groups store to say a partial
+// is complete): a marker byte, 16 bits drawn once per process and a 40-bit
+// call counter, so no two calls of a process share a tag, and neither
+// zero-filled memory nor any value the workspace holds otherwise (floats,
+// doubles, counts) looks like one.
+uint64_t next_call_tag();
+
 // Launch wrappers (defined in the .hip files).  Each returns a hipError_t.
 hipError_t launch_fill_uniforms(uint64_t seed, uint64_t counter0, int64_t n,
                                 float* out, hipStream_t s);

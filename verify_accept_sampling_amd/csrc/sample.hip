@@ -34,7 +34,6 @@
 // work-group first repeating the (gather-only) acceptance tests.
 #include <algorithm>
 #include <atomic>
-#include <random>
 
 #include "sample_device.h"
 
@@ -891,19 +890,6 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
 
 static int row_chunks(int V) { return (V + kRowChunkElems - 1) / kRowChunkElems; }
 
-// Completion tag of one one-launch call: a marker byte, 16 bits drawn once
-// per process and a 40-bit call counter, so no two calls of a process share
-// a tag, and neither zero-filled memory nor any value the workspace holds
-// otherwise (floats, doubles, counts) looks like one.
-static uint64_t call_tag() {
-  static const uint64_t process_bits = [] {
-    std::random_device rd;
-    return (uint64_t)(rd() & 0xffffu);
-  }();
-  static std::atomic<uint64_t> calls{0};
-  const uint64_t n = calls.fetch_add(1, std::memory_order_relaxed) + 1;
-  return (0xC3ull << 56) | (process_bits << 40) | (n & ((1ull << 40) - 1));
-}
 
 // Work-groups of the one-launch kernel resident per compute unit; the
 // first round of row-pass work-groups (compute units x this) sets how many
@@ -1006,7 +992,7 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
                         dim3((unsigned)(n_row + n_fin + (long)B * G2)), dim3(kThreads),
                         one_launch_lds<DT, NE>(0), s, target, draft, B, k, V, C1, C2, c, inv_t,
                         draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1,
-                        zr, fl, call_tag(), st, p2, cnt, E, n_early_rows, n_fin);
+                        zr, fl, next_call_tag(), st, p2, cnt, E, n_early_rows, n_fin);
   }
   hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>, dim3((unsigned)n_row),
                              dim3(kThreads), 0, s, target, draft, k, V, C1, c, draft_tokens,

@@ -618,9 +618,6 @@ __device__ __forceinline__ ReqState ld_dev_state(const ReqState* p) {
   return v;
 }
 
-// Polls of a ready slot before a wait gives up (a few seconds; a legitimate
-// wait lasts microseconds).
-constexpr long kSpinLimit = 1L << 20;
 
 // One thread waits until both words of a ready slot are set and returns
 // them.  False if the bound is reached.
@@ -636,11 +633,5 @@ __device__ __forceinline__ bool wait_slot(const uint64_t* slot, uint64_t& w0, ui
   return false;
 }
 
-// Wait until this wave's earlier stores have completed.
-__device__ __forceinline__ void wait_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 }  // namespace specv
