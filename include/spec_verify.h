@@ -170,6 +170,53 @@ int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes,
  * error code if the array is malformed.  Host only. */
 int spec_tree_depth(const int32_t* parent_host, int n_nodes);
 
+/* Rejected drafts of a chain verification, for KV-cache trimming.  The
+ * target's forward pass wrote a KV entry for each of the k drafted tokens;
+ * only those of the accepted prefix stay, and drafting resumes from the
+ * confirmed prefix (EAGLE-3 review, section on the full inference loop,
+ * step 5 "KV cache update").  A serving engine marks the others in a
+ * rejected-token mask and points their slot-mapping entries at a padding
+ * slot ("[vLLM] EAGLE" code walk, sections on rejected-token handling and on
+ * slot mapping / KV-cache management).
+ *   rejected[b, i] = 1 if i >= accepted_len[b], else 0   (i = 0 .. k-1);
+ *   slot_mapping (nullable): slot_mapping[b, i] = pad_slot where
+ *   rejected[b, i] = 1, left unchanged elsewhere.
+ * accepted_len: int32 [B] (as written by spec_verify_sample or
+ * spec_verify_greedy; any value is accepted, a value >= k rejects nothing).
+ * rejected: uint8 [B, k].  slot_mapping: int64 [B, k], updated in place.
+ * One small kernel on `stream`. */
+int spec_rejected_mask(const int32_t* accepted_len, int B, int k, uint8_t* rejected,
+                       int64_t* slot_mapping, int64_t pad_slot, void* stream);
+
+/* Rejected nodes of a tree verification, for KV-cache trimming (same
+ * sources as spec_rejected_mask).  Node j > 0 is kept iff it lies on the
+ * accepted root-to-node path; the root (node 0, the last confirmed token)
+ * is never rejected.
+ *   rejected[b, j] = 1 if j > 0 and j is not in out_path[b, 0..depth],
+ *   else 0;  slot_mapping (nullable) as for spec_rejected_mask.
+ * out_path: int32 [B, depth+1] as written by spec_verify_tree_greedy (node
+ * ids, -1 after the path's end; entries outside [0, n_nodes) mark nothing).
+ * depth: the tree depth D (spec_tree_depth), 0 <= D < n_nodes <= 1024.
+ * rejected: uint8 [B, n_nodes].  slot_mapping: int64 [B, n_nodes]. */
+int spec_tree_rejected_mask(const int32_t* out_path, int B, int n_nodes, int depth,
+                            uint8_t* rejected, int64_t* slot_mapping, int64_t pad_slot,
+                            void* stream);
+
+/* Parent array of a draft tree given as a list of choices ("[vLLM] EAGLE"
+ * code walk, section on tree-structured drafting: each node is the tuple of
+ * child ranks on the path from the root, listed level by level).  Host
+ * only.  Choice j is the sequence choices_host[j, 0 .. lengths_host[j]-1]
+ * (int32 [n_choices, width], entries >= 0); it becomes node j + 1, whose
+ * parent is the node of the same sequence without its last entry, or the
+ * root 0 for a one-entry choice.  Writes parent_host[0 .. n_choices]
+ * (parent[0] = -1) and returns n_nodes = n_choices + 1.  Errors: SPEC_EINVAL
+ * (null pointer, n_choices + 1 > 1024, width < 1, a length outside
+ * [1, width]); SPEC_ETREE (a negative entry, a choice listed twice, or a
+ * choice whose parent is not listed before it).  parent_host may be
+ * partly written on error. */
+int spec_tree_from_choices(const int32_t* choices_host, const int32_t* lengths_host,
+                           int n_choices, int width, int32_t* parent_host);
+
 /* Which kernels spec_verify_sample uses for raw logits.
  * SPEC_PATH_AUTO (the default): one launch (SPEC_KERNEL_FUSED) that reads
  *   every row once.  The rows of each request's early positions come first;
@@ -202,7 +249,8 @@ enum {
                                (acceptance tests, greedy rule, tree walk) */
   SPEC_KERNEL_DRAW = 1,     /* float64 residual / bonus pass + inverse-CDF draw */
   SPEC_KERNEL_UNIFORMS = 2, /* spec_fill_uniforms */
-  SPEC_KERNEL_FUSED = 3     /* one-launch sampling verification: row pass and draw */
+  SPEC_KERNEL_FUSED = 3,    /* one-launch sampling verification: row pass and draw */
+  SPEC_KERNEL_SERVING = 4   /* rejected-draft masks */
 };
 int spec_profile_enable(int on);
 int spec_profile_read(int kind, long* launches, double* total_ms);

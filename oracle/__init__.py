@@ -9,5 +9,7 @@ Modules
   rng     SplitMix64 uniforms from the published definition
   verify  greedy, sampling and tree-greedy verification in float64, with the
           per-decision margins used to classify disagreements
+  serving rejected-draft masks for KV-cache trimming and a draft tree's parent
+          array from its list of choices
 """
-from . import rng, verify  # noqa: F401
+from . import rng, serving, verify  # noqa: F401

@@ -28,6 +28,7 @@ __all__ = [
     "spec_workspace_bytes", "spec_fill_uniforms", "spec_verify_greedy",
     "spec_verify_sample", "spec_verify_tree_greedy", "spec_tree_depth", "spec_strerror",
     "spec_profile_enable", "spec_profile_read", "KERNEL_KINDS", "spec_sample_path",
+    "spec_rejected_mask", "spec_tree_rejected_mask", "spec_tree_from_choices",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -92,11 +93,17 @@ def load_library():
     lib.spec_profile_read.restype = c_int
     lib.spec_sample_path.argtypes = [c_int]
     lib.spec_sample_path.restype = c_int
+    lib.spec_rejected_mask.argtypes = [vp, c_int, c_int, vp, vp, c_i64, vp]
+    lib.spec_rejected_mask.restype = c_int
+    lib.spec_tree_rejected_mask.argtypes = [vp, c_int, c_int, c_int, vp, vp, c_i64, vp]
+    lib.spec_tree_rejected_mask.restype = c_int
+    lib.spec_tree_from_choices.argtypes = [vp, vp, c_int, c_int, vp]
+    lib.spec_tree_from_choices.restype = c_int
     _lib = lib
     return lib
 
 
-KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2, "fused": 3}
+KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2, "fused": 3, "serving": 4}
 SAMPLE_PATHS = {"auto": 0, "two_launch": 1, "early_exit": 2}
 
 
@@ -318,3 +325,73 @@ def spec_verify_tree_greedy(target: torch.Tensor, parent: Sequence[int],
                                        _ptr(acc), _ptr(out), _ptr(path), _ptr(ws), ws.numel(),
                                        _stream(dev)))
     return acc, out, path
+
+
+def _slot_arg(slot_mapping: Optional[torch.Tensor], shape, device) -> Optional[torch.Tensor]:
+    if slot_mapping is None:
+        return None
+    _need_cuda(slot_mapping, "slot_mapping")
+    if (slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != tuple(shape)
+            or not slot_mapping.is_contiguous() or slot_mapping.device != device):
+        raise ValueError(f"slot_mapping must be a contiguous int64 tensor of shape {tuple(shape)}"
+                         " on the outputs' device")
+    return slot_mapping
+
+
+def spec_rejected_mask(accepted_len: torch.Tensor, k: int,
+                       slot_mapping: Optional[torch.Tensor] = None, pad_slot: int = -1):
+    """Rejected drafts of a chain verification: bool [B, k], True where
+    i >= accepted_len[b].  With slot_mapping (int64 [B, k]), the rejected
+    entries are set to pad_slot in place."""
+    _need_cuda(accepted_len, "accepted_len")
+    if accepted_len.dtype != torch.int32 or accepted_len.dim() != 1:
+        raise ValueError("accepted_len must be int32 [B]")
+    accepted_len = accepted_len.contiguous()
+    B = accepted_len.shape[0]
+    dev = accepted_len.device
+    rej = torch.empty(B, k, dtype=torch.uint8, device=dev)
+    slots = _slot_arg(slot_mapping, (B, k), dev)
+    _check(load_library().spec_rejected_mask(_ptr(accepted_len), B, int(k), _ptr(rej),
+                                             _ptr(slots), int(pad_slot), _stream(dev)))
+    return rej.view(torch.bool)
+
+
+def spec_tree_rejected_mask(out_path: torch.Tensor, n_nodes: int,
+                            slot_mapping: Optional[torch.Tensor] = None, pad_slot: int = -1):
+    """Rejected nodes of a tree verification: bool [B, n_nodes], True for
+    every node j > 0 not on the accepted path out_path [B, D+1] (as
+    returned by spec_verify_tree_greedy).  With slot_mapping (int64
+    [B, n_nodes]), the rejected entries are set to pad_slot in place."""
+    _need_cuda(out_path, "out_path")
+    if out_path.dtype != torch.int32 or out_path.dim() != 2:
+        raise ValueError("out_path must be int32 [B, D+1]")
+    out_path = out_path.contiguous()
+    B, D1 = out_path.shape
+    dev = out_path.device
+    rej = torch.empty(B, n_nodes, dtype=torch.uint8, device=dev)
+    slots = _slot_arg(slot_mapping, (B, n_nodes), dev)
+    _check(load_library().spec_tree_rejected_mask(_ptr(out_path), B, int(n_nodes), D1 - 1,
+                                                  _ptr(rej), _ptr(slots), int(pad_slot),
+                                                  _stream(dev)))
+    return rej.view(torch.bool)
+
+
+def spec_tree_from_choices(choices: Sequence[Sequence[int]]) -> list:
+    """Parent array of a draft tree listed as choices (tuples of child ranks
+    from the root, parents listed before children): node j+1 is choices[j],
+    node 0 the root.  Host only."""
+    seqs = [[int(v) for v in c] for c in choices]
+    width = max([len(c) for c in seqs] + [1])
+    flat = (ctypes.c_int32 * max(1, len(seqs) * width))()
+    lens = (ctypes.c_int32 * max(1, len(seqs)))()
+    for j, c in enumerate(seqs):
+        lens[j] = len(c)
+        for i, v in enumerate(c):
+            flat[j * width + i] = v
+    parent = (ctypes.c_int32 * (len(seqs) + 1))()
+    rc = load_library().spec_tree_from_choices(ctypes.cast(flat, ctypes.c_void_p),
+                                               ctypes.cast(lens, ctypes.c_void_p), len(seqs),
+                                               width, ctypes.cast(parent, ctypes.c_void_p))
+    if rc < 0:
+        _check(rc)
+    return list(parent)

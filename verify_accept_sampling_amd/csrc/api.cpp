@@ -4,7 +4,9 @@
 #include <cstring>
 
 #include <atomic>
+#include <map>
 #include <random>
+#include <vector>
 
 #include "../../include/spec_verify.h"
 #include "internal.h"
@@ -177,6 +179,56 @@ int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes, i
       hipSuccess)
     return SPEC_EHIP;
   return SPEC_OK;
+}
+
+int spec_rejected_mask(const int32_t* accepted_len, int B, int k, uint8_t* rejected,
+                       int64_t* slot_mapping, int64_t pad_slot, void* stream) {
+  if (B < 0 || B > kMaxB || k < 0 || k > kMaxK) return SPEC_EINVAL;
+  if (B == 0 || k == 0) return SPEC_OK;
+  if (accepted_len == nullptr || rejected == nullptr) return SPEC_EINVAL;
+  if (launch_rejected_mask(accepted_len, nullptr, 0, B, k, rejected, slot_mapping, pad_slot,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPEC_EHIP;
+  return SPEC_OK;
+}
+
+int spec_tree_rejected_mask(const int32_t* out_path, int B, int n_nodes, int depth,
+                            uint8_t* rejected, int64_t* slot_mapping, int64_t pad_slot,
+                            void* stream) {
+  if (B < 0 || B > kMaxB || n_nodes < 1 || n_nodes > kMaxNodes || depth < 0 ||
+      depth >= n_nodes)
+    return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (out_path == nullptr || rejected == nullptr) return SPEC_EINVAL;
+  if (launch_rejected_mask(nullptr, out_path, depth + 1, B, n_nodes, rejected, slot_mapping,
+                           pad_slot, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPEC_EHIP;
+  return SPEC_OK;
+}
+
+int spec_tree_from_choices(const int32_t* choices_host, const int32_t* lengths_host,
+                           int n_choices, int width, int32_t* parent_host) {
+  if (n_choices < 0 || n_choices + 1 > kMaxNodes || width < 1 || parent_host == nullptr)
+    return SPEC_EINVAL;
+  if (n_choices > 0 && (choices_host == nullptr || lengths_host == nullptr)) return SPEC_EINVAL;
+  // Node j + 1 is choice j; a choice's parent is the node whose choice is
+  // the same sequence without its last entry (the root for one entry).
+  std::map<std::vector<int32_t>, int> node_of;
+  node_of[{}] = 0;
+  parent_host[0] = -1;
+  for (int j = 0; j < n_choices; ++j) {
+    const int len = lengths_host[j];
+    if (len < 1 || len > width) return SPEC_EINVAL;
+    const int32_t* c = choices_host + (long)j * width;
+    std::vector<int32_t> seq(c, c + len);
+    for (int32_t v : seq)
+      if (v < 0) return SPEC_ETREE;
+    const auto up = node_of.find(std::vector<int32_t>(seq.begin(), seq.end() - 1));
+    if (up == node_of.end()) return SPEC_ETREE;  // parent missing or listed later
+    if (!node_of.emplace(std::move(seq), j + 1).second) return SPEC_ETREE;  // listed twice
+    parent_host[j + 1] = up->second;
+  }
+  return n_choices + 1;
 }
 
 }  // extern "C"

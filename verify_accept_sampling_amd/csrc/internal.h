@@ -171,7 +171,8 @@ constexpr int kProfRowPass = 0;   // row statistics / argmax sweep + per-request
 constexpr int kProfDraw = 1;      // float64 residual / bonus pass + inverse-CDF draw
 constexpr int kProfUniforms = 2;  // spec_fill_uniforms
 constexpr int kProfFused = 3;     // one-launch sampling verification (row pass + draw)
-constexpr int kProfKinds = 4;
+constexpr int kProfServing = 4;   // rejected-draft masks
+constexpr int kProfKinds = 5;
 // While timing is enabled, prof_begin hands out a start/stop event pair that
 // the launch itself stamps (hipExtLaunchKernel records them from the
 // kernel's dispatch, so the interval is the kernel alone); otherwise both
@@ -205,6 +206,10 @@ uint64_t next_call_tag();
 // Launch wrappers (defined in the .hip files).  Each returns a hipError_t.
 hipError_t launch_fill_uniforms(uint64_t seed, uint64_t counter0, int64_t n,
                                 float* out, hipStream_t s);
+
+hipError_t launch_rejected_mask(const int32_t* accepted_len, const int32_t* path, int path_len,
+                                int B, int n_ent, uint8_t* rejected, int64_t* slots,
+                                int64_t pad_slot, hipStream_t s);
 
 // Process-wide choice of the sampling path (spec_sample_path).
 extern std::atomic<int> g_sample_path;

@@ -214,14 +214,15 @@ def sample_chain_llama3(B: int = 64, k: int = 8, V: int = 128256,
 # ---------------------------------------------------------------------------
 
 
-def static_tree_parents(branching=(4, 3, 2, 2, 1), n_keep: int = 60) -> np.ndarray:
-    """Parent array of a static draft tree (root = node 0, BFS order).
+def static_tree_choices(branching=(4, 3, 2, 2, 1), n_keep: int = 60) -> list:
+    """The nodes of a static draft tree as choices: tuples of 0-based
+    sibling ranks from the root, listed level by level.
 
-    The full tree with per-depth branching `branching` is built; every node is
-    named by its path of 0-based sibling ranks.  Nodes are ranked by (sum of the
-    ranks on the path, depth, path) and the first n_keep are kept, which is
-    closed under taking parents because a parent ranks strictly before each of
-    its children.  Kept nodes are numbered 1.. in (depth, path) order.
+    The full tree with per-depth branching `branching` is built.  Nodes are
+    ranked by (sum of the ranks on the path, depth, path) and the first n_keep
+    are kept, which is closed under taking parents because a parent ranks
+    strictly before each of its children.  They are listed in (depth, path)
+    order.
     """
     paths = []
 
@@ -236,7 +237,13 @@ def static_tree_parents(branching=(4, 3, 2, 2, 1), n_keep: int = 60) -> np.ndarr
 
     grow(())
     kept = sorted(paths, key=lambda p: (sum(p), len(p), p))[:n_keep]
-    kept = sorted(kept, key=lambda p: (len(p), p))
+    return sorted(kept, key=lambda p: (len(p), p))
+
+
+def static_tree_parents(branching=(4, 3, 2, 2, 1), n_keep: int = 60) -> np.ndarray:
+    """Parent array of the static draft tree of static_tree_choices (root =
+    node 0, node i + 1 = choice i)."""
+    kept = static_tree_choices(branching, n_keep)
     ids = {(): 0}
     for i, p in enumerate(kept):
         ids[p] = i + 1
