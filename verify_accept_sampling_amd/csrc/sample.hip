@@ -53,7 +53,8 @@ __device__ __forceinline__ bool row_chunk_stat(int b, int r, int chunk,
                                                const int32_t* __restrict__ draft_tokens,
                                                uint64_t* __restrict__ part,
                                                float* __restrict__ zrow,
-                                               const uint64_t* watch = nullptr) {
+                                               const uint64_t* watch = nullptr,
+                                               bool precheck = false) {
   const int R = 2 * k + 1;
   const long rowid = (long)b * R + r;
   const void* rp = stat_row<DT>(target, draft, b, r, k, V);
@@ -74,7 +75,7 @@ __device__ __forceinline__ bool row_chunk_stat(int b, int r, int chunk,
   else
     stats_sweep<DT, kThreads, WATCH>(rp, static_cast<uint32_t>((long)V * Elems<DT>::kBytes), g0,
                                      g1, c, m, mc, s, threadIdx.x, watch,
-                                     r <= k ? r : r - k - 1);
+                                     r <= k ? r : r - k - 1, precheck);
   // The chunk that holds the token also publishes the logit there.
   const bool own = x >= 0 && x < V && (long)x >= g0 * NE && (long)x < g1 * NE;
   float zx = 0.f;
@@ -408,7 +409,7 @@ __device__ __forceinline__ void position_major_row(long bid, int B, int k, int C
 // draw work-group takes it from there.
 template <int DT, int NE, bool EXIT = false>
 __device__ __forceinline__ void row_block(
-    long bid, bool one_launch, int B, const void* __restrict__ target,
+    long bid, bool one_launch, bool late, int B, const void* __restrict__ target,
     const void* __restrict__ draft, int k, int V, int C1, float c,
     const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms, uint64_t seed,
     uint64_t ctr0, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
@@ -425,11 +426,13 @@ __device__ __forceinline__ void row_block(
     r = static_cast<int>(bid / C1 % R);
   }
   // Early exit: rows after position 0 stop once the request is decided
-  // before their position (no probe values are asked for then).
+  // before their position (no probe values are asked for then).  Rows after
+  // the early positions (`late`) look before their second batch: most of
+  // their requests are decided by the time they start.
   const bool stored =
       EXIT && (r <= k ? r : r - k - 1) > 0
           ? row_chunk_stat<DT, NE, true>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens,
-                                         part, zrow, ready_slot(counters, b))
+                                         part, zrow, ready_slot(counters, b), late)
           : row_chunk_stat<DT, NE>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens, part,
                                    zrow);
   if (one_launch) {
@@ -792,9 +795,9 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
     uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, float* __restrict__ probe, uint64_t* __restrict__ part,
     float* __restrict__ zrow, ReqState* __restrict__ state, unsigned* __restrict__ counters) {
-  row_block<DT, NE>(blockIdx.x, false, 0, target, draft, k, V, C1, c, draft_tokens, uniforms, seed,
-                    ctr0, accepted_len, out_tokens, probe, part, zrow, nullptr, 0, state,
-                    counters);
+  row_block<DT, NE>(blockIdx.x, false, false, 0, target, draft, k, V, C1, c, draft_tokens,
+                    uniforms, seed, ctr0, accepted_len, out_tokens, probe, part, zrow, nullptr, 0,
+                    state, counters);
 }
 
 template <int DT, int NE, int KIND>
@@ -845,6 +848,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
   const long bid = blockIdx.x;
   const int G2 = draw_groups(C2, 1);
   long row = -1;  // row-pass index in position order
+  bool late = false;
   long draw = -1;
   if (bid < n_early_rows) {
     row = bid;
@@ -869,12 +873,13 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
       const long w = o % (2 * C1);
       row = pos < k ? (long)pos * per_pos + (long)b * 2 * C1 + w
                     : (long)k * per_pos + (long)b * C1 + w;
+      late = true;
     }
   }
   if (row >= 0) {
-    row_block<DT, NE, EXIT>(row, true, B, target, draft, k, V, C1, c, draft_tokens, uniforms,
-                            seed, ctr0, accepted_len, out_tokens, probe, part1, zrow, flags, tag,
-                            state, counters);
+    row_block<DT, NE, EXIT>(row, true, late, B, target, draft, k, V, C1, c, draft_tokens,
+                            uniforms, seed, ctr0, accepted_len, out_tokens, probe, part1, zrow,
+                            flags, tag, state, counters);
   } else {
     const RowPass rows{part1, zrow, flags, tag, C1, c};
     draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2), 1,

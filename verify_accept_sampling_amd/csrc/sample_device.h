@@ -115,25 +115,40 @@ __device__ __forceinline__ void stat_words(float& m, float& mc, double& s, const
 template <int DT, int NT, bool WATCH = false>
 __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, long g0, long g1,
                                             float c, float& m, float& mc, double& s, int tid,
-                                            const uint64_t* watch = nullptr, int pos = 0) {
+                                            const uint64_t* watch = nullptr, int pos = 0,
+                                            bool precheck = false) {
   constexpr int NE = Elems<DT>::kVec;
   constexpr uint32_t kStep = NT * kUnrollStats * 16u;
   const RowBuf buf(rp, row_bytes);
   long g = g0 + tid;
   uint32_t off = static_cast<uint32_t>(g) * 16u;
   const long span = (long)(kUnrollStats - 1) * NT;
-  // WATCH: the request's ready slot is read once per pair of batches (the
-  // value is used one pair later, so the read never stalls the stream); once
-  // it shows the request stopped before position `pos`, this row decides
-  // nothing and the wave stops, marking its partial with m = +inf.
+  // WATCH: the request's ready slot is read once per pair of batches; each
+  // read is used after the next batch's sums, whose data it precedes, so it
+  // never stalls the stream.  Once it shows the request stopped before
+  // position `pos`, this row decides nothing and the wave stops, marking its
+  // partial with m = +inf.  With `precheck` the first read is also used
+  // before the second batch is issued (one round trip without a second batch
+  // in flight, for rows whose request is likely decided already).
   uint64_t wv = 0;
   if constexpr (WATCH) wv = ld_dev(watch);
+  auto stopped = [&]() { return wv != 0 && (int)(uint32_t)wv - 1 < pos; };
   if (g + span < g1) {
     // Two word buffers used in turn (no register copies, which would wait
     // for the loads in flight).
     u32x4 wa[kUnrollStats], wb[kUnrollStats];
 #pragma unroll
     for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
+    if constexpr (WATCH) {
+      if (precheck) {  // wave-uniform
+        if (stopped()) {
+          m = INFINITY;
+          s = 0.0;
+          return;
+        }
+        wv = ld_dev(watch);
+      }
+    }
     for (;;) {
       g += (long)NT * kUnrollStats;
       off += kStep;
@@ -145,6 +160,14 @@ __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, 
       for (int u = 0; u < kUnrollStats; ++u) wb[u] = buf.load_nt(off, u * NT * 16u);
       __builtin_amdgcn_sched_barrier(0);
       stat_words<DT>(m, mc, s, wa, c);
+      if constexpr (WATCH) {
+        if (stopped()) {  // wave-uniform: one address
+          m = INFINITY;
+          s = 0.0;
+          return;
+        }
+        wv = ld_dev(watch);
+      }
       g += (long)NT * kUnrollStats;
       off += kStep;
       if (!(g + span < g1)) {
@@ -155,14 +178,6 @@ __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, 
       for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
       __builtin_amdgcn_sched_barrier(0);
       stat_words<DT>(m, mc, s, wb, c);
-      if constexpr (WATCH) {
-        if (wv != 0 && (int)(uint32_t)wv - 1 < pos) {  // wave-uniform: one address
-          m = INFINITY;
-          s = 0.0;
-          return;
-        }
-        wv = ld_dev(watch);
-      }
     }
   }
   for (; g < g1; g += NT, off += NT * 16u) {
