@@ -263,6 +263,54 @@ def bench_greedy(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_serving(args):
+    """One JSON line for the rejected-draft mask after a chain verification
+    at the headline shape (B=64, k=8), with the slot mapping padded in
+    place.  Bytes per launch: accepted_len read, the mask written, and the
+    rejected entries' 8-byte slots written; the launch is bound by its own
+    latency, not by HBM, and the line says so."""
+    import numpy as np
+    import torch
+
+    import verify_accept_sampling_amd as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, k = 64, 8
+    rng = np.random.default_rng(2024)
+    acc = torch.from_numpy(rng.integers(0, k + 1, size=B).astype(np.int32)).to(dev)
+    slots = torch.arange(B * k, dtype=torch.int64, device=dev).view(B, k)
+
+    def step(i):
+        return S.spec_rejected_mask(acc, k, slot_mapping=slots, pad_slot=-1)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = timed_steps(step, args.warmup, args.steps, profile=False)
+    timed_steps(step, args.warmup + args.steps, args.steps, profile=True)
+    n, ms = S.spec_profile_read("serving")
+    kern_us = ms / n * 1e3
+    rejected = int((k - acc.clamp(0, k)).sum().item())
+    nbytes = float(B * 4 + B * k + rejected * 8)
+    achieved = nbytes / (kern_us * 1e-6) / 1e9
+    result = {
+        "metric": "rejected-draft masks per second (chain, B=64, k=8, slot mapping padded)",
+        "value": 1.0 / (ms_step * 1e-3), "unit": "calls/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "rejected_mask_b64_k8", "B": B, "k": k},
+        "roofline": {"bound": "hbm", "kernel": "k_rejected_mask", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "note": "launch-latency bound: a few KB per launch"},
+        "kernels_avg_us": {"k_rejected_mask": kern_us},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def bench_probs(args):
     """One JSON line for the probability-row workload: B=512, k=8, V=128256
     float32 rows with a prescribed overlap alpha in {0.6, 0.8, 0.9}.  The
@@ -345,7 +393,7 @@ def main():
                     help="host only: turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) "
                          "into the row-statistics traffic file")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
-    ap.add_argument("--workload", choices=["sample", "probs"] + sorted(GREEDY_WORKLOADS),
+    ap.add_argument("--workload", choices=["sample", "probs", "serving"] + sorted(GREEDY_WORKLOADS),
                     default="sample",
                     help="sample (default): the headline sampling workload; probs: sampling on "
                          "probability rows (B=512); the others print a line for a greedy "
@@ -369,6 +417,9 @@ def main():
         sys.exit(2)
     if args.workload == "probs":
         bench_probs(args)
+        return
+    if args.workload == "serving":
+        bench_serving(args)
         return
     if args.workload != "sample":
         bench_greedy(args)
