@@ -606,3 +606,147 @@ def test_fixed_rows_sampler_without_drafts():
             r = O.verify_sample_request(t[b], None, np.zeros(0, np.int32), u[c, b], 1.0,
                                         "logits", "f32")
             assert token[c, b] == r.tokens[-1]
+
+
+# ---------------------------------------------------------------------------
+# Probe values: p_i(x_i), q_i(x_i) and the mass drawn from at the stop
+# ---------------------------------------------------------------------------
+#
+# The probe is what the 1e-5 probability tolerance is checked on, so the
+# oracle's probe_values is pinned against the decision function (itself pinned
+# by the law tests above) and against properties any softmax of z/T has:
+#   * the acceptance boundary in u that verify_sample_request exhibits at
+#     position i (found by bisection, the oracle used as a black box) equals
+#     min(1, p_i(x_i)/q_i(x_i)) from the probe;
+#   * summed over every token x, the probe's p_i(x) is 1 (logits);
+#   * ratios p_i(x)/p_i(y) = exp((z_x - z_y)/T): the temperature is applied;
+#   * the value at (b, i) depends on target row (b, i) and draft row (b, i)
+#     only: perturbing any other row, position or request leaves it unchanged;
+#   * probability rows are returned as given, bit for bit.
+# Planted mistakes (wrong position, wrong request, no temperature, target and
+# draft swapped) must each fail one of these.
+
+
+def _probe_rows(seed, B, k, V, dtype, T):
+    rng = np.random.default_rng(seed)
+    z = (rng.standard_normal((B, k + 1, V)) * 1.7).astype(np.float32)
+    y = (z[:, :k] + rng.standard_normal((B, k, V)) * 0.8).astype(np.float32)
+    toks = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    if dtype == "bf16":
+        return W.f32_to_bf16_bits(z), W.f32_to_bf16_bits(y), toks
+    return z, y, toks
+
+
+def _probe_pins_hold(fn, dtype, T, seed=31):
+    """True when probe function `fn` (signature of O.probe_values) satisfies
+    every property listed above on a small batch."""
+    B, k, V = 3, 3, 7
+    z, y, toks = _probe_rows(seed, B, k, V, dtype, T)
+    zf = W.logits_as_f32(z, dtype).astype(np.float64)
+    ok = True
+    for b in range(B):
+        pv, qv = fn(z, y, toks, T, "logits", dtype, b)
+        for i in range(k):
+            # acceptance boundary of the (pinned) decision function at position i
+            x = int(toks[b, i])
+
+            def accepts(ua, b=b, i=i):
+                u = np.full((k + 1, 2), 0.5)
+                u[:i, 0] = 0.0  # earlier positions: u = 0 accepts unless p = 0
+                u[i, 0] = ua
+                r = O.verify_sample_request(z[b], y[b], toks[b], u, T, "logits", dtype)
+                return r.accepted > i
+
+            # every earlier position must accept at u = 0 for the boundary at
+            # i to be visible; softmax values are never 0 here
+            want = _boundary(accepts)
+            got = min(1.0, pv[i] / qv[i])
+            ok &= abs(got - want) < 1e-12
+            # normalisation and temperature, over every token of the row
+            all_p = []
+            for xx in range(V):
+                t2 = toks.copy()
+                t2[b, i] = xx
+                all_p.append(fn(z, y, t2, T, "logits", dtype, b)[0][i])
+            all_p = np.array(all_p)
+            ok &= abs(all_p.sum() - 1.0) < 1e-12
+            ratio = all_p / all_p[0]
+            ok &= np.allclose(ratio, np.exp((zf[b, i] - zf[b, i, 0]) / T), rtol=1e-12, atol=0)
+    # locality: perturb every row but (b, i) of target and draft
+    b, i = 1, 2
+    pv, qv = fn(z, y, toks, T, "logits", dtype, b)
+    z2, y2 = z.copy(), y.copy()
+    rng = np.random.default_rng(seed + 1)
+    for bb in range(B):
+        for ii in range(k + 1):
+            if (bb, ii) != (b, i):
+                z2[bb, ii] = rng.permutation(z2[bb, ii])
+                if ii < k:
+                    y2[bb, ii] = rng.permutation(y2[bb, ii])
+    pv2, qv2 = fn(z2, y2, toks, T, "logits", dtype, b)
+    ok &= pv2[i] == pv[i] and qv2[i] == qv[i]
+    return bool(ok)
+
+
+@pytest.mark.parametrize("dtype,T", [("f32", 1.0), ("f32", 0.6), ("bf16", 0.8), ("bf16", 1.7)])
+def test_probe_values_pins(dtype, T):
+    assert _probe_pins_hold(O.probe_values, dtype, T)
+
+
+def test_probe_values_probability_rows_as_given():
+    rng = np.random.default_rng(8)
+    B, k, V = 2, 3, 9
+    p = rng.dirichlet(np.ones(V), size=(B, k + 1)).astype(np.float32)
+    q = rng.dirichlet(np.ones(V), size=(B, k)).astype(np.float32)
+    toks = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    toks[1, 1] = V  # out of range: 0 by definition
+    for b in range(B):
+        pv, qv = O.probe_values(p, q, toks, 1.0, "probs", "f32", b)
+        for i in range(k):
+            x = int(toks[b, i])
+            if 0 <= x < V:
+                assert pv[i] == float(p[b, i, x]) and qv[i] == float(q[b, i, x])
+            else:
+                assert pv[i] == 0.0 and qv[i] == 0.0
+
+
+def _planted_probe(old, new):
+    src = inspect.getsource(O.probe_values)
+    assert old in src, old
+    ns = dict(O.__dict__)
+    exec(src.replace(old, new), ns)
+    return ns["probe_values"]
+
+
+@pytest.mark.parametrize("old,new", [
+    ("zp = decode(target[b, i], dtype)", "zp = decode(target[b, (i + 1) % (k + 1)], dtype)"),
+    ("zq = decode(draft[b, i], dtype)", "zq = decode(draft[b, (i + 1) % k], dtype)"),
+    ("zp = decode(target[b, i], dtype)",
+     "zp = decode(target[(b + 1) % target.shape[0], i], dtype)"),
+    ("pv[i] = tempered_softmax(zp, temperature)[x]", "pv[i] = tempered_softmax(zp, 1.0)[x]"),
+    ("qv[i] = tempered_softmax(zq, temperature)[x]", "qv[i] = tempered_softmax(zp, temperature)[x]"),
+])
+def test_planted_probe_mistakes_fail(old, new):
+    assert not _probe_pins_hold(_planted_probe(old, new), "f32", 0.6)
+
+
+def test_bonus_mass_is_the_total_of_p():
+    """At the bonus position the draw is from p_k itself, so the mass drawn
+    from is sum_x p_k(x): 1 for logits (a softmax), and the sum of the given
+    values for probability rows (used as given, not renormalised)."""
+    rng = np.random.default_rng(14)
+    k, V = 2, 11
+    for T in (0.5, 1.0, 2.3):
+        z = (rng.standard_normal((k + 1, V)) * 2).astype(np.float32)
+        r = O.verify_sample_request(z, z[:k].copy(), np.array([1, 4]), np.full((k + 1, 2), 0.5),
+                                    T, "logits", "f32")
+        assert r.accepted == k
+        assert abs(r.residual_mass - 1.0) < 1e-12
+    p = rng.dirichlet(np.ones(V), size=k + 1).astype(np.float32)
+    p[k] *= np.float32(0.75)  # an unnormalised bonus row
+    r = O.verify_sample_request(p, p[:k].copy(), np.array([2, 3]), np.full((k + 1, 2), 0.5), 1.0,
+                                "probs", "f32")
+    assert r.accepted == k
+    want = math.fsum(float(v) for v in p[k])
+    assert abs(r.residual_mass - want) < 1e-15
+    assert abs(r.residual_mass - 0.75) < 1e-6
