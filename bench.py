@@ -433,7 +433,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    S.spec_sample_path(args.path)
+    schedule = {"auto": "one_launch"}.get(args.path, args.path)
     print("bench: generating B=64 k=8 V=128256 bf16 workload", file=sys.stderr, flush=True)
     wl = W.sample_chain_llama3()
     B, k, V = wl.B, wl.k, wl.V
@@ -450,7 +450,7 @@ def main():
     def step(i):
         t, d = copies[i % len(copies)]
         return S.spec_verify_sample(t, d, toks, wl.temperature, seed=wl.uniform_seed,
-                                    counter0=i * n_u, workspace=ws)
+                                    counter0=i * n_u, workspace=ws, schedule=schedule)
 
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib * 1024 * 1024

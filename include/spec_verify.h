@@ -25,15 +25,26 @@
  *    outputs are valid once that stream has been synchronised.
  *  - `ws` is a caller-owned device workspace of at least
  *    spec_workspace_bytes(B, n_pos, V) bytes.  It must be zero-filled before
- *    its first use.  Its first SPEC_WORKSPACE_COUNTER_BYTES bytes hold
- *    per-request completion counters and ready slots at fixed places;
- *    every call leaves them zero again when it completes, so one workspace
- *    serves calls of any shape without clearing it (the caller must not
- *    write to them); the rest is scratch that each call writes before
- *    reading.  Calls that share a workspace must be ordered on one stream.
+ *    its first use.  Its first SPEC_WORKSPACE_COUNTER_BYTES bytes are the
+ *    counter region: per-request completion counters, verdict words and
+ *    ready slots at fixed places, which every completed call leaves zero
+ *    again, so one workspace serves calls of any shape without clearing it;
+ *    then a status word (SPEC_STATUS_*, sticky) and the call epoch of
+ *    graph-captured calls.  The caller must not write to the counter region
+ *    other than through spec_workspace_reset.  The rest is scratch that
+ *    each call writes before reading.  Calls that share a workspace must be
+ *    ordered on one stream.
  *  - Return value: SPEC_OK, or a negative code.  Any code other than
  *    SPEC_EHIP means the arguments were rejected on the host and nothing was
  *    enqueued.  SPEC_EHIP reports a failed HIP launch.
+ *  - Device-side failure: the one-launch sampling kernels hand results
+ *    between work-groups through bounded waits.  A wait that gives up (it
+ *    never does while every work-group of the launch gets to run) sets
+ *    SPEC_STATUS_WAIT_GAVE_UP in the workspace status word and the request
+ *    it concerns gets accepted_len = -1 and out_tokens all -1.  The bit
+ *    stays set: until spec_workspace_reset, every one-launch sampling call on
+ *    that workspace writes those -1 outputs for every request.  Read it with
+ *    spec_workspace_status.
  *  - Inputs must be finite except that -inf marks a masked token.  Every
  *    row must hold at least one finite value.
  *  - A draft or node token outside [0, V) is a rejection (sampling) or a
@@ -52,7 +63,8 @@ extern "C" {
 #endif
 
 /* Bytes at the start of every workspace that must be zero before the first
- * call; each completed call leaves them zero. */
+ * call (the counter region); each completed call leaves its per-request
+ * words zero. */
 #define SPEC_WORKSPACE_COUNTER_BYTES (2097152 + 256)
 
 /* Element type of logit / probability tensors. */
@@ -134,13 +146,61 @@ int spec_verify_greedy(const void* target, int dtype, int B, int k, int V,
  * other entries 0.
  * Arithmetic: row statistics (max, log-sum-exp) in float32 with float64
  * merges; the acceptance ratio in float64; the residual / bonus draw in
- * float64 (normalisers, weights and running sums). */
+ * float64 (normalisers, weights and running sums).
+ * flags: one SPEC_SCHED_* value (how the work is scheduled; every schedule
+ * gives identical outputs), optionally or-ed with SPEC_FLAG_TEST_GIVE_UP;
+ * any other bit is SPEC_EINVAL.  SPEC_PROBS rows always take one draw
+ * kernel and ignore the schedule. */
 int spec_verify_sample(const void* target, const void* draft, int dtype, int kind,
                        int B, int k, int V, const int32_t* draft_tokens,
                        const float* uniforms, uint64_t seed, uint64_t counter0,
-                       float temperature, int32_t* accepted_len,
+                       float temperature, int flags, int32_t* accepted_len,
                        int32_t* out_tokens, float* probe, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* Schedules of spec_verify_sample for raw logits (the low four bits of
+ * `flags`).
+ * SPEC_SCHED_ONE_LAUNCH: one kernel that reads every row once.  The rows of
+ *   each request's early positions come first; most requests stop at one of
+ *   them (stop at the first rejection: EAGLE-3 review "Speculative
+ *   Decoding" step 3), so their draws run while the rows of later positions
+ *   stream.
+ * SPEC_SCHED_TWO_LAUNCH: the row pass, then the draw, as two kernels.
+ * SPEC_SCHED_EARLY_EXIT: as SPEC_SCHED_ONE_LAUNCH, except that the row pass
+ *   stops reading a row once its request is known to stop before that row's
+ *   position (such rows cannot change any output), so fewer bytes are read.
+ *   With probe values asked for, every row is read as with
+ *   SPEC_SCHED_ONE_LAUNCH.
+ * SPEC_SCHED_AUTO: SPEC_SCHED_ONE_LAUNCH.
+ * Graph capture: on a stream that is being captured (hipStreamIsCapturing),
+ * the one-launch schedules take their completion tags from a call epoch in
+ * the workspace and add a one-thread kernel that advances it, so every
+ * replay of the graph has tags of its own. */
+enum {
+  SPEC_SCHED_AUTO = 0,
+  SPEC_SCHED_ONE_LAUNCH = 1,
+  SPEC_SCHED_TWO_LAUNCH = 2,
+  SPEC_SCHED_EARLY_EXIT = 3
+};
+/* Test only: in a one-launch schedule, the row-pass work-group of request 0,
+ * position 0, chunk 0 never marks its chunk complete and every bounded wait
+ * gives up after 256 polls, so the failure path above runs while every
+ * kernel still exits normally. */
+#define SPEC_FLAG_TEST_GIVE_UP 0x100
+
+/* Workspace status word: byte offset in the workspace and its bits. */
+#define SPEC_WORKSPACE_STATUS_OFFSET 2097152
+#define SPEC_STATUS_WAIT_GAVE_UP 1u
+
+/* Waits for `stream` and reads the workspace status word into *status_host
+ * (0: no failure since the last reset).  ws: a workspace as above. */
+int spec_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status_host,
+                          void* stream);
+
+/* Enqueues on `stream` a kernel that zeroes the counter region (per-request
+ * words and status word; the call epoch is kept), so a workspace whose
+ * status is nonzero can be used again. */
+int spec_workspace_reset(void* ws, size_t ws_bytes, void* stream);
 
 /* Greedy tree verification (EAGLE-3 review, section on the full inference
  * loop: tree attention gives the target's distribution after every node, and
@@ -217,24 +277,6 @@ int spec_tree_rejected_mask(const int32_t* out_path, int B, int n_nodes, int dep
 int spec_tree_from_choices(const int32_t* choices_host, const int32_t* lengths_host,
                            int n_choices, int width, int32_t* parent_host);
 
-/* Which kernels spec_verify_sample uses for raw logits.
- * SPEC_PATH_AUTO (the default): one launch (SPEC_KERNEL_FUSED) that reads
- *   every row once.  The rows of each request's early positions come first;
- *   most requests stop at one of them (stop at the first rejection: EAGLE-3
- *   review "Speculative Decoding" step 3), so their draws run while the rows
- *   of later positions stream.
- * SPEC_PATH_TWO_LAUNCH: the row pass (SPEC_KERNEL_ROW_PASS), then the draw
- *   (SPEC_KERNEL_DRAW).
- * SPEC_PATH_EARLY_EXIT: as SPEC_PATH_AUTO, except that the row pass stops
- *   reading a row once its request is known to stop before that row's
- *   position (such rows cannot change any output), so fewer bytes are read.
- *   When probe values are asked for, every row is read as with
- *   SPEC_PATH_AUTO.
- * All follow the same rule with the same arithmetic and give identical
- * outputs.  The setting is process-wide and applies to calls made after it.
- * Returns the previous setting, or SPEC_EINVAL for an unknown mode. */
-enum { SPEC_PATH_AUTO = 0, SPEC_PATH_TWO_LAUNCH = 1, SPEC_PATH_EARLY_EXIT = 2 };
-int spec_sample_path(int mode);
 
 /* Optional per-kernel timing for measurement tools (not part of the
  * verification itself).  spec_profile_enable(1) clears the totals and, from
@@ -254,6 +296,11 @@ enum {
 };
 int spec_profile_enable(int on);
 int spec_profile_read(int kind, long* launches, double* total_ms);
+/* The durations (milliseconds, in launch order) of the timed launches of one
+ * kernel kind since spec_profile_enable(1): writes min(cap, count) of them to
+ * ms_host (HOST float[cap]) and the count to *n_host.  Waits for the
+ * recorded events. */
+int spec_profile_durations(int kind, float* ms_host, long cap, long* n_host);
 
 #ifdef __cplusplus
 }

@@ -79,9 +79,9 @@ def test_sample_rejects_bad_arguments(lib):
     ws = S.spec_workspace_bytes(2, 5, 100)
 
     def call(target=FAKE, draft=FAKE, dt=1, kind=0, B=2, k=4, V=100, toks=FAKE, u=None,
-             T=1.0, acc=FAKE, out=FAKE, probe=None, w=FAKE, wb=ws):
-        return f(target, draft, dt, kind, B, k, V, toks, u, 0, 0, ctypes.c_float(T), acc, out,
-                 probe, w, wb, None)
+             T=1.0, flags=0, acc=FAKE, out=FAKE, probe=None, w=FAKE, wb=ws):
+        return f(target, draft, dt, kind, B, k, V, toks, u, 0, 0, ctypes.c_float(T), flags, acc,
+                 out, probe, w, wb, None)
 
     assert call(dt=3) == EDTYPE
     assert call(kind=2) == EDTYPE
@@ -99,6 +99,9 @@ def test_sample_rejects_bad_arguments(lib):
     assert call(out=None) == EINVAL
     assert call(w=None) == EWORKSPACE
     assert call(wb=ws - 1) == EWORKSPACE
+    # flags: a schedule (0..3), optionally the test bit; anything else is rejected
+    for bad in (4, 15, 0x10, 0x200, -1, 0x100 | 7):
+        assert call(flags=bad) == EINVAL, bad
     assert call(B=0, target=None, draft=None, toks=None, acc=None, out=None, w=None) == 0
 
 
@@ -124,3 +127,24 @@ def test_fill_uniforms_argument_checks(lib):
     assert lib.spec_fill_uniforms(1, 0, -1, FAKE, None) == EINVAL
     assert lib.spec_fill_uniforms(1, 0, 5, None, None) == EINVAL
     assert lib.spec_fill_uniforms(1, 0, 0, None, None) == 0
+
+
+def test_workspace_status_and_reset_argument_checks(lib):
+    ws = S.spec_workspace_bytes(0, 1, 1)
+    v = ctypes.c_uint32(0)
+    assert lib.spec_workspace_status(None, ws, ctypes.byref(v), None) == EINVAL
+    assert lib.spec_workspace_status(FAKE, ws, None, None) == EINVAL
+    assert lib.spec_workspace_status(FAKE, ws - 1, ctypes.byref(v), None) == EWORKSPACE
+    assert lib.spec_workspace_reset(None, ws, None) == EINVAL
+    assert lib.spec_workspace_reset(FAKE, ws - 1, None) == EWORKSPACE
+
+
+def test_status_word_sits_in_the_counter_region():
+    import re
+
+    with open(S._HEADER) as f:
+        text = f.read()
+    counter = int(re.search(r"SPEC_WORKSPACE_COUNTER_BYTES \((\d+) \+ 256\)", text).group(1)) + 256
+    off = int(re.search(r"SPEC_WORKSPACE_STATUS_OFFSET (\d+)", text).group(1))
+    assert off + 12 <= counter  # status word, then the 8-byte epoch
+    assert S.spec_workspace_bytes(0, 1, 1) >= counter

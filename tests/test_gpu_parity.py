@@ -24,21 +24,22 @@ def _say(msg):
     print(msg, flush=True)
 
 
-# Whether _run_sample asks for probe values (set per sampling path).
-_WANT_PROBE = {"value": True}
+# Schedule of the sampling calls in _run_sample, and whether it asks for
+# probe values (set per schedule by the fixture below).
+_SCHED = {"value": "auto", "probe": True}
 
 
-@pytest.fixture(params=["auto", "two_launch", "early_exit"])
+@pytest.fixture(params=["one_launch", "two_launch", "early_exit"])
 def sample_path(request):
     """Run a sampling test through the one-launch kernel, the two-launch
-    kernels and the early-exit kernel.  Early exit reads every row when probe
-    values are asked for, so there the probe is left out and the outputs
-    alone are compared."""
-    prev = S.spec_sample_path(request.param)
-    _WANT_PROBE["value"] = request.param != "early_exit"
+    kernels and the early-exit kernel (the call's schedule argument).  Early
+    exit reads every row when probe values are asked for, so there the probe
+    is left out and the outputs alone are compared."""
+    _SCHED["value"] = request.param
+    _SCHED["probe"] = request.param != "early_exit"
     yield request.param
-    _WANT_PROBE["value"] = True
-    S.spec_sample_path(prev)
+    _SCHED["value"] = "auto"
+    _SCHED["probe"] = True
 
 
 # ---------------------------------------------------------------------------
@@ -160,7 +161,8 @@ def test_tree_shapes_chain_single_and_deep():
 
 def _run_sample(wl, seed=None, counter0=0, requests=None, use_array=True, max_mismatch=0,
                 probe=None):
-    probe = _WANT_PROBE["value"] if probe is None else probe
+    probe = _SCHED["probe"] if probe is None else probe
+    sched = _SCHED["value"]
     seed = wl.uniform_seed if seed is None else seed
     u = R.chain_uniforms(seed, wl.B, wl.k, counter0)
     tgt = to_device(wl.target, wl.dtype)
@@ -169,10 +171,11 @@ def _run_sample(wl, seed=None, counter0=0, requests=None, use_array=True, max_mi
     if use_array:
         ug = S.spec_fill_uniforms(seed, counter0, wl.B * (wl.k + 1) * 2).view(wl.B, wl.k + 1, 2)
         res_g = S.spec_verify_sample(tgt, dft, toks, wl.temperature, uniforms=ug, kind=wl.kind,
-                                     probe=probe)
+                                     probe=probe, schedule=sched)
     else:
         res_g = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=seed,
-                                     counter0=counter0, kind=wl.kind, probe=probe)
+                                     counter0=counter0, kind=wl.kind, probe=probe,
+                                     schedule=sched)
     torch.cuda.synchronize()
     acc_g, out_g = res_g[0].cpu().numpy(), res_g[1].cpu().numpy()
     check_chain_structure(acc_g, out_g, wl.draft_tokens, wl.V)
@@ -293,21 +296,17 @@ def test_sample_early_exit_matches_full_sweep(llama3_full):
     wl = llama3_full
     tgt, dft = to_device(wl.target, wl.dtype), to_device(wl.draft, wl.dtype)
     toks = ints_to_device(wl.draft_tokens)
-    prev = S.spec_sample_path("auto")
-    try:
-        for c in range(4):
-            ctr = c * wl.B * (wl.k + 1) * 2
-            outs = []
-            for path, probe in (("auto", False), ("early_exit", False), ("early_exit", True)):
-                S.spec_sample_path(path)
-                r = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=wl.uniform_seed,
-                                         counter0=ctr, probe=probe)
-                torch.cuda.synchronize()
-                outs.append((r[0].cpu().numpy(), r[1].cpu().numpy()))
-            for a, o in outs[1:]:
-                assert np.array_equal(a, outs[0][0]) and np.array_equal(o, outs[0][1])
-    finally:
-        S.spec_sample_path(prev)
+    for c in range(4):
+        ctr = c * wl.B * (wl.k + 1) * 2
+        outs = []
+        for path, probe in (("one_launch", False), ("early_exit", False), ("early_exit", True),
+                            ("two_launch", False)):
+            r = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=wl.uniform_seed,
+                                     counter0=ctr, probe=probe, schedule=path)
+            torch.cuda.synchronize()
+            outs.append((r[0].cpu().numpy(), r[1].cpu().numpy()))
+        for a, o in outs[1:]:
+            assert np.array_equal(a, outs[0][0]) and np.array_equal(o, outs[0][1])
 
 
 def test_sample_probs_small_and_empty_residual():
@@ -336,6 +335,7 @@ def test_sample_controlled_acceptance_full(controlled_full):
 
 
 COUNTER_BYTES = (2 << 20) + 256  # SPEC_WORKSPACE_COUNTER_BYTES: fixed region at the start
+PER_REQUEST_BYTES = 2 << 20      # its per-request words; then the status word, the epoch
 
 
 def test_workspace_reuse_with_stale_partials(sample_path):
@@ -349,15 +349,18 @@ def test_workspace_reuse_with_stale_partials(sample_path):
                         temperature=0.8, dtype="bf16")
     tgt, dft = to_device(wl.target, "bf16"), to_device(wl.draft, "bf16")
     toks = ints_to_device(wl.draft_tokens)
-    ref = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=5)
+    ref = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=5, schedule=sample_path)
     g = W.greedy_chain(B=7, k=3, V=999, seed=3)
     gref = S.spec_verify_greedy(to_device(g.target, "f32"), ints_to_device(g.draft_tokens))
     for _ in range(3):
-        got = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=5, workspace=ws)
+        got = S.spec_verify_sample(tgt, dft, toks, wl.temperature, seed=5, workspace=ws,
+                                   schedule=sample_path)
         assert all(torch.equal(a, b) for a, b in zip(ref, got))
         ggot = S.spec_verify_greedy(to_device(g.target, "f32"), ints_to_device(g.draft_tokens),
                                     workspace=ws)
         assert all(torch.equal(a, b) for a, b in zip(gref, ggot))
         torch.cuda.synchronize()
-        assert int(buf[:COUNTER_BYTES].count_nonzero()) == 0
+        # every per-request word back to zero; the status word stays zero
+        assert int(buf[:PER_REQUEST_BYTES + 8].count_nonzero()) == 0
+        assert S.spec_workspace_status(ws) == 0
         buf[COUNTER_BYTES:].fill_(0x5A)

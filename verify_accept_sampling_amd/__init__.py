@@ -12,6 +12,7 @@ is missing or a call fails, an exception is raised.
     spec_verify_sample(target, draft, draft_tokens, temperature, ...)
     spec_verify_tree_greedy(target, parent, node_tokens)
     spec_tree_depth(parent)
+    spec_workspace_status(workspace), spec_workspace_reset(workspace)
 """
 from __future__ import annotations
 
@@ -27,8 +28,10 @@ __all__ = [
     "SpecVerifyError", "Workspace", "library_path", "load_library", "declared_symbols",
     "spec_workspace_bytes", "spec_fill_uniforms", "spec_verify_greedy",
     "spec_verify_sample", "spec_verify_tree_greedy", "spec_tree_depth", "spec_strerror",
-    "spec_profile_enable", "spec_profile_read", "KERNEL_KINDS", "spec_sample_path",
+    "spec_profile_enable", "spec_profile_read", "spec_profile_durations", "KERNEL_KINDS",
+    "SCHEDULES",
     "spec_rejected_mask", "spec_tree_rejected_mask", "spec_tree_from_choices",
+    "spec_workspace_status", "spec_workspace_reset", "STATUS_WAIT_GAVE_UP",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +39,10 @@ _HEADER = os.path.join(os.path.dirname(_PKG), "include", "spec_verify.h")
 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_LOGITS, SPEC_PROBS = 0, 1
+# spec_verify_sample schedules (SPEC_SCHED_*) and the test-only flag
+SCHEDULES = {"auto": 0, "one_launch": 1, "two_launch": 2, "early_exit": 3}
+SPEC_FLAG_TEST_GIVE_UP = 0x100
+STATUS_WAIT_GAVE_UP = 1
 
 _lib = None
 
@@ -81,7 +88,7 @@ def load_library():
     lib.spec_verify_greedy.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]
     lib.spec_verify_greedy.restype = c_int
     lib.spec_verify_sample.argtypes = [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp, c_u64,
-                                       c_u64, c_f, vp, vp, vp, vp, c_size, vp]
+                                       c_u64, c_f, c_int, vp, vp, vp, vp, c_size, vp]
     lib.spec_verify_sample.restype = c_int
     lib.spec_verify_tree_greedy.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                             vp, c_size, vp]
@@ -91,8 +98,13 @@ def load_library():
     lib.spec_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_long),
                                       ctypes.POINTER(ctypes.c_double)]
     lib.spec_profile_read.restype = c_int
-    lib.spec_sample_path.argtypes = [c_int]
-    lib.spec_sample_path.restype = c_int
+    lib.spec_profile_durations.argtypes = [c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_long,
+                                           ctypes.POINTER(ctypes.c_long)]
+    lib.spec_profile_durations.restype = c_int
+    lib.spec_workspace_status.argtypes = [vp, c_size, ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.spec_workspace_status.restype = c_int
+    lib.spec_workspace_reset.argtypes = [vp, c_size, vp]
+    lib.spec_workspace_reset.restype = c_int
     lib.spec_rejected_mask.argtypes = [vp, c_int, c_int, vp, vp, c_i64, vp]
     lib.spec_rejected_mask.restype = c_int
     lib.spec_tree_rejected_mask.argtypes = [vp, c_int, c_int, c_int, vp, vp, c_i64, vp]
@@ -104,19 +116,6 @@ def load_library():
 
 
 KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2, "fused": 3, "serving": 4}
-SAMPLE_PATHS = {"auto": 0, "two_launch": 1, "early_exit": 2}
-
-
-def spec_sample_path(mode: str) -> str:
-    """Choose the kernels spec_verify_sample uses for raw logits ("auto": one
-    launch that reads every row; "two_launch": the row pass, then the draw;
-    "early_exit": one launch that stops reading rows past each request's
-    first rejection, unless probe values are asked for).  All give identical
-    outputs.  Returns the previous mode."""
-    prev = load_library().spec_sample_path(SAMPLE_PATHS[mode])
-    if prev < 0:
-        _check(prev)
-    return {v: k for k, v in SAMPLE_PATHS.items()}[prev]
 
 
 def spec_profile_enable(on: bool = True) -> None:
@@ -130,6 +129,17 @@ def spec_profile_read(kind: str):
     ms = ctypes.c_double(0.0)
     _check(load_library().spec_profile_read(KERNEL_KINDS[kind], ctypes.byref(n), ctypes.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def spec_profile_durations(kind: str) -> list:
+    """Each timed launch's duration (ms, in launch order) of one kernel kind
+    since enabling."""
+    lib = load_library()
+    n = ctypes.c_long(0)
+    _check(lib.spec_profile_durations(KERNEL_KINDS[kind], None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_float * max(1, n.value))()
+    _check(lib.spec_profile_durations(KERNEL_KINDS[kind], buf, n.value, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]
 
 
 def spec_strerror(code: int) -> str:
@@ -180,7 +190,10 @@ class Workspace:
     """Zero-filled device workspace, grown on demand (zeroed again on growth).
 
     Calls leave its completion counters at zero, so it needs no clearing
-    between calls of any shape."""
+    between calls of any shape.  Calls that share a workspace must be ordered
+    on one stream; the default workspaces are one per (device, stream).  A
+    buffer replaced on growth is released on the stream that allocated it
+    (torch's caching allocator orders its reuse on that stream)."""
 
     def __init__(self, device=None):
         self.device = torch.device(device if device is not None else "cuda")
@@ -192,17 +205,52 @@ class Workspace:
                                    device=self.device)
         return self.buf
 
+    def status(self) -> int:
+        """The workspace status word (waits for the current stream)."""
+        return spec_workspace_status(self)
+
+    def reset(self) -> None:
+        """Zero the counter region on the current stream (after a failure)."""
+        spec_workspace_reset(self)
+
 
 _default_ws = {}
 
 
+def _default_workspace(device) -> Workspace:
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (idx, _stream(torch.device("cuda", idx)).value)
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(torch.device("cuda", idx))
+    return ws
+
+
 def _workspace(ws: Optional[Workspace], device, nbytes: int) -> torch.Tensor:
     if ws is None:
-        key = torch.device(device).index
-        ws = _default_ws.get(key)
-        if ws is None:
-            ws = _default_ws[key] = Workspace(device)
+        ws = _default_workspace(device)
     return ws.get(nbytes)
+
+
+def spec_workspace_status(workspace: Optional[Workspace] = None, device="cuda") -> int:
+    """Status word of a workspace (0: no bounded wait gave up since the last
+    reset; STATUS_WAIT_GAVE_UP otherwise).  Waits for the current stream."""
+    ws = workspace if workspace is not None else _default_workspace(device)
+    buf = ws.get(spec_workspace_bytes(0, 1, 1))  # at least the counter region
+    v = ctypes.c_uint32(0)
+    _check(load_library().spec_workspace_status(_ptr(buf), buf.numel(), ctypes.byref(v),
+                                                _stream(buf.device)))
+    return int(v.value)
+
+
+def spec_workspace_reset(workspace: Optional[Workspace] = None, device="cuda") -> None:
+    """Zero the counter region of a workspace (per-request words and status)
+    on the current stream, so a workspace whose status is set can be used
+    again."""
+    ws = workspace if workspace is not None else _default_workspace(device)
+    buf = ws.get(spec_workspace_bytes(0, 1, 1))  # at least the counter region
+    _check(load_library().spec_workspace_reset(_ptr(buf), buf.numel(), _stream(buf.device)))
 
 
 def spec_fill_uniforms(seed: int, counter0: int, n: int,
@@ -239,16 +287,31 @@ def spec_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
     return acc, out
 
 
+def _out_arg(t, shape, dtype, dev, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _need_cuda(t, name)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or t.device != dev:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         "on the inputs' device")
+    return t
+
+
 def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
                        draft_tokens: torch.Tensor, temperature: float = 1.0,
                        uniforms: Optional[torch.Tensor] = None, seed: int = 0,
                        counter0: int = 0, kind: str = "logits", probe: bool = False,
-                       workspace: Optional[Workspace] = None):
+                       workspace: Optional[Workspace] = None, schedule: str = "auto",
+                       out=None, test_give_up: bool = False):
     """Sampling chain verification with min(1, p/q) acceptance.
 
     target [B, k+1, V], draft [B, k, V] (f32/bf16 logits, or f32 probabilities
     with kind="probs"), draft_tokens int32 [B, k], uniforms float32
     [B, k+1, 2] or None (then derived from seed/counter0 inside the kernels).
+    schedule: "auto", "one_launch", "two_launch" or "early_exit" (identical
+    outputs).  out: optional preallocated (accepted_len, out_tokens[, probe])
+    tensors, written in place and returned.  test_give_up: test only (see
+    SPEC_FLAG_TEST_GIVE_UP in the C header).
     Returns (accepted_len, out_tokens) or, with probe=True,
     (accepted_len, out_tokens, probe [B, k+1, 4])."""
     _need_cuda(target, "target")
@@ -267,20 +330,23 @@ def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
         if uniforms.dtype != torch.float32 or uniforms.numel() != B * kp1 * 2:
             raise ValueError("uniforms must be float32 [B, k+1, 2]")
     kind_code = {"logits": SPEC_LOGITS, "probs": SPEC_PROBS}[kind]
-    acc = torch.empty(B, dtype=torch.int32, device=dev)
-    out = torch.empty(B, kp1, dtype=torch.int32, device=dev)
-    pr = torch.empty(B, kp1, 4, dtype=torch.float32, device=dev) if probe else None
+    flags = SCHEDULES[schedule] | (SPEC_FLAG_TEST_GIVE_UP if test_give_up else 0)
+    outs = tuple(out) if out is not None else (None, None, None)
+    acc = _out_arg(outs[0], (B,), torch.int32, dev, "accepted_len")
+    tok = _out_arg(outs[1], (B, kp1), torch.int32, dev, "out_tokens")
+    pr = (_out_arg(outs[2] if len(outs) > 2 else None, (B, kp1, 4), torch.float32, dev, "probe")
+          if probe else None)
     lib = load_library()
     nbytes = spec_workspace_bytes(B, kp1, V)
     ws = _workspace(workspace, dev, nbytes)
     _check(lib.spec_verify_sample(
         _ptr(target), _ptr(draft if k > 0 else None), _dtype_code(target), kind_code, B, k, V,
         _ptr(draft_tokens if k > 0 else None), _ptr(uniforms),
-        int(seed) & (2 ** 64 - 1), int(counter0) & (2 ** 64 - 1), float(temperature),
-        _ptr(acc), _ptr(out), _ptr(pr), _ptr(ws), ws.numel(), _stream(dev)))
+        int(seed) & (2 ** 64 - 1), int(counter0) & (2 ** 64 - 1), float(temperature), flags,
+        _ptr(acc), _ptr(tok), _ptr(pr), _ptr(ws), ws.numel(), _stream(dev)))
     if probe:
-        return acc, out, pr
-    return acc, out
+        return acc, tok, pr
+    return acc, tok
 
 
 def _parent_array(parent) -> "ctypes.Array":

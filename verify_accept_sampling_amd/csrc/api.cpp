@@ -53,8 +53,6 @@ int tree_depth_checked(const int32_t* parent, int n_nodes) {
 }  // namespace
 
 namespace specv {
-std::atomic<int> g_sample_path{SPEC_PATH_AUTO};
-
 uint64_t next_call_tag() {
   static const uint64_t process_bits = [] {
     std::random_device rd;
@@ -67,12 +65,6 @@ uint64_t next_call_tag() {
 }  // namespace specv
 
 extern "C" {
-
-int spec_sample_path(int mode) {
-  if (mode != SPEC_PATH_AUTO && mode != SPEC_PATH_TWO_LAUNCH && mode != SPEC_PATH_EARLY_EXIT)
-    return SPEC_EINVAL;
-  return specv::g_sample_path.exchange(mode);
-}
 
 const char* spec_strerror(int code) {
   switch (code) {
@@ -124,10 +116,12 @@ int spec_verify_greedy(const void* target, int dtype, int B, int k, int V,
 
 int spec_verify_sample(const void* target, const void* draft, int dtype, int kind, int B, int k,
                        int V, const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
-                       uint64_t counter0, float temperature, int32_t* accepted_len,
+                       uint64_t counter0, float temperature, int flags, int32_t* accepted_len,
                        int32_t* out_tokens, float* probe, void* ws, size_t ws_bytes,
                        void* stream) {
   if (!valid_dtype(dtype) || (kind != SPEC_LOGITS && kind != SPEC_PROBS)) return SPEC_EDTYPE;
+  if ((flags & ~(0xF | SPEC_FLAG_TEST_GIVE_UP)) != 0 || (flags & 0xF) > SPEC_SCHED_EARLY_EXIT)
+    return SPEC_EINVAL;
   if (kind == SPEC_PROBS && dtype != SPEC_F32) return SPEC_EDTYPE;
   if (B < 0 || B > kMaxB || k < 0 || k > kMaxK || V < 1 || V > kMaxV) return SPEC_EINVAL;
   if (kind == SPEC_LOGITS) {
@@ -148,10 +142,39 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
   if (check_grid((long)B * C2) != SPEC_OK) return SPEC_EINVAL;
   WsLayout L;
   if (int rc = check_workspace(ws, ws_bytes, B, k + 1, V, &L)) return rc;
+  SampleMode mode;
+  mode.sched = (flags & 0xF) == SPEC_SCHED_AUTO ? SPEC_SCHED_ONE_LAUNCH : (flags & 0xF);
+  mode.test_give_up = (flags & SPEC_FLAG_TEST_GIVE_UP) != 0;
+  mode.capturing = false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) == hipSuccess)
+    mode.capturing = cs == hipStreamCaptureStatusActive;
+  else
+    (void)hipGetLastError();  // not capturing; leave no error for the launch check
   if (launch_sample(target, draft, dtype, kind, B, k, V, draft_tokens, uniforms, seed, counter0,
-                    temperature, accepted_len, out_tokens, probe, ws, L,
+                    temperature, mode, accepted_len, out_tokens, probe, ws, L,
                     static_cast<hipStream_t>(stream)) != hipSuccess)
     return SPEC_EHIP;
+  return SPEC_OK;
+}
+
+int spec_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status_host, void* stream) {
+  if (ws == nullptr || status_host == nullptr) return SPEC_EINVAL;
+  if (ws_bytes < kCounterRegionBytes) return SPEC_EWORKSPACE;
+  const auto s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, static_cast<const char*>(ws) + SPEC_WORKSPACE_STATUS_OFFSET,
+                     sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SPEC_EHIP;
+  *status_host = v;
+  return SPEC_OK;
+}
+
+int spec_workspace_reset(void* ws, size_t ws_bytes, void* stream) {
+  if (ws == nullptr) return SPEC_EINVAL;
+  if (ws_bytes < kCounterRegionBytes) return SPEC_EWORKSPACE;
+  if (launch_reset_counters(ws, static_cast<hipStream_t>(stream)) != hipSuccess) return SPEC_EHIP;
   return SPEC_OK;
 }
 

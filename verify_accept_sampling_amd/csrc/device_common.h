@@ -48,6 +48,10 @@ __device__ __forceinline__ uint64_t pack2(float a, float b) {
 __device__ __forceinline__ float unpack_lo(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v)); }
 __device__ __forceinline__ float unpack_hi(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
 
+__device__ __forceinline__ unsigned ld_dev_u32(const unsigned* p) {
+  return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void st_dev_f(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);

@@ -102,13 +102,19 @@ static_assert(sizeof(DrawPart) == 80, "DrawPart layout");
 // kernel's early acceptance tests, [3] unused, [4..7] its ready slot, two
 // 64-bit words that carry a request's packed draw state.  The one-launch
 // words of position j belong to request j with its two bytes swapped.
-// Every word is back to 0 when a call completes.  The last 256 bytes are
-// reserved.
+// Every per-request word is back to 0 when a call completes.  The last 256
+// bytes hold the workspace status word (sticky bits, SPEC_STATUS_*) and the
+// 64-bit call epoch of graph-captured one-launch calls.
 constexpr int kCountersPerReq = 8;
 constexpr int kVerdictWord = 2;
 constexpr int kReadySlotWord = 4;
 constexpr size_t kCounterRegionBytes = (size_t)kMaxB * kCountersPerReq * 4 + 256;
 static_assert(kCounterRegionBytes == SPEC_WORKSPACE_COUNTER_BYTES, "counter region");
+constexpr size_t kPerRequestWords = (size_t)kMaxB * kCountersPerReq;
+constexpr size_t kStatusWord = kPerRequestWords;     // uint32 index
+constexpr size_t kEpochWord = kPerRequestWords + 2;  // uint32 index of a uint64
+static_assert(kEpochWord % 2 == 0, "epoch word is 8-byte aligned");
+static_assert(SPEC_WORKSPACE_STATUS_OFFSET == kStatusWord * 4, "status word offset");
 
 // Workspace layout.  The counter region (kCounterRegionBytes) sits at a
 // fixed place whatever the call's shape; it must be zero before the first
@@ -211,9 +217,6 @@ hipError_t launch_rejected_mask(const int32_t* accepted_len, const int32_t* path
                                 int B, int n_ent, uint8_t* rejected, int64_t* slots,
                                 int64_t pad_slot, hipStream_t s);
 
-// Process-wide choice of the sampling path (spec_sample_path).
-extern std::atomic<int> g_sample_path;
-
 hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int V,
                                const int32_t* draft_tokens, int32_t* accepted_len,
                                int32_t* out_tokens, void* ws, const WsLayout& L,
@@ -225,11 +228,21 @@ hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
                               int32_t* out_tokens, int32_t* out_path, void* ws,
                               const WsLayout& L, hipStream_t s);
 
+// How one sampling call is run (from the call's flags and its stream).
+struct SampleMode {
+  int sched;       // SPEC_SCHED_ONE_LAUNCH, _TWO_LAUNCH or _EARLY_EXIT (never AUTO)
+  bool capturing;  // the stream is being captured into a graph
+  bool test_give_up;  // SPEC_FLAG_TEST_GIVE_UP
+};
+
 hipError_t launch_sample(const void* target, const void* draft, int dtype, int kind,
                          int B, int k, int V, const int32_t* draft_tokens,
                          const float* uniforms, uint64_t seed, uint64_t counter0,
-                         float temperature, int32_t* accepted_len,
+                         float temperature, const SampleMode& mode, int32_t* accepted_len,
                          int32_t* out_tokens, float* probe, void* ws,
                          const WsLayout& L, hipStream_t s);
+
+// Zeroes the counter region of a workspace except its call epoch.
+hipError_t launch_reset_counters(void* ws, hipStream_t s);
 
 }  // namespace specv

@@ -27,6 +27,7 @@ std::vector<Pair> g_pairs;
 size_t g_next = 0;
 double g_ms[kProfKinds] = {0};
 long g_count[kProfKinds] = {0};
+std::vector<float> g_each[kProfKinds];  // every timed launch's duration, in order
 
 // Fold every recorded pair into the totals (synchronising its end event).
 void drain_locked() {
@@ -36,6 +37,7 @@ void drain_locked() {
     if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
       g_ms[p.kind] += ms;
       g_count[p.kind] += 1;
+      g_each[p.kind].push_back(ms);
     }
     p.used = false;
   }
@@ -87,6 +89,7 @@ int spec_profile_enable(int on) {
     for (int i = 0; i < kProfKinds; ++i) {
       g_ms[i] = 0.0;
       g_count[i] = 0;
+      g_each[i].clear();
     }
     for (auto& p : g_pairs) p.used = false;
     g_next = 0;
@@ -104,6 +107,19 @@ int spec_profile_read(int kind, long* launches, double* total_ms) {
   drain_locked();
   *launches = g_count[kind];
   *total_ms = g_ms[kind];
+  return SPEC_OK;
+}
+
+int spec_profile_durations(int kind, float* ms_host, long cap, long* n_host) {
+  if (kind < 0 || kind >= kProfKinds || n_host == nullptr || cap < 0 ||
+      (cap > 0 && ms_host == nullptr))
+    return SPEC_EINVAL;
+  std::lock_guard<std::mutex> lk(g_mu);
+  drain_locked();
+  const auto& v = g_each[kind];
+  const long n = static_cast<long>(v.size()) < cap ? static_cast<long>(v.size()) : cap;
+  for (long i = 0; i < n; ++i) ms_host[i] = v[i];
+  *n_host = static_cast<long>(v.size());
   return SPEC_OK;
 }
 

@@ -155,10 +155,11 @@ __device__ __forceinline__ void write_probe_position(float* probe, int b, int i,
   pr[3] = 0.f;
 }
 
-// Outputs of the acceptance tests once n is known, by one wave:
+// Outputs of the acceptance tests once n is known, by one wave of the
+// request's last draw work-group (the one work-group that writes them):
 // accepted_len[b], the accepted prefix, the -1 padding, probe[b, i, 2] = 0
-// for i != n (probe[b, n, 2] belongs to the draw) and the other probe
-// entries of the bonus row k.
+// for i != n (probe[b, n, 2] is written with the drawn token) and the other
+// probe entries of the bonus row k.
 __device__ __forceinline__ void write_accept_outputs(int b, int k, int n,
                                                      const int32_t* __restrict__ draft_tokens,
                                                      int32_t* __restrict__ accepted_len,
@@ -185,16 +186,15 @@ __device__ __forceinline__ void write_accept_outputs(int b, int k, int n,
 // Lane i handles position i (and i + 64, ...); each lane keeps the draw
 // state of its first rejected position (or of the bonus row), and after the
 // wave minimum the owner of the first rejection supplies it.  Returns the
-// state in every lane, and with `write` stores the outputs and every probe
-// value other than probe[b, n, 2].
+// state in every lane and stores the probe values p_i(x_i), q_i(x_i) of the
+// tested positions (the request's draw writes the other outputs).
 __device__ __forceinline__ ReqState finalize_request(
     int b, int k, int V, int C1, float c, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
-    const uint64_t* __restrict__ part, const float* __restrict__ zrow, bool write,
-    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    const uint64_t* __restrict__ part, const float* __restrict__ zrow,
     float* __restrict__ probe) {
   const int lane = threadIdx.x & 63;
-  const bool want_probe = write && probe != nullptr;
+  const bool want_probe = probe != nullptr;
   int first = k;
   float cand_mp = 0.f, cand_mq = 0.f;  // draw state of this lane's hand-over row
   double cand_rho = 1.0;
@@ -217,7 +217,6 @@ __device__ __forceinline__ ReqState finalize_request(
   st.mp = __shfl(cand_mp, owner, 64);
   st.mq = __shfl(cand_mq, owner, 64);
   st.rho32 = __shfl(cand_rho, owner, 64);
-  if (write) write_accept_outputs(b, k, n, draft_tokens, accepted_len, out_tokens, probe);
   return st;
 }
 
@@ -251,12 +250,12 @@ __device__ __forceinline__ int finalize_progressive(
     const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms, uint64_t seed,
     uint64_t ctr0, const uint64_t* __restrict__ part, const float* __restrict__ zrow,
     const uint64_t* __restrict__ flags, uint64_t tag, float* __restrict__ probe, ReqState& st,
-    int& tested) {
+    int& tested, long spin_limit) {
   const int lane = threadIdx.x & 63;
   const bool want_probe = probe != nullptr;
   const int end = min(limit, k + 1);
   tested = base;
-  for (long spin = 0; spin < kSpinLimit; ++spin) {
+  for (long spin = 0; spin < spin_limit; ++spin) {
     if (base >= end) return kDeferred;
     const int i = base + lane;
     const bool have = i < end && position_complete(flags, b, i, k, C1, tag);
@@ -301,10 +300,11 @@ __device__ __forceinline__ void publish_state(unsigned* counters, int b, const R
 
 // Verdict word of request b's early acceptance tests (one-launch kernel):
 // 0 until they end; then kVerdictDecided | tested << 2 (the state is in the
-// ready slot, `tested` positions have probe values) or kVerdictDeferred |
-// next << 2 (positions from `next` on remain to be tested).  The request's
-// first draw work-group reads it and resets it.
-constexpr unsigned kVerdictDecided = 1, kVerdictDeferred = 2;
+// ready slot, `tested` positions have probe values), kVerdictDeferred |
+// next << 2 (positions from `next` on remain to be tested) or
+// kVerdictFailed (the wait for the rows gave up).  The request's first draw
+// work-group reads it and resets it.
+constexpr unsigned kVerdictDecided = 1, kVerdictDeferred = 2, kVerdictFailed = 3;
 __device__ __forceinline__ unsigned* verdict_word(unsigned* counters, int b) {
   return &counters[handover_pos(b) + kVerdictWord];
 }
@@ -316,32 +316,34 @@ __device__ __forceinline__ void early_finalize(
     int b, int k, int V, int C1, float c, int limit, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     const uint64_t* __restrict__ part, const float* __restrict__ zrow,
-    const uint64_t* __restrict__ flags, uint64_t tag, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ out_tokens, float* __restrict__ probe, unsigned* __restrict__ counters) {
+    const uint64_t* __restrict__ flags, uint64_t tag, float* __restrict__ probe,
+    unsigned* __restrict__ counters, long spin_limit) {
   // This wave decides when the request's draw can start: it issues first.
   __builtin_amdgcn_s_setprio(3);
   ReqState st;
   int tested = 0;
   const int res = finalize_progressive(b, k, V, C1, c, 0, limit, draft_tokens, uniforms, seed,
-                                       ctr0, part, zrow, flags, tag, probe, st, tested);
-  if (res == kTimedOut) return;  // never expected
+                                       ctr0, part, zrow, flags, tag, probe, st, tested,
+                                       spin_limit);
+  if ((threadIdx.x & 63) != 0) return;
   unsigned verdict;
   if (res == kDecided) {
-    if ((threadIdx.x & 63) == 0) publish_state(counters, b, st);
-    write_accept_outputs(b, k, st.n, draft_tokens, accepted_len, out_tokens, probe);
+    publish_state(counters, b, st);
     verdict = kVerdictDecided | (unsigned)tested << 2;
-  } else {
+  } else if (res == kDeferred) {
     verdict = kVerdictDeferred | (unsigned)tested << 2;
+  } else {  // the rows never appeared: the request fails loudly
+    note_give_up(counters);
+    verdict = kVerdictFailed;
   }
-  if ((threadIdx.x & 63) == 0)
-    __hip_atomic_store(verdict_word(counters, b), verdict, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(verdict_word(counters, b), verdict, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One thread waits until the verdict word is set, returns it and resets it.
-// 0 if the bound is reached.
-__device__ __forceinline__ unsigned take_verdict(unsigned* word) {
-  for (long spin = 0; spin < kSpinLimit; ++spin) {
+// 0 if the bound (`spin_limit` polls) is reached.
+__device__ __forceinline__ unsigned take_verdict(unsigned* word, long spin_limit) {
+  for (long spin = 0; spin < spin_limit; ++spin) {
     const unsigned v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v != 0) {
       __hip_atomic_store(word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -360,12 +362,13 @@ __device__ __forceinline__ void probe_remaining(
     int b, int k, int V, int C1, float c, int from, const int32_t* __restrict__ draft_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     const uint64_t* __restrict__ part, const float* __restrict__ zrow,
-    const uint64_t* __restrict__ flags, uint64_t tag, float* __restrict__ probe) {
+    const uint64_t* __restrict__ flags, uint64_t tag, float* __restrict__ probe,
+    unsigned* __restrict__ counters, long spin_limit) {
   const int lane = threadIdx.x & 63;
   for (int base = from; base < k; base += kWaveSize) {
     const int i = base + lane;
     bool done = i >= k;
-    for (long spin = 0; spin < kSpinLimit; ++spin) {
+    for (long spin = 0; spin < spin_limit; ++spin) {
       if (!done && position_complete(flags, b, i, k, C1, tag)) {
         const PosResult r = test_position(b, i, k, V, C1, c, draft_tokens, uniforms, seed, ctr0,
                                           part, zrow, true);
@@ -374,6 +377,10 @@ __device__ __forceinline__ void probe_remaining(
       }
       if (__ballot(!done) == 0) break;
       __builtin_amdgcn_s_sleep(32);
+    }
+    if (__ballot(!done) != 0) {  // these rows never appeared: the call fails loudly
+      if (lane == 0) note_give_up(counters);
+      return;
     }
   }
 }
@@ -407,15 +414,16 @@ __device__ __forceinline__ void position_major_row(long bid, int B, int k, int C
 // state.  One-launch kernel (rows in position order): the work-group tags
 // its chunk complete once its pair is published, and the request's first
 // draw work-group takes it from there.
+// `withhold` (test only): the work-group of request 0, target row 0, chunk 0
+// publishes its pair but never its completion tag.
 template <int DT, int NE, bool EXIT = false>
 __device__ __forceinline__ void row_block(
     long bid, bool one_launch, bool late, int B, const void* __restrict__ target,
     const void* __restrict__ draft, int k, int V, int C1, float c,
     const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms, uint64_t seed,
-    uint64_t ctr0, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probe, uint64_t* __restrict__ part, float* __restrict__ zrow,
-    uint64_t* __restrict__ flags, uint64_t tag, ReqState* __restrict__ state,
-    unsigned* __restrict__ counters) {
+    uint64_t ctr0, float* __restrict__ probe, uint64_t* __restrict__ part,
+    float* __restrict__ zrow, uint64_t* __restrict__ flags, uint64_t tag,
+    ReqState* __restrict__ state, unsigned* __restrict__ counters, bool withhold = false) {
   const int R = 2 * k + 1;
   int b, r, chunk;
   if (one_launch) {
@@ -437,8 +445,8 @@ __device__ __forceinline__ void row_block(
                                    zrow);
   if (one_launch) {
     // The tag follows the pair (and logit) once they are complete.
-    if (threadIdx.x == 0 && stored) {  // the thread that stored them
-      wait_stores();
+    if (threadIdx.x == 0 && stored && !(withhold && b == 0 && r == 0 && chunk == 0)) {
+      wait_stores();  // the thread that stored them
       st_dev(&flags[((long)b * R + r) * C1 + chunk], tag);
     }
     return;
@@ -450,7 +458,7 @@ __device__ __forceinline__ void row_block(
   // the request's draw can start: it issues first.
   __builtin_amdgcn_s_setprio(3);
   const ReqState st = finalize_request(b, k, V, C1, c, draft_tokens, uniforms, seed, ctr0, part,
-                                       zrow, true, accepted_len, out_tokens, probe);
+                                       zrow, probe);
   if ((threadIdx.x & 63) == 0) st_dev_state(&state[b], st);
 }
 
@@ -521,10 +529,15 @@ struct RowPass {
 // Draw of one work-group: chunk group grp of request b.  With kStateSlot,
 // work-group 0 of the request takes the verdict of the request's early
 // acceptance tests; if they left positions untested it tests those on one
-// wave as their rows complete, publishes the packed state in the request's
-// ready slot and writes the tests' outputs.  The request's other draw
-// work-groups wait for the ready slot, and the request's last draw
-// work-group clears it.
+// wave as their rows complete and publishes the packed state in the
+// request's ready slot.  The request's other draw work-groups wait for the
+// ready slot.  Every draw work-group takes the request's draw ticket, and
+// the last one writes the request's outputs (logits: all of them; the
+// accepted prefix of probability rows is written by work-group 0) and
+// clears the ready slot.  A wait that gives up sets the workspace status;
+// the request's work-groups then skip their sums, and the last one writes
+// accepted_len = -1 and out_tokens all -1, as it does whenever the status
+// word is set.
 template <int DT, int NE, int KIND, int HOW>
 __device__ __forceinline__ void draw_block(
     int b, int grp, int nb, const void* __restrict__ target, const void* __restrict__ draft,
@@ -532,14 +545,15 @@ __device__ __forceinline__ void draw_block(
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probe, const ReqState* __restrict__ state, const RowPass& rows,
-    DrawPart* __restrict__ part, unsigned* __restrict__ counters) {
+    DrawPart* __restrict__ part, unsigned* __restrict__ counters, long spin_limit) {
   const int G2 = draw_groups(C2, nb);
   __shared__ double tab[256];
   static_assert(kThreads == 256, "one table entry per thread");
   // The exp table's load is issued now and stored to shared memory after
   // the wait below, so the load and the first poll share one round trip.
   const double tv = KIND == 0 ? kExp2Frac256[threadIdx.x] : 0.0;
-  int n;
+  int n = 0;
+  bool ok = true;  // this work-group holds the request's state
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
     ReqState st;
@@ -551,53 +565,80 @@ __device__ __forceinline__ void draw_block(
         // the positions from some point on to this work-group.
         if (threadIdx.x < kWaveSize) {
           unsigned v = 0;
-          if (threadIdx.x == 0) v = take_verdict(verdict_word(counters, b));
+          if (threadIdx.x == 0) v = take_verdict(verdict_word(counters, b), spin_limit);
           v = __shfl(v, 0, 64);
           int tested = (int)(v >> 2);
-          int ok = (v & 3) == kVerdictDecided ? 1 : 0;
+          // gave_up: this wave's own wait gave up (a failed verdict was
+          // already noted by its finalizer)
+          bool gave_up = v == 0;
+          bool failed = gave_up || (v & 3) == kVerdictFailed;
           bool mine_ready = false;
           ReqState mine;
           if ((v & 3) == kVerdictDeferred) {
             __builtin_amdgcn_s_setprio(3);
             const int res = finalize_progressive(
                 b, k, V, rows.C1, rows.c, tested, INT_MAX, draft_tokens, uniforms, seed, ctr0,
-                rows.part, rows.zrow, rows.flags, rows.tag, probe, mine, tested);
+                rows.part, rows.zrow, rows.flags, rows.tag, probe, mine, tested, spin_limit);
             __builtin_amdgcn_s_setprio(0);
             if (res == kDecided) {
               if (threadIdx.x == 0) publish_state(counters, b, mine);
-              write_accept_outputs(b, k, mine.n, draft_tokens, accepted_len, out_tokens, probe);
-              ok = 1;
               mine_ready = true;
+            } else {
+              failed = gave_up = true;
             }
           }
-          if (ok && probe)  // positions after the first rejection, as their rows complete
+          if (!failed && probe)  // positions after the first rejection, as their rows complete
             probe_remaining(b, k, V, rows.C1, rows.c, tested, draft_tokens, uniforms, seed, ctr0,
-                            rows.part, rows.zrow, rows.flags, rows.tag, probe);
+                            rows.part, rows.zrow, rows.flags, rows.tag, probe, counters,
+                            spin_limit);
           if (threadIdx.x == 0) {
             uint64_t w0 = 0, w1 = 0;
-            if (mine_ready) pack_state(mine, w0, w1);
-            else if (ok) ok = wait_slot(ready_slot(counters, b), w0, w1) ? 1 : 0;
+            int good = 1;
+            if (failed) {
+              // Tell the request's other draw work-groups not to wait.
+              if (gave_up) note_give_up(counters);
+              uint64_t* slot = ready_slot(counters, b);
+              st_dev(&slot[0], kSlotFailed);
+              st_dev(&slot[1], kSlotFailed);
+              good = 0;
+            } else if (mine_ready) {
+              pack_state(mine, w0, w1);
+            } else if (!wait_slot(ready_slot(counters, b), w0, w1, spin_limit)) {
+              note_give_up(counters);
+              good = 0;
+            } else if (w0 == kSlotFailed) {
+              good = 0;
+            }
             s_w[0] = w0;
             s_w[1] = w1;
-            s_ok = ok;
+            s_ok = good;
           }
         }
       } else if (threadIdx.x == 0) {
         uint64_t w0 = 0, w1 = 0;
-        s_ok = wait_slot(ready_slot(counters, b), w0, w1) ? 1 : 0;
+        int good = 1;
+        if (!wait_slot(ready_slot(counters, b), w0, w1, spin_limit)) {
+          note_give_up(counters);
+          good = 0;
+        } else if (w0 == kSlotFailed) {
+          good = 0;
+        }
+        s_ok = good;
         s_w[0] = w0;
         s_w[1] = w1;
       }
       __syncthreads();
-      if (!s_ok) return;  // never expected: the request's rows or state did not appear
-      st = unpack_state(s_w[0], s_w[1], k);
+      ok = s_ok != 0;
+      if (ok) st = unpack_state(s_w[0], s_w[1], k);
     } else {
       st = ld_dev_state(&state[b]);
     }
-    n = min(max(st.n, 0), k);  // always a valid row index
-    mp = st.mp;
-    mq = st.mq;
-    rho32 = st.rho32;
+    if (ok) {
+      n = min(max(st.n, 0), k);  // always a valid row index
+      mp = st.mp;
+      mq = st.mq;
+      rho32 = st.rho32;
+    }
   } else {
     n = accept_scan_probs(static_cast<const float*>(target), static_cast<const float*>(draft), b,
                           k, V, draft_tokens, uniforms, seed, ctr0, grp == 0, accepted_len,
@@ -616,7 +657,7 @@ __device__ __forceinline__ void draw_block(
   // ---- this work-group's chunks: nb * kDrawChunksPerWave consecutive
   // chunks per wave ----
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  {
+  if (ok) {
     const int per_wave = nb * kDrawChunksPerWave;
     const int first = grp * nb * kDrawChunksPerGroup + wave * per_wave;
     DrawPart* pb = part + (long)b * C2;
@@ -637,6 +678,30 @@ __device__ __forceinline__ void draw_block(
   // Every other wave on this compute unit is bulk work of other requests,
   // while this one decides when its request ends: it issues first.
   __builtin_amdgcn_s_setprio(3);
+  // A failed request (this work-group has no state), or any give-up recorded
+  // in the workspace (sticky until it is reset): -1 outputs instead of a
+  // draw.  Every draw work-group of the request has passed its wait (each
+  // took the ticket after it), so the ready slot goes back to 0 for the next
+  // call either way.
+  auto fail_outputs = [&]() {
+    if (wave == 0) {
+      for (int i = lane; i <= k; i += kWaveSize) out_tokens[(long)b * (k + 1) + i] = -1;
+      if (lane == 0) {
+        accepted_len[b] = -1;
+        uint64_t* slot = ready_slot(counters, b);
+        st_dev(&slot[0], (uint64_t)0);
+        st_dev(&slot[1], (uint64_t)0);
+      }
+    }
+  };
+  unsigned status_v = 0;  // loaded now, used at the end: off the tail's critical path
+  if constexpr (HOW == kStateSlot) {
+    if (!ok) {  // block-uniform
+      fail_outputs();
+      return;
+    }
+    status_v = ld_dev_u32(status_word(counters));
+  }
   // Thread t owns chunk base + t of each tile of kThreads chunks.  With one
   // tile (V up to kThreads * kDrawChunk) the partials are loaded once and
   // every step below works on registers; with more tiles the corrected
@@ -676,7 +741,13 @@ __device__ __forceinline__ void draw_block(
   block_sum_dn<3>(sums);
   const double sp_tot = sums[0];
   const double rho = resid_w ? sums[0] / sums[1] : 1.0;
-  const bool any_redo = resid_w && sums[2] > 0.0;  // block-uniform
+  // The weights were summed at rho32 with the elements within kKinkBand of
+  // the kink left out; moving them linearly to rho is exact only while no
+  // other element changes sides, i.e. while rho stays well inside that band
+  // around rho32.  Otherwise (far-off float32 statistics: extreme
+  // temperatures or logit ranges) every chunk is recomputed exactly.
+  const bool drift = resid_w && !(fabs(rho - rho32) <= 0.5 * kKinkBand * rho32);
+  const bool any_redo = resid_w && (sums[2] > 0.0 || drift);  // block-uniform
   // Chunk totals of the draw weights at the exact rho: the linear part moved
   // to rho, plus the exact weights of the recorded kink-band elements; a
   // chunk with more of them than recorded is recomputed (one wave each).
@@ -684,7 +755,7 @@ __device__ __forceinline__ void draw_block(
   for (int base = 0; base < C2; base += kThreads) {
     const int cc = base + threadIdx.x;
     if (n_tiles > 1) load_chunk(cc);
-    const bool redo = resid_w && cnk > (double)kKinkSlots;
+    const bool redo = resid_w && cc < C2 && (drift || cnk > (double)kKinkSlots);
     if (resid_w && !redo) {
       cw = fmax(0.0, cw + (rho - rho32) * cdq);
       for (int j = 0; j < kKinkSlots; ++j)
@@ -766,6 +837,12 @@ __device__ __forceinline__ void draw_block(
   const int mode = use_w ? 0 : 1;
   // s_P is stored by one thread above; the search reads it after a barrier.
   int t = search_chunk<DT, KIND>(prow, qrow, V, cs, mode == 0, c1, c0p, c0q, rho, s_P, thr, tab);
+  if (status_v != 0) {  // block-uniform
+    fail_outputs();
+    return;
+  }
+  if (KIND == 0 && wave == 0)  // the acceptance tests' outputs: this work-group's alone
+    write_accept_outputs(b, k, n, draft_tokens, accepted_len, out_tokens, probe);
   if (threadIdx.x == 0) {
     if (!(grand > 0.0)) t = -1;  // rows without mass (invalid input)
     out_tokens[(long)b * (k + 1) + n] = t;
@@ -776,9 +853,6 @@ __device__ __forceinline__ void draw_block(
       else mass = mode == 0 ? grand : (resid ? 0.0 : grand);
       probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
-    // Every draw work-group of the request has passed its wait (each took
-    // the ticket after it): the ready slot goes back to 0 for the next
-    // call.
     if constexpr (HOW == kStateSlot) {
       uint64_t* slot = ready_slot(counters, b);
       st_dev(&slot[0], (uint64_t)0);
@@ -792,12 +866,10 @@ template <int DT, int NE>
 __global__ __launch_bounds__(kThreads) void k_row_stats(
     const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C1,
     float c, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
-    uint64_t seed, uint64_t ctr0, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ out_tokens, float* __restrict__ probe, uint64_t* __restrict__ part,
+    uint64_t seed, uint64_t ctr0, float* __restrict__ probe, uint64_t* __restrict__ part,
     float* __restrict__ zrow, ReqState* __restrict__ state, unsigned* __restrict__ counters) {
   row_block<DT, NE>(blockIdx.x, false, false, 0, target, draft, k, V, C1, c, draft_tokens,
-                    uniforms, seed, ctr0, accepted_len, out_tokens, probe, part, zrow, nullptr, 0,
-                    state, counters);
+                    uniforms, seed, ctr0, probe, part, zrow, nullptr, 0, state, counters);
 }
 
 template <int DT, int NE, int KIND>
@@ -814,7 +886,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(
                                          static_cast<int>(blockIdx.x % G2), nb, target, draft, k, V,
                                          C2, inv_t, draft_tokens, uniforms, seed, ctr0,
                                          accepted_len, out_tokens, probe, state, none, part,
-                                         counters);
+                                         counters, kSpinLimit);
 }
 
 // One-launch path.  Grid, in dispatch order:
@@ -835,6 +907,10 @@ __global__ __launch_bounds__(kThreads) void k_draw(
 // its request's rows, the other draw work-groups for the request's state),
 // so every wait ends.  EXIT: row-pass work-groups after position 0 stop
 // once their request is decided before their position.
+// tag: this call's completion tag, or 0 to derive it from the workspace's
+// call epoch (graph-captured calls; k_advance_epoch follows the kernel).
+// spin_limit: polls before a bounded wait gives up.  withhold: test only
+// (row_block).
 template <int DT, int NE, bool EXIT>
 __global__ __launch_bounds__(kThreads) void k_sample_one(
     const void* __restrict__ target, const void* __restrict__ draft, int B, int k, int V, int C1,
@@ -844,8 +920,9 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
     float* __restrict__ probe, uint64_t* __restrict__ part1, float* __restrict__ zrow,
     uint64_t* __restrict__ flags, uint64_t tag, ReqState* __restrict__ state,
     DrawPart* __restrict__ part2, unsigned* __restrict__ counters, int E, long n_early_rows,
-    int n_fin) {
+    int n_fin, long spin_limit, int withhold) {
   const long bid = blockIdx.x;
+  if (tag == 0) tag = epoch_tag(ld_dev(epoch_word(counters)));
   const int G2 = draw_groups(C2, 1);
   long row = -1;  // row-pass index in position order
   bool late = false;
@@ -856,7 +933,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
     const int b = static_cast<int>((bid - n_early_rows) * kWaves + (threadIdx.x >> 6));
     if (b < B)
       early_finalize(b, k, V, C1, c, E, draft_tokens, uniforms, seed, ctr0, part1, zrow, flags,
-                     tag, accepted_len, out_tokens, probe, counters);
+                     tag, probe, counters, spin_limit);
     return;
   } else {
     // Request b's rows of positions E .. k (target and draft row of each
@@ -878,15 +955,36 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
   }
   if (row >= 0) {
     row_block<DT, NE, EXIT>(row, true, late, B, target, draft, k, V, C1, c, draft_tokens,
-                            uniforms, seed, ctr0, accepted_len, out_tokens, probe, part1, zrow,
-                            flags, tag, state, counters);
+                            uniforms, seed, ctr0, probe, part1, zrow, flags, tag, state,
+                            counters, withhold != 0);
   } else {
     const RowPass rows{part1, zrow, flags, tag, C1, c};
     draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2), 1,
                                       target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
                                       seed, ctr0, accepted_len, out_tokens, probe, state, rows,
-                                      part2, counters);
+                                      part2, counters, spin_limit);
   }
+}
+
+// Graph-captured one-launch calls: the next call epoch, after the kernel.
+__global__ void k_advance_epoch(unsigned* __restrict__ counters) {
+  if (threadIdx.x == 0) {
+    uint64_t* e = epoch_word(counters);
+    st_dev(e, ld_dev(e) + 1);
+  }
+}
+
+// spec_workspace_reset: every word of the counter region but the epoch.
+__global__ __launch_bounds__(kThreads) void k_reset_counters(unsigned* __restrict__ counters) {
+  const long n = (long)(kCounterRegionBytes / 4);
+  for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long)gridDim.x * kThreads)
+    if (i != (long)kEpochWord && i != (long)kEpochWord + 1) counters[i] = 0u;
+}
+
+hipError_t launch_reset_counters(void* ws, hipStream_t s) {
+  hipLaunchKernelGGL(k_reset_counters, dim3(256), dim3(kThreads), 0, s,
+                     static_cast<unsigned*>(ws));
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -965,9 +1063,9 @@ static bool rows_aligned(const void* p, int V, int dtype) {
 template <int DT, int NE>
 static hipError_t launch_logits(const void* target, const void* draft, int B, int k, int V,
                           const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
-                          uint64_t ctr0, float temperature, int32_t* accepted_len,
-                          int32_t* out_tokens, float* probe, char* w, const WsLayout& L,
-                          hipStream_t s) {
+                          uint64_t ctr0, float temperature, const SampleMode& mode,
+                          int32_t* accepted_len, int32_t* out_tokens, float* probe, char* w,
+                          const WsLayout& L, hipStream_t s) {
   const int C1 = row_chunks(V);
   const int C2 = res_chunks(V);
   const float c = 1.4426950408889634f / temperature;
@@ -980,8 +1078,7 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   auto* zr = reinterpret_cast<float*>(w + L.zrow);
   const long n_row = (long)B * R * C1;
   const int G2 = draw_groups(C2, 1);
-  const int path = g_sample_path.load(std::memory_order_relaxed);
-  if (path != SPEC_PATH_TWO_LAUNCH) {
+  if (mode.sched != SPEC_SCHED_TWO_LAUNCH) {
     auto* fl = reinterpret_cast<uint64_t*>(w + L.flag);
     // Early positions: as many as the first round of resident work-groups
     // streams (at least one).
@@ -991,18 +1088,24 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
     const long n_early_rows = E > k ? n_row : (long)E * per_pos;
     const int n_fin = (B + kWaves - 1) / kWaves;
     // Early exit needs no probe values beyond each request's stop.
-    const bool exit_early = path == SPEC_PATH_EARLY_EXIT && probe == nullptr;
-    return launch_timed(kProfFused,
-                        exit_early ? &k_sample_one<DT, NE, true> : &k_sample_one<DT, NE, false>,
-                        dim3((unsigned)(n_row + n_fin + (long)B * G2)), dim3(kThreads),
-                        one_launch_lds<DT, NE>(0), s, target, draft, B, k, V, C1, C2, c, inv_t,
-                        draft_tokens, uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1,
-                        zr, fl, next_call_tag(), st, p2, cnt, E, n_early_rows, n_fin);
+    const bool exit_early = mode.sched == SPEC_SCHED_EARLY_EXIT && probe == nullptr;
+    // A captured launch is replayed as it is recorded, so its tag comes from
+    // the workspace's call epoch, advanced by a kernel after it.
+    const uint64_t tag = mode.capturing ? 0 : next_call_tag();
+    const long spin = mode.test_give_up ? 256 : kSpinLimit;
+    const hipError_t e = launch_timed(
+        kProfFused, exit_early ? &k_sample_one<DT, NE, true> : &k_sample_one<DT, NE, false>,
+        dim3((unsigned)(n_row + n_fin + (long)B * G2)), dim3(kThreads), one_launch_lds<DT, NE>(0),
+        s, target, draft, B, k, V, C1, C2, c, inv_t, draft_tokens, uniforms, seed, ctr0,
+        accepted_len, out_tokens, probe, p1, zr, fl, tag, st, p2, cnt, E, n_early_rows, n_fin,
+        spin, mode.test_give_up ? 1 : 0);
+    if (e != hipSuccess || !mode.capturing) return e;
+    hipLaunchKernelGGL(k_advance_epoch, dim3(1), dim3(kWaveSize), 0, s, cnt);
+    return hipGetLastError();
   }
   hipError_t e = launch_timed(kProfRowPass, &k_row_stats<DT, NE>, dim3((unsigned)n_row),
                              dim3(kThreads), 0, s, target, draft, k, V, C1, c, draft_tokens,
-                             uniforms, seed, ctr0, accepted_len, out_tokens, probe, p1, zr, st,
-                             cnt);
+                             uniforms, seed, ctr0, probe, p1, zr, st, cnt);
   if (e != hipSuccess) return e;
   return launch_timed(kProfDraw, &k_draw<DT, NE, 0>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
                       target, draft, k, V, C2, 1, inv_t, draft_tokens, uniforms, seed, ctr0,
@@ -1047,8 +1150,8 @@ static hipError_t launch_probs(const void* target, const void* draft, int B, int
 hipError_t launch_sample(const void* target, const void* draft, int dtype, int kind, int B,
                          int k, int V, const int32_t* draft_tokens, const float* uniforms,
                          uint64_t seed, uint64_t counter0, float temperature,
-                         int32_t* accepted_len, int32_t* out_tokens, float* probe, void* ws,
-                         const WsLayout& L, hipStream_t s) {
+                         const SampleMode& mode, int32_t* accepted_len, int32_t* out_tokens,
+                         float* probe, void* ws, const WsLayout& L, hipStream_t s) {
   char* w = static_cast<char*>(ws);
   const bool vec = rows_aligned(target, V, dtype) && (k == 0 || rows_aligned(draft, V, dtype));
   if (kind == 1) {
@@ -1061,17 +1164,17 @@ hipError_t launch_sample(const void* target, const void* draft, int dtype, int k
   } else if (dtype == 1) {
     if (vec)
       return launch_logits<1, 8>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
-                          temperature, accepted_len, out_tokens, probe, w, L, s);
+                          temperature, mode, accepted_len, out_tokens, probe, w, L, s);
     else
       return launch_logits<1, 1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
-                          temperature, accepted_len, out_tokens, probe, w, L, s);
+                          temperature, mode, accepted_len, out_tokens, probe, w, L, s);
   } else {
     if (vec)
       return launch_logits<0, 4>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
-                          temperature, accepted_len, out_tokens, probe, w, L, s);
+                          temperature, mode, accepted_len, out_tokens, probe, w, L, s);
     else
       return launch_logits<0, 1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
-                          temperature, accepted_len, out_tokens, probe, w, L, s);
+                          temperature, mode, accepted_len, out_tokens, probe, w, L, s);
   }
 }
 

@@ -634,10 +634,38 @@ __device__ __forceinline__ ReqState ld_dev_state(const ReqState* p) {
 }
 
 
+// Ready-slot value of a request whose acceptance tests gave up: both words
+// all ones (a published state never has 0xffffffff as its low word, n + 1).
+constexpr uint64_t kSlotFailed = ~0ull;
+
+// Workspace status word (sticky SPEC_STATUS_* bits) and the call epoch of
+// graph-captured calls, in the counter region's reserved tail.
+__device__ __forceinline__ unsigned* status_word(unsigned* counters) {
+  return &counters[kStatusWord];
+}
+__device__ __forceinline__ uint64_t* epoch_word(unsigned* counters) {
+  return reinterpret_cast<uint64_t*>(&counters[kEpochWord]);
+}
+// Completion tag of a graph-captured call from the workspace's call epoch:
+// a marker byte other than that of the host's per-call tags, so no tag of
+// one kind equals one of the other.
+__device__ __forceinline__ uint64_t epoch_tag(uint64_t epoch) {
+  return (0xC4ull << 56) | (epoch & ((1ull << 56) - 1));
+}
+// A bounded wait gave up: set the sticky status bit, and wait until the
+// atomic has completed, so that whatever this thread publishes next (a
+// failed verdict or slot, a ticket) is seen only after it.
+__device__ __forceinline__ void note_give_up(unsigned* counters) {
+  __hip_atomic_fetch_or(status_word(counters), (unsigned)SPEC_STATUS_WAIT_GAVE_UP,
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_stores();
+}
+
 // One thread waits until both words of a ready slot are set and returns
-// them.  False if the bound is reached.
-__device__ __forceinline__ bool wait_slot(const uint64_t* slot, uint64_t& w0, uint64_t& w1) {
-  for (long spin = 0; spin < kSpinLimit; ++spin) {
+// them.  False if the bound (`spin` polls) is reached.
+__device__ __forceinline__ bool wait_slot(const uint64_t* slot, uint64_t& w0, uint64_t& w1,
+                                          long spin_limit) {
+  for (long spin = 0; spin < spin_limit; ++spin) {
     w0 = ld_dev(&slot[0]);
     w1 = ld_dev(&slot[1]);
     if (w0 != 0 && w1 != 0) return true;
