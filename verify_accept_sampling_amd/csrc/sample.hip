@@ -513,7 +513,7 @@ __device__ int accept_scan_probs(const float* target, const float* draft, int b,
 // How a draw work-group learns its request's state.
 enum {
   kStateStored = 0,  // from the state array, written by an earlier launch
-  kStateSlot = 1,    // one-launch hand-over through the row count and ready slot
+  kStateSlot = 1,    // one-launch hand-over: verdict word, then the ready slot
 };
 
 // Row-pass outputs the request's first draw work-group reads.
@@ -557,7 +557,7 @@ __device__ __forceinline__ void draw_block(
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
   if (KIND == 0) {
     ReqState st;
-    if constexpr (HOW == kStateSlot) {
+    if constexpr (HOW != kStateStored) {
       __shared__ int s_ok;
       __shared__ uint64_t s_w[2];
       if (grp == 0) {  // work-group-uniform
@@ -695,7 +695,7 @@ __device__ __forceinline__ void draw_block(
     }
   };
   unsigned status_v = 0;  // loaded now, used at the end: off the tail's critical path
-  if constexpr (HOW == kStateSlot) {
+  if constexpr (HOW != kStateStored) {
     if (!ok) {  // block-uniform
       fail_outputs();
       return;
@@ -853,7 +853,7 @@ __device__ __forceinline__ void draw_block(
       else mass = mode == 0 ? grand : (resid ? 0.0 : grand);
       probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
-    if constexpr (HOW == kStateSlot) {
+    if constexpr (HOW != kStateStored) {
       uint64_t* slot = ready_slot(counters, b);
       st_dev(&slot[0], (uint64_t)0);
       st_dev(&slot[1], (uint64_t)0);
@@ -959,8 +959,8 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
                             counters, withhold != 0);
   } else {
     const RowPass rows{part1, zrow, flags, tag, C1, c};
-    draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2), 1,
-                                      target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
+    draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2),
+                                      1, target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
                                       seed, ctr0, accepted_len, out_tokens, probe, state, rows,
                                       part2, counters, spin_limit);
   }
@@ -1077,7 +1077,6 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   const long R = 2L * k + 1;
   auto* zr = reinterpret_cast<float*>(w + L.zrow);
   const long n_row = (long)B * R * C1;
-  const int G2 = draw_groups(C2, 1);
   if (mode.sched != SPEC_SCHED_TWO_LAUNCH) {
     auto* fl = reinterpret_cast<uint64_t*>(w + L.flag);
     // Early positions: as many as the first round of resident work-groups
@@ -1087,6 +1086,7 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
     const int E = (int)std::max(1L, std::min((long)k + 1, slots / per_pos));
     const long n_early_rows = E > k ? n_row : (long)E * per_pos;
     const int n_fin = (B + kWaves - 1) / kWaves;
+    const int G2 = draw_groups(C2, 1);
     // Early exit needs no probe values beyond each request's stop.
     const bool exit_early = mode.sched == SPEC_SCHED_EARLY_EXIT && probe == nullptr;
     // A captured launch is replayed as it is recorded, so its tag comes from
@@ -1107,6 +1107,7 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
                              dim3(kThreads), 0, s, target, draft, k, V, C1, c, draft_tokens,
                              uniforms, seed, ctr0, probe, p1, zr, st, cnt);
   if (e != hipSuccess) return e;
+  const int G2 = draw_groups(C2, 1);
   return launch_timed(kProfDraw, &k_draw<DT, NE, 0>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
                       target, draft, k, V, C2, 1, inv_t, draft_tokens, uniforms, seed, ctr0,
                       accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);

@@ -80,49 +80,96 @@ __device__ __forceinline__ float group_sum(float& m, float& mc, double& s, const
   return g;
 }
 
-// Fold kUnrollStats words (one per group) into (m, mc, s): group sums are
-// taken in order (a group may move the reference, which rescales s and
-// every later group), then added pairwise and once to s.
-template <int DT>
-__device__ __forceinline__ void stat_words(float& m, float& mc, double& s, const u32x4 (&w)[kUnrollStats],
-                                           float c) {
+// Sum of the terms 2^(x c - mc) of U words, pairwise in float32.  Every
+// term is below 2^64 exactly when the sum is (all terms are >= 0), so
+// `ok` records whether the reference was good enough for this batch.
+template <int DT, int U>
+__device__ __forceinline__ float batch_terms(const u32x4 (&w)[U], float c, float mc, bool& ok) {
   constexpr int NE = Elems<DT>::kVec;
-  float gs[kUnrollStats];
-  float mc0 = mc;
+  float gs[U];
 #pragma unroll
-  for (int u = 0; u < kUnrollStats; ++u) {
+  for (int u = 0; u < U; ++u) {
     float x[NE];
     unpack16<DT>(w[u], x);
-    gs[u] = group_sum<NE>(m, mc, s, x, c);
-    if (mc != mc0) {  // rare: the reference moved; rescale the earlier groups
-      const float f = (mc0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc0 - mc);
-#pragma unroll
-      for (int v = 0; v < u; ++v) gs[v] *= f;
-      mc0 = mc;
-    }
+    gs[u] = batch_sum<NE>(x, c, mc);
   }
 #pragma unroll
-  for (int w2 = 1; w2 < kUnrollStats; w2 *= 2)
+  for (int w2 = 1; w2 < U; w2 *= 2)
 #pragma unroll
-    for (int e = 0; e + w2 < kUnrollStats; e += 2 * w2) gs[e] += gs[e + w2];
-  s += (double)gs[0];
+    for (int e = 0; e + w2 < U; e += 2 * w2) gs[e] += gs[e + w2];
+  ok = ok && gs[0] < kBatchLimit;  // false for inf / NaN too
+  return gs[0];
 }
 
-// Groups (16-byte words) [g0, g1) of one row shared by NT threads; this
-// thread (index tid) takes every NT-th word.  Software pipelined: the next
-// iteration's kUnrollStats loads are issued before the current words are
-// folded in, so every wave keeps loads in flight while it computes.
-template <int DT, int NT, bool WATCH = false>
+// Largest element of U words.
+template <int DT, int U>
+__device__ __forceinline__ float batch_max(const u32x4 (&w)[U]) {
+  constexpr int NE = Elems<DT>::kVec;
+  float lm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float x[NE];
+    unpack16<DT>(w[u], x);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) lm = fmaxf(lm, x[e]);
+  }
+  return lm;
+}
+
+// Fold a batch of U words, kUnrollStats at a time: a scheduling barrier
+// between the parts keeps the compiler from unpacking the whole batch at
+// once.  No branch: a batch whose sum is not below kBatchLimit (a value far
+// above the reference, or no finite reference yet) only clears `ok`, and
+// the caller recomputes the statistic.
+template <int DT, int U>
+__device__ __forceinline__ void stat_batch(double& s, const u32x4 (&w)[U], float c, float mc,
+                                           bool& ok) {
+  if constexpr (U <= kUnrollStats) {
+    s += (double)batch_terms<DT, U>(w, c, mc, ok);
+  } else {
+    static_assert(U % kUnrollStats == 0, "batch of whole parts");
+#pragma unroll
+    for (int p = 0; p < U / kUnrollStats; ++p) {
+      s += (double)batch_terms<DT, kUnrollStats>(
+          *reinterpret_cast<const u32x4(*)[kUnrollStats]>(&w[p * kUnrollStats]), c, mc, ok);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Bit pattern of a 16-byte word of -inf elements (terms of 0).
+template <int DT>
+__device__ __forceinline__ u32x4 neg_inf_word() {
+  const uint32_t v = DT == 1 ? 0xff80ff80u : 0xff800000u;
+  return u32x4{v, v, v, v};
+}
+
+// Groups (16-byte words) [g0, g1) of one row shared by NT threads.  Batch i
+// gives this thread (index tid) the groups g0 + i NT U + u NT + tid, u < U.
+// The batch count is uniform, so the loop is too; the last batch may be
+// partial: its groups at or past g1 count as -inf (loads past the row's end
+// read zeros and never reach memory).  Software pipelined over two word
+// buffers used in turn: the next batch's U loads are issued before the
+// current batch is folded in, so every wave keeps loads in flight while it
+// computes.
+// The reference m is the largest element of the thread's first batch, and
+// every later batch is summed against it without a branch.  If a batch sum
+// reaches kBatchLimit (an element more than 64/c above m, or nothing finite
+// in the first batch), the thread's statistic is recomputed after the loop
+// from memory with the lazy reference of group_sum: rare, and kept out of
+// the streaming loop, whose speed it would otherwise cost.
+template <int DT, int NT, bool WATCH = false, int U = kUnrollStats>
 __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, long g0, long g1,
                                             float c, float& m, float& mc, double& s, int tid,
                                             const uint64_t* watch = nullptr, int pos = 0,
                                             bool precheck = false) {
   constexpr int NE = Elems<DT>::kVec;
-  constexpr uint32_t kStep = NT * kUnrollStats * 16u;
+  constexpr uint32_t kStep = NT * U * 16u;
   const RowBuf buf(rp, row_bytes);
-  long g = g0 + tid;
-  uint32_t off = static_cast<uint32_t>(g) * 16u;
-  const long span = (long)(kUnrollStats - 1) * NT;
+  const uint32_t off0 = static_cast<uint32_t>(g0 + tid) * 16u;
+  const long n = g1 - g0;
+  const int nb = static_cast<int>((n + (long)NT * U - 1) / ((long)NT * U));  // uniform
+  const bool partial = n % ((long)NT * U) != 0;  // the last batch is partial
   // WATCH: the request's ready slot is read once per pair of batches; each
   // read is used after the next batch's sums, whose data it precedes, so it
   // never stalls the stream.  Once it shows the request stopped before
@@ -133,12 +180,26 @@ __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, 
   uint64_t wv = 0;
   if constexpr (WATCH) wv = ld_dev(watch);
   auto stopped = [&]() { return wv != 0 && (int)(uint32_t)wv - 1 < pos; };
-  if (g + span < g1) {
+  auto load = [&](u32x4 (&w)[U], int i) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = buf.load_nt(off0 + (uint32_t)i * kStep, u * NT * 16u);
+  };
+  // Groups of batch i at or past g1 (only in a partial last batch) become -inf.
+  auto mask = [&](u32x4 (&w)[U], int i) {
+    if (partial && i == nb - 1) {  // uniform
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (g0 + (long)i * NT * U + (long)u * NT + tid >= g1) w[u] = neg_inf_word<DT>();
+    }
+  };
+  bool ok = true;
+  double acc = 0.0;
+  float lmc = -INFINITY;
+  if (nb > 0) {
     // Two word buffers used in turn (no register copies, which would wait
     // for the loads in flight).
-    u32x4 wa[kUnrollStats], wb[kUnrollStats];
-#pragma unroll
-    for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
+    u32x4 wa[U], wb[U];
+    load(wa, 0);
     if constexpr (WATCH) {
       if (precheck) {  // wave-uniform
         if (stopped()) {
@@ -149,17 +210,21 @@ __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, 
         wv = ld_dev(watch);
       }
     }
-    for (;;) {
-      g += (long)NT * kUnrollStats;
-      off += kStep;
-      if (!(g + span < g1)) {
-        stat_words<DT>(m, mc, s, wa, c);
-        break;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnrollStats; ++u) wb[u] = buf.load_nt(off, u * NT * 16u);
+    if (nb > 1) load(wb, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mask(wa, 0);
+    const float lm = batch_max<DT, U>(wa);
+    lmc = mul_rn(lm, c);
+    stat_batch<DT, U>(acc, wa, c, lmc, ok);
+    if (lm == -INFINITY) ok = false;  // nothing finite yet: recompute
+    if (!ok) lmc = -INFINITY;
+    m = lm;
+    int i = 2;
+    for (; i < nb; i += 2) {
+      load(wa, i);
       __builtin_amdgcn_sched_barrier(0);
-      stat_words<DT>(m, mc, s, wa, c);
+      mask(wb, i - 1);
+      stat_batch<DT, U>(acc, wb, c, lmc, ok);
       if constexpr (WATCH) {
         if (stopped()) {  // wave-uniform: one address
           m = INFINITY;
@@ -168,24 +233,34 @@ __device__ __forceinline__ void stats_sweep(const void* rp, uint32_t row_bytes, 
         }
         wv = ld_dev(watch);
       }
-      g += (long)NT * kUnrollStats;
-      off += kStep;
-      if (!(g + span < g1)) {
-        stat_words<DT>(m, mc, s, wb, c);
-        break;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnrollStats; ++u) wa[u] = buf.load_nt(off, u * NT * 16u);
+      if (i + 1 < nb) load(wb, i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      stat_words<DT>(m, mc, s, wb, c);
+      mask(wa, i);
+      stat_batch<DT, U>(acc, wa, c, lmc, ok);
+    }
+    if (i == nb) {  // batch nb - 1 is in wb
+      mask(wb, nb - 1);
+      stat_batch<DT, U>(acc, wb, c, lmc, ok);
     }
   }
-  for (; g < g1; g += NT, off += NT * 16u) {
-    float x[NE];
-    unpack16<DT>(buf.load_nt(off, 0), x);
-    const float gsum = group_sum<NE>(m, mc, s, x, c);  // may rescale s first
-    s += (double)gsum;
+  if (__ballot(!ok) != 0) {  // rare: recompute this thread's groups from memory
+    if (!ok) {
+      float rm = -INFINITY, rmc = -INFINITY;
+      double rs = 0.0;
+      for (long g = g0 + tid; g < g1; g += NT) {
+        float x[NE];
+        unpack16<DT>(buf.load_nt(static_cast<uint32_t>(g) * 16u, 0), x);
+        const float gsum = group_sum<NE>(rm, rmc, rs, x, c);  // may rescale rs first
+        rs += (double)gsum;
+      }
+      m = rm;
+      lmc = rmc;
+      acc = rs;
+    }
   }
+  // Fold into the caller's (m, mc, s) (empty on entry).
+  mc = lmc;
+  s = acc;
 }
 
 // Scalar form for rows that are not 16-byte aligned: elements [e0, e1).
