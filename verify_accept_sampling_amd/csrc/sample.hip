@@ -895,17 +895,22 @@ __global__ __launch_bounds__(kThreads) void k_draw(
 //      work-groups streams);
 //   2. the finalizer work-groups, one request per wave, which test each
 //      request's early positions as their rows complete;
-//   3. for each request b in turn: the row-pass work-groups of b's positions
-//      E .. k, then b's draw work-groups.
+//   3. for each request b in turn but the last n_tail: the row-pass
+//      work-groups of b's positions E .. k, then b's draw work-groups;
+//   4. the draw work-groups of the last n_tail requests, then their rows of
+//      positions E .. k.
 // Most requests stop at one of their early positions, so their states are
 // ready about when the first round of row-pass work-groups ends, and their
-// draws run while the rows of later positions and requests stream.  A
-// request the finalizers leave undecided is finished by its first draw
-// work-group, whose remaining rows precede it.  Work-groups are dispatched
-// in index order and every wait is for work earlier in the grid (a
-// finalizer for early rows, a first draw work-group for its finalizer and
-// its request's rows, the other draw work-groups for the request's state),
-// so every wait ends.  EXIT: row-pass work-groups after position 0 stop
+// draws run while the rows of later positions and requests stream; the
+// grid ends with rows that no draw waits for (4.).  A request the
+// finalizers leave undecided is finished by its first draw work-group from
+// its remaining rows.  Work-groups are dispatched in index order.  Every
+// wait in 1.-3. is for work earlier in the grid (a finalizer for early
+// rows, a first draw work-group for its finalizer and its request's rows,
+// the other draw work-groups for the request's state); in 4. a draw
+// work-group may wait for rows after it, but those draw work-groups are at
+// most half of the resident ones, so the other half keep taking the rows
+// and every wait ends.  EXIT: row-pass work-groups after position 0 stop
 // once their request is decided before their position.
 // tag: this call's completion tag, or 0 to derive it from the workspace's
 // call epoch (graph-captured calls; k_advance_epoch follows the kernel).
@@ -920,7 +925,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
     float* __restrict__ probe, uint64_t* __restrict__ part1, float* __restrict__ zrow,
     uint64_t* __restrict__ flags, uint64_t tag, ReqState* __restrict__ state,
     DrawPart* __restrict__ part2, unsigned* __restrict__ counters, int E, long n_early_rows,
-    int n_fin, long spin_limit, int withhold) {
+    int n_fin, long spin_limit, int withhold, int n_tail) {
   const long bid = blockIdx.x;
   if (tag == 0) tag = epoch_tag(ld_dev(epoch_word(counters)));
   const int G2 = draw_groups(C2, 1);
@@ -937,11 +942,28 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
     return;
   } else {
     // Request b's rows of positions E .. k (target and draft row of each
-    // position, then the bonus row), then its draw work-groups.
+    // position, then the bonus row), then its draw work-groups; for the last
+    // n_tail requests, all their draw work-groups first, then all their
+    // later rows, so that the grid ends with rows nobody waits for.
     const long L = E > k ? 0 : (2L * (k - E) + 1) * C1;
     const long j = bid - n_early_rows - n_fin;
-    const int b = static_cast<int>(j / (L + G2));
-    const long o = j % (L + G2);
+    const int Bh = B - n_tail;
+    int b;
+    long o;
+    if (j < (long)Bh * (L + G2)) {
+      b = static_cast<int>(j / (L + G2));
+      o = j % (L + G2);
+    } else {
+      const long j2 = j - (long)Bh * (L + G2);
+      if (j2 < (long)n_tail * G2) {
+        b = Bh + static_cast<int>(j2 / G2);
+        o = L + j2 % G2;
+      } else {
+        const long j3 = j2 - (long)n_tail * G2;
+        b = Bh + static_cast<int>(j3 / (L > 0 ? L : 1));
+        o = j3 % (L > 0 ? L : 1);
+      }
+    }
     if (o >= L) {
       draw = (long)b * G2 + (o - L);
     } else {
@@ -998,7 +1020,25 @@ static int row_chunks(int V) { return (V + kRowChunkElems - 1) / kRowChunkElems;
 // first round of row-pass work-groups (compute units x this) sets how many
 // positions are early.  Measured at B = 64, k = 8, V = 128256 bf16: six per
 // unit needs the kernel held to 80 VGPRs, which spills, and is slower.
-constexpr int kOneLaunchGroupsPerCU = 5;
+#ifndef SPEC_ONE_LAUNCH_GROUPS_PER_CU
+#define SPEC_ONE_LAUNCH_GROUPS_PER_CU 5
+#endif
+constexpr int kOneLaunchGroupsPerCU = SPEC_ONE_LAUNCH_GROUPS_PER_CU;
+
+// Requests at the end of the one-launch grid whose draws precede their
+// later rows (at most this many), and the share of resident work-groups
+// their draws may take (1 / kTailDrawSlotFraction).  Measured at B = 64,
+// k = 8, V = 128256 bf16 (one-launch kernel): 0, 4, 8, 15, 20, 30 such
+// requests gave 63.8, 63.6, 62.9, 62.1, 61.7 and 61.4 us; 45 and 64 (more
+// than half the resident work-groups) 63.5 and 65.5 us.
+#ifndef SPEC_TAIL_REQUESTS
+#define SPEC_TAIL_REQUESTS 65536
+#endif
+constexpr int kTailRequests = SPEC_TAIL_REQUESTS;
+#ifndef SPEC_TAIL_DRAW_SLOT_FRACTION
+#define SPEC_TAIL_DRAW_SLOT_FRACTION 2
+#endif
+constexpr long kTailDrawSlotFraction = SPEC_TAIL_DRAW_SLOT_FRACTION;
 
 // Compute units of the current device.
 static int device_cus() {
@@ -1087,6 +1127,15 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
     const long n_early_rows = E > k ? n_row : (long)E * per_pos;
     const int n_fin = (B + kWaves - 1) / kWaves;
     const int G2 = draw_groups(C2, 1);
+    // The last n_tail requests' draw work-groups precede their later rows.
+    // Such a draw work-group may wait for rows after it in the grid (a
+    // request its finalizer left undecided), so their number stays within
+    // 1 / kTailDrawSlotFraction of the resident work-groups: the rest keep
+    // taking those rows, and every wait ends.
+    const int n_tail =
+        E > k ? 0
+              : (int)std::min((long)std::min(B, kTailRequests),
+                              slots / kTailDrawSlotFraction / std::max(1, G2));
     // Early exit needs no probe values beyond each request's stop.
     const bool exit_early = mode.sched == SPEC_SCHED_EARLY_EXIT && probe == nullptr;
     // A captured launch is replayed as it is recorded, so its tag comes from
@@ -1098,7 +1147,7 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
         dim3((unsigned)(n_row + n_fin + (long)B * G2)), dim3(kThreads), one_launch_lds<DT, NE>(0),
         s, target, draft, B, k, V, C1, C2, c, inv_t, draft_tokens, uniforms, seed, ctr0,
         accepted_len, out_tokens, probe, p1, zr, fl, tag, st, p2, cnt, E, n_early_rows, n_fin,
-        spin, mode.test_give_up ? 1 : 0);
+        spin, mode.test_give_up ? 1 : 0, n_tail);
     if (e != hipSuccess || !mode.capturing) return e;
     hipLaunchKernelGGL(k_advance_epoch, dim3(1), dim3(kWaveSize), 0, s, cnt);
     return hipGetLastError();
