@@ -130,30 +130,122 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, p
     print(json.dumps(out))
 
 
-def cpu_baseline(wl, budget_s: float):
-    """The float64 oracle, as it stands, on the same workload: request after
-    request (repeating the batch with fresh uniforms) until the time budget
-    is spent, on one host thread."""
+# ---------------------------------------------------------------------------
+# cpu_baseline leg: the float64 oracle on the timed steps' own inputs
+# ---------------------------------------------------------------------------
+#
+# Step i of the timed GPU pass verifies the workload with the uniforms at
+# counter0 = i * B * (k+1) * 2.  The oracle legs run the same steps (their
+# requests one by one, as the oracle stands), so their outputs double as the
+# correctness gate of the GPU pass.  They run before anything touches the GPU
+# (the all-cores leg forks a process pool).
+
+_LEG = {}  # the workload, shared with forked workers (copy-on-write)
+
+
+def _oracle_request(step: int, b: int):
+    """Oracle outputs of request b at timed step `step`, with what the gate
+    needs to classify a disagreement: (accepted, tokens, accept margins by
+    position, draw margin)."""
     import oracle.rng as R
     import oracle.verify as O
 
+    wl, n_u = _LEG["wl"], _LEG["n_u"]
+    u = R.uniforms(wl.uniform_seed, step * n_u + b * (wl.k + 1) * 2, (wl.k + 1) * 2)
+    r = O.verify_sample_request(wl.target[b], wl.draft[b] if wl.k > 0 else None,
+                                wl.draft_tokens[b], u.reshape(wl.k + 1, 2), wl.temperature,
+                                wl.kind, wl.dtype)
+    acc_m = {d.position: d.margin for d in r.decisions if d.kind == "accept"}
+    draw_m = [d.margin for d in r.decisions if d.kind == "resample"][0]
+    return r.accepted, list(r.tokens), acc_m, draw_m
+
+
+def _oracle_steps(steps, budget_s: float, t0=None):
+    """Whole steps (every request) in order until the budget is spent."""
+    t0 = time.perf_counter() if t0 is None else t0
+    out = {}
+    wl = _LEG["wl"]
+    for st in steps:
+        if time.perf_counter() - t0 >= budget_s:
+            break
+        out[st] = [_oracle_request(st, b) for b in range(wl.B)]
+    return out
+
+
+def _pool_worker(args):
+    steps, budget_s = args
+    return _oracle_steps(steps, budget_s)
+
+
+def oracle_legs(wl, first_step: int, n_steps: int, budget_s: float, label: str):
+    """(1-core leg, all-cores leg, oracle outputs by step).  Each leg runs
+    whole timed steps for about budget_s seconds."""
+    import multiprocessing as mp
+
+    _LEG["wl"] = wl
+    _LEG["n_u"] = wl.B * (wl.k + 1) * 2
+    steps = list(range(first_step, first_step + n_steps))
+    print(f"bench: cpu baseline, 1 core ({budget_s:.0f} s)", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    done = 0
-    rep = 0
-    while time.perf_counter() - t0 < budget_s:
-        u = R.chain_uniforms(wl.uniform_seed, wl.B, wl.k, rep * wl.B * (wl.k + 1) * 2)
-        for b in range(wl.B):
-            O.verify_sample(wl.target, wl.draft, wl.draft_tokens, u, wl.temperature, wl.kind,
-                            wl.dtype, requests=[b])
-            done += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        rep += 1
-    dt = time.perf_counter() - t0
-    return {"value": done * (wl.k + 1) / dt, "unit": "verified positions/s", "cores": 1,
+    res1 = _oracle_steps(steps, budget_s, t0)
+    dt1 = time.perf_counter() - t0
+    pos1 = len(res1) * wl.B * (wl.k + 1)
+    one = {"value": pos1 / dt1, "unit": "verified positions/s", "cores": 1, "kind": "oracle",
+           "sample": f"{len(res1)} timed steps ({len(res1) * wl.B} requests) of the {label} "
+                     f"workload, {dt1:.1f} s on 1 host thread"}
+    cores = min(16, len(os.sched_getaffinity(0)))
+    # the steps the 1-core leg did not reach first, then the others again
+    rest = steps[len(res1):] + steps[:len(res1)]
+    print(f"bench: cpu baseline, {cores} processes ({budget_s:.0f} s)", file=sys.stderr,
+          flush=True)
+    chunks = [(rest[w::cores], budget_s) for w in range(cores)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        parts = pool.map(_pool_worker, chunks)
+    dtn = time.perf_counter() - t0
+    resn = {}
+    for p_ in parts:
+        resn.update(p_)
+    posn = len(resn) * wl.B * (wl.k + 1)
+    allc = {"value": posn / dtn, "unit": "verified positions/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{done} requests of the B=64, k=8, V=128256 bf16 workload "
-                      f"(batch repeated with fresh uniforms), {dt:.1f} s on 1 host thread"}
+            "sample": f"{len(resn)} timed steps ({len(resn) * wl.B} requests) of the {label} "
+                      f"workload, {dtn:.1f} s in {cores} processes (one request at a time "
+                      f"each)"}
+    res = dict(res1)
+    res.update(resn)
+    return one, allc, res
+
+
+FLAG_BAND = 1e-5
+
+
+def correctness_gate(acc_steps, out_steps, first_step: int, oracle_res):
+    """Compare the GPU outputs of the timed steps the oracle legs covered.
+    A disagreement is allowed only when its first differing decision (the
+    acceptance test at the earlier stop, else the draw) lies within 1e-5 of
+    its boundary in the oracle."""
+    g = dict(steps=0, requests=0, decisions=0, accept_decisions=0, draw_decisions=0, flagged=0,
+             mismatches=0, unflagged=0)
+    for st, reqs in sorted(oracle_res.items()):
+        i = st - first_step
+        g["steps"] += 1
+        for b, (n_o, toks_o, acc_m, draw_m) in enumerate(reqs):
+            g["requests"] += 1
+            g["accept_decisions"] += len(acc_m)
+            g["draw_decisions"] += 1
+            g["flagged"] += sum(1 for m in acc_m.values() if m < FLAG_BAND)
+            g["flagged"] += int(draw_m < FLAG_BAND)
+            n_g = int(acc_steps[i, b])
+            toks_g = [int(t) for t in out_steps[i, b, : n_g + 1]] if 0 <= n_g else []
+            if n_g == n_o and toks_g == toks_o:
+                continue
+            g["mismatches"] += 1
+            m = acc_m.get(min(n_g, n_o), 0.0) if n_g != n_o else draw_m
+            if not (0 <= n_g and m < FLAG_BAND):
+                g["unflagged"] += 1
+    g["decisions"] = g["accept_decisions"] + g["draw_decisions"]
+    return g
 
 
 # Extra workloads (not the headline line): greedy chain and tree greedy.
@@ -393,11 +485,15 @@ def main():
                     help="host only: turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) "
                          "into the row-statistics traffic file")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
-    ap.add_argument("--workload", choices=["sample", "probs", "serving"] + sorted(GREEDY_WORKLOADS),
+    ap.add_argument("--no-early-exit", action="store_true",
+                    help="skip the extra early-exit pass on the timed steps' inputs")
+    ap.add_argument("--workload",
+                    choices=sorted(SAMPLE_WORKLOADS) + ["probs", "serving"]
+                    + sorted(GREEDY_WORKLOADS),
                     default="sample",
-                    help="sample (default): the headline sampling workload; probs: sampling on "
-                         "probability rows (B=512); the others print a line for a greedy "
-                         "kernel")
+                    help="sample (default): the headline sampling workload; sample_v32000: "
+                         "B=8 k=4 V=32000; probs: sampling on probability rows (B=512); the "
+                         "others print a line for a greedy or serving kernel")
     ap.add_argument("--path", choices=sorted(KERNELS), default="auto",
                     help="auto: the one-launch kernel; two_launch: row pass, then draw; "
                          "early_exit: the one-launch kernel that stops reading rows past each "
@@ -421,36 +517,77 @@ def main():
     if args.workload == "serving":
         bench_serving(args)
         return
-    if args.workload != "sample":
+    if args.workload not in SAMPLE_WORKLOADS:
         bench_greedy(args)
         return
+    bench_sample(args)
 
+
+# Sampling workloads with a bench line: name -> (generator, label, traffic file suffix)
+SAMPLE_WORKLOADS = {
+    "sample": ("sample_chain_llama3", "B=64 k=8 V=128256 bf16 T=0.7",
+               "sample_chain_b64_k8_v128256_bf16_t0.7"),
+    "sample_v32000": ("sample_chain_v32000", "B=8 k=4 V=32000 bf16 T=1",
+                      "sample_chain_b8_k4_v32000_bf16_t1"),
+}
+
+
+def _pct(xs, q):
     import numpy as np
+
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q)) if len(xs) else None
+
+
+def bench_sample(args):
+    """The sampling chain line (headline or the V=32000 workload)."""
+    import numpy as np
+
+    import workloads as W
+
+    gen, label, wname = SAMPLE_WORKLOADS[args.workload]
+    headline = args.workload == "sample"
+    print(f"bench: generating {label} workload", file=sys.stderr, flush=True)
+    wl = getattr(W, gen)()
+    B, k, V = wl.B, wl.k, wl.V
+    n_u = B * (k + 1) * 2
+    first = args.warmup  # counter base of the first timed step
+
+    # CPU legs first: the all-cores leg forks, which must happen before any
+    # GPU use in this process.
+    legs = None
+    if not args.no_cpu_baseline:
+        legs = oracle_legs(wl, first, args.steps, args.cpu_seconds, label)
+
     import torch
 
     import verify_accept_sampling_amd as S
-    import workloads as W
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    schedule = {"auto": "one_launch"}.get(args.path, args.path)
-    print("bench: generating B=64 k=8 V=128256 bf16 workload", file=sys.stderr, flush=True)
-    wl = W.sample_chain_llama3()
-    B, k, V = wl.B, wl.k, wl.V
 
     def dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     tgt0, dft0 = dev_bf16(wl.target), dev_bf16(wl.draft)
-    copies = [(tgt0, dft0)] + [(tgt0.clone(), dft0.clone()) for _ in range(args.copies - 1)]
+    # Enough input copies that the rotation's footprint exceeds the 256 MB
+    # Infinity Cache (one copy of the headline workload is 279 MB).
+    step_in_bytes = (wl.target.nbytes + wl.draft.nbytes)
+    n_copies = args.copies if headline else max(args.copies, -(-(600 << 20) // step_in_bytes))
+    copies = [(tgt0, dft0)] + [(tgt0.clone(), dft0.clone()) for _ in range(n_copies - 1)]
     toks = torch.from_numpy(wl.draft_tokens).to(dev)
     ws = S.Workspace(dev)
-    n_u = B * (k + 1) * 2
+    schedule = {"auto": "one_launch"}.get(args.path, args.path)
+    # Preallocated outputs: one pair per timed step (kept for the gate), one
+    # scratch pair for warmup and profiling passes.
+    acc_all = torch.empty((args.steps, B), dtype=torch.int32, device=dev)
+    out_all = torch.empty((args.steps, B, k + 1), dtype=torch.int32, device=dev)
+    scratch = (torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B, k + 1), dtype=torch.int32, device=dev))
 
-    def step(i):
+    def run(i, out, sched=schedule):
         t, d = copies[i % len(copies)]
-        return S.spec_verify_sample(t, d, toks, wl.temperature, seed=wl.uniform_seed,
-                                    counter0=i * n_u, workspace=ws, schedule=schedule)
+        S.spec_verify_sample(t, d, toks, wl.temperature, seed=wl.uniform_seed,
+                             counter0=i * n_u, workspace=ws, schedule=sched, out=out)
 
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib * 1024 * 1024
@@ -465,47 +602,71 @@ def main():
 
     print(f"bench: warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        step(i)
+        run(i, scratch)
     torch.cuda.synchronize()
 
-    accs = []
-    ms_step = timed_steps(step, args.warmup, args.steps, profile=False, keep=accs)
-    timed_steps(step, args.warmup + args.steps, args.steps, profile=True)
-    kern = {}
-    for name in ("fused", "row_pass", "draw"):
-        n, ms = S.spec_profile_read(name)
-        if n:
-            kern[name] = {"launches": n, "avg_us": ms / n * 1e3}
+    # 1. the timed pass: K steps between two events, outputs kept
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for j in range(args.steps):
+        run(first + j, (acc_all[j], out_all[j]))
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
     print(f"bench: timed {args.steps} steps, {ms_step * 1e3:.1f} us/step", file=sys.stderr,
           flush=True)
 
-    acc_all = torch.stack(accs).cpu().numpy()
+    # 2. step-time spread: an event between consecutive steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for j in range(args.steps):
+        run(first + j, scratch)
+        evs[j + 1].record()
+    torch.cuda.synchronize()
+    step_ms = [evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps)]
+
+    # 3. kernel durations: dispatch-stamped events around every launch
+    def profiled(sched):
+        S.spec_profile_enable(True)
+        for j in range(args.steps):
+            run(first + j, scratch, sched)
+        torch.cuda.synchronize()
+        S.spec_profile_enable(False)
+        return {kind: S.spec_profile_durations(kind) for kind in ("fused", "row_pass", "draw")}
+
+    durs = profiled(schedule)
+    kern = {n: {"launches": len(v), "avg_us": sum(v) / len(v) * 1e3,
+                "p10_us": _pct(v, 10) * 1e3, "p50_us": _pct(v, 50) * 1e3,
+                "p90_us": _pct(v, 90) * 1e3} for n, v in durs.items() if v}
+
+    acc_np = acc_all.cpu().numpy()
+    out_np = out_all.cpu().numpy()
     row_bytes = V * 2
     pass1_bytes = B * (2 * k + 1) * row_bytes
-    assert pass1_bytes == ALGO_ROW_BYTES
     # rows the final token is drawn from: target and draft row n after a
     # rejection, target row k for the bonus; each read once more, plus the
     # searched chunk of each
-    drawn_rows = (acc_all < k).sum(axis=1) + B
+    drawn_rows = (acc_np < k).sum(axis=1) + B
     draw_bytes = drawn_rows * row_bytes + drawn_rows * min(V, DRAW_CHUNK) * 2
-    if args.path == "early_exit":
-        # Bytes each call must read: per request the target rows 0..n and
-        # the draft rows 0..min(n, k-1) (a request's outputs depend on
-        # nothing else), plus the draw's re-read.
-        need_rows = (np.minimum(acc_all + 1, k + 1) + np.minimum(acc_all + 1, k)).sum(axis=1)
-        step_bytes = float(np.mean(need_rows * row_bytes + draw_bytes))
+    # bytes each call must read: per request the target rows 0..n and the
+    # draft rows 0..min(n, k-1) (a request's outputs depend on nothing else),
+    # plus the draw's re-read
+    need_rows = (np.minimum(acc_np + 1, k + 1) + np.minimum(acc_np + 1, k)).sum(axis=1)
+    must_bytes = float(np.mean(need_rows * row_bytes + draw_bytes))
+    full_bytes = float(np.mean(pass1_bytes + draw_bytes))
+    if args.path == "two_launch":
+        dom_name, dom, dom_bytes = "row_pass", kern["row_pass"], float(pass1_bytes)
     else:
-        step_bytes = float(np.mean(pass1_bytes + draw_bytes))
-    kernel = KERNELS[args.path]
-    if args.path in ("auto", "early_exit"):
-        dom, dom_bytes = kern["fused"]["avg_us"], step_bytes
-    else:
-        dom, dom_bytes = kern["row_pass"]["avg_us"], float(pass1_bytes)
-    achieved = dom_bytes / (dom * 1e-6) / 1e9
-    traffic = measured_traffic(args.path)
+        dom_name = "fused"
+        dom = kern["fused"]
+        dom_bytes = must_bytes if args.path == "early_exit" else full_bytes
+    achieved = dom_bytes / (dom["avg_us"] * 1e-6) / 1e9
+    traffic = measured_traffic(args.path) if headline else None
     positions = B * (k + 1)
     result = {
-        "metric": METRIC,
+        "metric": METRIC if headline else f"verified positions/sec ({label})",
         "value": positions / (ms_step * 1e-3),
         "unit": "verified positions/s",
         "n_gpus": 1,
@@ -517,26 +678,71 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "sample_chain_b64_k8_v128256_bf16_t0.7", "B": B, "k": k, "V": V,
+        "config": {"workload": wname, "B": B, "k": k, "V": V,
                    "logits": "bf16", "temperature": wl.temperature, "input_copies": len(copies),
                    "draw_arithmetic": "f64", "path": args.path},
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": KERNELS[args.path], "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes},
-        "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "kernel_us": {"avg": dom["avg_us"], "p10": dom["p10_us"], "p50": dom["p50_us"],
+                      "p90": dom["p90_us"], "launches": dom["launches"]},
+        "step_us": {"p10": _pct(step_ms, 10) * 1e3, "p50": _pct(step_ms, 50) * 1e3,
+                    "p90": _pct(step_ms, 90) * 1e3},
+        "step_hbm_gbps": (must_bytes if args.path == "early_exit" else full_bytes)
+        / (ms_step * 1e-3) / 1e9,
         "bytes_basis": ("must-read rows up to each request's first rejection + draw re-read"
                         if args.path == "early_exit" else "every logit row once + draw re-read"),
-        "step_algorithmic_bytes": step_bytes,
         "kernels_avg_us": {n: v["avg_us"] for n, v in kern.items()},
-        "mean_accepted": float(acc_all.mean()),
-        "mean_emitted": float(acc_all.mean() + 1),
+        "mean_accepted": float(acc_np.mean()),
+        "mean_emitted": float(acc_np.mean() + 1),
     }
-    if not args.no_cpu_baseline:
-        print(f"bench: cpu baseline ({args.cpu_seconds:.0f} s budget)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+
+    # 4. the early-exit schedule on the same steps (outputs must be identical)
+    if args.path != "early_exit" and not args.no_early_exit:
+        acc_e = torch.empty_like(acc_all)
+        out_e = torch.empty_like(out_all)
+        torch.cuda.synchronize()
+        ev0.record()
+        for j in range(args.steps):
+            run(first + j, (acc_e[j], out_e[j]), "early_exit")
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_e = ev0.elapsed_time(ev1) / args.steps
+        de = profiled("early_exit")["fused"]
+        us_e = sum(de) / len(de) * 1e3
+        result["early_exit"] = {
+            "value": positions / (ms_e * 1e-3), "ms_per_step": ms_e,
+            "kernel_avg_us": us_e, "kernel_p10_us": _pct(de, 10) * 1e3,
+            "kernel_p90_us": _pct(de, 90) * 1e3,
+            "must_read_bytes_per_launch": must_bytes,
+            "achieved_gbps_over_must_read": must_bytes / (us_e * 1e-6) / 1e9,
+            "frac_over_must_read": must_bytes / (us_e * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+            "outputs_identical": bool(torch.equal(acc_e, acc_all) and torch.equal(out_e, out_all)),
+        }
+
+    status = S.spec_workspace_status(ws)
+    result["workspace_status"] = status
+    gate = None
+    if legs is not None:
+        one, allc, res = legs
+        result["cpu_baseline"] = allc
+        result["cpu_baseline_1core"] = one
+        gate = correctness_gate(acc_np, out_np, first, res)
+        result["correctness_gate"] = gate
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    bad = []
+    if status != 0:
+        bad.append(f"workspace status {status}")
+    if gate is not None and gate["unflagged"]:
+        bad.append(f"{gate['unflagged']} requests disagree with the oracle away from any "
+                   "decision boundary")
+    if "early_exit" in result and not result["early_exit"]["outputs_identical"]:
+        bad.append("early-exit outputs differ from the full sweep's")
+    if bad:
+        print("bench: FAILED: " + "; ".join(bad), file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 if __name__ == "__main__":
