@@ -81,7 +81,8 @@ enum {
   SPEC_EDTYPE = -2,     /* unsupported dtype / kind combination */
   SPEC_EWORKSPACE = -3, /* workspace null or smaller than required */
   SPEC_EHIP = -4,       /* a HIP launch failed */
-  SPEC_ETREE = -5       /* parent array is not a tree in BFS-compatible order */
+  SPEC_ETREE = -5,      /* parent array is not a tree in BFS-compatible order */
+  SPEC_ESCRATCH = -6    /* shape needs more than SPEC_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Human-readable text for a return code (static storage). */
@@ -201,6 +202,28 @@ int spec_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status_host
  * words and status word; the call epoch is kept), so a workspace whose
  * status is nonzero can be used again. */
 int spec_workspace_reset(void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * spec_verify_sample without a workspace argument.  It allocates nothing:
+ * its scratch (counters, row statistics, per-request state, draw partials)
+ * is a static device array of SPEC_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends.  A shape whose
+ * spec_workspace_bytes(B, k+1, V) exceeds that size returns SPEC_ESCRATCH
+ * and enqueues nothing.  `stream` must belong to the current device (else
+ * SPEC_EINVAL).  Each call first clears, with a kernel on `stream`, the
+ * counters its requests use and the status word, so a call whose bounded
+ * wait gave up (its outputs are -1) leaves nothing behind for the next.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and may give wrong
+ * outputs.  Arguments, outputs and the other return codes are those of
+ * spec_verify_sample. */
+#define SPEC_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int spec_verify_sample_noalloc(const void* target, const void* draft, int dtype, int kind,
+                               int B, int k, int V, const int32_t* draft_tokens,
+                               const float* uniforms, uint64_t seed, uint64_t counter0,
+                               float temperature, int flags, int32_t* accepted_len,
+                               int32_t* out_tokens, float* probe, void* stream);
 
 /* Greedy tree verification (EAGLE-3 review, section on the full inference
  * loop: tree attention gives the target's distribution after every node, and

@@ -10,6 +10,7 @@ is missing or a call fails, an exception is raised.
     spec_fill_uniforms(seed, counter0, n, out=None)
     spec_verify_greedy(target, draft_tokens)
     spec_verify_sample(target, draft, draft_tokens, temperature, ...)
+    spec_verify_sample_noalloc(target, draft, draft_tokens, temperature, ...)
     spec_verify_tree_greedy(target, parent, node_tokens)
     spec_tree_depth(parent)
     spec_workspace_status(workspace), spec_workspace_reset(workspace)
@@ -27,7 +28,7 @@ import torch
 __all__ = [
     "SpecVerifyError", "Workspace", "library_path", "load_library", "declared_symbols",
     "spec_workspace_bytes", "spec_fill_uniforms", "spec_verify_greedy",
-    "spec_verify_sample", "spec_verify_tree_greedy", "spec_tree_depth", "spec_strerror",
+    "spec_verify_sample", "spec_verify_sample_noalloc", "spec_verify_tree_greedy", "spec_tree_depth", "spec_strerror",
     "spec_profile_enable", "spec_profile_read", "spec_profile_durations", "KERNEL_KINDS",
     "SCHEDULES",
     "spec_rejected_mask", "spec_tree_rejected_mask", "spec_tree_from_choices",
@@ -43,6 +44,8 @@ SPEC_LOGITS, SPEC_PROBS = 0, 1
 SCHEDULES = {"auto": 0, "one_launch": 1, "two_launch": 2, "early_exit": 3}
 SPEC_FLAG_TEST_GIVE_UP = 0x100
 STATUS_WAIT_GAVE_UP = 1
+SPEC_ESCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # SPEC_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -90,6 +93,9 @@ def load_library():
     lib.spec_verify_sample.argtypes = [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp, c_u64,
                                        c_u64, c_f, c_int, vp, vp, vp, vp, c_size, vp]
     lib.spec_verify_sample.restype = c_int
+    lib.spec_verify_sample_noalloc.argtypes = [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp,
+                                               c_u64, c_u64, c_f, c_int, vp, vp, vp, vp]
+    lib.spec_verify_sample_noalloc.restype = c_int
     lib.spec_verify_tree_greedy.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                             vp, c_size, vp]
     lib.spec_verify_tree_greedy.restype = c_int
@@ -297,23 +303,9 @@ def _out_arg(t, shape, dtype, dev, name):
     return t
 
 
-def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
-                       draft_tokens: torch.Tensor, temperature: float = 1.0,
-                       uniforms: Optional[torch.Tensor] = None, seed: int = 0,
-                       counter0: int = 0, kind: str = "logits", probe: bool = False,
-                       workspace: Optional[Workspace] = None, schedule: str = "auto",
-                       out=None, test_give_up: bool = False):
-    """Sampling chain verification with min(1, p/q) acceptance.
-
-    target [B, k+1, V], draft [B, k, V] (f32/bf16 logits, or f32 probabilities
-    with kind="probs"), draft_tokens int32 [B, k], uniforms float32
-    [B, k+1, 2] or None (then derived from seed/counter0 inside the kernels).
-    schedule: "auto", "one_launch", "two_launch" or "early_exit" (identical
-    outputs).  out: optional preallocated (accepted_len, out_tokens[, probe])
-    tensors, written in place and returned.  test_give_up: test only (see
-    SPEC_FLAG_TEST_GIVE_UP in the C header).
-    Returns (accepted_len, out_tokens) or, with probe=True,
-    (accepted_len, out_tokens, probe [B, k+1, 4])."""
+def _sample_args(target, draft, draft_tokens, uniforms, kind, schedule, out, probe,
+                 test_give_up):
+    """Checks and marshalling shared by both sampling entry points."""
     _need_cuda(target, "target")
     B, kp1, V = target.shape
     k = kp1 - 1
@@ -336,14 +328,60 @@ def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
     tok = _out_arg(outs[1], (B, kp1), torch.int32, dev, "out_tokens")
     pr = (_out_arg(outs[2] if len(outs) > 2 else None, (B, kp1, 4), torch.float32, dev, "probe")
           if probe else None)
+    return B, k, V, dev, kind_code, flags, acc, tok, pr
+
+
+def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
+                       draft_tokens: torch.Tensor, temperature: float = 1.0,
+                       uniforms: Optional[torch.Tensor] = None, seed: int = 0,
+                       counter0: int = 0, kind: str = "logits", probe: bool = False,
+                       workspace: Optional[Workspace] = None, schedule: str = "auto",
+                       out=None, test_give_up: bool = False):
+    """Sampling chain verification with min(1, p/q) acceptance.
+
+    target [B, k+1, V], draft [B, k, V] (f32/bf16 logits, or f32 probabilities
+    with kind="probs"), draft_tokens int32 [B, k], uniforms float32
+    [B, k+1, 2] or None (then derived from seed/counter0 inside the kernels).
+    schedule: "auto", "one_launch", "two_launch" or "early_exit" (identical
+    outputs).  out: optional preallocated (accepted_len, out_tokens[, probe])
+    tensors, written in place and returned.  test_give_up: test only (see
+    SPEC_FLAG_TEST_GIVE_UP in the C header).
+    Returns (accepted_len, out_tokens) or, with probe=True,
+    (accepted_len, out_tokens, probe [B, k+1, 4])."""
+    B, k, V, dev, kind_code, flags, acc, tok, pr = _sample_args(
+        target, draft, draft_tokens, uniforms, kind, schedule, out, probe, test_give_up)
     lib = load_library()
-    nbytes = spec_workspace_bytes(B, kp1, V)
+    nbytes = spec_workspace_bytes(B, k + 1, V)
     ws = _workspace(workspace, dev, nbytes)
     _check(lib.spec_verify_sample(
         _ptr(target), _ptr(draft if k > 0 else None), _dtype_code(target), kind_code, B, k, V,
         _ptr(draft_tokens if k > 0 else None), _ptr(uniforms),
         int(seed) & (2 ** 64 - 1), int(counter0) & (2 ** 64 - 1), float(temperature), flags,
         _ptr(acc), _ptr(tok), _ptr(pr), _ptr(ws), ws.numel(), _stream(dev)))
+    if probe:
+        return acc, tok, pr
+    return acc, tok
+
+
+def spec_verify_sample_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor],
+                               draft_tokens: torch.Tensor, temperature: float = 1.0,
+                               uniforms: Optional[torch.Tensor] = None, seed: int = 0,
+                               counter0: int = 0, kind: str = "logits", probe: bool = False,
+                               schedule: str = "auto", out=None, test_give_up: bool = False):
+    """spec_verify_sample on the library's static per-GPU scratch array (no
+    workspace; the C call allocates nothing; pass `out` to allocate nothing
+    here either).  Calls that overlap on one GPU race.  Raises
+    SpecVerifyError (SPEC_ESCRATCH) for shapes beyond NOALLOC_SCRATCH_BYTES."""
+    B, k, V, dev, kind_code, flags, acc, tok, pr = _sample_args(
+        target, draft, draft_tokens, uniforms, kind, schedule, out, probe, test_give_up)
+    lib = load_library()
+    if dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError("spec_verify_sample_noalloc: the inputs must be on the current device")
+    _check(lib.spec_verify_sample_noalloc(
+        _ptr(target), _ptr(draft if k > 0 else None), _dtype_code(target), kind_code, B, k, V,
+        _ptr(draft_tokens if k > 0 else None), _ptr(uniforms),
+        int(seed) & (2 ** 64 - 1), int(counter0) & (2 ** 64 - 1), float(temperature), flags,
+        _ptr(acc), _ptr(tok), _ptr(pr), _stream(dev)))
     if probe:
         return acc, tok, pr
     return acc, tok

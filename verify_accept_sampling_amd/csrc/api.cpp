@@ -74,6 +74,9 @@ const char* spec_strerror(int code) {
     case SPEC_EWORKSPACE: return "workspace missing or smaller than spec_workspace_bytes()";
     case SPEC_EHIP: return "HIP launch failed";
     case SPEC_ETREE: return "parent array is not a tree with parent[0] = -1 and parent[j] < j";
+    case SPEC_ESCRATCH:
+      return "shape needs more scratch than the no-alloc entry point's static array "
+             "(SPEC_NOALLOC_SCRATCH_BYTES); use spec_verify_sample with a workspace";
     default: return "unknown error code";
   }
 }
@@ -114,11 +117,16 @@ int spec_verify_greedy(const void* target, int dtype, int B, int k, int V,
   return SPEC_OK;
 }
 
-int spec_verify_sample(const void* target, const void* draft, int dtype, int kind, int B, int k,
-                       int V, const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
-                       uint64_t counter0, float temperature, int flags, int32_t* accepted_len,
-                       int32_t* out_tokens, float* probe, void* ws, size_t ws_bytes,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both sampling entry points; on success *mode and *L are
+// filled in for the launch.
+int check_sample(const void* target, const void* draft, int dtype, int kind, int B, int k,
+                 int V, const int32_t* draft_tokens, float temperature, int flags,
+                 int32_t* accepted_len, int32_t* out_tokens, void* stream, SampleMode* mode,
+                 WsLayout* L) {
   if (!valid_dtype(dtype) || (kind != SPEC_LOGITS && kind != SPEC_PROBS)) return SPEC_EDTYPE;
   if ((flags & ~(0xF | SPEC_FLAG_TEST_GIVE_UP)) != 0 || (flags & 0xF) > SPEC_SCHED_EARLY_EXIT)
     return SPEC_EINVAL;
@@ -140,20 +148,64 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
   if (check_grid((long)B * (2L * k + 1) * row_chunks_for(V) + finalizers + draws) != SPEC_OK)
     return SPEC_EINVAL;
   if (check_grid((long)B * C2) != SPEC_OK) return SPEC_EINVAL;
-  WsLayout L;
-  if (int rc = check_workspace(ws, ws_bytes, B, k + 1, V, &L)) return rc;
-  SampleMode mode;
-  mode.sched = (flags & 0xF) == SPEC_SCHED_AUTO ? SPEC_SCHED_ONE_LAUNCH : (flags & 0xF);
-  mode.test_give_up = (flags & SPEC_FLAG_TEST_GIVE_UP) != 0;
-  mode.capturing = false;
+  *L = ws_layout(B, k + 1, V);
+  mode->sched = (flags & 0xF) == SPEC_SCHED_AUTO ? SPEC_SCHED_ONE_LAUNCH : (flags & 0xF);
+  mode->test_give_up = (flags & SPEC_FLAG_TEST_GIVE_UP) != 0;
+  mode->capturing = false;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) == hipSuccess)
-    mode.capturing = cs == hipStreamCaptureStatusActive;
+    mode->capturing = cs == hipStreamCaptureStatusActive;
   else
     (void)hipGetLastError();  // not capturing; leave no error for the launch check
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_sample(const void* target, const void* draft, int dtype, int kind, int B, int k,
+                       int V, const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
+                       uint64_t counter0, float temperature, int flags, int32_t* accepted_len,
+                       int32_t* out_tokens, float* probe, void* ws, size_t ws_bytes,
+                       void* stream) {
+  SampleMode mode;
+  WsLayout L;
+  if (int rc = check_sample(target, draft, dtype, kind, B, k, V, draft_tokens, temperature,
+                            flags, accepted_len, out_tokens, stream, &mode, &L))
+    return rc;
+  if (B == 0) return SPEC_OK;
+  if (ws == nullptr || ws_bytes < L.total) return SPEC_EWORKSPACE;
   if (launch_sample(target, draft, dtype, kind, B, k, V, draft_tokens, uniforms, seed, counter0,
                     temperature, mode, accepted_len, out_tokens, probe, ws, L,
                     static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPEC_EHIP;
+  return SPEC_OK;
+}
+
+int spec_verify_sample_noalloc(const void* target, const void* draft, int dtype, int kind,
+                               int B, int k, int V, const int32_t* draft_tokens,
+                               const float* uniforms, uint64_t seed, uint64_t counter0,
+                               float temperature, int flags, int32_t* accepted_len,
+                               int32_t* out_tokens, float* probe, void* stream) {
+  SampleMode mode;
+  WsLayout L;
+  if (int rc = check_sample(target, draft, dtype, kind, B, k, V, draft_tokens, temperature,
+                            flags, accepted_len, out_tokens, stream, &mode, &L))
+    return rc;
+  if (B == 0) return SPEC_OK;
+  if (L.total > kNoAllocScratchBytes) return SPEC_ESCRATCH;
+  const auto s = static_cast<hipStream_t>(stream);
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || hipStreamGetDevice(s, &sdev) != hipSuccess)
+    return SPEC_EHIP;
+  if (sdev != dev) return SPEC_EINVAL;
+  void* scratch_ptr = nullptr;
+  if (noalloc_scratch(dev, &scratch_ptr) != hipSuccess) return SPEC_EHIP;
+  if (launch_clear_requests(scratch_ptr, B, s) != hipSuccess) return SPEC_EHIP;
+  if (launch_sample(target, draft, dtype, kind, B, k, V, draft_tokens, uniforms, seed, counter0,
+                    temperature, mode, accepted_len, out_tokens, probe, scratch_ptr, L, s) !=
+      hipSuccess)
     return SPEC_EHIP;
   return SPEC_OK;
 }

@@ -245,4 +245,12 @@ hipError_t launch_sample(const void* target, const void* draft, int dtype, int k
 // Zeroes the counter region of a workspace except its call epoch.
 hipError_t launch_reset_counters(void* ws, hipStream_t s);
 
+// Device address of the no-alloc scratch array on `device`, which must be
+// the current device (looked up once per device, then cached).
+constexpr size_t kNoAllocScratchBytes = SPEC_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(int device, void** ptr);
+// Zeroes the counter words of requests 0..B-1 and the status word of a
+// workspace (the call epoch is kept).
+hipError_t launch_clear_requests(void* ws, int B, hipStream_t s);
+
 }  // namespace specv

@@ -34,6 +34,7 @@
 // work-group first repeating the (gather-only) acceptance tests.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "sample_device.h"
 
@@ -1006,6 +1007,57 @@ __global__ __launch_bounds__(kThreads) void k_reset_counters(unsigned* __restric
 hipError_t launch_reset_counters(void* ws, hipStream_t s) {
   hipLaunchKernelGGL(k_reset_counters, dim3(256), dim3(kThreads), 0, s,
                      static_cast<unsigned*>(ws));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-alloc entry point
+// ---------------------------------------------------------------------------
+//
+// A file-scope device array: each GPU the library runs on holds its own
+// copy, at its own address, until the process ends.  In host code the name
+// is a stand-in, not a device address, so host code only ever uses the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+hipError_t noalloc_scratch(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 256 != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
+// The words a call over requests 0..B-1 uses: each request's own eight
+// (tickets) and the eight at its hand-over position (verdict, ready slot),
+// plus the status word.  A kernel, not a memset, so the clear can sit in a
+// captured graph.
+__global__ __launch_bounds__(kThreads) void k_clear_requests(unsigned* __restrict__ counters,
+                                                             int B) {
+  const long i = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (i < (long)B * kCountersPerReq) {
+    const int b = static_cast<int>(i / kCountersPerReq);
+    const int j = static_cast<int>(i % kCountersPerReq);
+    counters[(long)b * kCountersPerReq + j] = 0u;
+    counters[handover_pos(b) + j] = 0u;
+  }
+  if (i == 0) counters[kStatusWord] = 0u;
+}
+
+hipError_t launch_clear_requests(void* ws, int B, hipStream_t s) {
+  const long n = std::max(1L, (long)B * kCountersPerReq);
+  hipLaunchKernelGGL(k_clear_requests, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, static_cast<unsigned*>(ws), B);
   return hipGetLastError();
 }
 
