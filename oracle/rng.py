@@ -79,3 +79,11 @@ def chain_uniforms(seed: int, B: int, k: int, counter0: int = 0) -> np.ndarray:
     ((b * (k+1)) + i) * 2 + slot, offset by counter0.
     """
     return uniforms(seed, counter0, B * (k + 1) * 2).reshape(B, k + 1, 2)
+
+
+def tree_uniforms(seed: int, B: int, N: int, counter0: int = 0) -> np.ndarray:
+    """Uniforms for a tree call, shape [B, N, 2]: slot 0 of node j decides
+    node j's test, slot 1 drives the draw if the request stops at node j.
+    Flat counter ((b * N) + j) * 2 + slot, offset by counter0 (the chain
+    layout with k + 1 = N)."""
+    return uniforms(seed, counter0, B * N * 2).reshape(B, N, 2)

@@ -427,3 +427,114 @@ def verify_tree_greedy(target: np.ndarray, parent: np.ndarray,
         path[b, : len(r.path)] = r.path
         results.append(r)
     return acc, out, path, results
+
+
+# ---------------------------------------------------------------------------
+# Tree sampling
+# ---------------------------------------------------------------------------
+#
+# The EAGLE-3 review (section on the full inference loop, step 4 "Strict
+# Acceptance") says only that sampling over the tree applies the min(1, p/q)
+# test with residual correction so that the target distribution is kept.
+# The order over siblings is not on the pages; the reading taken is
+# SpecInfer's multi-step speculative sampling (Miao et al., ASPLOS 2024):
+# at the current node the children are tried in increasing node index, each
+# with the test u < p(x)/q(x) against the current target distribution p;
+# after a rejection p becomes normalise(max(0, p - q)) (q, the draft's
+# distribution at the node, is the one every child there was drawn from);
+# the first accepted child becomes the current node, with p reset to the
+# target's distribution there; when no child is accepted (or the node has
+# none) one token is drawn from the current p by inverse CDF.
+
+
+def _children(parent) -> list:
+    N = len(parent)
+    kids = [[] for _ in range(N)]
+    for j in range(1, N):
+        kids[int(parent[j])].append(j)
+    return kids
+
+
+def verify_tree_sample_request(target: np.ndarray, draft: np.ndarray, parent,
+                               node_tokens: np.ndarray, u: np.ndarray,
+                               temperature: float, kind: str, dtype: str) -> RequestResult:
+    """One request.  target [N, V] and draft [N, V] raw rows (row j: the
+    target's / the draft's distribution after node j's prefix; node j's
+    children were drawn from draft row j), parent [N] (parent[0] = -1,
+    parent[j] < j), node_tokens [N] (entry 0 unused), u [N, 2]: u[j, 0]
+    decides node j's test, u[j, 1] drives the draw if the request stops at
+    node j.
+
+    Decisions: "accept" (node j: margin |u - p(x)/q(x)|), "residual" (after
+    each rejection: margin = the mass of max(0, p - q), outcome 1 if p was
+    replaced, 0 if that mass is zero and p is kept), "resample" (the draw at
+    the stop node)."""
+    V = target.shape[1]
+    kids = _children(parent)
+
+    def dist(rows, j):
+        row = decode(rows[j], dtype)
+        if kind == "logits":
+            return tempered_softmax(row, temperature)
+        return row  # probabilities, used as given
+
+    decisions = []
+    path = [0]
+    cur = 0
+    while True:
+        p = dist(target, cur)
+        q = dist(draft, cur) if kids[cur] else None
+        nxt = None
+        for c in kids[cur]:
+            x = int(node_tokens[c])
+            if 0 <= x < V:
+                px, qx = float(p[x]), float(q[x])
+                accept = u[c, 0] * qx < px
+                ratio = px / qx if qx > 0.0 else math.inf
+                margin = abs(float(u[c, 0]) - ratio)
+            else:
+                accept, margin = False, math.inf
+            decisions.append(Decision("accept", c, margin, int(accept)))
+            if accept:
+                nxt = c
+                break
+            w = np.maximum(0.0, p - q)
+            mass = float(np.sum(w))
+            if mass > 0.0:
+                p = w / mass
+            decisions.append(Decision("residual", c, mass, int(mass > 0.0)))
+        if nxt is None:
+            t, m2, total = inverse_cdf(p, float(u[cur, 1]))
+            decisions.append(Decision("resample", cur, m2, t))
+            toks = [int(node_tokens[j]) for j in path[1:]] + [t]
+            return RequestResult(len(path) - 1, toks, decisions, residual_mass=total, path=path)
+        path.append(nxt)
+        cur = nxt
+
+
+def verify_tree_sample(target: np.ndarray, draft: np.ndarray, parent, node_tokens: np.ndarray,
+                       uniforms: np.ndarray, temperature: float, kind: str, dtype: str,
+                       requests=None):
+    """Batch tree sampling verification.
+
+    target [B, N, V], draft [B, N, V], parent [N], node_tokens [B, N],
+    uniforms [B, N, 2].  Returns (accepted_len [B], out_tokens [B, D+1],
+    out_path [B, D+1], results dict b -> result), D the tree depth; rows of
+    requests outside `requests` stay -1."""
+    B, N, _ = target.shape
+    depth = np.zeros(N, dtype=np.int64)
+    for j in range(1, N):
+        depth[j] = depth[parent[j]] + 1
+    D = int(depth.max()) if N else 0
+    acc = np.full(B, -1, dtype=np.int32)
+    out = np.full((B, D + 1), -1, dtype=np.int32)
+    path = np.full((B, D + 1), -1, dtype=np.int32)
+    results = {}
+    for b in (range(B) if requests is None else requests):
+        r = verify_tree_sample_request(target[b], draft[b], parent, node_tokens[b], uniforms[b],
+                                       temperature, kind, dtype)
+        acc[b] = r.accepted
+        out[b, : len(r.tokens)] = r.tokens
+        path[b, : len(r.path)] = r.path
+        results[b] = r
+    return acc, out, path, results
