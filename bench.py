@@ -403,6 +403,185 @@ def bench_serving(args):
     print(json.dumps(result), flush=True)
 
 
+def _tree_oracle_steps(args_tuple):
+    """Oracle outputs of whole timed steps of the tree workload (shared
+    through _LEG) until the budget is spent."""
+    steps, budget_s = args_tuple
+    import oracle.rng as R
+    import oracle.verify as O
+
+    wl = _LEG["wl"]
+    t0 = time.perf_counter()
+    out = {}
+    for st in steps:
+        if time.perf_counter() - t0 >= budget_s:
+            break
+        u = R.tree_uniforms(wl.uniform_seed, wl.B, wl.n_nodes, st * wl.B * wl.n_nodes * 2)
+        _, _, _, res = O.verify_tree_sample(wl.target, wl.draft, wl.parent, wl.node_tokens, u,
+                                            wl.temperature, wl.kind, wl.dtype)
+        out[st] = res
+    return out
+
+
+def bench_tree_sample(args):
+    """One JSON line for tree sampling verification: the static tree (1 root
+    + 60 nodes, branching 4, 3, 2, 2, 1) with draft logits, B=16,
+    V=128256, bf16, T=0.7.  Algorithmic bytes of a call: every target row
+    and the draft rows of nodes with children once (the row statistics),
+    both rows of a node once per sibling-rank mass pass, and the stop node's
+    rows drawn from."""
+    import numpy as np
+
+    import workloads as W
+
+    print("bench: generating the tree sampling workload", file=sys.stderr, flush=True)
+    wl = W.tree_sample()
+    B, N, V = wl.B, wl.n_nodes, wl.V
+    first = args.warmup
+    n_u = B * N * 2
+    res_cpu = None
+    one = None
+    if not args.no_cpu_baseline:
+        import multiprocessing as mp
+
+        _LEG["wl"] = wl
+        steps = list(range(first, first + args.steps))
+        print(f"bench: cpu baseline, 1 core ({args.cpu_seconds:.0f} s)", file=sys.stderr,
+              flush=True)
+        t0 = time.perf_counter()
+        res1 = _tree_oracle_steps((steps, args.cpu_seconds))
+        dt1 = time.perf_counter() - t0
+        one = {"value": len(res1) * B / dt1, "unit": "verified requests/s", "cores": 1,
+               "kind": "oracle", "sample": f"{len(res1)} timed steps ({len(res1) * B} requests), "
+                                           f"{dt1:.1f} s on 1 host thread"}
+        cores = min(16, len(os.sched_getaffinity(0)))
+        rest = steps[len(res1):] + steps[:len(res1)]
+        t0 = time.perf_counter()
+        with mp.get_context("fork").Pool(cores) as pool:
+            parts = pool.map(_tree_oracle_steps,
+                             [(rest[w::cores], args.cpu_seconds) for w in range(cores)])
+        dtn = time.perf_counter() - t0
+        res_cpu = dict(res1)
+        n_all = 0
+        for p_ in parts:
+            n_all += len(p_)
+            res_cpu.update(p_)
+        allc = {"value": n_all * B / dtn, "unit": "verified requests/s", "cores": cores,
+                "kind": "oracle", "sample": f"{n_all} timed steps ({n_all * B} requests), "
+                                            f"{dtn:.1f} s in {cores} processes"}
+
+    import torch
+
+    import verify_accept_sampling_amd as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0d, d0d = dev_bf16(wl.target), dev_bf16(wl.draft)
+    n_copies = max(args.copies, 2)  # 0.5 GB per copy
+    copies = [(t0d, d0d)] + [(t0d.clone(), d0d.clone()) for _ in range(n_copies - 1)]
+    toks = torch.from_numpy(wl.node_tokens).to(dev)
+    parent = wl.parent.tolist()
+    ws = S.Workspace(dev)
+    D = int(W.tree_depths(wl.parent).max())
+    acc_all = torch.empty((args.steps, B), dtype=torch.int32, device=dev)
+    out_all = torch.empty((args.steps, B, D + 1), dtype=torch.int32, device=dev)
+    path_all = torch.empty((args.steps, B, D + 1), dtype=torch.int32, device=dev)
+    scratch = (torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+               torch.empty((B, D + 1), dtype=torch.int32, device=dev))
+
+    def run(i, out):
+        t, d = copies[i % len(copies)]
+        S.spec_verify_tree_sample(t, d, parent, toks, wl.temperature, seed=wl.uniform_seed,
+                                  counter0=i * n_u, workspace=ws, out=out)
+
+    for i in range(args.warmup):
+        run(i, scratch)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for j in range(args.steps):
+        run(first + j, (acc_all[j], out_all[j], path_all[j]))
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    S.spec_profile_enable(True)
+    for j in range(args.steps):
+        run(first + j, scratch)
+    torch.cuda.synchronize()
+    S.spec_profile_enable(False)
+    kinds = ("tree_stats", "tree_mass", "tree_walk", "tree_draw")
+    kern = {}
+    for kk in kinds:
+        d = S.spec_profile_durations(kk)
+        if d:
+            kern[kk] = {"launches": len(d), "avg_us": sum(d) / len(d) * 1e3,
+                        "p10_us": _pct(d, 10) * 1e3, "p90_us": _pct(d, 90) * 1e3}
+    # bytes
+    kids = [[] for _ in range(N)]
+    for j in range(1, N):
+        kids[parent[j]].append(j)
+    n_int = sum(1 for k_ in kids if k_)
+    mass_units = sum(max(0, len(k_) - 1) for k_ in kids)
+    row = V * 2
+    stats_bytes = float(B * (N + n_int) * row)
+    acc_np = acc_all.cpu().numpy()
+    path_np = path_all.cpu().numpy()
+    out_np = out_all.cpu().numpy()
+    # draw: the stop node's target row, and its draft row after a rejection
+    drawn = 0
+    for jj in range(args.steps):
+        for b in range(B):
+            s_node = int(path_np[jj, b, acc_np[jj, b]])
+            drawn += 2 if kids[s_node] else 1
+    draw_bytes = drawn / args.steps * row
+    mass_bytes = float(B * mass_units * 2 * row)
+    step_bytes = stats_bytes + mass_bytes + draw_bytes
+    st_us = kern["tree_stats"]["avg_us"]
+    achieved = stats_bytes / (st_us * 1e-6) / 1e9
+    gate = None
+    if res_cpu is not None:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from parity_helpers import compare_tree_sample
+
+        gate = dict(steps=0, requests=0, flagged=0, mismatches=0, unflagged=0)
+        for st, res in sorted(res_cpu.items()):
+            j = st - first
+            g = compare_tree_sample(acc_np[j], out_np[j], path_np[j], res, wl.parent, range(B))
+            gate["steps"] += 1
+            for key in ("requests", "flagged", "mismatches", "unflagged"):
+                gate[key] += g[key]
+    result = {
+        "metric": "verified requests/s (tree sampling, 61-node tree, B=16, V=128256, bf16, T=0.7)",
+        "value": B / (ms_step * 1e-3), "unit": "verified requests/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "tree_sample_b16_n61_v128256_bf16_t0.7", "B": B, "nodes": N,
+                   "V": V, "logits": "bf16", "temperature": wl.temperature,
+                   "input_copies": len(copies), "draw_arithmetic": "f64"},
+        "roofline": {"bound": "hbm", "kernel": "k_tree_stats", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": stats_bytes},
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "kernels": kern,
+        "mean_accepted": float(acc_np.mean()),
+        "cpu_baseline": allc if res_cpu is not None else None,
+        "cpu_baseline_1core": one,
+        "correctness_gate": gate,
+    }
+    print(json.dumps(result), flush=True)
+    if gate is not None and gate["unflagged"]:
+        print("bench: FAILED: tree sampling outputs disagree with the oracle away from any "
+              "decision boundary", file=sys.stderr, flush=True)
+        sys.exit(1)
+
+
 def bench_probs(args):
     """One JSON line for the probability-row workload: B=512, k=8, V=128256
     float32 rows with a prescribed overlap alpha in {0.6, 0.8, 0.9}.  The
@@ -488,7 +667,7 @@ def main():
     ap.add_argument("--no-early-exit", action="store_true",
                     help="skip the extra early-exit pass on the timed steps' inputs")
     ap.add_argument("--workload",
-                    choices=sorted(SAMPLE_WORKLOADS) + ["probs", "serving"]
+                    choices=sorted(SAMPLE_WORKLOADS) + ["probs", "serving", "tree_sample"]
                     + sorted(GREEDY_WORKLOADS),
                     default="sample",
                     help="sample (default): the headline sampling workload; sample_v32000: "
@@ -516,6 +695,9 @@ def main():
         return
     if args.workload == "serving":
         bench_serving(args)
+        return
+    if args.workload == "tree_sample":
+        bench_tree_sample(args)
         return
     if args.workload not in SAMPLE_WORKLOADS:
         bench_greedy(args)

@@ -249,6 +249,44 @@ int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes,
                             int32_t* out_tokens, int32_t* out_path, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* Sampling verification over a draft tree (EAGLE-3 review, section on the
+ * full inference loop, step 4 "Strict Acceptance": over the tree, the
+ * min(1, p/q) test with residual correction, which keeps the target
+ * distribution).  The pages give no rule for several siblings; the one used
+ * is SpecInfer's multi-step speculative sampling (Miao et al., ASPLOS 2024).
+ * Node 0 is the root; node j > 0 has parent parent_host[j] < j and carries
+ * token node_tokens[b, j] (column 0 is ignored).  target[b, j] and
+ * draft[b, j] are the target's and the draft's rows after node j's prefix
+ * (node j's children were drawn from the draft's; draft rows of nodes
+ * without children are not read).  For each request b, with p_j, q_j the
+ * rows' distributions as in spec_verify_sample:
+ *   n := 0 (the root), r := p_0.  For the children c of n in increasing
+ *   index, x = node_tokens[b, c]: c is accepted iff 0 <= x < V and
+ *   u_acc(c) < r(x) / q_n(x) (a zero q_n(x) accepts iff r(x) > 0).  On
+ *   acceptance n := c, r := p_c, and the children of c are tried.  On
+ *   rejection r := normalise(max(0, r - q_n)), unless that is all zero
+ *   (then r stays).  When no child of n is accepted (or n has none), t is
+ *   drawn from r by inverse CDF with u_res(n) (t = min{ j : C_j > u_res *
+ *   C_{V-1} }, C the running sum over ascending token id) and the request
+ *   stops.
+ *   accepted_len[b] = depth(n); out_tokens[b] (int32 [B, D+1], D the tree
+ *   depth) = the tokens of the path's nodes below the root, t, then -1;
+ *   out_path[b] (nullable, int32 [B, D+1]) = node ids root .. n, then -1.
+ * Uniforms: u_acc(c) = u[b, c, 0], u_res(n) = u[b, n, 1], where u is
+ * `uniforms` (device float [B, n_nodes, 2]) or, when NULL, the values
+ * spec_fill_uniforms(seed, counter0, ...) would write to such an array.
+ * dtype, kind and temperature as in spec_verify_sample.  Arithmetic:
+ * float32 row statistics (logits); tests, residual masses and the draw in
+ * float64.  Workspace: spec_workspace_bytes(B, n_nodes, V).  One call
+ * enqueues five kernels (four for SPEC_PROBS) plus one per sibling rank
+ * above 0 that occurs in the tree. */
+int spec_verify_tree_sample(const void* target, const void* draft, int dtype, int kind, int B,
+                            int n_nodes, int V, const int32_t* parent_host,
+                            const int32_t* node_tokens, const float* uniforms, uint64_t seed,
+                            uint64_t counter0, float temperature, int32_t* accepted_len,
+                            int32_t* out_tokens, int32_t* out_path, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* Depth D of the tree described by parent_host (see above), or a negative
  * error code if the array is malformed.  Host only. */
 int spec_tree_depth(const int32_t* parent_host, int n_nodes);
@@ -315,7 +353,11 @@ enum {
   SPEC_KERNEL_DRAW = 1,     /* float64 residual / bonus pass + inverse-CDF draw */
   SPEC_KERNEL_UNIFORMS = 2, /* spec_fill_uniforms */
   SPEC_KERNEL_FUSED = 3,    /* one-launch sampling verification: row pass and draw */
-  SPEC_KERNEL_SERVING = 4   /* rejected-draft masks */
+  SPEC_KERNEL_SERVING = 4,  /* rejected-draft masks */
+  SPEC_KERNEL_TREE_STATS = 5, /* tree sampling: row statistics */
+  SPEC_KERNEL_TREE_MASS = 6,  /* tree sampling: residual-mass rounds */
+  SPEC_KERNEL_TREE_WALK = 7,  /* tree sampling: table setup and the walk */
+  SPEC_KERNEL_TREE_DRAW = 8   /* tree sampling: draw weights and the pick */
 };
 int spec_profile_enable(int on);
 int spec_profile_read(int kind, long* launches, double* total_ms);

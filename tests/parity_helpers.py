@@ -96,3 +96,56 @@ def check_probe(probe_g, wl, acc_g, acc_o, results, requests, detail=None):
     if detail is not None:
         detail.append(where)
     return worst
+
+
+def compare_tree_sample(acc_g, out_g, path_g, results, parent, requests):
+    """Classify tree-sampling disagreements by the first differing decision.
+
+    Where the GPU's and the oracle's paths part, the first child of the
+    parting node that one side accepted and the other rejected decides; the
+    disagreement is flagged when that test, or a residual mass at that node
+    before it, lies within FLAG_BAND of its boundary in the oracle.  Equal
+    paths with different tokens are classified by the draw (and the stop
+    node's residual masses)."""
+    kids = [[] for _ in range(len(parent))]
+    for j in range(1, len(parent)):
+        kids[int(parent[j])].append(j)
+    st = dict(requests=0, accept_decisions=0, draw_decisions=0, flagged=0, mismatches=0,
+              unflagged=0, unflagged_requests=[])
+    for b in requests:
+        r = results[b]
+        st["requests"] += 1
+        st["accept_decisions"] += sum(1 for d in r.decisions if d.kind == "accept")
+        st["draw_decisions"] += 1
+        st["flagged"] += sum(1 for d in r.decisions if d.margin < FLAG_BAND)
+        n_g = int(acc_g[b])
+        pg = [int(v) for v in path_g[b, : n_g + 1]] if n_g >= 0 else []
+        tg = [int(v) for v in out_g[b, : n_g + 1]] if n_g >= 0 else []
+        if n_g == r.accepted and pg == r.path and tg == r.tokens:
+            continue
+        st["mismatches"] += 1
+        if n_g < 0 or not pg or pg[0] != 0:
+            st["unflagged"] += 1
+            st["unflagged_requests"].append((b, "invalid", n_g, None))
+            continue
+        d = 1
+        while d < len(pg) and d < len(r.path) and pg[d] == r.path[d]:
+            d += 1
+        node = r.path[d - 1]
+        at_node = [x for x in r.decisions if x.position in kids[node]]
+        if d == len(pg) and d == len(r.path):  # same stop node: the draw
+            cand = [x for x in r.decisions if x.kind == "resample"]
+            cand += [x for x in at_node if x.kind == "residual"]
+        else:
+            g_child = pg[d] if d < len(pg) else None
+            o_child = r.path[d] if d < len(r.path) else None
+            order = kids[node]
+            idx = [order.index(c) for c in (g_child, o_child) if c is not None]
+            first = order[min(idx)]
+            cand = [x for x in at_node if x.kind == "accept" and x.position == first]
+            cand += [x for x in at_node if x.kind == "residual" and order.index(x.position)
+                     < order.index(first)]
+        if not any(x.margin < FLAG_BAND for x in cand):
+            st["unflagged"] += 1
+            st["unflagged_requests"].append((b, node, pg, r.path))
+    return st

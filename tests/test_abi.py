@@ -123,14 +123,47 @@ def test_tree_rejects_bad_arguments(lib):
     assert f(None, 1, 0, 4, 100, pp, None, None, None, None, None, 0, None) == 0
 
 
+def test_tree_sample_rejects_bad_arguments(lib):
+    f = lib.spec_verify_tree_sample
+    parent = (ctypes.c_int32 * 4)(-1, 0, 0, 1)
+    badp = (ctypes.c_int32 * 4)(-1, 0, 3, 1)
+    ws = S.spec_workspace_bytes(2, 4, 100)
+    pp = ctypes.cast(parent, ctypes.c_void_p)
+
+    def call(target=FAKE, draft=FAKE, dtype=1, kind=0, B=2, N=4, V=100, par=pp, toks=FAKE,
+             T=1.0, acc=FAKE, out=FAKE, w=FAKE, wb=ws):
+        return f(target, draft, dtype, kind, B, N, V, par, toks, None, 1, 0, T, acc, out, None,
+                 w, wb, None)
+
+    assert call(dtype=5) == EDTYPE
+    assert call(kind=1, dtype=1) == EDTYPE  # probability rows are float32
+    assert call(kind=1, dtype=0, T=0.5) == EINVAL  # probabilities take T = 1
+    assert call(T=0.0) == EINVAL
+    assert call(T=float("inf")) == EINVAL
+    assert call(par=ctypes.cast(badp, ctypes.c_void_p)) == ETREE
+    assert call(par=None) == EINVAL
+    assert call(N=0) == EINVAL
+    assert call(N=1025) == EINVAL
+    assert call(target=None) == EINVAL
+    assert call(draft=None) == EINVAL
+    assert call(toks=None) == EINVAL
+    assert call(acc=None) == EINVAL
+    assert call(w=None) == EWORKSPACE
+    assert call(wb=ws - 1) == EWORKSPACE
+    assert call(B=0, target=None, draft=None, toks=None, acc=None, out=None, w=None) == 0
+
+
 def test_fill_uniforms_argument_checks(lib):
     assert lib.spec_fill_uniforms(1, 0, -1, FAKE, None) == EINVAL
     assert lib.spec_fill_uniforms(1, 0, 5, None, None) == EINVAL
     assert lib.spec_fill_uniforms(1, 0, 0, None, None) == 0
 
 
+COUNTER_BYTES = (2097152 + 256)  # SPEC_WORKSPACE_COUNTER_BYTES
+
+
 def test_workspace_status_and_reset_argument_checks(lib):
-    ws = S.spec_workspace_bytes(0, 1, 1)
+    ws = COUNTER_BYTES  # the two calls need the counter region only
     v = ctypes.c_uint32(0)
     assert lib.spec_workspace_status(None, ws, ctypes.byref(v), None) == EINVAL
     assert lib.spec_workspace_status(FAKE, ws, None, None) == EINVAL

@@ -12,6 +12,7 @@ is missing or a call fails, an exception is raised.
     spec_verify_sample(target, draft, draft_tokens, temperature, ...)
     spec_verify_sample_noalloc(target, draft, draft_tokens, temperature, ...)
     spec_verify_tree_greedy(target, parent, node_tokens)
+    spec_verify_tree_sample(target, draft, parent, node_tokens, temperature, ...)
     spec_tree_depth(parent)
     spec_workspace_status(workspace), spec_workspace_reset(workspace)
 """
@@ -28,7 +29,8 @@ import torch
 __all__ = [
     "SpecVerifyError", "Workspace", "library_path", "load_library", "declared_symbols",
     "spec_workspace_bytes", "spec_fill_uniforms", "spec_verify_greedy",
-    "spec_verify_sample", "spec_verify_sample_noalloc", "spec_verify_tree_greedy", "spec_tree_depth", "spec_strerror",
+    "spec_verify_sample", "spec_verify_sample_noalloc", "spec_verify_tree_greedy",
+    "spec_verify_tree_sample", "spec_tree_depth", "spec_strerror",
     "spec_profile_enable", "spec_profile_read", "spec_profile_durations", "KERNEL_KINDS",
     "SCHEDULES",
     "spec_rejected_mask", "spec_tree_rejected_mask", "spec_tree_from_choices",
@@ -99,6 +101,9 @@ def load_library():
     lib.spec_verify_tree_greedy.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, vp,
                                             vp, c_size, vp]
     lib.spec_verify_tree_greedy.restype = c_int
+    lib.spec_verify_tree_sample.argtypes = [vp, vp, c_int, c_int, c_int, c_int, c_int, vp, vp,
+                                            vp, c_u64, c_u64, c_f, vp, vp, vp, vp, c_size, vp]
+    lib.spec_verify_tree_sample.restype = c_int
     lib.spec_profile_enable.argtypes = [c_int]
     lib.spec_profile_enable.restype = c_int
     lib.spec_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_long),
@@ -121,7 +126,8 @@ def load_library():
     return lib
 
 
-KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2, "fused": 3, "serving": 4}
+KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2, "fused": 3, "serving": 4,
+                "tree_stats": 5, "tree_mass": 6, "tree_walk": 7, "tree_draw": 8}
 
 
 def spec_profile_enable(on: bool = True) -> None:
@@ -429,6 +435,56 @@ def spec_verify_tree_greedy(target: torch.Tensor, parent: Sequence[int],
                                        _ptr(acc), _ptr(out), _ptr(path), _ptr(ws), ws.numel(),
                                        _stream(dev)))
     return acc, out, path
+
+
+def spec_verify_tree_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
+                            parent: Sequence[int], node_tokens: torch.Tensor,
+                            temperature: float = 1.0, uniforms: Optional[torch.Tensor] = None,
+                            seed: int = 0, counter0: int = 0, kind: str = "logits",
+                            want_path: bool = True, workspace: Optional[Workspace] = None,
+                            out=None):
+    """Sampling verification over a draft tree (siblings tried in index
+    order, residual carried between them).  target, draft [B, N, V] (draft
+    row j: the distribution node j's children were drawn from), parent (host
+    sequence of N ints), node_tokens int32 [B, N], uniforms float32
+    [B, N, 2] or None (seed/counter0).  out: optional preallocated
+    (accepted_len, out_tokens[, out_path]).  Returns (accepted_len [B],
+    out_tokens [B, D+1], out_path [B, D+1] or None)."""
+    _need_cuda(target, "target")
+    B, N, V = target.shape
+    dev = target.device
+    if N > 1:
+        _need_cuda(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, N, V):
+            raise ValueError("draft must match target's dtype and shape [B, N, V]")
+    _need_cuda(node_tokens, "node_tokens")
+    if node_tokens.dtype != torch.int32 or tuple(node_tokens.shape) != (B, N):
+        raise ValueError("node_tokens must be int32 [B, N]")
+    if uniforms is not None:
+        _need_cuda(uniforms, "uniforms")
+        if uniforms.dtype != torch.float32 or uniforms.numel() != B * N * 2:
+            raise ValueError("uniforms must be float32 [B, N, 2]")
+    arr, n = _parent_array(parent)
+    if n != N:
+        raise ValueError("parent must have one entry per node")
+    lib = load_library()
+    D = int(lib.spec_tree_depth(ctypes.cast(arr, ctypes.c_void_p), n))
+    if D < 0:
+        _check(D)
+    outs = tuple(out) if out is not None else (None, None, None)
+    acc = _out_arg(outs[0], (B,), torch.int32, dev, "accepted_len")
+    tok = _out_arg(outs[1], (B, D + 1), torch.int32, dev, "out_tokens")
+    path = (_out_arg(outs[2] if len(outs) > 2 else None, (B, D + 1), torch.int32, dev,
+                     "out_path") if want_path else None)
+    kind_code = {"logits": SPEC_LOGITS, "probs": SPEC_PROBS}[kind]
+    nbytes = spec_workspace_bytes(B, N, V)
+    ws = _workspace(workspace, dev, nbytes)
+    _check(lib.spec_verify_tree_sample(
+        _ptr(target), _ptr(draft if N > 1 else None), _dtype_code(target), kind_code, B, N, V,
+        ctypes.cast(arr, ctypes.c_void_p), _ptr(node_tokens), _ptr(uniforms),
+        int(seed) & (2 ** 64 - 1), int(counter0) & (2 ** 64 - 1), float(temperature),
+        _ptr(acc), _ptr(tok), _ptr(path), _ptr(ws), ws.numel(), _stream(dev)))
+    return acc, tok, path
 
 
 def _slot_arg(slot_mapping: Optional[torch.Tensor], shape, device) -> Optional[torch.Tensor]:

@@ -256,6 +256,57 @@ int spec_verify_tree_greedy(const void* target, int dtype, int B, int n_nodes, i
   return SPEC_OK;
 }
 
+int spec_verify_tree_sample(const void* target, const void* draft, int dtype, int kind, int B,
+                            int n_nodes, int V, const int32_t* parent_host,
+                            const int32_t* node_tokens, const float* uniforms, uint64_t seed,
+                            uint64_t counter0, float temperature, int32_t* accepted_len,
+                            int32_t* out_tokens, int32_t* out_path, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!valid_dtype(dtype) || (kind != SPEC_LOGITS && kind != SPEC_PROBS)) return SPEC_EDTYPE;
+  if (kind == SPEC_PROBS && dtype != SPEC_F32) return SPEC_EDTYPE;
+  if (B < 0 || B > kMaxB || n_nodes < 1 || n_nodes > kMaxNodes || V < 1 || V > kMaxV)
+    return SPEC_EINVAL;
+  if (kind == SPEC_LOGITS) {
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return SPEC_EINVAL;
+    const float c = 1.4426950408889634f / temperature;
+    if (!std::isfinite(c)) return SPEC_EINVAL;
+  } else if (temperature != 1.f) {
+    return SPEC_EINVAL;
+  }
+  const int D = tree_depth_checked(parent_host, n_nodes);
+  if (D < 0) return D;
+  if (B == 0) return SPEC_OK;
+  if (target == nullptr || accepted_len == nullptr || out_tokens == nullptr) return SPEC_EINVAL;
+  if (n_nodes > 1 && (draft == nullptr || node_tokens == nullptr)) return SPEC_EINVAL;
+  // The same shape k_tree_setup derives on the device.
+  static thread_local TreeShape shape;
+  shape = TreeShape();
+  shape.depth = D;
+  {
+    std::vector<int> nchild(n_nodes, 0);
+    for (int j = 1; j < n_nodes; ++j) {
+      const int r = nchild[parent_host[j]]++;
+      if (r >= 1) ++shape.rank_count[r];
+      if (r > shape.max_rank) shape.max_rank = r;
+    }
+    for (int u = 0; u < n_nodes; ++u) shape.n_internal += nchild[u] > 0;
+  }
+  const long C2 = (V + kDrawChunk - 1) / kDrawChunk;
+  if (check_grid((long)B * (n_nodes + shape.n_internal) * row_chunks_for(V)) != SPEC_OK ||
+      check_grid((long)B * n_nodes * C2) != SPEC_OK)
+    return SPEC_EINVAL;
+  WsLayout L;
+  if (int rc = check_workspace(ws, ws_bytes, B, n_nodes, V, &L)) return rc;
+  TreeArgs tree;
+  std::memset(&tree, 0, sizeof(tree));
+  for (int j = 0; j < n_nodes; ++j) tree.parent[j] = static_cast<int16_t>(parent_host[j]);
+  if (launch_tree_sample(target, draft, dtype, kind, B, n_nodes, V, tree, shape, node_tokens,
+                         uniforms, seed, counter0, temperature, accepted_len, out_tokens,
+                         out_path, ws, L, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPEC_EHIP;
+  return SPEC_OK;
+}
+
 int spec_rejected_mask(const int32_t* accepted_len, int B, int k, uint8_t* rejected,
                        int64_t* slot_mapping, int64_t pad_slot, void* stream) {
   if (B < 0 || B > kMaxB || k < 0 || k > kMaxK) return SPEC_EINVAL;

@@ -124,6 +124,11 @@ static_assert(SPEC_WORKSPACE_STATUS_OFFSET == kStatusWord * 4, "status word offs
 // has a tag of its own, so a tag left by an earlier call (or any other
 // content) is never taken for a current one.  The other regions are written
 // before they are read within each call.
+// Tree-sampling regions: the tree tables (nine int32 tables of kMaxNodes)
+// and the per-request draw state.
+constexpr size_t kTreeTableBytes = 10 * (size_t)kMaxNodes * 4;
+constexpr size_t kTreeDrawBytes = 32;
+
 struct WsLayout {
   size_t count;  // counter region, always at offset 0
   size_t part1;  // uint64 [rows * row_chunks]: packed (max, sum) or (value, index)
@@ -131,6 +136,9 @@ struct WsLayout {
   size_t zrow;   // float [rows]: each row's logit at its draft token
   size_t state;  // ReqState [B]
   size_t part2;  // DrawPart [B * res_chunks]
+  size_t part3;  // double [B * n_pos * res_chunks]: tree sampling's residual masses
+  size_t tree;   // tree tables (kTreeTableBytes)
+  size_t tstate; // tree sampling's draw state, kTreeDrawBytes per request
   size_t total;
 };
 
@@ -157,6 +165,12 @@ inline WsLayout ws_layout(int B, int n_pos, int V) {
   off = align_up(off + (size_t)B * sizeof(ReqState), 256);
   L.part2 = off;
   off = align_up(off + (size_t)B * (size_t)res_chunks(V) * sizeof(DrawPart), 256);
+  L.part3 = off;
+  off = align_up(off + (size_t)B * (size_t)n_pos * (size_t)res_chunks(V) * 8, 256);
+  L.tree = off;
+  off = align_up(off + kTreeTableBytes, 256);
+  L.tstate = off;
+  off = align_up(off + (size_t)B * kTreeDrawBytes, 256);
   L.total = off;
   return L;
 }
@@ -178,7 +192,11 @@ constexpr int kProfDraw = 1;      // float64 residual / bonus pass + inverse-CDF
 constexpr int kProfUniforms = 2;  // spec_fill_uniforms
 constexpr int kProfFused = 3;     // one-launch sampling verification (row pass + draw)
 constexpr int kProfServing = 4;   // rejected-draft masks
-constexpr int kProfKinds = 5;
+constexpr int kProfTreeStats = 5; // tree sampling: row statistics
+constexpr int kProfTreeMass = 6;  // tree sampling: residual-mass rounds
+constexpr int kProfTreeWalk = 7;  // tree sampling: table setup and the walk
+constexpr int kProfTreeDraw = 8;  // tree sampling: draw weights and the pick
+constexpr int kProfKinds = 9;
 // While timing is enabled, prof_begin hands out a start/stop event pair that
 // the launch itself stamps (hipExtLaunchKernel records them from the
 // kernel's dispatch, so the interval is the kernel alone); otherwise both
@@ -225,6 +243,23 @@ hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int 
 hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
                               int V, const TreeArgs& tree, int depth,
                               const int32_t* node_tokens, int32_t* accepted_len,
+                              int32_t* out_tokens, int32_t* out_path, void* ws,
+                              const WsLayout& L, hipStream_t s);
+
+// Host-side shape of a tree, the same as the tables k_tree_setup writes:
+// depth, nodes with a child, the highest sibling rank and how many
+// children have each rank.
+struct TreeShape {
+  int depth = 0;
+  int n_internal = 0;
+  int max_rank = 0;
+  int rank_count[kMaxNodes] = {0};
+};
+
+hipError_t launch_tree_sample(const void* target, const void* draft, int dtype, int kind, int B,
+                              int N, int V, const TreeArgs& tree, const TreeShape& shape,
+                              const int32_t* node_tokens, const float* uniforms, uint64_t seed,
+                              uint64_t counter0, float temperature, int32_t* accepted_len,
                               int32_t* out_tokens, int32_t* out_path, void* ws,
                               const WsLayout& L, hipStream_t s);
 

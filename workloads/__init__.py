@@ -282,6 +282,76 @@ def tree_greedy(B: int = 16, V: int = 128256, seed: int = 1004,
                         meta=dict(seed=seed, p_match=p_match, std=std))
 
 
+@dataclass
+class TreeSampleWorkload:
+    """Tree sampling inputs.
+
+    target, draft  [B, N, V] logits after every node's prefix (node j's
+                   children were drawn from the draft's row j)
+    parent         [N] int32, parent[0] = -1, parent[j] < j
+    node_tokens    [B, N] int32 (column 0, the root, is ignored)
+    """
+
+    name: str
+    target: np.ndarray
+    draft: np.ndarray
+    parent: np.ndarray
+    node_tokens: np.ndarray
+    kind: str
+    dtype: str
+    temperature: float
+    uniform_seed: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return int(self.target.shape[0])
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.target.shape[1])
+
+    @property
+    def V(self) -> int:
+        return int(self.target.shape[2])
+
+
+def tree_sample(B: int = 16, V: int = 128256, seed: int = 1006, uniform_seed: int = 2006,
+                parent: Optional[np.ndarray] = None, target_std: float = 3.0,
+                noise_std: float = 1.5, temperature: float = 0.7, n_peaks: int = 20,
+                peak_boost: float = 8.0, dtype: str = "bf16") -> TreeSampleWorkload:
+    """The static tree (60 nodes, branching 4, 3, 2, 2, 1 by default) with
+    draft logits: target z ~ N(0, target_std^2) (+peak_boost on n_peaks
+    distinct ids per row), draft y = z + N(0, noise_std^2), both rounded to
+    dtype; every child of node j draws its token independently from
+    softmax(y[b, j] / T) by Gumbel-max."""
+    if parent is None:
+        parent = static_tree_parents()
+    parent = np.asarray(parent, dtype=np.int32)
+    N = len(parent)
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((B, N, V), dtype=np.float32) * np.float32(target_std)
+    if n_peaks > 0:
+        for b in range(B):
+            for j in range(N):
+                ids = rng.choice(V, size=min(n_peaks, V), replace=False)
+                z[b, j, ids] += np.float32(peak_boost)
+    target = f32_to_bf16_bits(z) if dtype == "bf16" else z
+    zt = logits_as_f32(target, dtype)
+    y = zt + rng.standard_normal((B, N, V), dtype=np.float32) * np.float32(noise_std)
+    draft = f32_to_bf16_bits(y) if dtype == "bf16" else y.astype(np.float32)
+    yq = logits_as_f32(draft, dtype)
+    T = float(np.float32(temperature))
+    toks = np.zeros((B, N), dtype=np.int32)
+    for j in range(1, N):
+        toks[:, j] = gumbel_max_draw(rng, yq[:, parent[j], :].astype(np.float64) / T)
+    toks[:, 0] = -7  # root column is ignored by the verifier
+    return TreeSampleWorkload("tree_sample", target, draft, parent, toks, "logits", dtype, T,
+                              uniform_seed, meta=dict(seed=seed, target_std=target_std,
+                                                      noise_std=noise_std, n_peaks=n_peaks,
+                                                      peak_boost=peak_boost))
+
+
 # ---------------------------------------------------------------------------
 # Workload 5: controlled acceptance, fp32 probabilities
 # ---------------------------------------------------------------------------
