@@ -172,7 +172,8 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
  *   position (such rows cannot change any output), so fewer bytes are read.
  *   With probe values asked for, every row is read as with
  *   SPEC_SCHED_ONE_LAUNCH.
- * SPEC_SCHED_AUTO: SPEC_SCHED_ONE_LAUNCH.
+ * SPEC_SCHED_AUTO: SPEC_SCHED_EARLY_EXIT (the fastest; every schedule gives
+ *   the same outputs).
  * Graph capture: on a stream that is being captured (hipStreamIsCapturing),
  * the one-launch schedules take their completion tags from a call epoch in
  * the workspace and add a one-thread kernel that advances it, so every
