@@ -172,8 +172,10 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
  *   position (such rows cannot change any output), so fewer bytes are read.
  *   With probe values asked for, every row is read as with
  *   SPEC_SCHED_ONE_LAUNCH.
- * SPEC_SCHED_AUTO: SPEC_SCHED_EARLY_EXIT (the fastest; every schedule gives
- *   the same outputs).
+ * SPEC_SCHED_AUTO: SPEC_SCHED_EARLY_EXIT when the row pass needs more than
+ *   one round of resident work-groups (B * (2k+1) * ceil(V / 65536) above
+ *   five per compute unit), else SPEC_SCHED_ONE_LAUNCH: the faster of the two
+ *   for the shape (every schedule gives the same outputs).
  * Graph capture: on a stream that is being captured (hipStreamIsCapturing),
  * the one-launch schedules take their completion tags from a call epoch in
  * the workspace and add a one-thread kernel that advances it, so every

@@ -149,9 +149,7 @@ int check_sample(const void* target, const void* draft, int dtype, int kind, int
     return SPEC_EINVAL;
   if (check_grid((long)B * C2) != SPEC_OK) return SPEC_EINVAL;
   *L = ws_layout(B, k + 1, V);
-  // AUTO: the early-exit schedule (with probe values asked for it reads
-  // every row, as the one-launch schedule does).
-  mode->sched = (flags & 0xF) == SPEC_SCHED_AUTO ? SPEC_SCHED_EARLY_EXIT : (flags & 0xF);
+  mode->sched = flags & 0xF;
   mode->test_give_up = (flags & SPEC_FLAG_TEST_GIVE_UP) != 0;
   mode->capturing = false;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;

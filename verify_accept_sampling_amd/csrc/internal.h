@@ -265,7 +265,7 @@ hipError_t launch_tree_sample(const void* target, const void* draft, int dtype, 
 
 // How one sampling call is run (from the call's flags and its stream).
 struct SampleMode {
-  int sched;       // SPEC_SCHED_ONE_LAUNCH, _TWO_LAUNCH or _EARLY_EXIT (never AUTO)
+  int sched;       // a SPEC_SCHED_* value (AUTO is resolved at the launch, from the shape)
   bool capturing;  // the stream is being captured into a graph
   bool test_give_up;  // SPEC_FLAG_TEST_GIVE_UP
 };

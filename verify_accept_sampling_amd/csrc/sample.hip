@@ -38,7 +38,24 @@
 
 #include "sample_device.h"
 
+#ifndef SPEC_GATE_GBPS
+#define SPEC_GATE_GBPS 3300
+#endif
+
 namespace specv {
+
+// Early-exit schedule: the rows of early positions after position 0 first
+// wait about as long as position 0's rows take to stream at this rate (GB/s),
+// so that position 0 has the memory system to itself and most requests are
+// decided before those rows start (a row of a decided request then stops
+// after its first batch).  Measured at B = 64, k = 8, V = 128256 bf16 (mean
+// accepted 0.57): no wait 55.2 us; 2300, 2700, 3000, 3300, 3600, 4000 GB/s
+// 55.9, 54.1, 53.1, 53.0, 53.4, 55.5 us.  Waiting instead for each request's
+// position-0 outcome (polling a progress word the finalizer publishes) gave
+// 54.3-54.7 us: the polls and the extra stores cost more than they save.
+// Workloads whose requests mostly accept position 0 gain nothing from the
+// wait and lose part of the memory system to it for its duration.
+constexpr long kGateGBps = SPEC_GATE_GBPS;
 
 // Statistic of chunk `chunk` (of C1) of row r of request b: the sweep, the
 // block reduction, and thread 0's coherent stores of the (reference, sum)
@@ -424,7 +441,8 @@ __device__ __forceinline__ void row_block(
     const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms, uint64_t seed,
     uint64_t ctr0, float* __restrict__ probe, uint64_t* __restrict__ part,
     float* __restrict__ zrow, uint64_t* __restrict__ flags, uint64_t tag,
-    ReqState* __restrict__ state, unsigned* __restrict__ counters, bool withhold = false) {
+    ReqState* __restrict__ state, unsigned* __restrict__ counters, bool withhold = false,
+    int gate_ticks = 0) {
   const int R = 2 * k + 1;
   int b, r, chunk;
   if (one_launch) {
@@ -434,6 +452,11 @@ __device__ __forceinline__ void row_block(
     b = static_cast<int>(bid / C1 / R);
     r = static_cast<int>(bid / C1 % R);
   }
+  if (EXIT && one_launch && !late && r != 0 && r != k + 1) {  // work-group-uniform
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)gate_ticks)
+      __builtin_amdgcn_s_sleep(8);
+  }
   // Early exit: rows after position 0 stop once the request is decided
   // before their position (no probe values are asked for then).  Rows after
   // the early positions (`late`) look before their second batch: most of
@@ -441,7 +464,8 @@ __device__ __forceinline__ void row_block(
   const bool stored =
       EXIT && (r <= k ? r : r - k - 1) > 0
           ? row_chunk_stat<DT, NE, true>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens,
-                                         part, zrow, ready_slot(counters, b), late)
+                                         part, zrow, ready_slot(counters, b),
+                                         late || gate_ticks > 0)
           : row_chunk_stat<DT, NE>(b, r, chunk, target, draft, k, V, C1, c, draft_tokens, part,
                                    zrow);
   if (one_launch) {
@@ -926,7 +950,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
     float* __restrict__ probe, uint64_t* __restrict__ part1, float* __restrict__ zrow,
     uint64_t* __restrict__ flags, uint64_t tag, ReqState* __restrict__ state,
     DrawPart* __restrict__ part2, unsigned* __restrict__ counters, int E, long n_early_rows,
-    int n_fin, long spin_limit, int withhold, int n_tail) {
+    int n_fin, long spin_limit, int withhold, int n_tail, int gate_ticks) {
   const long bid = blockIdx.x;
   if (tag == 0) tag = epoch_tag(ld_dev(epoch_word(counters)));
   const int G2 = draw_groups(C2, 1);
@@ -979,7 +1003,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
   if (row >= 0) {
     row_block<DT, NE, EXIT>(row, true, late, B, target, draft, k, V, C1, c, draft_tokens,
                             uniforms, seed, ctr0, probe, part1, zrow, flags, tag, state,
-                            counters, withhold != 0);
+                            counters, withhold != 0, gate_ticks);
   } else {
     const RowPass rows{part1, zrow, flags, tag, C1, c};
     draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2),
@@ -1175,8 +1199,16 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
     // streams (at least one).
     const long per_pos = (long)B * 2 * C1;
     const long slots = (long)device_cus() * kOneLaunchGroupsPerCU;
+    // AUTO: early exit when the row pass takes more than one round of
+    // resident work-groups (then rows started after the first decisions can
+    // be skipped); with fewer rows every row is in flight from the start and
+    // the one-launch schedule is faster (B = 8, k = 4, V = 32000 bf16: 22.1
+    // us against 24.0 us with early exit).
+    const int sched = mode.sched != SPEC_SCHED_AUTO ? mode.sched
+                      : n_row > slots              ? SPEC_SCHED_EARLY_EXIT
+                                                   : SPEC_SCHED_ONE_LAUNCH;
     // Early exit needs no probe values beyond each request's stop.
-    const bool exit_early = mode.sched == SPEC_SCHED_EARLY_EXIT && probe == nullptr;
+    const bool exit_early = sched == SPEC_SCHED_EARLY_EXIT && probe == nullptr;
     // Measured at B = 64, k = 8, V = 128256 bf16 with early exit: E = 2, 3,
     // 4, 5 (this rule), 6, 7, 9 gave 63.2, 59.9, 57.4, 55.4, 56.9, 60.8 and
     // 65.8 us; row chunks of 32K or 16K elements instead of 64K (so that the
@@ -1198,12 +1230,15 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
     // the workspace's call epoch, advanced by a kernel after it.
     const uint64_t tag = mode.capturing ? 0 : next_call_tag();
     const long spin = mode.test_give_up ? 256 : kSpinLimit;
+    // The early-exit gate in ticks of the 100 MHz clock (at most 1 ms).
+    const long pos0_bytes = (long)B * 2 * V * (DT == 1 ? 2 : 4);
+    const int gate_ticks = exit_early ? (int)std::min(100000L, pos0_bytes / 10 / kGateGBps) : 0;
     const hipError_t e = launch_timed(
         kProfFused, exit_early ? &k_sample_one<DT, NE, true> : &k_sample_one<DT, NE, false>,
         dim3((unsigned)(n_row + n_fin + (long)B * G2)), dim3(kThreads), one_launch_lds<DT, NE>(0),
         s, target, draft, B, k, V, C1, C2, c, inv_t, draft_tokens, uniforms, seed, ctr0,
         accepted_len, out_tokens, probe, p1, zr, fl, tag, st, p2, cnt, E, n_early_rows, n_fin,
-        spin, mode.test_give_up ? 1 : 0, n_tail);
+        spin, mode.test_give_up ? 1 : 0, n_tail, gate_ticks);
     if (e != hipSuccess || !mode.capturing) return e;
     hipLaunchKernelGGL(k_advance_epoch, dim3(1), dim3(kWaveSize), 0, s, cnt);
     return hipGetLastError();
