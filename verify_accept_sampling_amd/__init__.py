@@ -59,7 +59,9 @@ class SpecVerifyError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, "libspecverify.so")
+    """The in-tree library, or the one SPEC_VERIFY_LIBRARY names (the
+    host-sanitized build of the CPU tests)."""
+    return os.environ.get("SPEC_VERIFY_LIBRARY") or os.path.join(_PKG, "libspecverify.so")
 
 
 def declared_symbols() -> list:
