@@ -597,10 +597,19 @@ __device__ __forceinline__ void search_terms(const void* prow, const void* qrow,
   j0 = (long)chunk * kDrawChunk + (long)threadIdx.x * kSearchPerThread;
   const float fill = KIND == 0 ? -INFINITY : 0.f;
   float zp[kSearchPerThread], zq[kSearchPerThread];
+  // Unconditional loads (index clamped, then replaced by the fill), so they
+  // are all in flight together instead of one round trip each.
+  const void* qsrc = resid ? qrow : prow;
 #pragma unroll
   for (int e = 0; e < kSearchPerThread; ++e) {
-    zp[e] = (j0 + e < V) ? load_elem<DT>(prow, j0 + e) : fill;
-    zq[e] = (resid && j0 + e < V) ? load_elem<DT>(qrow, j0 + e) : fill;
+    const long j = min(j0 + e, (long)V - 1);
+    zp[e] = load_elem<DT>(prow, j);
+    zq[e] = load_elem<DT>(qsrc, j);
+  }
+#pragma unroll
+  for (int e = 0; e < kSearchPerThread; ++e) {
+    if (!(j0 + e < V)) zp[e] = fill;
+    if (!(resid && j0 + e < V)) zq[e] = fill;
   }
   // Runs once per request on a cold instruction cache: rolled.
 #pragma unroll 1
