@@ -48,9 +48,31 @@ SCHEDULE_OF = {"auto": "auto", "one_launch": "one_launch", "two_launch": "two_la
                "early_exit": "early_exit"}
 
 
-def traffic_file(path: str) -> str:
-    suffix = "_early_exit" if SCHEDULE_OF[path] in ("auto", "early_exit") else ""
-    return os.path.join(ROOT, "profiles", f"{KERNELS[path]}_b64_k8_v128256{suffix}_traffic.json")
+# Kernel sources each traffic summary is keyed to.
+COMMON_SOURCES = ["verify_accept_sampling_amd/csrc/device_common.h",
+                  "verify_accept_sampling_amd/csrc/device_math.h",
+                  "verify_accept_sampling_amd/csrc/internal.h"]
+SAMPLE_SOURCES = ["verify_accept_sampling_amd/csrc/sample.hip",
+                  "verify_accept_sampling_amd/csrc/sample_device.h"] + COMMON_SOURCES
+PROBS_SOURCES = ["verify_accept_sampling_amd/csrc/probs.hip",
+                 "verify_accept_sampling_amd/csrc/sample_device.h"] + COMMON_SOURCES
+# Traffic summaries: key (a --path of the headline workload, or "probs") ->
+# (dominant kernel, file tag, workload, sources).
+TRAFFIC = {
+    "auto": ("k_sample_one", "b64_k8_v128256_early_exit", "B=64 k=8 V=128256 bf16",
+             SAMPLE_SOURCES),
+    "early_exit": ("k_sample_one", "b64_k8_v128256_early_exit", "B=64 k=8 V=128256 bf16",
+                   SAMPLE_SOURCES),
+    "one_launch": ("k_sample_one", "b64_k8_v128256", "B=64 k=8 V=128256 bf16", SAMPLE_SOURCES),
+    "two_launch": ("k_row_stats", "b64_k8_v128256", "B=64 k=8 V=128256 bf16", SAMPLE_SOURCES),
+    "probs": ("k_probs_rows", "b512_k8_v128256", "B=512 k=8 V=128256 fp32 probabilities",
+              PROBS_SOURCES),
+}
+
+
+def traffic_file(key: str) -> str:
+    kernel, tag, _, _ = TRAFFIC[key]
+    return os.path.join(ROOT, "profiles", f"{kernel}_{tag}_traffic.json")
 
 
 # Algorithmic bytes of the row pass at this workload: every logit of the
@@ -58,31 +80,27 @@ def traffic_file(path: str) -> str:
 ALGO_ROW_BYTES = 64 * 17 * 128256 * 2
 # Elements of the chunk the inverse-CDF search reads again.
 DRAW_CHUNK = 512
-KERNEL_SOURCES = ["verify_accept_sampling_amd/csrc/sample.hip",
-                  "verify_accept_sampling_amd/csrc/sample_device.h",
-                  "verify_accept_sampling_amd/csrc/device_common.h",
-                  "verify_accept_sampling_amd/csrc/device_math.h",
-                  "verify_accept_sampling_amd/csrc/internal.h"]
+PROBS_PICK_CHUNK = 2048  # elements of the chunk the probability-row draw searches
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(path: str):
-    """HBM bytes per launch of the dominant kernel of sampling path `path`
-    from the committed rocprofv3 counter summary, or None if absent or taken
-    on other kernel sources."""
+def measured_traffic(key: str):
+    """HBM bytes per launch of the dominant kernel of `key` (a headline
+    path, or "probs") from the committed rocprofv3 counter summary, or None
+    if absent or taken on other kernel sources."""
     try:
-        with open(traffic_file(path)) as f:
+        with open(traffic_file(key)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha(TRAFFIC[key][3]):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -107,14 +125,14 @@ def _pmc_means(csv_path: str, counter: str, kernel: str):
     return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, path: str):
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, key: str):
     """Turn the FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch) into HBM
     bytes per launch of `kernel`.  Each counter is scaled by what it reads
     for a plain elementwise copy of copy_mib MiB (which reads and writes
     exactly that many bytes), and the result is written next to the
     kernel-source hash it was taken on."""
     nbytes = copy_mib * 1024 * 1024
-    kernel = KERNELS[path]
+    kernel, _, workload, sources = TRAFFIC[key]
     fetch, nf = _pmc_means(fetch_csv, "FETCH_SIZE", kernel)
     write, nw = _pmc_means(write_csv, "WRITE_SIZE", kernel)
     f_scale = nbytes / (fetch["copy"] * 1024.0)
@@ -122,8 +140,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, p
     rd = fetch["row"] * 1024.0 * f_scale
     wr = write["row"] * 1024.0 * w_scale
     out = {
-        "kernel": kernel, "path": path, "workload": "B=64 k=8 V=128256 bf16",
-        "kernel_source_sha": kernel_source_sha(),
+        "kernel": kernel, "path": key, "workload": workload,
+        "kernel_source_sha": kernel_source_sha(sources),
         "fetch_kib_per_dispatch": fetch["row"], "write_kib_per_dispatch": write["row"],
         "copy_bytes": nbytes, "copy_fetch_kib": fetch["copy"], "copy_write_kib": write["copy"],
         "fetch_scale": f_scale, "write_scale": w_scale,
@@ -132,7 +150,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, command: str, p
         "hbm_bytes_per_launch": rd + wr,
         "command": command,
     }
-    with open(traffic_file(path), "w") as f:
+    with open(traffic_file(key), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -264,6 +282,23 @@ GREEDY_WORKLOADS = {
 }
 GREEDY_KERNELS = {"tree": "k_tree_greedy", "greedy_b64": "k_greedy_chain",
                   "greedy_b1": "k_greedy_chain"}
+
+
+def copy_calibration(mib: int, dev):
+    """A plain elementwise copy (negation) of `mib` MiB of float32, three
+    times: the reference kernel that scales the HBM counters."""
+    if mib <= 0:
+        return
+    import torch
+
+    nb = mib * 1024 * 1024
+    src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)  # one elementwise kernel: reads nb bytes, writes nb
+    torch.cuda.synchronize()
+    del src, dst
+    print(f"bench: copy calibration, 3 x {mib} MiB", file=sys.stderr, flush=True)
 
 
 def timed_steps(step, first, steps, profile, keep=None):
@@ -592,22 +627,32 @@ def bench_tree_sample(args):
 
 def bench_probs(args):
     """One JSON line for the probability-row workload: B=512, k=8, V=128256
-    float32 rows with a prescribed overlap alpha in {0.6, 0.8, 0.9}.  The
-    acceptance tests gather p(x) and q(x); the draw reads each request's
-    rows drawn from (target and draft row n after a rejection, target row k
-    for the bonus) once, so those rows are the algorithmic bytes."""
+    float32 rows with a prescribed overlap alpha in {0.6, 0.8, 0.9}.  Two
+    kernels: k_probs_rows (acceptance tests, then one pass over each
+    request's rows drawn from -- target and draft row n after a rejection,
+    target row k at the bonus -- into per-chunk sums) and k_probs_pick (the
+    draw from those sums, reading one 2048-element chunk of those rows
+    again).  The row pass is the dominant kernel; its algorithmic bytes are
+    the rows drawn from and the gathered acceptance-test values."""
     import numpy as np
-    import torch
 
-    import verify_accept_sampling_amd as S
     import workloads as W
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     print("bench: generating B=512 k=8 V=128256 fp32 probability rows", file=sys.stderr,
           flush=True)
     wl = W.controlled_acceptance()
     B, k, V = wl.B, wl.k, wl.V
+    first = args.warmup  # counter base of the first timed step
+    legs = None
+    if not args.no_cpu_baseline:
+        legs = oracle_legs(wl, first, args.steps, args.cpu_seconds, "probability-row")
+
+    import torch
+
+    import verify_accept_sampling_amd as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
     t0 = torch.from_numpy(wl.target).to(dev)
     d0 = torch.from_numpy(wl.draft).to(dev)
     n_copies = max(1, min(args.copies, 2))  # 4.5 GB per copy, far beyond the caches
@@ -615,28 +660,37 @@ def bench_probs(args):
     toks = torch.from_numpy(wl.draft_tokens).to(dev)
     ws = S.Workspace(dev)
     n_u = B * (k + 1) * 2
+    acc_all = torch.empty((args.steps, B), dtype=torch.int32, device=dev)
+    out_all = torch.empty((args.steps, B, k + 1), dtype=torch.int32, device=dev)
+    scratch = (torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B, k + 1), dtype=torch.int32, device=dev))
 
-    def step(i):
+    def run(i, out):
         t, d = copies[i % len(copies)]
-        return S.spec_verify_sample(t, d, toks, 1.0, seed=wl.uniform_seed, counter0=i * n_u,
-                                    kind="probs", workspace=ws)
+        S.spec_verify_sample(t, d, toks, 1.0, seed=wl.uniform_seed, counter0=i * n_u,
+                             kind="probs", workspace=ws, out=out)
+        return out
+
+    copy_calibration(args.copy_calibration_mib, dev)
 
     print(f"bench: warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        step(i)
+        run(i, scratch)
     torch.cuda.synchronize()
-    accs = []
-    ms_step = timed_steps(step, args.warmup, args.steps, profile=False, keep=accs)
-    timed_steps(step, args.warmup + args.steps, args.steps, profile=True)
-    n, ms = S.spec_profile_read("draw")
-    kern_us = ms / n * 1e3
-    acc_all = torch.stack(accs).cpu().numpy()
+    ms_step = timed_steps(lambda i: run(i, (acc_all[i - first], out_all[i - first])), first,
+                          args.steps, profile=False)
+    timed_steps(lambda i: run(i, scratch), first + args.steps, args.steps, profile=True)
+    rows_d = np.asarray(S.spec_profile_durations("row_pass")) * 1e3
+    pick_d = np.asarray(S.spec_profile_durations("draw")) * 1e3
+    acc_np, out_np = acc_all.cpu().numpy(), out_all.cpu().numpy()
     row_bytes = V * 4
-    drawn_rows = (acc_all < k).sum(axis=1) + B
-    gathers = np.minimum(acc_all + 1, k).sum(axis=1) * 2 * 4
-    nbytes = float(np.mean(drawn_rows * row_bytes + drawn_rows * min(V, DRAW_CHUNK) * 4
-                           + gathers))
-    achieved = nbytes / (kern_us * 1e-6) / 1e9
+    drawn_rows = (acc_np < k).sum(axis=1) + B  # per step: two rows at a rejection, one at the bonus
+    gathers = np.minimum(acc_np + 1, k).sum(axis=1) * 2 * 4
+    rows_bytes = float(np.mean(drawn_rows * row_bytes + gathers))
+    pick_bytes = float(np.mean(drawn_rows * min(V, PROBS_PICK_CHUNK) * 4))
+    rows_us, pick_us = float(rows_d.mean()), float(pick_d.mean())
+    achieved = rows_bytes / (rows_us * 1e-6) / 1e9
+    step_bytes = rows_bytes + pick_bytes
     result = {
         "metric": "verified positions/s (sampling, probability rows, B=512, k=8, V=128256, fp32)",
         "value": B * (k + 1) / (ms_step * 1e-3),
@@ -646,14 +700,35 @@ def bench_probs(args):
         "dtype": "f64", "data": "synthetic",
         "config": {"workload": "probs_b512_k8_v128256_f32", "B": B, "k": k, "V": V,
                    "alphas": [0.6, 0.8, 0.9], "input_copies": len(copies)},
-        "roofline": {"bound": "hbm", "kernel": "k_draw", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "k_probs_rows", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
-        "kernels_avg_us": {"k_draw": kern_us},
-        "mean_accepted": float(acc_all.mean()),
-        "cpu_baseline": None,
+                     "traffic": measured_traffic("probs"),
+                     "algorithmic_bytes_per_launch": rows_bytes},
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "kernels_avg_us": {"k_probs_rows": rows_us, "k_probs_pick": pick_us},
+        "kernel_p10_p90_us": {"k_probs_rows": [float(np.percentile(rows_d, 10)),
+                                               float(np.percentile(rows_d, 90))],
+                              "k_probs_pick": [float(np.percentile(pick_d, 10)),
+                                               float(np.percentile(pick_d, 90))]},
+        "mean_accepted": float(acc_np.mean()),
+        "workspace_status": S.spec_workspace_status(ws),
     }
+    gate = None
+    if legs is not None:
+        one, allc, res = legs
+        result["cpu_baseline"] = allc
+        result["cpu_baseline_1core"] = one
+        gate = correctness_gate(acc_np, out_np, first, res)
+        result["correctness_gate"] = gate
+    else:
+        result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    if gate is not None and gate["unflagged"]:
+        print("bench: FAILED: probability-row outputs disagree with the oracle away from any "
+              "decision boundary", file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 def main():
@@ -695,7 +770,7 @@ def main():
         if args.copy_calibration_mib <= 0:
             raise SystemExit("--summarize-pmc needs --copy-calibration-mib of the profiled runs")
         summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.pmc_command,
-                      args.path)
+                      "probs" if args.workload == "probs" else args.path)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -783,16 +858,7 @@ def bench_sample(args):
         S.spec_verify_sample(t, d, toks, wl.temperature, seed=wl.uniform_seed,
                              counter0=i * n_u, workspace=ws, schedule=sched, out=out)
 
-    if args.copy_calibration_mib > 0:
-        nb = args.copy_calibration_mib * 1024 * 1024
-        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)  # one elementwise kernel: reads nb bytes, writes nb
-        torch.cuda.synchronize()
-        del src, dst
-        print(f"bench: copy calibration, 3 x {args.copy_calibration_mib} MiB", file=sys.stderr,
-              flush=True)
+    copy_calibration(args.copy_calibration_mib, dev)
 
     print(f"bench: warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):

@@ -329,6 +329,14 @@ def test_sample_probs_wide_vocabulary():
     _run_sample(wl)
 
 
+def test_sample_probs_many_chunks():
+    # more draw chunks per row than a work-group has threads, so the chunk
+    # search runs over several tiles; 16-byte aligned rows and element loads
+    for V in (600000, 600001):
+        wl = W.controlled_acceptance(B=3, k=2, V=V, seed=33, uniform_seed=34, logit_std=1.0)
+        _run_sample(wl)
+
+
 def test_sample_controlled_acceptance_full(controlled_full):
     _say("sample probs B=512 k=8 V=128256")
     _run_sample(controlled_full)

@@ -270,6 +270,16 @@ struct SampleMode {
   bool test_give_up;  // SPEC_FLAG_TEST_GIVE_UP
 };
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// Sampling verification on float32 probability rows (probs.hip); vec: rows
+// 16-byte aligned and shorter than 2 GiB.
+hipError_t launch_probs(const void* target, const void* draft, int B, int k, int V,
+                        const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
+                        uint64_t ctr0, int32_t* accepted_len, int32_t* out_tokens, float* probe,
+                        bool vec, void* ws, const WsLayout& L, hipStream_t s);
+
 hipError_t launch_sample(const void* target, const void* draft, int dtype, int kind,
                          int B, int k, int V, const int32_t* draft_tokens,
                          const float* uniforms, uint64_t seed, uint64_t counter0,

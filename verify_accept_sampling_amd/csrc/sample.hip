@@ -30,8 +30,7 @@
 // the kernel).  The two-launch form (k_row_stats, then k_draw) computes the
 // same thing, with the acceptance tests in the request's last row-pass
 // work-group (by ticket).
-// Probabilities path (rows given as distributions): k_draw alone, each
-// work-group first repeating the (gather-only) acceptance tests.
+// Rows given as probabilities have a kernel of their own (probs.hip).
 #include <algorithm>
 #include <atomic>
 #include <mutex>
@@ -487,54 +486,6 @@ __device__ __forceinline__ void row_block(
   if ((threadIdx.x & 63) == 0) st_dev_state(&state[b], st);
 }
 
-// Acceptance tests on probability rows: u * q(x) < p(x), exact in float64
-// for float32 inputs.  Every thread returns n; with `write` the accepted
-// prefix and the probe values are stored, except probe[b, n, 2], which the
-// request's finishing work-group owns.
-__device__ int accept_scan_probs(const float* target, const float* draft, int b, int k, int V,
-                                 const int32_t* draft_tokens, const float* uniforms,
-                                 uint64_t seed, uint64_t ctr0, bool write,
-                                 int32_t* accepted_len, int32_t* out_tokens, float* probe) {
-  // k <= 1023, so each thread handles at most 4 positions.
-  float pv[4] = {0.f, 0.f, 0.f, 0.f}, qv[4] = {0.f, 0.f, 0.f, 0.f};
-  int first = k;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int i = threadIdx.x + s * kThreads;
-    if (i >= k) break;
-    const int x = draft_tokens[(long)b * k + i];
-    bool accept = false;
-    if (x >= 0 && x < V) {
-      pv[s] = target[((long)b * (k + 1) + i) * V + x];
-      qv[s] = draft[((long)b * k + i) * V + x];
-      const float u = get_uniform(uniforms, seed, ctr0, b, i, 0, k);
-      accept = (double)u * (double)qv[s] < (double)pv[s];
-    }
-    if (!accept) first = min(first, i);
-  }
-  const int n = block_min_i(first);
-  if (write) {
-    if (probe) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int i = threadIdx.x + s * kThreads;
-        if (i > k) break;
-        float* pr = probe + ((long)b * (k + 1) + i) * 4;
-        pr[0] = i < k ? pv[s] : 0.f;
-        pr[1] = i < k ? qv[s] : 0.f;
-        if (i != n) pr[2] = 0.f;
-        pr[3] = 0.f;
-      }
-    }
-    for (int i = threadIdx.x; i <= k; i += kThreads) {
-      if (i < n) out_tokens[(long)b * (k + 1) + i] = draft_tokens[(long)b * k + i];
-      else if (i > n) out_tokens[(long)b * (k + 1) + i] = -1;
-    }
-    if (threadIdx.x == 0) accepted_len[b] = n;
-  }
-  return n;
-}
-
 // How a draw work-group learns its request's state.
 enum {
   kStateStored = 0,  // from the state array, written by an earlier launch
@@ -557,13 +508,11 @@ struct RowPass {
 // wave as their rows complete and publishes the packed state in the
 // request's ready slot.  The request's other draw work-groups wait for the
 // ready slot.  Every draw work-group takes the request's draw ticket, and
-// the last one writes the request's outputs (logits: all of them; the
-// accepted prefix of probability rows is written by work-group 0) and
-// clears the ready slot.  A wait that gives up sets the workspace status;
+// the last one writes the request's outputs and clears the ready slot.  A wait that gives up sets the workspace status;
 // the request's work-groups then skip their sums, and the last one writes
 // accepted_len = -1 and out_tokens all -1, as it does whenever the status
 // word is set.
-template <int DT, int NE, int KIND, int HOW>
+template <int DT, int NE, int HOW>
 __device__ __forceinline__ void draw_block(
     int b, int grp, int nb, const void* __restrict__ target, const void* __restrict__ draft,
     int k, int V, int C2, double inv_t, const int32_t* __restrict__ draft_tokens,
@@ -576,11 +525,11 @@ __device__ __forceinline__ void draw_block(
   static_assert(kThreads == 256, "one table entry per thread");
   // The exp table's load is issued now and stored to shared memory after
   // the wait below, so the load and the first poll share one round trip.
-  const double tv = KIND == 0 ? kExp2Frac256[threadIdx.x] : 0.0;
+  const double tv = kExp2Frac256[threadIdx.x];
   int n = 0;
   bool ok = true;  // this work-group holds the request's state
   double mp = 0.0, mq = 0.0, rho32 = 1.0;
-  if (KIND == 0) {
+  {
     ReqState st;
     if constexpr (HOW != kStateStored) {
       __shared__ int s_ok;
@@ -664,12 +613,8 @@ __device__ __forceinline__ void draw_block(
       mq = st.mq;
       rho32 = st.rho32;
     }
-  } else {
-    n = accept_scan_probs(static_cast<const float*>(target), static_cast<const float*>(draft), b,
-                          k, V, draft_tokens, uniforms, seed, ctr0, grp == 0, accepted_len,
-                          out_tokens, probe);
   }
-  if (KIND == 0) tab[threadIdx.x] = tv;
+  tab[threadIdx.x] = tv;
   __syncthreads();
   const bool resid = n < k;
   const double c1 = inv_t * kInvLn2x256, c0p = -mp * c1, c0q = -mq * c1;
@@ -688,10 +633,10 @@ __device__ __forceinline__ void draw_block(
     DrawPart* pb = part + (long)b * C2;
     if (first < C2) {  // wave-uniform
       if (resid)
-        wave_draw_chunks<DT, NE, KIND, true>(prow, qrow, V, C2, first, per_wave, c1, c0p, c0q,
+        wave_draw_chunks<DT, NE, 0, true>(prow, qrow, V, C2, first, per_wave, c1, c0p, c0q,
                                              rho32, tab, pb);
       else
-        wave_draw_chunks<DT, NE, KIND, false>(prow, qrow, V, C2, first, per_wave, c1, c0p, c0q,
+        wave_draw_chunks<DT, NE, 0, false>(prow, qrow, V, C2, first, per_wave, c1, c0p, c0q,
                                               rho32, tab, pb);
     }
   }
@@ -750,7 +695,7 @@ __device__ __forceinline__ void draw_block(
       }
     }
   };
-  const bool resid_w = KIND == 0 && resid;  // weights move with rho
+  const bool resid_w = resid;  // weights move with rho
   __shared__ int s_cs;      // chunk holding the threshold
   __shared__ double s_P;    // weight of the chunks before it
   if (threadIdx.x == 0) s_cs = INT_MAX;  // ordered by the reduction's barriers
@@ -798,7 +743,7 @@ __device__ __forceinline__ void draw_block(
       for (int idx = wave; idx < nr; idx += kWaves) {  // wave-uniform
         const int t2 = s_list[idx];
         const double wx =
-            wave_chunk_w_exact<DT, KIND>(prow, qrow, V, base + t2, c1, c0p, c0q, rho, tab);
+            wave_chunk_w_exact<DT, 0>(prow, qrow, V, base + t2, c1, c0p, c0q, rho, tab);
         if (lane == 0) s_wx[t2] = wx;
       }
       __syncthreads();
@@ -861,21 +806,19 @@ __device__ __forceinline__ void draw_block(
   const int cs = s_cs == INT_MAX ? C2 - 1 : s_cs;
   const int mode = use_w ? 0 : 1;
   // s_P is stored by one thread above; the search reads it after a barrier.
-  int t = search_chunk<DT, KIND>(prow, qrow, V, cs, mode == 0, c1, c0p, c0q, rho, s_P, thr, tab);
+  int t = search_chunk<DT, 0>(prow, qrow, V, cs, mode == 0, c1, c0p, c0q, rho, s_P, thr, tab);
   if (status_v != 0) {  // block-uniform
     fail_outputs();
     return;
   }
-  if (KIND == 0 && wave == 0)  // the acceptance tests' outputs: this work-group's alone
+  if (wave == 0)  // the acceptance tests' outputs: this work-group's alone
     write_accept_outputs(b, k, n, draft_tokens, accepted_len, out_tokens, probe);
   if (threadIdx.x == 0) {
     if (!(grand > 0.0)) t = -1;  // rows without mass (invalid input)
     out_tokens[(long)b * (k + 1) + n] = t;
     if (probe) {
       // Mass of the distribution drawn from, in probability units.
-      double mass;
-      if (KIND == 0) mass = resid ? (mode == 0 ? grand / sp_tot : 0.0) : 1.0;
-      else mass = mode == 0 ? grand : (resid ? 0.0 : grand);
+      const double mass = resid ? (mode == 0 ? grand / sp_tot : 0.0) : 1.0;
       probe[((long)b * (k + 1) + n) * 4 + 2] = (float)mass;
     }
     if constexpr (HOW != kStateStored) {
@@ -897,7 +840,7 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(
                     uniforms, seed, ctr0, probe, part, zrow, nullptr, 0, state, counters);
 }
 
-template <int DT, int NE, int KIND>
+template <int DT, int NE>
 __global__ __launch_bounds__(kThreads) void k_draw(
     const void* __restrict__ target, const void* __restrict__ draft, int k, int V, int C2, int nb,
     double inv_t, const int32_t* __restrict__ draft_tokens, const float* __restrict__ uniforms,
@@ -907,7 +850,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(
     unsigned* __restrict__ counters) {
   const int G2 = draw_groups(C2, nb);
   const RowPass none{nullptr, nullptr, nullptr, 0, 0, 0.f};
-  draw_block<DT, NE, KIND, kStateStored>(static_cast<int>(blockIdx.x / G2),
+  draw_block<DT, NE, kStateStored>(static_cast<int>(blockIdx.x / G2),
                                          static_cast<int>(blockIdx.x % G2), nb, target, draft, k, V,
                                          C2, inv_t, draft_tokens, uniforms, seed, ctr0,
                                          accepted_len, out_tokens, probe, state, none, part,
@@ -1006,7 +949,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_one(
                             counters, withhold != 0, gate_ticks);
   } else {
     const RowPass rows{part1, zrow, flags, tag, C1, c};
-    draw_block<DT, NE, 0, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2),
+    draw_block<DT, NE, kStateSlot>(static_cast<int>(draw / G2), static_cast<int>(draw % G2),
                                       1, target, draft, k, V, C2, inv_t, draft_tokens, uniforms,
                                       seed, ctr0, accepted_len, out_tokens, probe, state, rows,
                                       part2, counters, spin_limit);
@@ -1117,7 +1060,7 @@ constexpr int kTailRequests = SPEC_TAIL_REQUESTS;
 constexpr long kTailDrawSlotFraction = SPEC_TAIL_DRAW_SLOT_FRACTION;
 
 // Compute units of the current device.
-static int device_cus() {
+int device_cus() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1248,43 +1191,8 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
                              uniforms, seed, ctr0, probe, p1, zr, st, cnt);
   if (e != hipSuccess) return e;
   const int G2 = draw_groups(C2, 1);
-  return launch_timed(kProfDraw, &k_draw<DT, NE, 0>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
+  return launch_timed(kProfDraw, &k_draw<DT, NE>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
                       target, draft, k, V, C2, 1, inv_t, draft_tokens, uniforms, seed, ctr0,
-                      accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);
-}
-
-template <int NE>
-static hipError_t launch_probs(const void* target, const void* draft, int B, int k, int V,
-                         const int32_t* draft_tokens, const float* uniforms, uint64_t seed,
-                         uint64_t ctr0, int32_t* accepted_len, int32_t* out_tokens,
-                         float* probe, char* w, const WsLayout& L, hipStream_t s) {
-  const int C2 = res_chunks(V);
-  auto* st = reinterpret_cast<ReqState*>(w + L.state);
-  auto* p2 = reinterpret_cast<DrawPart*>(w + L.part2);
-  auto* cnt = reinterpret_cast<unsigned*>(w + L.count);
-  // Probability rows need little float64 work per element, so a draw
-  // work-group takes several batches of chunks: about two and a half rounds
-  // of resident work-groups in all (fewer acceptance scans, stores and
-  // tickets per byte, while later rounds still cover the load latency).
-  // Measured at B = 512, V = 128256: 1 batch 140.5 us, 2 118.8, 3 117.7
-  // (this rule), 7 (one round) 123.1.
-  static std::atomic<int> per_cu_cached{0};
-  int per_cu = per_cu_cached.load(std::memory_order_relaxed);
-  if (per_cu <= 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&k_draw<0, NE, 1>), kThreads, 0) !=
-            hipSuccess ||
-        per_cu <= 0)
-      per_cu = 1;
-    per_cu_cached.store(per_cu, std::memory_order_relaxed);
-  }
-  const long slots = (long)device_cus() * per_cu;
-  const int g1 = draw_groups(C2, 1);
-  const int want = (int)std::max(1L, std::min((long)g1, (5 * slots + 2L * B - 1) / (2L * B)));
-  const int nb = (g1 + want - 1) / want;
-  const int G2 = draw_groups(C2, nb);
-  return launch_timed(kProfDraw, &k_draw<0, NE, 1>, dim3((unsigned)(B * G2)), dim3(kThreads), 0, s,
-                      target, draft, k, V, C2, nb, 1.0, draft_tokens, uniforms, seed, ctr0,
                       accepted_len, out_tokens, probe, (const ReqState*)st, p2, cnt);
 }
 
@@ -1296,12 +1204,8 @@ hipError_t launch_sample(const void* target, const void* draft, int dtype, int k
   char* w = static_cast<char*>(ws);
   const bool vec = rows_aligned(target, V, dtype) && (k == 0 || rows_aligned(draft, V, dtype));
   if (kind == 1) {
-    if (vec)
-      return launch_probs<4>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
-                      accepted_len, out_tokens, probe, w, L, s);
-    else
-      return launch_probs<1>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
-                      accepted_len, out_tokens, probe, w, L, s);
+    return launch_probs(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
+                        accepted_len, out_tokens, probe, vec, ws, L, s);
   } else if (dtype == 1) {
     if (vec)
       return launch_logits<1, 8>(target, draft, B, k, V, draft_tokens, uniforms, seed, counter0,
