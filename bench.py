@@ -393,9 +393,33 @@ def bench_greedy(args):
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": None, "algorithmic_bytes_per_launch": nbytes},
         "kernels_avg_us": {GREEDY_KERNELS[name]: kern_us},
-        "cpu_baseline": None,
     }
+    # Gate: the outputs on every input copy against the oracle, which must
+    # agree exactly (argmax and integer comparisons only).  The oracle's
+    # time on the same workload is the CPU baseline (one host thread).
+    import oracle.verify as O
+
+    t_cpu = time.perf_counter()
+    if name == "tree":
+        want = O.verify_tree_greedy(wl.target, wl.parent, wl.node_tokens, dtype)[:2]
+    else:
+        want = O.verify_greedy(wl.target, wl.draft_tokens, dtype)[:2]
+    dt_cpu = time.perf_counter() - t_cpu
+    mism = 0
+    for i in range(len(copies)):
+        got = step(i)
+        mism += int((got[0].cpu().numpy() != want[0]).sum())
+        mism += int((got[1].cpu().numpy() != want[1]).sum())
+    result["correctness_gate"] = {"input_copies": len(copies), "requests": B * len(copies),
+                                  "mismatched_outputs": mism}
+    result["cpu_baseline"] = {"value": positions / dt_cpu, "unit": "verified positions/s",
+                              "cores": 1, "kind": "oracle",
+                              "sample": f"the whole workload ({B} requests) once, {dt_cpu:.2f} s "
+                                        f"on 1 host thread"}
     print(json.dumps(result), flush=True)
+    if mism:
+        print("bench: FAILED: greedy outputs differ from the oracle", file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 def bench_serving(args):

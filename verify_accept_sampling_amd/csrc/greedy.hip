@@ -167,8 +167,34 @@ __global__ __launch_bounds__(kThreads) void k_greedy_chain(
     int32_t* __restrict__ out_tokens, uint64_t* __restrict__ part,
     unsigned* __restrict__ counters) {
   const int n_pos = k + 1;
+  // Thread i < k loads draft token i of this work-group's request now; only
+  // the request's last work-group uses it, by then long arrived, so its
+  // finish waits on one round trip (the partials) instead of two.
+  const int b0 = static_cast<int>(blockIdx.x / C1 / n_pos);
+  const int my_tok = (int)threadIdx.x < k ? draft_tokens[(long)b0 * k + threadIdx.x] : -1;
   int b;
   if (!argmax_chunk<DT, NE>(target, n_pos, V, C1, part, counters, b)) return;
+  if (n_pos <= kWaveSize) {
+    // One wave finishes, lane j on position j, with no work-group barrier.
+    if (threadIdx.x >= kWaveSize) return;
+    const int lane = threadIdx.x;
+    int am = 0;
+    if (lane < n_pos) {
+      const long row = (long)b * n_pos + lane;
+      float v = -INFINITY;
+      int i = INT_MAX;
+      for (int c = 0; c < C1; ++c) {
+        const uint64_t p = ld_dev(&part[row * C1 + c]);
+        am_merge(v, i, unpack_lo(p), __float_as_int(unpack_hi(p)));
+      }
+      am = (i == INT_MAX) ? 0 : i;  // all-(-inf) rows resolve to index 0
+    }
+    const uint64_t mm = __ballot(lane < k && my_tok != am);
+    const int n = mm != 0 ? __builtin_ctzll(mm) : k;
+    if (lane < n_pos) out_tokens[(long)b * n_pos + lane] = lane < n ? my_tok : lane == n ? am : -1;
+    if (lane == 0) accepted_len[b] = n;
+    return;
+  }
   __shared__ int amax[kMaxK + 1];
   merge_argmax_rows(part, b, n_pos, C1, amax);
   int first = k;
