@@ -9,8 +9,9 @@ the C ABI.
 * Shapes that span the kernels' cases: float32 and bfloat16 logits, ragged V
   (the scalar loads), probability rows, a 20-deep chain, a 9-child star, a
   random 300-node tree (the full-size table setup), a root with no
-  children, out-of-range node tokens, and a root whose draft row equals its
-  target row so the residual after a rejection is empty.
+  children, a 100-child star (children in two tiles of the walk),
+  out-of-range node tokens, and a root whose draft row equals its target
+  row so the residual after a rejection is empty.
 * Statistics: with every child's token drawn from the draft at its parent,
   the first emitted token follows the target's root distribution
   (chi-square over 40000 requests).
@@ -142,6 +143,21 @@ def test_out_of_range_tokens_and_empty_residual():
                if any(d.kind == "residual" and d.outcome == 0 for d in res[b].decisions))
     assert kept > 0
     assert st["mismatches"] == 0
+
+
+def test_wide_star_children_past_one_wave():
+    # 100 children at the root: the walk takes them in tiles of 64; the
+    # first 70 are made to fail (out-of-range tokens) in even requests, so
+    # the tests reach the second tile through 70 residual updates
+    _say("tree sampling: a 100-child star, 70 forced rejections")
+    parent = np.array([-1] + [0] * 100, dtype=np.int32)
+    wl = W.tree_sample(B=8, V=1024, seed=21, uniform_seed=22, parent=parent, target_std=2.0,
+                       noise_std=1.0, temperature=1.0, n_peaks=0, dtype="bf16")
+    wl.node_tokens[::2, 1:71] = wl.V + 1
+    acc, out, path = _run_gpu(wl)
+    st = _check(wl, acc, out, path)
+    assert st["mismatches"] == 0
+    assert all(path[b, 1] > 70 or acc[b] == 0 for b in range(0, wl.B, 2))
 
 
 def test_probability_rows():

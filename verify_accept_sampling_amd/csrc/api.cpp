@@ -289,7 +289,10 @@ int spec_verify_tree_sample(const void* target, const void* draft, int dtype, in
       if (r >= 1) ++shape.rank_count[r];
       if (r > shape.max_rank) shape.max_rank = r;
     }
-    for (int u = 0; u < n_nodes; ++u) shape.n_internal += nchild[u] > 0;
+    for (int u = 0; u < n_nodes; ++u) {
+      shape.has_child[u] = nchild[u] > 0;
+      shape.n_internal += nchild[u] > 0;
+    }
   }
   const long C2 = (V + kDrawChunk - 1) / kDrawChunk;
   if (check_grid((long)B * (n_nodes + shape.n_internal) * row_chunks_for(V)) != SPEC_OK ||

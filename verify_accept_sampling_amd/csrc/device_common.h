@@ -250,6 +250,17 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ double wave_inclusive_scan_d(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = shfl_up_d(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
 // Exclusive prefix sum over the lanes of a wave.
 __device__ __forceinline__ double wave_exclusive_scan_d(double v) {
   const int lane = threadIdx.x & 63;

@@ -247,13 +247,14 @@ hipError_t launch_tree_greedy(const void* target, int dtype, int B, int n_nodes,
                               const WsLayout& L, hipStream_t s);
 
 // Host-side shape of a tree, the same as the tables k_tree_setup writes:
-// depth, nodes with a child, the highest sibling rank and how many
-// children have each rank.
+// depth, nodes with a child, the highest sibling rank, how many children
+// have each rank, and which nodes have a child.
 struct TreeShape {
   int depth = 0;
   int n_internal = 0;
   int max_rank = 0;
   int rank_count[kMaxNodes] = {0};
+  bool has_child[kMaxNodes] = {false};
 };
 
 hipError_t launch_tree_sample(const void* target, const void* draft, int dtype, int kind, int B,

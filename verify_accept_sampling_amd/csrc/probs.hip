@@ -104,17 +104,6 @@ __device__ int accept_scan_probs(const float* target, const float* draft, int b,
   return n;
 }
 
-// Inclusive prefix sum across the wave.
-__device__ __forceinline__ double wave_inclusive_scan_d(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < kWaveSize; d <<= 1) {
-    const double o = shfl_up_d(v, d);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
 // The draw weight of one element pair: max(0, p - q), 0 for NaN.
 __device__ __forceinline__ double resid_weight(double p, double q) {
   const double d = p - q;
@@ -216,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void k_probs_rows(
   const bool resid = n < k;
   const float* prow = target + ((long)b * (k + 1) + n) * V;
   const float* qrow = resid ? draft + ((long)b * k + n) * V : prow;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   ProbsPart* rp = part + (long)b * C;
   // This wave's chunks: m consecutive ones (fewer at the end of the row).
   const int c0 = (g * kWaves + wave) * m;

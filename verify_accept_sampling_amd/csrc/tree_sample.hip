@@ -33,9 +33,10 @@
 //                    parent;
 //   k_tree_walk      one wave per request: the tests, the accepted path, the
 //                    outputs but the final token, and the draw state;
-//   k_tree_draw_part per (request, chunk) the chunk's draw-weight total;
-//   k_tree_pick      one wave per request: chunk by running total, then the
-//                    element, by the same per-chunk scan as k_tree_draw_part.
+//   k_tree_draw      per (request, chunk) the chunk's draw-weight total;
+//                    the request's last work-group (completion ticket) then
+//                    picks the chunk by running total and the element by
+//                    the same per-chunk scan, on one wave.
 #include <algorithm>
 
 #include "sample_device.h"
@@ -80,62 +81,76 @@ struct TreeDraw {
 // Setup
 // ---------------------------------------------------------------------------
 
+// Every table entry is computed by its own thread from the parent array in
+// shared memory (O(N) per entry, N <= NMAX): no sequential pass.  Run by a
+// whole work-group.
 template <int NMAX>
-__global__ __launch_bounds__(kThreads) void k_tree_setup(TreeArgsN<NMAX> tree, int N,
-                                                        int* __restrict__ tables) {
-  __shared__ int nchild[NMAX], first[NMAX], next[NMAX], rank[NMAX], depth[NMAX];
-  __shared__ int internal[NMAX], ranked[NMAX], rank_off[NMAX], fill[NMAX];
-  for (int j = threadIdx.x; j < NMAX; j += kThreads) {
-    nchild[j] = 0;
-    first[j] = next[j] = -1;
-    rank[j] = depth[j] = 0;
-    internal[j] = ranked[j] = rank_off[j] = fill[j] = 0;
-  }
+__device__ __forceinline__ void tree_setup_block(const TreeArgsN<NMAX>& tree, int N,
+                                                 int* __restrict__ tables) {
+  __shared__ int par[NMAX], nch[NMAX], rank[NMAX];
+  int* const t_parent = tables + kTabParent * kMaxNodes;
+  for (int j = threadIdx.x; j < N; j += kThreads) par[j] = j == 0 ? -1 : tree.parent[j];
   __syncthreads();
-  if (threadIdx.x == 0) {  // O(N), sequential: N <= NMAX
-    // From the last node down, so each child list is ascending.
-    for (int j = N - 1; j >= 1; --j) {
-      const int u = tree.parent[j];
-      next[j] = first[u];
-      first[u] = j;
-      ++nchild[u];
-    }
-    int max_rank = 0, n_int = 0;
-    for (int u = 0; u < N; ++u) {  // parents precede their children
-      int r = 0;
-      for (int j = first[u]; j >= 0; j = next[j]) {
-        rank[j] = r++;
-        depth[j] = depth[u] + 1;
+  // Per node: its rank among its siblings (children in increasing index),
+  // its next sibling, its number of children, its first child, its depth.
+  for (int j = threadIdx.x; j < N; j += kThreads) {
+    const int u = par[j];
+    int r = 0, nx = -1, nc = 0, fc = -1;
+    for (int i = 1; i < N; ++i) {
+      const int pi = par[i];
+      if (j > 0 && pi == u) {
+        if (i < j) ++r;
+        else if (i > j && nx < 0) nx = i;
       }
-      if (r > 0) internal[n_int++] = u;
-      if (r - 1 > max_rank) max_rank = r - 1;
+      if (pi == j) {
+        if (fc < 0) fc = i;
+        ++nc;
+      }
     }
-    // Children of rank >= 1 grouped by rank (counting sort), ascending
-    // index within a rank.
-    for (int j = 1; j < N; ++j)
-      if (rank[j] >= 1) ++fill[rank[j]];
-    int pos = 0;
-    for (int r = 1; r <= max_rank; ++r) {
-      rank_off[r - 1] = pos;
-      pos += fill[r];
-      fill[r] = rank_off[r - 1];
-    }
-    rank_off[max_rank] = pos;
-    for (int j = 1; j < N; ++j)
-      if (rank[j] >= 1) ranked[fill[rank[j]]++] = j;
+    int d = 0;
+    for (int x = j; x > 0; x = par[x]) ++d;  // parents precede their children
+    nch[j] = nc;
+    rank[j] = r;
+    t_parent[j] = u;
+    tables[kTabNChild * kMaxNodes + j] = nc;
+    tables[kTabFirst * kMaxNodes + j] = fc;
+    tables[kTabNext * kMaxNodes + j] = nx;
+    tables[kTabRank * kMaxNodes + j] = r;
+    tables[kTabDepth * kMaxNodes + j] = d;
   }
   __syncthreads();
   for (int j = threadIdx.x; j < N; j += kThreads) {
-    tables[kTabParent * kMaxNodes + j] = j == 0 ? -1 : tree.parent[j];
-    tables[kTabNChild * kMaxNodes + j] = nchild[j];
-    tables[kTabFirst * kMaxNodes + j] = first[j];
-    tables[kTabNext * kMaxNodes + j] = next[j];
-    tables[kTabRank * kMaxNodes + j] = rank[j];
-    tables[kTabDepth * kMaxNodes + j] = depth[j];
-    tables[kTabInternal * kMaxNodes + j] = internal[j];
-    tables[kTabRanked * kMaxNodes + j] = ranked[j];
-    tables[kTabRankOff * kMaxNodes + j] = rank_off[j];
+    // The nodes with a child, ascending; the children of rank >= 1 grouped
+    // by rank, ascending index within a rank; rank r's offset at entry
+    // r - 1 (r = 1 .. max rank + 1).  Entries past each list's length are 0.
+    int n_int = 0, n_ranked = 0, max_rank = 0;
+    int before_int = 0, lower_rank = 0, same_rank_before = 0, off = 0;
+    for (int i = 0; i < N; ++i) {
+      const int ri = rank[i];
+      if (nch[i] > 0) {
+        ++n_int;
+        if (i < j) ++before_int;
+      }
+      if (i >= 1 && ri >= 1) {
+        ++n_ranked;
+        max_rank = max(max_rank, ri);
+        if (ri < rank[j]) ++lower_rank;
+        if (ri == rank[j] && i < j) ++same_rank_before;
+        if (ri < j + 1) ++off;
+      }
+    }
+    if (nch[j] > 0) tables[kTabInternal * kMaxNodes + before_int] = j;
+    if (j >= n_int) tables[kTabInternal * kMaxNodes + j] = 0;
+    if (j >= 1 && rank[j] >= 1) tables[kTabRanked * kMaxNodes + lower_rank + same_rank_before] = j;
+    if (j >= n_ranked) tables[kTabRanked * kMaxNodes + j] = 0;
+    tables[kTabRankOff * kMaxNodes + j] = j <= max_rank ? off : 0;
   }
+}
+
+template <int NMAX>
+__global__ __launch_bounds__(kThreads) void k_tree_setup(TreeArgsN<NMAX> tree, int N,
+                                                        int* __restrict__ tables) {
+  tree_setup_block<NMAX>(tree, N, tables);
 }
 
 // ---------------------------------------------------------------------------
@@ -219,6 +234,28 @@ __device__ __forceinline__ double chunk_scan(const void* prow, const void* qrow,
   return __shfl(excl + acc, 63, 64);
 }
 
+// Total of one chunk's weights (as chunk_scan's, without the running sums:
+// one butterfly instead of a scan).  For the mass rounds, whose chunk totals
+// no other kernel recomputes.
+template <int DT, int NE, int KIND>
+__device__ __forceinline__ double chunk_total(const void* prow, const void* qrow, int V,
+                                              long chunk, double C, const TermCoef& k,
+                                              const double* tab) {
+  const int lane = threadIdx.x & 63;
+  const long j0 = chunk * kDrawChunk + (long)lane * kSegPerThread;
+  constexpr uint32_t fill = run_fill<DT, KIND>();
+  RunWords<DT> rp, rq;
+  load_run_words<DT, NE>(prow, j0, V, fill, rp);
+  load_run_words<DT, NE>(qrow, j0, V, fill, rq);
+  double acc = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSegPerThread; ++e) {
+    const double a = tterm<KIND>(run_elem<DT>(rp, e), k.c1, k.c0p, k.ip, tab);
+    acc += fmax(0.0, a - C * tterm<KIND>(run_elem<DT>(rq, e), k.c1, k.c0q, k.iq, tab));
+  }
+  return wave_sum_d(acc);
+}
+
 // Sum of n chunk partials in a fixed order (lane l: entries l, l+64, ...,
 // then a symmetric butterfly), the same value in every lane.
 __device__ __forceinline__ double wave_sum_fixed(const double* p, long n, long stride = 1) {
@@ -257,10 +294,18 @@ __device__ __forceinline__ void residual_state(const int* tables, const double* 
 // Row statistic of one chunk of one row: rows 0 .. N-1 of a request are
 // the target rows, rows N .. N + n_int - 1 the draft rows of the nodes with
 // children.
-template <int DT, int NE>
+// SETUP (trees of up to kSmallTree nodes): the nodes with a child come in
+// the argument `internal` and work-group 0 also writes the tree tables for
+// the launches after this one (no launch of its own).  Otherwise they come
+// from the tables k_tree_setup wrote.
+template <int DT, int NE, bool SETUP>
 __global__ __launch_bounds__(kThreads) void k_tree_stats(
     const void* __restrict__ target, const void* __restrict__ draft, int N, int n_int, int V,
-    int C1, float c, const int* __restrict__ tables, uint64_t* __restrict__ part) {
+    int C1, float c, TreeArgsN<kSmallTree> tree, TreeArgsN<kSmallTree> internal,
+    int* __restrict__ tables, uint64_t* __restrict__ part) {
+  if constexpr (SETUP) {
+    if (blockIdx.x == 0) tree_setup_block<kSmallTree>(tree, N, tables);
+  }
   const long idx = blockIdx.x;
   const int chunk = static_cast<int>(idx % C1);
   const int rr = static_cast<int>((idx / C1) % (N + n_int));
@@ -273,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(
     slot = rr;
     rp = static_cast<const char*>(target) + ((long)b * N + node) * V * eb;
   } else {
-    node = tree_tab(tables, kTabInternal)[rr - N];
+    node = SETUP ? internal.parent[rr - N] : tree_tab(tables, kTabInternal)[rr - N];
     slot = N + node;
     rp = static_cast<const char*>(draft) + ((long)b * N + node) * V * eb;
   }
@@ -335,13 +380,38 @@ __global__ __launch_bounds__(kThreads) void k_tree_mass(
   for (int t = 0; t < kTreeChunksPerWave; ++t) {
     const long ch = (long)g * kTreeChunksPerGroup + wave * kTreeChunksPerWave + t;
     if (ch >= C2) break;  // wave-uniform
-    double run[kSegPerThread], base;
-    const double tot = chunk_scan<DT, NE, KIND>(prow, qrow, V, ch, C, true, k, tab, run, base);
+    const double tot = chunk_total<DT, NE, KIND>(prow, qrow, V, ch, C, k, tab);
     if (lane == 0) out[ch] = tot;
   }
 }
 
-// The walk: one wave per request.
+// tree_rows on one wave: the partials of both rows are loaded by the lanes
+// at once (one round trip), then folded in chunk order as tree_rows does,
+// so the statistics are the same numbers.
+__device__ __forceinline__ RowPair tree_rows_wave(const uint64_t* part, int b, int N, int u,
+                                                  int C1, float c) {
+  const int lane = threadIdx.x & 63;
+  const long base_a = ((long)b * 2 * N + u) * C1, base_b = ((long)b * 2 * N + N + u) * C1;
+  RowPair r;
+  r.mp = r.mq = -INFINITY;
+  r.sp = r.sq = 0.0;
+  for (int c0 = 0; c0 < C1; c0 += kWaveSize / 2) {  // wave-uniform
+    const int n = min(kWaveSize / 2, C1 - c0);
+    const int half = lane >> 5, i = lane & 31;
+    uint64_t w = 0;
+    if (i < n) w = ld_dev(&part[(half ? base_b : base_a) + c0 + i]);
+    for (int j = 0; j < n; ++j) {
+      fold_partial(r.mp, r.sp, __shfl(w, j, kWaveSize), c);
+      fold_partial(r.mq, r.sq, __shfl(w, 32 + j, kWaveSize), c);
+    }
+  }
+  return r;
+}
+
+// The walk: one wave per request.  The tree tables come into shared memory
+// once per work-group and the request's node tokens once per wave; at each
+// node the children's tokens, values and uniforms are fetched by their own
+// lanes together, and the tests then run in child order.
 template <int DT, int KIND>
 __global__ __launch_bounds__(kThreads) void k_tree_walk(
     const void* __restrict__ target, const void* __restrict__ draft, int B, int N, int V, int C1,
@@ -352,52 +422,74 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_path) {
   __shared__ double tab[256];
+  __shared__ int s_nchild[kMaxNodes], s_first[kMaxNodes], s_next[kMaxNodes];
+  __shared__ int s_tok[kWaves][kMaxNodes];
   __shared__ int s_path[kWaves][kMaxNodes];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = static_cast<int>(blockIdx.x) * kWaves + wave;
   if (KIND == 0) tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
+  for (int j = threadIdx.x; j < N; j += kThreads) {
+    s_nchild[j] = tree_tab(tables, kTabNChild)[j];
+    s_first[j] = tree_tab(tables, kTabFirst)[j];
+    s_next[j] = tree_tab(tables, kTabNext)[j];
+  }
+  int* tok = s_tok[wave];
+  if (b < B)
+    for (int j = lane; j < N; j += kWaveSize) tok[j] = node_tokens[(long)b * N + j];
   __syncthreads();
-  const int b = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (b >= B) return;  // wave-uniform
-  const int lane = threadIdx.x & 63;
   const long eb = Elems<DT>::kBytes;
-  const int* nchild = tree_tab(tables, kTabNChild);
-  const int* first = tree_tab(tables, kTabFirst);
-  const int* next = tree_tab(tables, kTabNext);
-  int* path = s_path[threadIdx.x >> 6];
+  int* path = s_path[wave];
   int cur = 0, depth = 0;
   double cf = 0.0, cp = 0.0;
   if (lane == 0) path[0] = 0;
   for (;;) {
-    const int m = nchild[cur];
+    const int m = s_nchild[cur];
     if (m == 0) break;  // a leaf: the bonus draw from its target row
     RowPair rows{};
-    if (KIND == 0) rows = tree_rows(part, b, N, cur, C1, c, true);
+    if (KIND == 0) rows = tree_rows_wave(part, b, N, cur, C1, c);
     const TermCoef k = term_coef<KIND>(rows, c);
     const char* prow = static_cast<const char*>(target) + ((long)b * N + cur) * V * eb;
     const char* qrow = static_cast<const char*>(draft) + ((long)b * N + cur) * V * eb;
     double C = 0.0, M = 1.0;
     int acc = -1;
-    int i = 0;
-    for (int j = first[cur]; j >= 0; j = next[j], ++i) {
-      if (i > 0) {
-        const double cn = C + M;
-        const double F = wave_sum_fixed(mpart + ((long)b * N + j) * C2, C2);
-        if (F > 0.0) {
-          C = cn;
-          M = F;
+    int i0 = 0;
+    for (int j0 = s_first[cur]; j0 >= 0;) {  // children in tiles of 64, in order
+      // lane i: child i0 + i (its node, token, values at the token, uniform)
+      const int n_here = min(kWaveSize, m - i0);
+      int j = j0;
+      for (int s = 0; s < lane && s < n_here - 1; ++s) j = s_next[j];
+      double px = 0.0, qx = 0.0, uu = 0.0;
+      bool valid = false;
+      if (lane < n_here) {
+        const int x = tok[j];
+        valid = x >= 0 && x < V;
+        const int xs = valid ? x : 0;
+        px = tterm<KIND>(load_elem<DT>(prow, xs), k.c1, k.c0p, k.ip, tab);
+        qx = tterm<KIND>(load_elem<DT>(qrow, xs), k.c1, k.c0q, k.iq, tab);
+        uu = (double)get_uniform(uniforms, seed, ctr0, b, j, 0, N - 1);
+      }
+      for (int i = 0; i < n_here; ++i) {  // wave-uniform
+        const int ji = __shfl(j, i, kWaveSize);
+        if (i0 + i > 0) {
+          const double cn = C + M;
+          const double F = wave_sum_fixed(mpart + ((long)b * N + ji) * C2, C2);
+          if (F > 0.0) {
+            C = cn;
+            M = F;
+          }
+        }
+        const double pxi = __shfl(px, i, kWaveSize), qxi = __shfl(qx, i, kWaveSize);
+        const double ui = __shfl(uu, i, kWaveSize);
+        if (__shfl((int)valid, i, kWaveSize) && ui * qxi * M < fmax(0.0, pxi - C * qxi)) {
+          acc = ji;
+          break;
         }
       }
-      const int x = node_tokens[(long)b * N + j];
-      bool accept = false;
-      if (x >= 0 && x < V) {
-        const double px = tterm<KIND>(load_elem<DT>(prow, x), k.c1, k.c0p, k.ip, tab);
-        const double qx = tterm<KIND>(load_elem<DT>(qrow, x), k.c1, k.c0q, k.iq, tab);
-        const double u = (double)get_uniform(uniforms, seed, ctr0, b, j, 0, N - 1);
-        accept = u * qx * M < fmax(0.0, px - C * qx);
-      }
-      if (accept) {
-        acc = j;
-        break;
-      }
+      if (acc >= 0) break;
+      i0 += n_here;
+      if (i0 >= m) break;
+      j0 = s_next[__shfl(j, kWaveSize - 1, kWaveSize)];  // after the tile's last child
     }
     if (acc < 0) {  // every child rejected: draw from the residual
       cf = C + M;
@@ -410,11 +502,10 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
   }
   wave_lds_sync();
   // Outputs: the accepted path's tokens then -1 (the final token comes from
-  // k_tree_pick), the path, the draw state.
+  // k_tree_draw), the path, the draw state.
   for (int d = lane; d <= D; d += kWaveSize) {
     const int node = d <= depth ? path[d] : -1;
-    if (d >= 1 && d <= depth)
-      out_tokens[(long)b * (D + 1) + d - 1] = node_tokens[(long)b * N + node];
+    if (d >= 1 && d <= depth) out_tokens[(long)b * (D + 1) + d - 1] = tok[node];
     if (d > depth) out_tokens[(long)b * (D + 1) + d] = -1;
     if (out_path != nullptr) out_path[(long)b * (D + 1) + d] = node;
   }
@@ -429,98 +520,68 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
   }
 }
 
-// Draw weights of the stop node: chunk totals at cf (entry 0) and, after a
-// rejection, at cp (entry 1, used only if cf's weights have no mass).
+// The draw of request b by one wave, from the chunk totals dp (entry 0 at
+// cf, entry 1 at cp, as k_tree_draw stored them in this launch: coherent
+// loads): t = min{ j : P(c) + run_c(j) > u * total }, P(c) the running total
+// of the chunks before chunk c in chunk order.
 template <int DT, int NE, int KIND>
-__global__ __launch_bounds__(kThreads) void k_tree_draw_part(
-    const void* __restrict__ target, const void* __restrict__ draft, int N, int V, int C1, int C2,
-    float c, const TreeDraw* __restrict__ tstate, const uint64_t* __restrict__ part,
-    double* __restrict__ dpart) {
-  __shared__ double tab[256];
-  __shared__ RowPair s_rows;
-  const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
-  const int g = static_cast<int>(blockIdx.x % G);
-  const int b = static_cast<int>(blockIdx.x / G);
-  const TreeDraw st = tstate[b];
-  const bool use_q = st.cf > 0.0;
-  if (KIND == 0) {
-    tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
-    if (threadIdx.x == 0) s_rows = tree_rows(part, b, N, st.node, C1, c, use_q);
-  }
-  __syncthreads();
-  RowPair rows{};
-  if (KIND == 0) rows = s_rows;
-  const TermCoef k = term_coef<KIND>(rows, c);
-  const long eb = Elems<DT>::kBytes;
-  const void* prow = static_cast<const char*>(target) + ((long)b * N + st.node) * V * eb;
-  const void* qrow = static_cast<const char*>(draft) + ((long)b * N + st.node) * V * eb;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = 0; t < kTreeChunksPerWave; ++t) {
-    const long ch = (long)g * kTreeChunksPerGroup + wave * kTreeChunksPerWave + t;
-    if (ch >= C2) break;  // wave-uniform
-    double run[kSegPerThread], base;
-    const double tf =
-        chunk_scan<DT, NE, KIND>(prow, qrow, V, ch, st.cf, use_q, k, tab, run, base);
-    double tp = 0.0;
-    if (use_q)
-      tp = chunk_scan<DT, NE, KIND>(prow, qrow, V, ch, st.cp, st.cp > 0.0, k, tab, run, base);
-    if (lane == 0) {
-      dpart[((long)b * C2 + ch) * 2] = tf;
-      dpart[((long)b * C2 + ch) * 2 + 1] = tp;
-    }
-  }
-}
-
-// The draw: t = min{ j : P(c) + run_c(j) > u * total }, P(c) the running
-// total of the chunks before chunk c in chunk order.
-template <int DT, int NE, int KIND>
-__global__ __launch_bounds__(kThreads) void k_tree_pick(
-    const void* __restrict__ target, const void* __restrict__ draft, int B, int N, int V, int C1,
+__device__ __forceinline__ void tree_pick_wave(
+    const void* __restrict__ target, const void* __restrict__ draft, int b, int N, int V, int C1,
     int C2, int D, float c, const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
-    const TreeDraw* __restrict__ tstate, const uint64_t* __restrict__ part,
-    const double* __restrict__ dpart, int32_t* __restrict__ out_tokens) {
-  __shared__ double tab[256];
-  if (KIND == 0) tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
-  __syncthreads();
-  const int b = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (b >= B) return;  // wave-uniform
+    const TreeDraw& st, const uint64_t* __restrict__ part, const double* __restrict__ dp,
+    const double* tab, int32_t* __restrict__ out_tokens) {
   const int lane = threadIdx.x & 63;
-  const TreeDraw st = tstate[b];
-  const double* dp = dpart + (long)b * C2 * 2;
   int which = 0;
   double C = st.cf;
   bool use_q = st.cf > 0.0;
-  if (use_q && !(wave_sum_fixed(dp, C2, 2) > 0.0)) {  // empty residual: the weights before it
-    which = 1;
-    C = st.cp;
-    use_q = st.cp > 0.0;
+  if (use_q) {  // empty residual: the weights before the last rejection
+    double any = 0.0;
+    for (int ch = lane; ch < C2; ch += kWaveSize) any += ld_dev_d(&dp[(long)ch * 2]);
+    if (!(wave_sum_d(any) > 0.0)) {
+      which = 1;
+      C = st.cp;
+      use_q = st.cp > 0.0;
+    }
   }
-  // Running chunk totals, in chunk order, on lane 0 (the prefix the chunk
-  // scan's sums are added to; one order everywhere).
+  // Running chunk totals in chunk order: tiles of 64 chunks, lane l on
+  // chunk base + l, a wave scan per tile.  The grand total and the search
+  // below run the same scans, so they see the same prefixes.
   const double u = (double)get_uniform(uniforms, seed, ctr0, b, st.node, 1, N - 1);
+  auto tile = [&](int base, double running, double& v, double& excl) {
+    const int ch = base + lane;
+    v = ch < C2 ? ld_dev_d(&dp[(long)ch * 2 + which]) : 0.0;
+    const double inc = wave_inclusive_scan_d(v);
+    excl = running + (inc - v);
+    return running + __shfl(inc, 63, 64);  // running total after the tile
+  };
   double total = 0.0;
-  if (lane == 0)
-    for (int ch = 0; ch < C2; ++ch) total += dp[(long)ch * 2 + which];
-  total = __shfl(total, 0, 64);
+  for (int base = 0; base < C2; base += kWaveSize) {  // wave-uniform
+    double v, excl;
+    total = tile(base, total, v, excl);
+  }
   int tok = -1;
   if (total > 0.0) {
     const double thr = u * total;
+    // The first chunk whose running total exceeds thr, and the total of
+    // the chunks before it (past the end, a last-bit difference: the last).
     int sel = C2 - 1;
-    double P = 0.0;
-    if (lane == 0) {
-      double run = 0.0;
-      for (int ch = 0; ch < C2; ++ch) {
-        const double nx = run + dp[(long)ch * 2 + which];
-        if (nx > thr) {
-          sel = ch;
-          break;
-        }
-        run = nx;
+    double P = 0.0, running = 0.0;
+    for (int base = 0; base < C2; base += kWaveSize) {  // wave-uniform
+      double v, excl;
+      const double after = tile(base, running, v, excl);
+      const uint64_t mh = __ballot(base + lane < C2 && excl + v > thr);
+      if (mh != 0) {
+        const int f = __builtin_ctzll(mh);
+        sel = base + f;
+        P = __shfl(excl, f, 64);
+        break;
       }
-      P = run;
+      if (base + kWaveSize >= C2) {
+        P = __shfl(excl, C2 - 1 - base, 64);
+        break;
+      }
+      running = after;
     }
-    sel = __shfl(sel, 0, 64);
-    P = __shfl(P, 0, 64);
     RowPair rows{};
     if (KIND == 0) rows = tree_rows(part, b, N, st.node, C1, c, use_q);
     const TermCoef k = term_coef<KIND>(rows, c);
@@ -552,6 +613,62 @@ __global__ __launch_bounds__(kThreads) void k_tree_pick(
   if (lane == 0) out_tokens[(long)b * (D + 1) + st.depth] = tok;
 }
 
+// Draw weights of the stop node: chunk totals at cf (entry 0) and, after a
+// rejection, at cp (entry 1, used only if cf's weights have no mass); the
+// request's last work-group (completion ticket) then draws the token on one
+// wave.
+template <int DT, int NE, int KIND>
+__global__ __launch_bounds__(kThreads) void k_tree_draw(
+    const void* __restrict__ target, const void* __restrict__ draft, int N, int V, int C1, int C2,
+    int D, float c, const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    const TreeDraw* __restrict__ tstate, const uint64_t* __restrict__ part,
+    double* __restrict__ dpart, unsigned* __restrict__ counters,
+    int32_t* __restrict__ out_tokens) {
+  __shared__ double tab[256];
+  __shared__ RowPair s_rows;
+  const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
+  const int g = static_cast<int>(blockIdx.x % G);
+  const int b = static_cast<int>(blockIdx.x / G);
+  const TreeDraw st = tstate[b];
+  const bool use_q = st.cf > 0.0;
+  if (KIND == 0) {
+    tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
+    if (threadIdx.x == 0) s_rows = tree_rows(part, b, N, st.node, C1, c, use_q);
+  }
+  __syncthreads();
+  RowPair rows{};
+  if (KIND == 0) rows = s_rows;
+  const TermCoef k = term_coef<KIND>(rows, c);
+  const long eb = Elems<DT>::kBytes;
+  const void* prow = static_cast<const char*>(target) + ((long)b * N + st.node) * V * eb;
+  const void* qrow = static_cast<const char*>(draft) + ((long)b * N + st.node) * V * eb;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double* dp = dpart + (long)b * C2 * 2;
+  for (int t = 0; t < kTreeChunksPerWave; ++t) {
+    const long ch = (long)g * kTreeChunksPerGroup + wave * kTreeChunksPerWave + t;
+    if (ch >= C2) break;  // wave-uniform
+    double run[kSegPerThread], base;
+    const double tf =
+        chunk_scan<DT, NE, KIND>(prow, qrow, V, ch, st.cf, use_q, k, tab, run, base);
+    double tp = 0.0;
+    if (use_q)
+      tp = chunk_scan<DT, NE, KIND>(prow, qrow, V, ch, st.cp, st.cp > 0.0, k, tab, run, base);
+    if (lane == 0) {
+      st_dev_d(&dp[ch * 2], tf);
+      st_dev_d(&dp[ch * 2 + 1], tp);
+    }
+  }
+  wait_stores();  // every wave's totals complete before the ticket below
+  __syncthreads();
+  if (!block_arrive(&counters[(long)b * kCountersPerReq + 1], (unsigned)G)) return;
+  if (wave != 0) return;
+  // The last work-group of request b: it decides when the request ends
+  // while the others stream, so it issues first.
+  __builtin_amdgcn_s_setprio(3);
+  tree_pick_wave<DT, NE, KIND>(target, draft, b, N, V, C1, C2, D, c, uniforms, seed, ctr0, st,
+                               part, dp, tab, out_tokens);
+}
+
 // ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
@@ -579,23 +696,35 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
   auto* dpart = reinterpret_cast<double*>(w + L.part2);
   auto* tstate = reinterpret_cast<TreeDraw*>(w + L.tstate);
   static_assert(sizeof(TreeDraw) <= kTreeDrawBytes, "draw state fits its region");
-  hipError_t e;
-  if (N <= kSmallTree) {
-    // a small argument block: launches with a 2 KiB one start much later
-    TreeArgsN<kSmallTree> small;
-    for (int j = 0; j < kSmallTree; ++j) small.parent[j] = j < N ? tree.parent[j] : 0;
-    e = launch_timed(kProfTreeWalk, &k_tree_setup<kSmallTree>, dim3(1), dim3(kThreads), 0, s,
-                     small, N, tables);
-  } else {
+  hipError_t e = hipSuccess;
+  // Small trees: small argument blocks (launches with a 2 KiB one start
+  // much later), and with logits the tables come from the row-statistics
+  // launch (its first work-group), not a launch of their own.
+  const bool small = N <= kSmallTree;
+  TreeArgsN<kSmallTree> small_tree{}, internal{};
+  if (small) {
+    for (int j = 0; j < N; ++j) small_tree.parent[j] = tree.parent[j];
+    int n = 0;
+    for (int j = 0; j < N; ++j)
+      if (shape.has_child[j]) internal.parent[n++] = (int16_t)j;
+  }
+  if (!small)
     e = launch_timed(kProfTreeWalk, &k_tree_setup<kMaxNodes>, dim3(1), dim3(kThreads), 0, s,
                      tree, N, tables);
-  }
+  else if (KIND != 0)
+    e = launch_timed(kProfTreeWalk, &k_tree_setup<kSmallTree>, dim3(1), dim3(kThreads), 0, s,
+                     small_tree, N, tables);
   if (e != hipSuccess) return e;
   if (KIND == 0) {
     const long blocks = (long)B * (N + shape.n_internal) * C1;
-    e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE>, dim3((unsigned)blocks),
-                     dim3(kThreads), 0, s, target, draft, N, shape.n_internal, V, C1, c,
-                     (const int*)tables, part);
+    if (small)
+      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, true>, dim3((unsigned)blocks),
+                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, V, C1, c,
+                       small_tree, internal, tables, part);
+    else
+      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, false>, dim3((unsigned)blocks),
+                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, V, C1, c,
+                       small_tree, internal, tables, part);
     if (e != hipSuccess) return e;
   }
   const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
@@ -614,14 +743,10 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
                    ctr0, (const int*)tables, (const uint64_t*)part, (const double*)mpart, tstate,
                    accepted_len, out_tokens, out_path);
   if (e != hipSuccess) return e;
-  e = launch_timed(kProfTreeDraw, &k_tree_draw_part<DT, NE, KIND>, dim3((unsigned)((long)B * G)),
-                   dim3(kThreads), 0, s, target, draft, N, V, C1, C2, c,
-                   (const TreeDraw*)tstate, (const uint64_t*)part, dpart);
-  if (e != hipSuccess) return e;
-  return launch_timed(kProfTreeDraw, &k_tree_pick<DT, NE, KIND>, dim3(wgs), dim3(kThreads), 0, s,
-                      target, draft, B, N, V, C1, C2, shape.depth, c, uniforms, seed, ctr0,
-                      (const TreeDraw*)tstate, (const uint64_t*)part, (const double*)dpart,
-                      out_tokens);
+  return launch_timed(kProfTreeDraw, &k_tree_draw<DT, NE, KIND>, dim3((unsigned)((long)B * G)),
+                      dim3(kThreads), 0, s, target, draft, N, V, C1, C2, shape.depth, c,
+                      uniforms, seed, ctr0, (const TreeDraw*)tstate, (const uint64_t*)part,
+                      dpart, reinterpret_cast<unsigned*>(w + L.count), out_tokens);
 }
 
 hipError_t launch_tree_sample(const void* target, const void* draft, int dtype, int kind, int B,
