@@ -295,7 +295,8 @@ int spec_verify_tree_sample(const void* target, const void* draft, int dtype, in
     }
   }
   const long C2 = (V + kDrawChunk - 1) / kDrawChunk;
-  if (check_grid((long)B * (n_nodes + shape.n_internal) * row_chunks_for(V)) != SPEC_OK ||
+  if (check_grid((long)B * (2L * shape.n_internal * tree_xchunks(V) +
+                            (long)n_nodes * row_chunks_for(V))) != SPEC_OK ||
       check_grid((long)B * n_nodes * C2) != SPEC_OK)
     return SPEC_EINVAL;
   WsLayout L;

@@ -124,10 +124,17 @@ static_assert(SPEC_WORKSPACE_STATUS_OFFSET == kStatusWord * 4, "status word offs
 // has a tag of its own, so a tag left by an earlier call (or any other
 // content) is never taken for a current one.  The other regions are written
 // before they are read within each call.
-// Tree-sampling regions: the tree tables (nine int32 tables of kMaxNodes)
-// and the per-request draw state.
+// Tree-sampling regions: the tree tables (nine int32 tables of kMaxNodes),
+// the per-request draw state and the float64 row statistics.
 constexpr size_t kTreeTableBytes = 10 * (size_t)kMaxNodes * 4;
 constexpr size_t kTreeDrawBytes = 32;
+constexpr size_t kTreeStatBytes = 16;  // float64 row statistic of one row chunk
+// Tree rows that carry the float64 statistic are cut into chunks of this
+// many elements (one work-group each: float64 terms are ALU work).
+constexpr int kTreeStatChunk = 16384;
+__host__ __device__ inline int tree_xchunks(int V) {
+  return (V + kTreeStatChunk - 1) / kTreeStatChunk;
+}
 
 struct WsLayout {
   size_t count;  // counter region, always at offset 0
@@ -139,6 +146,7 @@ struct WsLayout {
   size_t part3;  // double [B * n_pos * res_chunks]: tree sampling's residual masses
   size_t tree;   // tree tables (kTreeTableBytes)
   size_t tstate; // tree sampling's draw state, kTreeDrawBytes per request
+  size_t xstat;  // tree sampling's float64 row statistics, [rows * row_chunks]
   size_t total;
 };
 
@@ -171,6 +179,8 @@ inline WsLayout ws_layout(int B, int n_pos, int V) {
   off = align_up(off + kTreeTableBytes, 256);
   L.tstate = off;
   off = align_up(off + (size_t)B * kTreeDrawBytes, 256);
+  L.xstat = off;
+  off = align_up(off + rows * (size_t)tree_xchunks(V) * kTreeStatBytes, 256);
   L.total = off;
   return L;
 }

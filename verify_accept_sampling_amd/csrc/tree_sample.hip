@@ -157,36 +157,98 @@ __global__ __launch_bounds__(kThreads) void k_tree_setup(TreeArgsN<NMAX> tree, i
 // Shared pieces
 // ---------------------------------------------------------------------------
 
-// Row statistics (reference M, sum S) of target row u and draft row u of
-// request b, whose chunk partials k_tree_stats stored at rows b*2N + u and
-// b*2N + N + u.
+// Float64 row statistic of one chunk of a row: a reference m (a logit) and
+// S = sum over the chunk of e^{(x - m)/T}, every term a float64 exp.  The
+// rows of nodes with children (both of their rows) carry this statistic,
+// so that the tests, the masses and the draws there use the distributions
+// softmax(z/T) to float64 precision, as the oracle does; a leaf's target
+// row keeps the float32 statistic (only its reference is used: its bonus
+// draw normalises its own weights).
+struct TreeStat64 {
+  double m, s;
+};
+
+
+// (m, s) <- the pair's merge at the larger reference; exp2_256(0) = 1
+// exactly, so the side that holds it keeps its sum.
+__device__ __forceinline__ void ms64_merge(float& m, double& s, float m2, double s2, double c1,
+                                           const double* tab) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  if (m == m2) {  // the usual case: both sides kept the row's first reference
+    s += s2;
+    return;
+  }
+  const float mn = fmaxf(m, m2);
+  s = s * exp2_256(((double)m - (double)mn) * c1, tab) +
+      s2 * exp2_256(((double)m2 - (double)mn) * c1, tab);
+  m = mn;
+}
+
+// Row statistics of target row u and draft row u of request b.  Nodes with
+// children (`internal`): the float64 statistics k_tree_stats stored at
+// slots b*2N + u and b*2N + N + u (tree_xchunks(V) chunks each), merged in
+// chunk order.  A leaf: the
+// reference of its target row's float32 statistic, with S = 1 (its weights
+// are normalised by their own total).
 struct RowPair {
   float mp, mq;
   double sp, sq;
 };
-__device__ __forceinline__ RowPair tree_rows(const uint64_t* part, int b, int N, int u, int C1,
-                                             float c, bool with_q) {
+__device__ __forceinline__ RowPair node_rows(const TreeStat64* xs, const uint64_t* part, int b,
+                                             int N, int u, int V, int C1, float c, double c1,
+                                             const double* tab, bool internal) {
   RowPair r;
+  r.mp = r.mq = -INFINITY;
+  r.sp = r.sq = 0.0;
   const long base = (long)b * 2 * N;
-  merge_two_rows(part, (base + u) * C1, (base + N + u) * C1, with_q, C1, c, r.mp, r.sp, r.mq,
-                 r.sq);
+  if (internal) {
+    const int Cx = tree_xchunks(V);
+    const TreeStat64* xa = xs + (base + u) * Cx;
+    const TreeStat64* xd = xs + (base + N + u) * Cx;
+    constexpr int kBatch = 8;  // loads requested together
+    for (int c0 = 0; c0 < Cx; c0 += kBatch) {
+      TreeStat64 a[kBatch], d[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int ch = min(c0 + i, Cx - 1);
+        a[i] = xa[ch];
+        d[i] = xd[ch];
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (c0 + i < Cx) {
+          ms64_merge(r.mp, r.sp, (float)a[i].m, a[i].s, c1, tab);
+          ms64_merge(r.mq, r.sq, (float)d[i].m, d[i].s, c1, tab);
+        }
+      }
+    }
+  } else {
+    float mq;
+    double sq;
+    merge_two_rows(part, (base + u) * C1, (base + N + u) * C1, false, C1, c, r.mp, r.sp, mq, sq);
+    r.sp = 1.0;
+  }
   return r;
 }
 
-// Normalised-term coefficients: p_j = 2^(t/256) / S with
-// t = z * 256 c - 256 fl32(M c), i.e. 2^(z c - fl32(M c)) / S, the
-// distribution the float32 row statistic describes.  Probability rows are
-// used as given.
+// Term coefficients: p_j = 2^(t/256) / S with t = z c1 - fl(m c1),
+// c1 = 256 / (T ln 2), i.e. e^{(z - m)/T} / S.  Probability rows are used
+// as given.
 struct TermCoef {
   double c1, c0p, c0q, ip, iq;
 };
 template <int KIND>
-__device__ __forceinline__ TermCoef term_coef(const RowPair& r, float c) {
+__device__ __forceinline__ TermCoef term_coef(const RowPair& r, double c1) {
   TermCoef k;
   if (KIND == 0) {
-    k.c1 = 256.0 * (double)c;
-    k.c0p = -256.0 * (double)mul_rn(r.mp, c);
-    k.c0q = -256.0 * (double)mul_rn(r.mq, c);
+    k.c1 = c1;
+    k.c0p = -((double)r.mp * c1);
+    k.c0q = -((double)r.mq * c1);
     k.ip = 1.0 / r.sp;
     k.iq = 1.0 / r.sq;
   } else {
@@ -291,37 +353,153 @@ __device__ __forceinline__ void residual_state(const int* tables, const double* 
 // Kernels
 // ---------------------------------------------------------------------------
 
-// Row statistic of one chunk of one row: rows 0 .. N-1 of a request are
-// the target rows, rows N .. N + n_int - 1 the draft rows of the nodes with
-// children.
-// SETUP (trees of up to kSmallTree nodes): the nodes with a child come in
-// the argument `internal` and work-group 0 also writes the tree tables for
-// the launches after this one (no launch of its own).  Otherwise they come
-// from the tables k_tree_setup wrote.
+// Float64 statistic of this thread's groups g0 + tid, g0 + tid + NT, ...
+// below g1 (16-byte words of NE elements; NE = 1: elements), relative to
+// the reference m0 on entry (the row's first element, the same for every
+// chunk of the row, so that the chunks' sums add without rescaling; -inf
+// when that element is not finite).  The reference moves up (rescaling the
+// sum) only when an element exceeds it by more than kRefSlack in the scaled
+// exponent, so every term and the sum stay far below overflow, and a first
+// finite element sets it when there is none.
+constexpr double kRefSlack = 256.0 * 400.0;  // terms below 2^400
+template <int DT, int NE>
+__device__ __forceinline__ void stats64_thread(const void* rp, uint32_t row_bytes, long g0,
+                                               long g1, double c1, const double* tab, float& m,
+                                               double& s) {
+  s = 0.0;
+  double mc = m == -INFINITY ? 0.0 : -((double)m * c1);
+  const double lim = kRefSlack / c1;  // in logit units
+  auto fold = [&](const float (&x)[NE]) {
+    float bm = x[0];
+#pragma unroll
+    for (int e = 1; e < NE; ++e) bm = fmaxf(bm, x[e]);
+    if ((double)bm > (double)m + lim) {  // rare: a first finite element, or far above
+      if (m != -INFINITY) s *= exp2_256(((double)m - (double)bm) * c1, tab);
+      m = bm;
+      mc = -((double)m * c1);
+    }
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) s += exp2_256(fma((double)x[e], c1, mc), tab);
+    }
+  };
+  if constexpr (NE == 1) {
+    for (long g = g0 + threadIdx.x; g < g1; g += kThreads) {
+      const float x[1] = {load_elem<DT>(rp, g)};
+      fold(x);
+    }
+  } else {
+    // All of a chunk's words (up to U per thread) are requested before any
+    // is used; a word past g1 is not loaded (its offset is past the row's
+    // buffer) and not used.
+    constexpr int U = 8;
+    const RowBuf buf(rp, row_bytes);
+    for (long g = g0 + threadIdx.x; g < g1; g += (long)U * kThreads) {
+      u32x4 w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        w[u] = buf.load_nt(g + (long)u * kThreads < g1
+                               ? static_cast<uint32_t>(g + (long)u * kThreads) * 16u
+                               : 0xfffffff0u,
+                           0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (g + (long)u * kThreads < g1) {
+          float x[NE];
+          unpack16<DT>(w[u], x);
+          fold(x);
+        }
+      }
+    }
+  }
+}
+
+// Work-group merge of the threads' float64 statistics; the result is valid
+// in thread 0.
+__device__ __forceinline__ void block_reduce_ms64(float& m, double& s, double c1,
+                                                  const double* tab) {
+  __shared__ float sm[kWaves];
+  __shared__ double ss[kWaves];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = shfl_xor_f(m, o);
+    const double s2 = shfl_xor_d(s, o);
+    ms64_merge(m, s, m2, s2, c1, tab);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    sm[wave] = m;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = sm[0];
+    s = ss[0];
+    for (int w = 1; w < kWaves; ++w) ms64_merge(m, s, sm[w], ss[w], c1, tab);
+  }
+}
+
+// Row statistics.  The grid has two parts:
+//   A. the rows of the nodes with children -- per request the target rows,
+//      then the draft rows, of nodes internal[0 .. n_int-1] -- in chunks of
+//      kTreeStatChunk elements, with the float64 statistic (xstat), first,
+//      so that these long work-groups start in the first round;
+//   B. the target rows of the leaves, in C1 chunks, with the float32
+//      statistic (part).
+// SETUP (trees of up to kSmallTree nodes): the nodes with and without a
+// child come in the arguments `internal` and `leaves`, and work-group 0
+// also writes the tree tables for the launches after this one (no launch
+// of its own).  Otherwise the nodes with a child come from the tables
+// k_tree_setup wrote, and part B covers every target row, those of nodes
+// with a child leaving at once.
 template <int DT, int NE, bool SETUP>
 __global__ __launch_bounds__(kThreads) void k_tree_stats(
-    const void* __restrict__ target, const void* __restrict__ draft, int N, int n_int, int V,
-    int C1, float c, TreeArgsN<kSmallTree> tree, TreeArgsN<kSmallTree> internal,
-    int* __restrict__ tables, uint64_t* __restrict__ part) {
+    const void* __restrict__ target, const void* __restrict__ draft, int N, int n_int, int n_b,
+    int V, int C1, float c, double c1, TreeArgsN<kSmallTree> tree,
+    TreeArgsN<kSmallTree> internal, TreeArgsN<kSmallTree> leaves, int* __restrict__ tables,
+    uint64_t* __restrict__ part, TreeStat64* __restrict__ xstat) {
+  __shared__ double tab[256];
   if constexpr (SETUP) {
     if (blockIdx.x == 0) tree_setup_block<kSmallTree>(tree, N, tables);
   }
-  const long idx = blockIdx.x;
-  const int chunk = static_cast<int>(idx % C1);
-  const int rr = static_cast<int>((idx / C1) % (N + n_int));
-  const int b = static_cast<int>(idx / C1 / (N + n_int));
+  const int Cx = tree_xchunks(V);
   const long eb = Elems<DT>::kBytes;
-  int node, slot;
-  const void* rp;
-  if (rr < N) {
-    node = rr;
-    slot = rr;
-    rp = static_cast<const char*>(target) + ((long)b * N + node) * V * eb;
-  } else {
-    node = SETUP ? internal.parent[rr - N] : tree_tab(tables, kTabInternal)[rr - N];
-    slot = N + node;
-    rp = static_cast<const char*>(draft) + ((long)b * N + node) * V * eb;
+  const long nA = (long)gridDim.x - (long)n_b;  // part B has n_b work-groups
+  const long idx = blockIdx.x;
+  if (idx < nA) {  // part A: float64
+    const int chunk = static_cast<int>(idx % Cx);
+    const int j = static_cast<int>((idx / Cx) % (2 * n_int));
+    const int b = static_cast<int>(idx / Cx / (2 * n_int));
+    const int jj = j < n_int ? j : j - n_int;
+    const int node = SETUP ? internal.parent[jj] : tree_tab(tables, kTabInternal)[jj];
+    const bool is_draft = j >= n_int;
+    const void* rp = static_cast<const char*>(is_draft ? draft : target) +
+                     ((long)b * N + node) * V * eb;
+    const int slot = is_draft ? N + node : node;
+    const long n_groups = V / NE;
+    const long gpc = (n_groups + Cx - 1) / Cx;
+    const long g0 = (long)chunk * gpc;
+    const long g1 = min(g0 + gpc, n_groups);
+    tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
+    __syncthreads();
+    const float z0 = load_elem<DT>(rp, 0);
+    float m = z0 > -INFINITY && z0 < INFINITY ? z0 : -INFINITY;
+    double s;
+    stats64_thread<DT, NE>(rp, static_cast<uint32_t>((long)V * eb), g0, g1, c1, tab, m, s);
+    block_reduce_ms64(m, s, c1, tab);
+    if (threadIdx.x == 0) xstat[((long)b * 2 * N + slot) * Cx + chunk] = TreeStat64{m, s};
+    return;
   }
+  // part B: float32
+  const long i2 = idx - nA;
+  const int n_rows = SETUP ? N - n_int : N;
+  const int chunk = static_cast<int>(i2 % C1);
+  const int j = static_cast<int>((i2 / C1) % n_rows);
+  const int b = static_cast<int>(i2 / C1 / n_rows);
+  const int node = SETUP ? leaves.parent[j] : j;
+  if (!SETUP && tree_tab(tables, kTabNChild)[node] > 0) return;  // in part A
+  const void* rp = static_cast<const char*>(target) + ((long)b * N + node) * V * eb;
   const long n_groups = V / NE;
   const long gpc = (n_groups + C1 - 1) / C1;
   const long g0 = (long)chunk * gpc;
@@ -334,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(
     stats_sweep<DT, kThreads>(rp, static_cast<uint32_t>((long)V * eb), g0, g1, c, m, mc, s,
                               threadIdx.x);
   block_reduce_ms(m, s, c);
-  if (threadIdx.x == 0) part[((long)b * 2 * N + slot) * C1 + chunk] = pack2(m, (float)s);
+  if (threadIdx.x == 0) part[((long)b * 2 * N + node) * C1 + chunk] = pack2(m, (float)s);
 }
 
 // Work-groups cover kTreeChunksPerGroup consecutive chunks of one row pair.
@@ -346,8 +524,9 @@ constexpr int kTreeChunksPerGroup = kWaves * kTreeChunksPerWave;
 template <int DT, int NE, int KIND>
 __global__ __launch_bounds__(kThreads) void k_tree_mass(
     const void* __restrict__ target, const void* __restrict__ draft, int N, int V, int C1,
-    int C2, float c, int r, int n_units, const int* __restrict__ tables,
-    const uint64_t* __restrict__ part, double* __restrict__ mpart) {
+    int C2, float c, double c1, int r, int n_units, const int* __restrict__ tables,
+    const uint64_t* __restrict__ part, const TreeStat64* __restrict__ xstat,
+    double* __restrict__ mpart) {
   __shared__ double tab[256];
   __shared__ RowPair s_rows;
   __shared__ double s_C;
@@ -359,19 +538,20 @@ __global__ __launch_bounds__(kThreads) void k_tree_mass(
   const int j = tree_tab(tables, kTabRanked)[tree_tab(tables, kTabRankOff)[r - 1] + unit];
   const int u = tree_tab(tables, kTabParent)[j];
   if (KIND == 0) tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
+  __syncthreads();
   if (threadIdx.x < kWaveSize) {
     double C, M;
     residual_state(tables, mpart, b, N, C2, u, r - 1, C, M);
     if (threadIdx.x == 0) {
       s_C = C + M;
-      if (KIND == 0) s_rows = tree_rows(part, b, N, u, C1, c, true);
+      if (KIND == 0) s_rows = node_rows(xstat, part, b, N, u, V, C1, c, c1, tab, true);
     }
   }
   __syncthreads();
   const double C = s_C;
   RowPair rows{};
   if (KIND == 0) rows = s_rows;
-  const TermCoef k = term_coef<KIND>(rows, c);
+  const TermCoef k = term_coef<KIND>(rows, c1);
   const long eb = Elems<DT>::kBytes;
   const void* prow = static_cast<const char*>(target) + ((long)b * N + u) * V * eb;
   const void* qrow = static_cast<const char*>(draft) + ((long)b * N + u) * V * eb;
@@ -385,29 +565,6 @@ __global__ __launch_bounds__(kThreads) void k_tree_mass(
   }
 }
 
-// tree_rows on one wave: the partials of both rows are loaded by the lanes
-// at once (one round trip), then folded in chunk order as tree_rows does,
-// so the statistics are the same numbers.
-__device__ __forceinline__ RowPair tree_rows_wave(const uint64_t* part, int b, int N, int u,
-                                                  int C1, float c) {
-  const int lane = threadIdx.x & 63;
-  const long base_a = ((long)b * 2 * N + u) * C1, base_b = ((long)b * 2 * N + N + u) * C1;
-  RowPair r;
-  r.mp = r.mq = -INFINITY;
-  r.sp = r.sq = 0.0;
-  for (int c0 = 0; c0 < C1; c0 += kWaveSize / 2) {  // wave-uniform
-    const int n = min(kWaveSize / 2, C1 - c0);
-    const int half = lane >> 5, i = lane & 31;
-    uint64_t w = 0;
-    if (i < n) w = ld_dev(&part[(half ? base_b : base_a) + c0 + i]);
-    for (int j = 0; j < n; ++j) {
-      fold_partial(r.mp, r.sp, __shfl(w, j, kWaveSize), c);
-      fold_partial(r.mq, r.sq, __shfl(w, 32 + j, kWaveSize), c);
-    }
-  }
-  return r;
-}
-
 // The walk: one wave per request.  The tree tables come into shared memory
 // once per work-group and the request's node tokens once per wave; at each
 // node the children's tokens, values and uniforms are fetched by their own
@@ -415,9 +572,9 @@ __device__ __forceinline__ RowPair tree_rows_wave(const uint64_t* part, int b, i
 template <int DT, int KIND>
 __global__ __launch_bounds__(kThreads) void k_tree_walk(
     const void* __restrict__ target, const void* __restrict__ draft, int B, int N, int V, int C1,
-    int C2, int D, float c, const int32_t* __restrict__ node_tokens,
+    int C2, int D, double c1, const int32_t* __restrict__ node_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
-    const int* __restrict__ tables, const uint64_t* __restrict__ part,
+    const int* __restrict__ tables, const TreeStat64* __restrict__ xstat,
     const double* __restrict__ mpart, TreeDraw* __restrict__ tstate,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_path) {
@@ -447,8 +604,10 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
     const int m = s_nchild[cur];
     if (m == 0) break;  // a leaf: the bonus draw from its target row
     RowPair rows{};
-    if (KIND == 0) rows = tree_rows_wave(part, b, N, cur, C1, c);
-    const TermCoef k = term_coef<KIND>(rows, c);
+    // every lane merges the chunk statistics itself (uniform loads, one
+    // round trip; the same numbers as in the other kernels)
+    if (KIND == 0) rows = node_rows(xstat, nullptr, b, N, cur, V, 0, 0.f, c1, tab, true);
+    const TermCoef k = term_coef<KIND>(rows, c1);
     const char* prow = static_cast<const char*>(target) + ((long)b * N + cur) * V * eb;
     const char* qrow = static_cast<const char*>(draft) + ((long)b * N + cur) * V * eb;
     double C = 0.0, M = 1.0;
@@ -527,9 +686,10 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
 template <int DT, int NE, int KIND>
 __device__ __forceinline__ void tree_pick_wave(
     const void* __restrict__ target, const void* __restrict__ draft, int b, int N, int V, int C1,
-    int C2, int D, float c, const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
-    const TreeDraw& st, const uint64_t* __restrict__ part, const double* __restrict__ dp,
-    const double* tab, int32_t* __restrict__ out_tokens) {
+    int C2, int D, float c, double c1, const float* __restrict__ uniforms, uint64_t seed,
+    uint64_t ctr0, const TreeDraw& st, const uint64_t* __restrict__ part,
+    const TreeStat64* __restrict__ xstat, const double* __restrict__ dp, const double* tab,
+    int32_t* __restrict__ out_tokens) {
   const int lane = threadIdx.x & 63;
   int which = 0;
   double C = st.cf;
@@ -583,8 +743,8 @@ __device__ __forceinline__ void tree_pick_wave(
       running = after;
     }
     RowPair rows{};
-    if (KIND == 0) rows = tree_rows(part, b, N, st.node, C1, c, use_q);
-    const TermCoef k = term_coef<KIND>(rows, c);
+    if (KIND == 0) rows = node_rows(xstat, part, b, N, st.node, V, C1, c, c1, tab, st.cf > 0.0);
+    const TermCoef k = term_coef<KIND>(rows, c1);
     const long eb = Elems<DT>::kBytes;
     const void* prow = static_cast<const char*>(target) + ((long)b * N + st.node) * V * eb;
     const void* qrow = static_cast<const char*>(draft) + ((long)b * N + st.node) * V * eb;
@@ -620,10 +780,10 @@ __device__ __forceinline__ void tree_pick_wave(
 template <int DT, int NE, int KIND>
 __global__ __launch_bounds__(kThreads) void k_tree_draw(
     const void* __restrict__ target, const void* __restrict__ draft, int N, int V, int C1, int C2,
-    int D, float c, const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
+    int D, float c, double c1, const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     const TreeDraw* __restrict__ tstate, const uint64_t* __restrict__ part,
-    double* __restrict__ dpart, unsigned* __restrict__ counters,
-    int32_t* __restrict__ out_tokens) {
+    const TreeStat64* __restrict__ xstat, double* __restrict__ dpart,
+    unsigned* __restrict__ counters, int32_t* __restrict__ out_tokens) {
   __shared__ double tab[256];
   __shared__ RowPair s_rows;
   const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
@@ -633,12 +793,13 @@ __global__ __launch_bounds__(kThreads) void k_tree_draw(
   const bool use_q = st.cf > 0.0;
   if (KIND == 0) {
     tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
-    if (threadIdx.x == 0) s_rows = tree_rows(part, b, N, st.node, C1, c, use_q);
+    __syncthreads();
+    if (threadIdx.x == 0) s_rows = node_rows(xstat, part, b, N, st.node, V, C1, c, c1, tab, use_q);
   }
   __syncthreads();
   RowPair rows{};
   if (KIND == 0) rows = s_rows;
-  const TermCoef k = term_coef<KIND>(rows, c);
+  const TermCoef k = term_coef<KIND>(rows, c1);
   const long eb = Elems<DT>::kBytes;
   const void* prow = static_cast<const char*>(target) + ((long)b * N + st.node) * V * eb;
   const void* qrow = static_cast<const char*>(draft) + ((long)b * N + st.node) * V * eb;
@@ -665,8 +826,8 @@ __global__ __launch_bounds__(kThreads) void k_tree_draw(
   // The last work-group of request b: it decides when the request ends
   // while the others stream, so it issues first.
   __builtin_amdgcn_s_setprio(3);
-  tree_pick_wave<DT, NE, KIND>(target, draft, b, N, V, C1, C2, D, c, uniforms, seed, ctr0, st,
-                               part, dp, tab, out_tokens);
+  tree_pick_wave<DT, NE, KIND>(target, draft, b, N, V, C1, C2, D, c, c1, uniforms, seed, ctr0,
+                               st, part, xstat, dp, tab, out_tokens);
 }
 
 // ---------------------------------------------------------------------------
@@ -690,23 +851,29 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
   const int C1 = (V + kRowChunkElems - 1) / kRowChunkElems;
   const int C2 = res_chunks(V);
   const float c = KIND == 0 ? 1.4426950408889634f / temperature : 1.f;
+  // 256 / (T ln 2) in float64 (the float64 terms' scale, as the oracle's T)
+  const double c1 = KIND == 0 ? (1.0 / (double)temperature) * kInvLn2x256 : 0.0;
+  auto* xstat = reinterpret_cast<TreeStat64*>(w + L.xstat);
   auto* tables = reinterpret_cast<int*>(w + L.tree);
   auto* part = reinterpret_cast<uint64_t*>(w + L.part1);
   auto* mpart = reinterpret_cast<double*>(w + L.part3);
   auto* dpart = reinterpret_cast<double*>(w + L.part2);
   auto* tstate = reinterpret_cast<TreeDraw*>(w + L.tstate);
   static_assert(sizeof(TreeDraw) <= kTreeDrawBytes, "draw state fits its region");
+  static_assert(sizeof(TreeStat64) == kTreeStatBytes, "float64 statistic fits its region");
   hipError_t e = hipSuccess;
   // Small trees: small argument blocks (launches with a 2 KiB one start
   // much later), and with logits the tables come from the row-statistics
   // launch (its first work-group), not a launch of their own.
   const bool small = N <= kSmallTree;
-  TreeArgsN<kSmallTree> small_tree{}, internal{};
+  TreeArgsN<kSmallTree> small_tree{}, internal{}, leaves{};
   if (small) {
     for (int j = 0; j < N; ++j) small_tree.parent[j] = tree.parent[j];
-    int n = 0;
-    for (int j = 0; j < N; ++j)
-      if (shape.has_child[j]) internal.parent[n++] = (int16_t)j;
+    int ni = 0, nl = 0;
+    for (int j = 0; j < N; ++j) {
+      if (shape.has_child[j]) internal.parent[ni++] = (int16_t)j;
+      else leaves.parent[nl++] = (int16_t)j;
+    }
   }
   if (!small)
     e = launch_timed(kProfTreeWalk, &k_tree_setup<kMaxNodes>, dim3(1), dim3(kThreads), 0, s,
@@ -716,15 +883,16 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
                      small_tree, N, tables);
   if (e != hipSuccess) return e;
   if (KIND == 0) {
-    const long blocks = (long)B * (N + shape.n_internal) * C1;
+    const long nA = (long)B * 2 * shape.n_internal * tree_xchunks(V);
+    const long nB = (long)B * (small ? N - shape.n_internal : N) * C1;
     if (small)
-      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, true>, dim3((unsigned)blocks),
-                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, V, C1, c,
-                       small_tree, internal, tables, part);
+      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, true>, dim3((unsigned)(nA + nB)),
+                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, (int)nB, V, C1,
+                       c, c1, small_tree, internal, leaves, tables, part, xstat);
     else
-      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, false>, dim3((unsigned)blocks),
-                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, V, C1, c,
-                       small_tree, internal, tables, part);
+      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, false>, dim3((unsigned)(nA + nB)),
+                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, (int)nB, V, C1,
+                       c, c1, small_tree, internal, leaves, tables, part, xstat);
     if (e != hipSuccess) return e;
   }
   const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
@@ -733,20 +901,21 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
     if (n_units == 0) continue;
     e = launch_timed(kProfTreeMass, &k_tree_mass<DT, NE, KIND>,
                      dim3((unsigned)((long)B * n_units * G)), dim3(kThreads), 0, s, target,
-                     draft, N, V, C1, C2, c, r, n_units, (const int*)tables,
-                     (const uint64_t*)part, mpart);
+                     draft, N, V, C1, C2, c, c1, r, n_units, (const int*)tables,
+                     (const uint64_t*)part, (const TreeStat64*)xstat, mpart);
     if (e != hipSuccess) return e;
   }
   const unsigned wgs = (unsigned)((B + kWaves - 1) / kWaves);
   e = launch_timed(kProfTreeWalk, &k_tree_walk<DT, KIND>, dim3(wgs), dim3(kThreads), 0, s,
-                   target, draft, B, N, V, C1, C2, shape.depth, c, node_tokens, uniforms, seed,
-                   ctr0, (const int*)tables, (const uint64_t*)part, (const double*)mpart, tstate,
+                   target, draft, B, N, V, C1, C2, shape.depth, c1, node_tokens, uniforms, seed,
+                   ctr0, (const int*)tables, (const TreeStat64*)xstat, (const double*)mpart, tstate,
                    accepted_len, out_tokens, out_path);
   if (e != hipSuccess) return e;
   return launch_timed(kProfTreeDraw, &k_tree_draw<DT, NE, KIND>, dim3((unsigned)((long)B * G)),
-                      dim3(kThreads), 0, s, target, draft, N, V, C1, C2, shape.depth, c,
+                      dim3(kThreads), 0, s, target, draft, N, V, C1, C2, shape.depth, c, c1,
                       uniforms, seed, ctr0, (const TreeDraw*)tstate, (const uint64_t*)part,
-                      dpart, reinterpret_cast<unsigned*>(w + L.count), out_tokens);
+                      (const TreeStat64*)xstat, dpart, reinterpret_cast<unsigned*>(w + L.count),
+                      out_tokens);
 }
 
 hipError_t launch_tree_sample(const void* target, const void* draft, int dtype, int kind, int B,
