@@ -2,7 +2,8 @@
 the same header): Tang's table-driven method, 2^(t/256), against the C
 library's long double exp2l, over the whole range it serves (every table
 entry, arguments down to the underflow clamp, and the positive arguments a
-reference below the row maximum produces)."""
+reference below the row maximum produces); and of its degree-3 variant for
+summed terms against its truncation bound (ln2/512)^4 / 24."""
 import os
 import shutil
 import subprocess
@@ -51,6 +52,23 @@ int main() {
                              -1074.0 * 256.0, -1075.5 * 256.0};
   for (double t : specials) check(t);
   std::printf("checked %ld worst_ulp %.3f at %a\n", n, worst, worst_t);
+  // the degree-3 variant for summed terms: relative error below 1.5e-13,
+  // and never above the exact value by more than rounding (2^-51 relative)
+  double worst3 = 0.0, above3 = 0.0;
+  auto check3 = [&](double t) {
+    const long double ref = exp2l((long double)t / 256.0L);
+    if (ref < 2.2250738585072014e-308L) return;
+    const long double got = specv::exp2_256_sum(t, specv::kExp2Frac256);
+    const double rel = (double)((got - ref) / ref);
+    if (-rel > worst3) worst3 = -rel;
+    if (rel > above3) above3 = rel;
+  };
+  for (int i = 0; i < 2000000; ++i) check3(narrow(g));
+  for (int i = 0; i < 1000000; ++i) check3(wide(g));
+  for (int i = 0; i < 200000; ++i) check3(above(g));
+  for (int j = -2000; j <= 2000; ++j) check3(j + 0.5), check3(j - 0.5);  // |f| = 1/2: the bound
+  std::printf("deg3_below %.3e deg3_above %.3e zero3 %a\n", worst3, above3,
+              specv::exp2_256_sum(0.0, specv::kExp2Frac256));
   std::printf("minus_inf %a below_range %a zero %a\n",
               specv::exp2_256(-INFINITY, specv::kExp2Frac256),
               specv::exp2_256(-1200.0 * 256.0, specv::kExp2Frac256),
@@ -78,3 +96,7 @@ def test_exp_nonpos_accuracy():
     worst = float(words[words.index("worst_ulp") + 1])
     assert worst < 3.0, out
     assert "minus_inf 0x0p+0" in out and "below_range 0x0p+0" in out and "zero 0x1p+0" in out, out
+    below3 = float(words[words.index("deg3_below") + 1])
+    above3 = float(words[words.index("deg3_above") + 1])
+    assert below3 < 1.5e-13 and above3 < 2.0 ** -51, out
+    assert "zero3 0x1p+0" in out, out

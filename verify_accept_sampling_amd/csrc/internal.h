@@ -135,6 +135,12 @@ constexpr int kTreeStatChunk = 16384;
 __host__ __device__ inline int tree_xchunks(int V) {
   return (V + kTreeStatChunk - 1) / kTreeStatChunk;
 }
+// Tree sampling's residual masses: one partial per chunk of this many
+// elements of a row pair (at most res_chunks(V) per row: they fit part3).
+constexpr int kTreeMassChunk = 8192;
+__host__ __device__ inline int tree_mchunks(int V) {
+  return (V + kTreeMassChunk - 1) / kTreeMassChunk;
+}
 
 struct WsLayout {
   size_t count;  // counter region, always at offset 0

@@ -262,6 +262,12 @@ __device__ __forceinline__ double tterm(float z, double c1, double c0, double in
                                         const double* tab) {
   return KIND == 0 ? exp2_256(fma((double)z, c1, c0), tab) * inv : (double)z;
 }
+// tterm for terms that are only summed (the residual masses).
+template <int KIND>
+__device__ __forceinline__ double tterm_sum(float z, double c1, double c0, double inv,
+                                            const double* tab) {
+  return KIND == 0 ? exp2_256_sum(fma((double)z, c1, c0), tab) * inv : (double)z;
+}
 
 // One chunk of kDrawChunk elements by one wave: lane l holds the running
 // sums (inclusive) of the weights w_j = max(0, p_j - C q_j) (p_j when !use_q)
@@ -296,26 +302,32 @@ __device__ __forceinline__ double chunk_scan(const void* prow, const void* qrow,
   return __shfl(excl + acc, 63, 64);
 }
 
-// Total of one chunk's weights (as chunk_scan's, without the running sums:
-// one butterfly instead of a scan).  For the mass rounds, whose chunk totals
-// no other kernel recomputes.
+// The totals chunk_scan returns for one chunk at two factors, C = cf (with
+// q when use_f) and C = cp (with q when use_p), from one evaluation of the
+// chunk's terms: the same sums in the same order, so each total is
+// bit-identical to chunk_scan's at that factor.
 template <int DT, int NE, int KIND>
-__device__ __forceinline__ double chunk_total(const void* prow, const void* qrow, int V,
-                                              long chunk, double C, const TermCoef& k,
-                                              const double* tab) {
+__device__ __forceinline__ void chunk_totals2(const void* prow, const void* qrow, int V,
+                                              long chunk, double cf, bool use_f, double cp,
+                                              bool use_p, const TermCoef& k, const double* tab,
+                                              double& tf, double& tp) {
   const int lane = threadIdx.x & 63;
   const long j0 = chunk * kDrawChunk + (long)lane * kSegPerThread;
   constexpr uint32_t fill = run_fill<DT, KIND>();
   RunWords<DT> rp, rq;
   load_run_words<DT, NE>(prow, j0, V, fill, rp);
   load_run_words<DT, NE>(qrow, j0, V, fill, rq);
-  double acc = 0.0;
+  double af = 0.0, ap = 0.0;
 #pragma unroll
   for (int e = 0; e < kSegPerThread; ++e) {
     const double a = tterm<KIND>(run_elem<DT>(rp, e), k.c1, k.c0p, k.ip, tab);
-    acc += fmax(0.0, a - C * tterm<KIND>(run_elem<DT>(rq, e), k.c1, k.c0q, k.iq, tab));
+    const double q = tterm<KIND>(run_elem<DT>(rq, e), k.c1, k.c0q, k.iq, tab);
+    af += use_f ? fmax(0.0, a - cf * q) : a;
+    ap += use_p ? fmax(0.0, a - cp * q) : a;
   }
-  return wave_sum_d(acc);
+  const double ef = wave_exclusive_scan_d(af), ep = wave_exclusive_scan_d(ap);
+  tf = __shfl(ef + af, 63, 64);
+  tp = __shfl(ep + ap, 63, 64);
 }
 
 // Sum of n chunk partials in a fixed order (lane l: entries l, l+64, ...,
@@ -331,7 +343,7 @@ __device__ __forceinline__ double wave_sum_fixed(const double* p, long n, long s
 // mass rounds' partials (mpart row of child j = masses at its parent for
 // the test of j).  Wave-uniform.
 __device__ __forceinline__ void residual_state(const int* tables, const double* mpart, int b,
-                                               int N, int C2, int u, int r, double& C,
+                                               int N, int Cm, int u, int r, double& C,
                                                double& M) {
   C = 0.0;
   M = 1.0;
@@ -341,7 +353,7 @@ __device__ __forceinline__ void residual_state(const int* tables, const double* 
     j = tree_tab(tables, kTabNext)[j];
     if (j < 0) break;
     const double cn = C + M;
-    const double F = wave_sum_fixed(mpart + ((long)b * N + j) * C2, C2);
+    const double F = wave_sum_fixed(mpart + ((long)b * N + j) * Cm, Cm);
     if (F > 0.0) {
       C = cn;
       M = F;
@@ -362,26 +374,44 @@ __device__ __forceinline__ void residual_state(const int* tables, const double* 
 // exponent, so every term and the sum stay far below overflow, and a first
 // finite element sets it when there is none.
 constexpr double kRefSlack = 256.0 * 400.0;  // terms below 2^400
+constexpr int kStatU = 8;  // words per thread requested together
+
+// Words g, g + NT, ... (kStatU of them) of a row; a word at or past g1 is
+// not loaded (its offset is past the row's buffer) and reads as 0.
+__device__ __forceinline__ void stats64_load(const RowBuf& buf, long g, long g1,
+                                             u32x4 (&w)[kStatU]) {
+#pragma unroll
+  for (int u = 0; u < kStatU; ++u) {
+    const long gu = g + (long)u * kThreads;
+    w[u] = buf.load_nt(gu < g1 ? static_cast<uint32_t>(gu) * 16u : 0xfffffff0u, 0);
+  }
+}
+
+// With 16-byte words (NE > 1) the caller has already requested the first
+// kStatU words (w0, from stats64_load at g0 + tid), so that their latency
+// overlaps its set-up.
 template <int DT, int NE>
 __device__ __forceinline__ void stats64_thread(const void* rp, uint32_t row_bytes, long g0,
                                                long g1, double c1, const double* tab, float& m,
-                                               double& s) {
+                                               double& s, const u32x4 (&w0)[kStatU]) {
   s = 0.0;
+  // With no reference yet (m = -inf) every element seen is -inf: its term,
+  // clamped, is 0 at any mc.
   double mc = m == -INFINITY ? 0.0 : -((double)m * c1);
   const double lim = kRefSlack / c1;  // in logit units
+  float mlim = (float)((double)m + lim);
   auto fold = [&](const float (&x)[NE]) {
     float bm = x[0];
 #pragma unroll
     for (int e = 1; e < NE; ++e) bm = fmaxf(bm, x[e]);
-    if ((double)bm > (double)m + lim) {  // rare: a first finite element, or far above
+    if (bm > mlim) {  // rare: a first finite element, or far above
       if (m != -INFINITY) s *= exp2_256(((double)m - (double)bm) * c1, tab);
       m = bm;
       mc = -((double)m * c1);
+      mlim = (float)((double)m + lim);
     }
-    if (m != -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < NE; ++e) s += exp2_256(fma((double)x[e], c1, mc), tab);
-    }
+    for (int e = 0; e < NE; ++e) s += exp2_256_sum(fma((double)x[e], c1, mc), tab);
   };
   if constexpr (NE == 1) {
     for (long g = g0 + threadIdx.x; g < g1; g += kThreads) {
@@ -389,27 +419,23 @@ __device__ __forceinline__ void stats64_thread(const void* rp, uint32_t row_byte
       fold(x);
     }
   } else {
-    // All of a chunk's words (up to U per thread) are requested before any
-    // is used; a word past g1 is not loaded (its offset is past the row's
-    // buffer) and not used.
-    constexpr int U = 8;
-    const RowBuf buf(rp, row_bytes);
-    for (long g = g0 + threadIdx.x; g < g1; g += (long)U * kThreads) {
-      u32x4 w[U];
+    auto fold_words = [&](const u32x4 (&w)[kStatU], long g) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        w[u] = buf.load_nt(g + (long)u * kThreads < g1
-                               ? static_cast<uint32_t>(g + (long)u * kThreads) * 16u
-                               : 0xfffffff0u,
-                           0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < kStatU; ++u) {
         if (g + (long)u * kThreads < g1) {
           float x[NE];
           unpack16<DT>(w[u], x);
           fold(x);
         }
       }
+    };
+    fold_words(w0, g0 + threadIdx.x);
+    const RowBuf buf(rp, row_bytes);
+    for (long g = g0 + threadIdx.x + (long)kStatU * kThreads; g < g1;
+         g += (long)kStatU * kThreads) {
+      u32x4 w[kStatU];
+      stats64_load(buf, g, g1, w);
+      fold_words(w, g);
     }
   }
 }
@@ -481,12 +507,15 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(
     const long gpc = (n_groups + Cx - 1) / Cx;
     const long g0 = (long)chunk * gpc;
     const long g1 = min(g0 + gpc, n_groups);
+    const uint32_t row_bytes = static_cast<uint32_t>((long)V * eb);
+    u32x4 w0[kStatU];
+    if constexpr (NE > 1) stats64_load(RowBuf(rp, row_bytes), g0 + threadIdx.x, g1, w0);
+    const float z0 = load_elem<DT>(rp, 0);
     tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
     __syncthreads();
-    const float z0 = load_elem<DT>(rp, 0);
     float m = z0 > -INFINITY && z0 < INFINITY ? z0 : -INFINITY;
     double s;
-    stats64_thread<DT, NE>(rp, static_cast<uint32_t>((long)V * eb), g0, g1, c1, tab, m, s);
+    stats64_thread<DT, NE>(rp, row_bytes, g0, g1, c1, tab, m, s, w0);
     block_reduce_ms64(m, s, c1, tab);
     if (threadIdx.x == 0) xstat[((long)b * 2 * N + slot) * Cx + chunk] = TreeStat64{m, s};
     return;
@@ -515,36 +544,62 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(
   if (threadIdx.x == 0) part[((long)b * 2 * N + node) * C1 + chunk] = pack2(m, (float)s);
 }
 
-// Work-groups cover kTreeChunksPerGroup consecutive chunks of one row pair.
+// Work-groups of the draw cover kTreeChunksPerGroup consecutive chunks of
+// the stop node's row pair.
 constexpr int kTreeChunksPerWave = 2;
 constexpr int kTreeChunksPerGroup = kWaves * kTreeChunksPerWave;
 
 // Mass round r: unit = a child j of rank r (its parent u has more than r
-// children); the chunk sums of max(0, p_u - C_r q_u).
+// children); one work-group per (request, unit, chunk of kTreeMassChunk
+// elements) sums max(0, p_u - C_r q_u) over its chunk.  Every word of the
+// chunk is requested before any is used; the work-group's sum is taken in
+// a fixed order (lanes, then waves), so the partials are reproducible.
 template <int DT, int NE, int KIND>
 __global__ __launch_bounds__(kThreads) void k_tree_mass(
-    const void* __restrict__ target, const void* __restrict__ draft, int N, int V, int C1,
-    int C2, float c, double c1, int r, int n_units, const int* __restrict__ tables,
-    const uint64_t* __restrict__ part, const TreeStat64* __restrict__ xstat,
-    double* __restrict__ mpart) {
+    const void* __restrict__ target, const void* __restrict__ draft, int N, int V, int Cm,
+    double c1, int r, int n_units, const int* __restrict__ tables,
+    const TreeStat64* __restrict__ xstat, double* __restrict__ mpart) {
   __shared__ double tab[256];
   __shared__ RowPair s_rows;
   __shared__ double s_C;
-  const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
+  __shared__ double s_red[kWaves];
   const long idx = blockIdx.x;
-  const int g = static_cast<int>(idx % G);
-  const int unit = static_cast<int>((idx / G) % n_units);
-  const int b = static_cast<int>(idx / G / n_units);
+  const int chunk = static_cast<int>(idx % Cm);
+  const int unit = static_cast<int>((idx / Cm) % n_units);
+  const int b = static_cast<int>(idx / Cm / n_units);
   const int j = tree_tab(tables, kTabRanked)[tree_tab(tables, kTabRankOff)[r - 1] + unit];
   const int u = tree_tab(tables, kTabParent)[j];
+  const long eb = Elems<DT>::kBytes;
+  const void* prow = static_cast<const char*>(target) + ((long)b * N + u) * V * eb;
+  const void* qrow = static_cast<const char*>(draft) + ((long)b * N + u) * V * eb;
+  const long e0 = (long)chunk * kTreeMassChunk;
+  const long e1 = min(e0 + (long)kTreeMassChunk, (long)V);
+  // With 16-byte words the chunk's words are requested first: they do not
+  // depend on the residual state the first wave works out below.  A word
+  // past the chunk is not loaded (its offset is past the row's buffer).
+  constexpr int W = NE > 1 ? kTreeMassChunk / (kThreads * NE) : 1;  // words per thread and row
+  static_assert(NE == 1 || kTreeMassChunk % (kThreads * NE) == 0, "whole words per thread");
+  const long g0 = e0 / NE + threadIdx.x, g1 = e1 / NE;
+  u32x4 wp[W], wq[W];
+  if constexpr (NE > 1) {
+    const uint32_t row_bytes = static_cast<uint32_t>((long)V * eb);
+    const RowBuf bp(prow, row_bytes), bq(qrow, row_bytes);
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const long g = g0 + (long)i * kThreads;
+      const uint32_t off = g < g1 ? static_cast<uint32_t>(g) * 16u : 0xfffffff0u;
+      wp[i] = bp.load_nt(off, 0);
+      wq[i] = bq.load_nt(off, 0);
+    }
+  }
   if (KIND == 0) tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
   __syncthreads();
   if (threadIdx.x < kWaveSize) {
     double C, M;
-    residual_state(tables, mpart, b, N, C2, u, r - 1, C, M);
+    residual_state(tables, mpart, b, N, Cm, u, r - 1, C, M);
     if (threadIdx.x == 0) {
       s_C = C + M;
-      if (KIND == 0) s_rows = node_rows(xstat, part, b, N, u, V, C1, c, c1, tab, true);
+      if (KIND == 0) s_rows = node_rows(xstat, nullptr, b, N, u, V, 0, 0.f, c1, tab, true);
     }
   }
   __syncthreads();
@@ -552,16 +607,36 @@ __global__ __launch_bounds__(kThreads) void k_tree_mass(
   RowPair rows{};
   if (KIND == 0) rows = s_rows;
   const TermCoef k = term_coef<KIND>(rows, c1);
-  const long eb = Elems<DT>::kBytes;
-  const void* prow = static_cast<const char*>(target) + ((long)b * N + u) * V * eb;
-  const void* qrow = static_cast<const char*>(draft) + ((long)b * N + u) * V * eb;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  double* out = mpart + ((long)b * N + j) * C2;
-  for (int t = 0; t < kTreeChunksPerWave; ++t) {
-    const long ch = (long)g * kTreeChunksPerGroup + wave * kTreeChunksPerWave + t;
-    if (ch >= C2) break;  // wave-uniform
-    const double tot = chunk_total<DT, NE, KIND>(prow, qrow, V, ch, C, k, tab);
-    if (lane == 0) out[ch] = tot;
+  double acc = 0.0;
+  if constexpr (NE == 1) {
+    for (long e = e0 + threadIdx.x; e < e1; e += kThreads) {
+      const double a = tterm_sum<KIND>(load_elem<DT>(prow, e), k.c1, k.c0p, k.ip, tab);
+      acc += fmax(0.0, a - C * tterm_sum<KIND>(load_elem<DT>(qrow, e), k.c1, k.c0q, k.iq, tab));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if (g0 + (long)i * kThreads < g1) {
+        float xp[NE], xq[NE];
+        unpack16<DT>(wp[i], xp);
+        unpack16<DT>(wq[i], xq);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const double a = tterm_sum<KIND>(xp[e], k.c1, k.c0p, k.ip, tab);
+          acc += fmax(0.0, a - C * tterm_sum<KIND>(xq[e], k.c1, k.c0q, k.iq, tab));
+        }
+      }
+    }
+  }
+  acc = wave_sum_d(acc);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) s_red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += s_red[w];
+    mpart[((long)b * N + j) * Cm + chunk] = t;
   }
 }
 
@@ -571,8 +646,8 @@ __global__ __launch_bounds__(kThreads) void k_tree_mass(
 // lanes together, and the tests then run in child order.
 template <int DT, int KIND>
 __global__ __launch_bounds__(kThreads) void k_tree_walk(
-    const void* __restrict__ target, const void* __restrict__ draft, int B, int N, int V, int C1,
-    int C2, int D, double c1, const int32_t* __restrict__ node_tokens,
+    const void* __restrict__ target, const void* __restrict__ draft, int B, int N, int V, int Cm,
+    int D, double c1, const int32_t* __restrict__ node_tokens,
     const float* __restrict__ uniforms, uint64_t seed, uint64_t ctr0,
     const int* __restrict__ tables, const TreeStat64* __restrict__ xstat,
     const double* __restrict__ mpart, TreeDraw* __restrict__ tstate,
@@ -632,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
         const int ji = __shfl(j, i, kWaveSize);
         if (i0 + i > 0) {
           const double cn = C + M;
-          const double F = wave_sum_fixed(mpart + ((long)b * N + ji) * C2, C2);
+          const double F = wave_sum_fixed(mpart + ((long)b * N + ji) * Cm, Cm);
           if (F > 0.0) {
             C = cn;
             M = F;
@@ -808,12 +883,14 @@ __global__ __launch_bounds__(kThreads) void k_tree_draw(
   for (int t = 0; t < kTreeChunksPerWave; ++t) {
     const long ch = (long)g * kTreeChunksPerGroup + wave * kTreeChunksPerWave + t;
     if (ch >= C2) break;  // wave-uniform
-    double run[kSegPerThread], base;
-    const double tf =
-        chunk_scan<DT, NE, KIND>(prow, qrow, V, ch, st.cf, use_q, k, tab, run, base);
-    double tp = 0.0;
-    if (use_q)
-      tp = chunk_scan<DT, NE, KIND>(prow, qrow, V, ch, st.cp, st.cp > 0.0, k, tab, run, base);
+    double tf, tp = 0.0;
+    if (use_q) {
+      chunk_totals2<DT, NE, KIND>(prow, qrow, V, ch, st.cf, true, st.cp, st.cp > 0.0, k, tab, tf,
+                                  tp);
+    } else {
+      double run[kSegPerThread], base;
+      tf = chunk_scan<DT, NE, KIND>(prow, qrow, V, ch, st.cf, false, k, tab, run, base);
+    }
     if (lane == 0) {
       st_dev_d(&dp[ch * 2], tf);
       st_dev_d(&dp[ch * 2 + 1], tp);
@@ -895,19 +972,20 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
                        c, c1, small_tree, internal, leaves, tables, part, xstat);
     if (e != hipSuccess) return e;
   }
-  const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
+  const int Cm = tree_mchunks(V);
   for (int r = 1; r <= shape.max_rank; ++r) {
     const int n_units = shape.rank_count[r];
     if (n_units == 0) continue;
     e = launch_timed(kProfTreeMass, &k_tree_mass<DT, NE, KIND>,
-                     dim3((unsigned)((long)B * n_units * G)), dim3(kThreads), 0, s, target,
-                     draft, N, V, C1, C2, c, c1, r, n_units, (const int*)tables,
-                     (const uint64_t*)part, (const TreeStat64*)xstat, mpart);
+                     dim3((unsigned)((long)B * n_units * Cm)), dim3(kThreads), 0, s, target,
+                     draft, N, V, Cm, c1, r, n_units, (const int*)tables,
+                     (const TreeStat64*)xstat, mpart);
     if (e != hipSuccess) return e;
   }
+  const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
   const unsigned wgs = (unsigned)((B + kWaves - 1) / kWaves);
   e = launch_timed(kProfTreeWalk, &k_tree_walk<DT, KIND>, dim3(wgs), dim3(kThreads), 0, s,
-                   target, draft, B, N, V, C1, C2, shape.depth, c1, node_tokens, uniforms, seed,
+                   target, draft, B, N, V, Cm, shape.depth, c1, node_tokens, uniforms, seed,
                    ctr0, (const int*)tables, (const TreeStat64*)xstat, (const double*)mpart, tstate,
                    accepted_len, out_tokens, out_path);
   if (e != hipSuccess) return e;
