@@ -124,7 +124,7 @@ static_assert(SPEC_WORKSPACE_STATUS_OFFSET == kStatusWord * 4, "status word offs
 // has a tag of its own, so a tag left by an earlier call (or any other
 // content) is never taken for a current one.  The other regions are written
 // before they are read within each call.
-// Tree-sampling regions: the tree tables (nine int32 tables of kMaxNodes),
+// Tree-sampling regions: the tree tables (ten int32 tables of kMaxNodes),
 // the per-request draw state and the float64 row statistics.
 constexpr size_t kTreeTableBytes = 10 * (size_t)kMaxNodes * 4;
 constexpr size_t kTreeDrawBytes = 32;

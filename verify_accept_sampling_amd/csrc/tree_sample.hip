@@ -59,6 +59,7 @@ enum TreeTable {
   kTabRank,      // index among its siblings (0 = lowest)
   kTabDepth,
   kTabInternal,  // nodes with a child, ascending
+  kTabLeaf,      // nodes without a child, ascending
   kTabRanked,    // children of rank >= 1, by (rank, index)
   kTabRankOff,   // kTabRanked offset of rank r (entry r - 1), r = 1 .. max rank + 1
   kTabCount
@@ -120,9 +121,10 @@ __device__ __forceinline__ void tree_setup_block(const TreeArgsN<NMAX>& tree, in
   }
   __syncthreads();
   for (int j = threadIdx.x; j < N; j += kThreads) {
-    // The nodes with a child, ascending; the children of rank >= 1 grouped
-    // by rank, ascending index within a rank; rank r's offset at entry
-    // r - 1 (r = 1 .. max rank + 1).  Entries past each list's length are 0.
+    // The nodes with a child, ascending; those without, ascending; the
+    // children of rank >= 1 grouped by rank, ascending index within a
+    // rank; rank r's offset at entry r - 1 (r = 1 .. max rank + 1).
+    // Entries past each list's length are 0.
     int n_int = 0, n_ranked = 0, max_rank = 0;
     int before_int = 0, lower_rank = 0, same_rank_before = 0, off = 0;
     for (int i = 0; i < N; ++i) {
@@ -140,7 +142,9 @@ __device__ __forceinline__ void tree_setup_block(const TreeArgsN<NMAX>& tree, in
       }
     }
     if (nch[j] > 0) tables[kTabInternal * kMaxNodes + before_int] = j;
+    else tables[kTabLeaf * kMaxNodes + (j - before_int)] = j;  // leaves below j: j - before_int
     if (j >= n_int) tables[kTabInternal * kMaxNodes + j] = 0;
+    if (j >= N - n_int) tables[kTabLeaf * kMaxNodes + j] = 0;
     if (j >= 1 && rank[j] >= 1) tables[kTabRanked * kMaxNodes + lower_rank + same_rank_before] = j;
     if (j >= n_ranked) tables[kTabRanked * kMaxNodes + j] = 0;
     tables[kTabRankOff * kMaxNodes + j] = j <= max_rank ? off : 0;
@@ -466,34 +470,27 @@ __device__ __forceinline__ void block_reduce_ms64(float& m, double& s, double c1
   }
 }
 
-// Row statistics.  The grid has two parts:
-//   A. the rows of the nodes with children -- per request the target rows,
-//      then the draft rows, of nodes internal[0 .. n_int-1] -- in chunks of
-//      kTreeStatChunk elements, with the float64 statistic (xstat), first,
-//      so that these long work-groups start in the first round;
-//   B. the target rows of the leaves, in C1 chunks, with the float32
-//      statistic (part).
-// SETUP (trees of up to kSmallTree nodes): the nodes with and without a
-// child come in the arguments `internal` and `leaves`, and work-group 0
-// also writes the tree tables for the launches after this one (no launch
-// of its own).  Otherwise the nodes with a child come from the tables
-// k_tree_setup wrote, and part B covers every target row, those of nodes
-// with a child leaving at once.
+// Float64 row statistics of the rows of the nodes with children -- per
+// request the target rows, then the draft rows, of nodes internal[0 ..
+// n_int-1] -- in chunks of kTreeStatChunk elements (xstat).  SETUP (trees
+// of up to kSmallTree nodes): the nodes with a child come in the argument
+// `internal`, and work-group 0 also writes the tree tables for the launches
+// after this one (no launch of its own); otherwise they come from the
+// tables k_tree_setup wrote.
 template <int DT, int NE, bool SETUP>
 __global__ __launch_bounds__(kThreads) void k_tree_stats(
-    const void* __restrict__ target, const void* __restrict__ draft, int N, int n_int, int n_b,
-    int V, int C1, float c, double c1, TreeArgsN<kSmallTree> tree,
-    TreeArgsN<kSmallTree> internal, TreeArgsN<kSmallTree> leaves, int* __restrict__ tables,
-    uint64_t* __restrict__ part, TreeStat64* __restrict__ xstat) {
+    const void* __restrict__ target, const void* __restrict__ draft, int N, int n_int, int V,
+    double c1, TreeArgsN<kSmallTree> tree, TreeArgsN<kSmallTree> internal,
+    int* __restrict__ tables, TreeStat64* __restrict__ xstat) {
   __shared__ double tab[256];
   if constexpr (SETUP) {
     if (blockIdx.x == 0) tree_setup_block<kSmallTree>(tree, N, tables);
   }
+  if (n_int == 0) return;  // a launch for the tables alone
   const int Cx = tree_xchunks(V);
   const long eb = Elems<DT>::kBytes;
-  const long nA = (long)gridDim.x - (long)n_b;  // part B has n_b work-groups
   const long idx = blockIdx.x;
-  if (idx < nA) {  // part A: float64
+  {
     const int chunk = static_cast<int>(idx % Cx);
     const int j = static_cast<int>((idx / Cx) % (2 * n_int));
     const int b = static_cast<int>(idx / Cx / (2 * n_int));
@@ -518,16 +515,22 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(
     stats64_thread<DT, NE>(rp, row_bytes, g0, g1, c1, tab, m, s, w0);
     block_reduce_ms64(m, s, c1, tab);
     if (threadIdx.x == 0) xstat[((long)b * 2 * N + slot) * Cx + chunk] = TreeStat64{m, s};
-    return;
   }
-  // part B: float32
-  const long i2 = idx - nA;
-  const int n_rows = SETUP ? N - n_int : N;
+}
+
+// Float32 statistic (part) of one chunk of a leaf's target row: its bonus
+// draw normalises its own weights, so only the reference is used.  Work
+// item i2 of B * n_leaf * C1.
+template <int DT, int NE>
+__device__ __forceinline__ void leaf_stats_block(const void* __restrict__ target, int N, int V,
+                                                 int C1, float c, int n_leaf,
+                                                 const int* __restrict__ tables,
+                                                 uint64_t* __restrict__ part, long i2) {
+  const long eb = Elems<DT>::kBytes;
   const int chunk = static_cast<int>(i2 % C1);
-  const int j = static_cast<int>((i2 / C1) % n_rows);
-  const int b = static_cast<int>(i2 / C1 / n_rows);
-  const int node = SETUP ? leaves.parent[j] : j;
-  if (!SETUP && tree_tab(tables, kTabNChild)[node] > 0) return;  // in part A
+  const int j = static_cast<int>((i2 / C1) % n_leaf);
+  const int b = static_cast<int>(i2 / C1 / n_leaf);
+  const int node = tree_tab(tables, kTabLeaf)[j];
   const void* rp = static_cast<const char*>(target) + ((long)b * N + node) * V * eb;
   const long n_groups = V / NE;
   const long gpc = (n_groups + C1 - 1) / C1;
@@ -640,11 +643,18 @@ __global__ __launch_bounds__(kThreads) void k_tree_mass(
   }
 }
 
+// Dynamic shared memory of k_tree_walk: the exp table, then three int
+// tables of N entries and two per wave.
+inline size_t tree_walk_lds(int N) { return 256 * sizeof(double) + (3 + 2 * kWaves) * (size_t)N * 4; }
+
 // The walk: one wave per request.  The tree tables come into shared memory
 // once per work-group and the request's node tokens once per wave; at each
 // node the children's tokens, values and uniforms are fetched by their own
-// lanes together, and the tests then run in child order.
-template <int DT, int KIND>
+// lanes together, and the tests then run in child order.  Work-groups from
+// n_walk on instead compute the leaves' row statistics (logits), which only
+// the draw after this launch reads: streaming work beside the walk's
+// latency-bound waves.
+template <int DT, int NE, int KIND>
 __global__ __launch_bounds__(kThreads) void k_tree_walk(
     const void* __restrict__ target, const void* __restrict__ draft, int B, int N, int V, int Cm,
     int D, double c1, const int32_t* __restrict__ node_tokens,
@@ -652,12 +662,22 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
     const int* __restrict__ tables, const TreeStat64* __restrict__ xstat,
     const double* __restrict__ mpart, TreeDraw* __restrict__ tstate,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_path) {
-  __shared__ double tab[256];
-  __shared__ int s_nchild[kMaxNodes], s_first[kMaxNodes], s_next[kMaxNodes];
-  __shared__ int s_tok[kWaves][kMaxNodes];
-  __shared__ int s_path[kWaves][kMaxNodes];
+    int32_t* __restrict__ out_path, int n_walk, int C1, float c, int n_leaf,
+    uint64_t* __restrict__ part) {
+  if ((int)blockIdx.x >= n_walk) {
+    if constexpr (KIND == 0)
+      leaf_stats_block<DT, NE>(target, N, V, C1, c, n_leaf, tables, part,
+                               (long)blockIdx.x - n_walk);
+    return;
+  }
+  extern __shared__ __align__(16) unsigned char walk_lds[];
+  double* tab = reinterpret_cast<double*>(walk_lds);
+  int* s_nchild = reinterpret_cast<int*>(tab + 256);
+  int* s_first = s_nchild + N;
+  int* s_next = s_first + N;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int* tok = s_next + N + wave * N;
+  int* path = s_next + N + (kWaves + wave) * N;
   const int b = static_cast<int>(blockIdx.x) * kWaves + wave;
   if (KIND == 0) tab[threadIdx.x] = kExp2Frac256[threadIdx.x];
   for (int j = threadIdx.x; j < N; j += kThreads) {
@@ -665,13 +685,11 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
     s_first[j] = tree_tab(tables, kTabFirst)[j];
     s_next[j] = tree_tab(tables, kTabNext)[j];
   }
-  int* tok = s_tok[wave];
   if (b < B)
     for (int j = lane; j < N; j += kWaveSize) tok[j] = node_tokens[(long)b * N + j];
   __syncthreads();
   if (b >= B) return;  // wave-uniform
   const long eb = Elems<DT>::kBytes;
-  int* path = s_path[wave];
   int cur = 0, depth = 0;
   double cf = 0.0, cp = 0.0;
   if (lane == 0) path[0] = 0;
@@ -943,14 +961,12 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
   // much later), and with logits the tables come from the row-statistics
   // launch (its first work-group), not a launch of their own.
   const bool small = N <= kSmallTree;
-  TreeArgsN<kSmallTree> small_tree{}, internal{}, leaves{};
+  TreeArgsN<kSmallTree> small_tree{}, internal{};
   if (small) {
     for (int j = 0; j < N; ++j) small_tree.parent[j] = tree.parent[j];
-    int ni = 0, nl = 0;
-    for (int j = 0; j < N; ++j) {
+    int ni = 0;
+    for (int j = 0; j < N; ++j)
       if (shape.has_child[j]) internal.parent[ni++] = (int16_t)j;
-      else leaves.parent[nl++] = (int16_t)j;
-    }
   }
   if (!small)
     e = launch_timed(kProfTreeWalk, &k_tree_setup<kMaxNodes>, dim3(1), dim3(kThreads), 0, s,
@@ -960,16 +976,15 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
                      small_tree, N, tables);
   if (e != hipSuccess) return e;
   if (KIND == 0) {
-    const long nA = (long)B * 2 * shape.n_internal * tree_xchunks(V);
-    const long nB = (long)B * (small ? N - shape.n_internal : N) * C1;
+    const long nA = std::max(1L, (long)B * 2 * shape.n_internal * tree_xchunks(V));
     if (small)
-      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, true>, dim3((unsigned)(nA + nB)),
-                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, (int)nB, V, C1,
-                       c, c1, small_tree, internal, leaves, tables, part, xstat);
+      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, true>, dim3((unsigned)nA),
+                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, V, c1,
+                       small_tree, internal, tables, xstat);
     else
-      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, false>, dim3((unsigned)(nA + nB)),
-                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, (int)nB, V, C1,
-                       c, c1, small_tree, internal, leaves, tables, part, xstat);
+      e = launch_timed(kProfTreeStats, &k_tree_stats<DT, NE, false>, dim3((unsigned)nA),
+                       dim3(kThreads), 0, s, target, draft, N, shape.n_internal, V, c1,
+                       small_tree, internal, tables, xstat);
     if (e != hipSuccess) return e;
   }
   const int Cm = tree_mchunks(V);
@@ -983,11 +998,15 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
     if (e != hipSuccess) return e;
   }
   const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
-  const unsigned wgs = (unsigned)((B + kWaves - 1) / kWaves);
-  e = launch_timed(kProfTreeWalk, &k_tree_walk<DT, KIND>, dim3(wgs), dim3(kThreads), 0, s,
-                   target, draft, B, N, V, Cm, shape.depth, c1, node_tokens, uniforms, seed,
-                   ctr0, (const int*)tables, (const TreeStat64*)xstat, (const double*)mpart, tstate,
-                   accepted_len, out_tokens, out_path);
+  const int wgs = (B + kWaves - 1) / kWaves;
+  // the leaves' row statistics (logits) ride in the walk's launch
+  const int n_leaf = N - shape.n_internal;
+  const long n_leaf_wgs = KIND == 0 ? (long)B * n_leaf * C1 : 0;
+  e = launch_timed(kProfTreeWalk, &k_tree_walk<DT, NE, KIND>, dim3((unsigned)(wgs + n_leaf_wgs)),
+                   dim3(kThreads), tree_walk_lds(N), s, target, draft, B, N, V, Cm, shape.depth,
+                   c1, node_tokens, uniforms, seed, ctr0, (const int*)tables,
+                   (const TreeStat64*)xstat, (const double*)mpart, tstate, accepted_len,
+                   out_tokens, out_path, wgs, C1, c, n_leaf, part);
   if (e != hipSuccess) return e;
   return launch_timed(kProfTreeDraw, &k_tree_draw<DT, NE, KIND>, dim3((unsigned)((long)B * G)),
                       dim3(kThreads), 0, s, target, draft, N, V, C1, C2, shape.depth, c, c1,
