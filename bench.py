@@ -37,6 +37,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+# Float64 vector issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one
+# fp64 add, multiply, fma, max, round or scale per lane per clock; the
+# published 78.6 TFLOP/s counts an fma as two flops).
+PEAK_FP64_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# fp64 operations per element of a float64 row statistic: the scaled
+# argument (fma), the clamp (max), the split into n and f (round, subtract),
+# the degree-3 polynomial (3 fma), the table product (mul), the scaling by
+# 2^(n/256 integer part) (ldexp) and the accumulation (add).
+TREE_STAT_OPS_PER_ELEM = 10
 METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B=64 k=8 V=128256"
 # Dominant kernel of each path, and the committed rocprofv3 counter summary of
 # its HBM traffic at this workload.
@@ -493,10 +502,13 @@ def _tree_oracle_steps(args_tuple):
 def bench_tree_sample(args):
     """One JSON line for tree sampling verification: the static tree (1 root
     + 60 nodes, branching 4, 3, 2, 2, 1) with draft logits, B=16,
-    V=128256, bf16, T=0.7.  Algorithmic bytes of a call: every target row
-    and the draft rows of nodes with children once (the row statistics),
-    both rows of a node once per sibling-rank mass pass, and the stop node's
-    rows drawn from."""
+    V=128256, bf16, T=0.7.  Algorithmic bytes of a call: both rows of the
+    nodes with children once (their float64 statistics), the leaves' target
+    rows once (float32 statistics), both rows of a node once per
+    sibling-rank mass pass, and the stop node's rows drawn from.  The
+    dominant kernel, k_tree_stats, is bound by float64 arithmetic (one exp
+    term per element): its roofline is fp64 operations against the vector
+    issue rate."""
     import numpy as np
 
     import workloads as W
@@ -595,7 +607,9 @@ def bench_tree_sample(args):
     n_int = sum(1 for k_ in kids if k_)
     mass_units = sum(max(0, len(k_) - 1) for k_ in kids)
     row = V * 2
-    stats_bytes = float(B * (N + n_int) * row)
+    stats_bytes = float(B * 2 * n_int * row)
+    stats_ops = float(B * 2 * n_int * V * TREE_STAT_OPS_PER_ELEM)
+    leaf_bytes = float(B * (N - n_int) * row)
     acc_np = acc_all.cpu().numpy()
     path_np = path_all.cpu().numpy()
     out_np = out_all.cpu().numpy()
@@ -607,9 +621,9 @@ def bench_tree_sample(args):
             drawn += 2 if kids[s_node] else 1
     draw_bytes = drawn / args.steps * row
     mass_bytes = float(B * mass_units * 2 * row)
-    step_bytes = stats_bytes + mass_bytes + draw_bytes
+    step_bytes = stats_bytes + leaf_bytes + mass_bytes + draw_bytes
     st_us = kern["tree_stats"]["avg_us"]
-    achieved = stats_bytes / (st_us * 1e-6) / 1e9
+    achieved = stats_ops / (st_us * 1e-6) / 1e12
     gate = None
     if res_cpu is not None:
         sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -631,9 +645,12 @@ def bench_tree_sample(args):
         "config": {"workload": "tree_sample_b16_n61_v128256_bf16_t0.7", "B": B, "nodes": N,
                    "V": V, "logits": "bf16", "temperature": wl.temperature,
                    "input_copies": len(copies), "draw_arithmetic": "f64"},
-        "roofline": {"bound": "hbm", "kernel": "k_tree_stats", "achieved": achieved,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": None, "algorithmic_bytes_per_launch": stats_bytes},
+        "roofline": {"bound": "alu", "kernel": "k_tree_stats", "achieved": achieved,
+                     "peak": PEAK_FP64_TOPS, "unit": "Tops/s (fp64)",
+                     "frac": achieved / PEAK_FP64_TOPS, "traffic": None,
+                     "algorithmic_ops_per_launch": stats_ops,
+                     "algorithmic_bytes_per_launch": stats_bytes,
+                     "hbm_gbps": stats_bytes / (st_us * 1e-6) / 1e9},
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "kernels": kern,
