@@ -10,8 +10,10 @@ the C ABI.
   (the scalar loads), probability rows, a 20-deep chain, a 9-child star, a
   random 300-node tree (the full-size table setup), a root with no
   children, a 100-child star (children in two tiles of the walk),
-  out-of-range node tokens, and a root whose draft row equals its target
-  row so the residual after a rejection is empty.
+  out-of-range node tokens, a root whose draft row equals its target row
+  so the residual after a rejection is empty, and masked (-inf) logits
+  with logits spread wide at a low temperature (the float64 statistics'
+  reference handling).
 * Statistics: with every child's token drawn from the draft at its parent,
   the first emitted token follows the target's root distribution
   (chi-square over 40000 requests).
@@ -158,6 +160,45 @@ def test_wide_star_children_past_one_wave():
     st = _check(wl, acc, out, path)
     assert st["mismatches"] == 0
     assert all(path[b, 1] > 70 or acc[b] == 0 for b in range(0, wl.B, 2))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_masked_and_wide_low_temperature_logits(dt):
+    """The float64 row statistics' reference: rows whose first element is
+    masked (-inf), a first 16384-element chunk wholly masked, about 30% of
+    every row masked, and logits spread so wide at T = 0.1 that elements
+    exceed a row's first element by far more than 400 binades of the
+    scaled exponent (the reference moves up, and chunks with different
+    references merge by rescaling).  Masked tokens are never emitted."""
+    _say(f"tree sampling: masked and wide low-temperature logits, {dt}")
+    rng = np.random.default_rng(31)
+    parent = np.array([-1, 0, 0, 0, 1, 1, 2, 4, 4, 6], dtype=np.int32)
+    B, V = 12, 40000
+    wl = W.tree_sample(B=B, V=V, seed=33, uniform_seed=34, parent=parent, target_std=20.0,
+                       noise_std=4.0, temperature=0.1, n_peaks=0, dtype=dt)
+    N = wl.n_nodes
+    mask = rng.random((B, N, V)) < 0.3
+    mask[::2, :, 0] = True             # the first element of every other request's rows
+    mask[1::3, :3, :16384] = True      # a whole first statistics chunk
+    neg = np.uint16(0xFF80) if dt == "bf16" else np.float32(-np.inf)
+    for arr in (wl.target, wl.draft):
+        arr[mask] = neg
+    # node tokens: drawn again from the masked draft at the parent
+    yq = W.logits_as_f32(wl.draft, dt).astype(np.float64) / wl.temperature
+    for j in range(1, N):
+        for b in range(B):
+            row = yq[b, parent[j]]
+            pr = np.exp(row - row.max())
+            wl.node_tokens[b, j] = rng.choice(V, p=pr / pr.sum())
+    acc, out, path = _run_gpu(wl)
+    st = _check(wl, acc, out, path)
+    assert st["mismatches"] == 0
+    zt = W.logits_as_f32(wl.target, dt)
+    for b in range(B):
+        n = int(acc[b])
+        node = int(path[b, n])
+        tok = int(out[b, n])
+        assert tok >= 0 and np.isfinite(zt[b, node, tok]), (b, node, tok)
 
 
 def test_probability_rows():
