@@ -283,6 +283,42 @@ def correctness_gate(acc_steps, out_steps, first_step: int, oracle_res):
     return g
 
 
+def probe_and_emitted_check(wl, acc_steps, probe_np):
+    """Two more checks of the timed outputs against the oracle on the same
+    inputs.  (i) The probe of one call, p_i(x_i) and q_i(x_i) for every draft
+    position, against the oracle's float64 values: the largest absolute
+    difference (the pages' softmax probabilities, 1e-5 at most).  (ii) The
+    mean emitted tokens over the timed steps against its expectation: every
+    step sees the same rows and draft tokens with fresh uniforms, so request
+    b accepts position i with probability a_i = min(1, p_i(x_i)/q_i(x_i))
+    while the ones before it were accepted, and emits 1 + sum over n = 1..k
+    of prod_{i<n} a_i tokens on average (the expected-token formula with
+    these per-position rates).  Reported with the standard error of the
+    per-step means and its z score."""
+    import numpy as np
+
+    import oracle.verify as O
+
+    B, k = wl.B, wl.k
+    pv = np.zeros((B, k))
+    qv = np.zeros((B, k))
+    for b in range(B):
+        pv[b], qv[b] = O.probe_values(wl.target, wl.draft, wl.draft_tokens, wl.temperature,
+                                      wl.kind, wl.dtype, b)
+    dp = float(max(np.abs(probe_np[:, :k, 0] - pv).max(), np.abs(probe_np[:, :k, 1] - qv).max()))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        a = np.where(qv > 0, np.minimum(1.0, pv / np.where(qv > 0, qv, 1.0)), 0.0)
+    expect = 1.0 + np.cumprod(a, axis=1).sum(axis=1)  # per request
+    emitted = acc_steps.astype(np.float64) + 1.0
+    per_step = emitted.mean(axis=1)
+    se = float(per_step.std(ddof=1) / np.sqrt(len(per_step))) if len(per_step) > 1 else None
+    mean = float(per_step.mean())
+    e = float(expect.mean())
+    return ({"max_abs_dp": dp, "positions": int(B * k), "tolerance": 1e-5},
+            {"mean": mean, "expected": e, "se": se,
+             "z": (mean - e) / se if se else None, "steps": int(len(per_step))})
+
+
 # Extra workloads (not the headline line): greedy chain and tree greedy.
 GREEDY_WORKLOADS = {
     "tree": "tree greedy, B=16, 61 nodes (1 root + 60, depth 5), V=128256, bf16",
@@ -762,13 +798,27 @@ def bench_probs(args):
         result["cpu_baseline"] = allc
         result["cpu_baseline_1core"] = one
         gate = correctness_gate(acc_np, out_np, first, res)
+        t, d = copies[first % len(copies)]
+        _, _, pr = S.spec_verify_sample(t, d, toks, 1.0, seed=wl.uniform_seed,
+                                        counter0=first * n_u, kind="probs", workspace=ws,
+                                        probe=True)
+        torch.cuda.synchronize()
+        gate["probe"], gate["emitted"] = probe_and_emitted_check(wl, acc_np, pr.cpu().numpy())
         result["correctness_gate"] = gate
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    bad = []
     if gate is not None and gate["unflagged"]:
-        print("bench: FAILED: probability-row outputs disagree with the oracle away from any "
-              "decision boundary", file=sys.stderr, flush=True)
+        bad.append("probability-row outputs disagree with the oracle away from any decision "
+                   "boundary")
+    if gate is not None and gate["probe"]["max_abs_dp"] > 1e-5:
+        bad.append(f"probe values differ from the oracle by {gate['probe']['max_abs_dp']:.2e}")
+    if gate is not None and gate["emitted"]["z"] is not None and abs(gate["emitted"]["z"]) > 6:
+        bad.append(f"mean emitted tokens {gate['emitted']['mean']:.4f} is "
+                   f"{gate['emitted']['z']:.1f} standard errors from its expectation")
+    if bad:
+        print("bench: FAILED: " + "; ".join(bad), file=sys.stderr, flush=True)
         sys.exit(1)
 
 
@@ -1036,6 +1086,12 @@ def bench_sample(args):
         result["cpu_baseline"] = allc
         result["cpu_baseline_1core"] = one
         gate = correctness_gate(acc_np, out_np, first, res)
+        # one more call with the probe, on the first timed step's inputs
+        t, d = copies[first % len(copies)]
+        _, _, pr = S.spec_verify_sample(t, d, toks, wl.temperature, seed=wl.uniform_seed,
+                                        counter0=first * n_u, workspace=ws, probe=True)
+        torch.cuda.synchronize()
+        gate["probe"], gate["emitted"] = probe_and_emitted_check(wl, acc_np, pr.cpu().numpy())
         result["correctness_gate"] = gate
     else:
         result["cpu_baseline"] = None
@@ -1046,6 +1102,11 @@ def bench_sample(args):
     if gate is not None and gate["unflagged"]:
         bad.append(f"{gate['unflagged']} requests disagree with the oracle away from any "
                    "decision boundary")
+    if gate is not None and gate["probe"]["max_abs_dp"] > 1e-5:
+        bad.append(f"probe values differ from the oracle by {gate['probe']['max_abs_dp']:.2e}")
+    if gate is not None and gate["emitted"]["z"] is not None and abs(gate["emitted"]["z"]) > 6:
+        bad.append(f"mean emitted tokens {gate['emitted']['mean']:.4f} is "
+                   f"{gate['emitted']['z']:.1f} standard errors from its expectation")
     for name_, sch in result.get("schedules", {}).items():
         if not sch["outputs_identical"]:
             bad.append(f"the {name_} schedule's outputs differ from the timed schedule's")

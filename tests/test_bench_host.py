@@ -54,3 +54,25 @@ def test_correctness_gate_counts_flagged_and_unflagged_mismatches():
     assert g["steps"] == 1 and g["requests"] == 4
     assert g["mismatches"] == 3 and g["unflagged"] == 1
     assert g["draw_decisions"] == 4 and g["accept_decisions"] == 8
+
+
+def test_probe_and_emitted_check_on_hand_made_rows():
+    """Probability rows with p_0(x_0) = 0.2, q_0(x_0) = 0.4 (accept 1/2) and
+    p_1(x_1) = 0.3, q_1(x_1) = 0.1 (accept 1): 1 + 1/2 + 1/2 = 2 emitted
+    tokens expected; a probe off by 3e-6 reads 3e-6."""
+    import types
+
+    target = np.array([[[0.1, 0.2, 0.3, 0.4], [0.4, 0.1, 0.3, 0.2], [0.25, 0.25, 0.25, 0.25]]],
+                      dtype=np.float32)
+    draft = np.array([[[0.3, 0.4, 0.2, 0.1], [0.5, 0.2, 0.1, 0.2]]], dtype=np.float32)
+    wl = types.SimpleNamespace(B=1, k=2, target=target, draft=draft,
+                               draft_tokens=np.array([[1, 2]], np.int32), temperature=1.0,
+                               kind="probs", dtype="f32")
+    probe = np.zeros((1, 3, 4), np.float32)
+    probe[0, 0, :2] = [0.2, 0.4]
+    probe[0, 1, :2] = [0.3, 0.1 + 3e-6]
+    acc = np.array([[1], [0], [2], [1]], np.int32)  # 2, 1, 3, 2 emitted: mean 2
+    pr, em = bench.probe_and_emitted_check(wl, acc, probe)
+    assert abs(pr["max_abs_dp"] - 3e-6) < 1e-7 and pr["positions"] == 2
+    assert abs(em["expected"] - 2.0) < 1e-7
+    assert abs(em["mean"] - 2.0) < 1e-12 and em["steps"] == 4 and abs(em["z"]) < 1e-6
