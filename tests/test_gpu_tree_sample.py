@@ -13,7 +13,8 @@ the C ABI.
   out-of-range node tokens, a root whose draft row equals its target row
   so the residual after a rejection is empty, and masked (-inf) logits
   with logits spread wide at a low temperature (the float64 statistics'
-  reference handling).
+  reference handling); a call captured into a HIP graph and replayed on
+  new inputs, with eager calls of another shape in between.
 * Statistics: with every child's token drawn from the draft at its parent,
   the first emitted token follows the target's root distribution
   (chi-square over 40000 requests).
@@ -199,6 +200,65 @@ def test_masked_and_wide_low_temperature_logits(dt):
         node = int(path[b, n])
         tok = int(out[b, n])
         assert tok >= 0 and np.isfinite(zt[b, node, tok]), (b, node, tok)
+
+
+def test_graph_capture_and_replay():
+    """A tree-sampling call captured into a HIP graph and replayed on new
+    inputs (copied into the captured tensors), with an eager call of another
+    tree and shape on the same workspace between replays: every replay and
+    every eager call matches the oracle (the draw's completion tickets and
+    the tables leave the workspace ready for the next call)."""
+    _say("tree sampling: graph capture and replay")
+    parent = np.array([-1, 0, 0, 0, 1, 1, 2, 4, 4, 5], dtype=np.int32)
+    B, V, T = 8, 20000, 0.9
+    wls = [W.tree_sample(B=B, V=V, seed=80 + r, uniform_seed=90 + r, parent=parent,
+                         target_std=2.0, noise_std=1.0, temperature=T, n_peaks=0, dtype="bf16")
+           for r in range(3)]
+    N = len(parent)
+    dev = torch.device("cuda")
+    tgt = to_device(wls[0].target, "bf16")
+    dft = to_device(wls[0].draft, "bf16")
+    toks = ints_to_device(wls[0].node_tokens)
+    ug = torch.empty(B, N, 2, dtype=torch.float32, device=dev)
+    D = int(W.tree_depths(parent).max())
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
+    path = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
+    ws = S.Workspace(dev)
+    ws.get(S.spec_workspace_bytes(16, 61, 128256))
+
+    def call():
+        S.spec_verify_tree_sample(tgt, dft, parent.tolist(), toks, T, uniforms=ug,
+                                  workspace=ws, out=(acc, out, path))
+
+    u0 = R.tree_uniforms(wls[0].uniform_seed, B, N, 0)
+    ug.copy_(torch.from_numpy(np.ascontiguousarray(u0, np.float32)))
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    other = W.tree_sample(B=5, V=3001, seed=95, uniform_seed=96,
+                          parent=np.array([-1, 0, 0, 1, 1, 1, 2], np.int32), target_std=2.0,
+                          noise_std=1.0, temperature=1.0, n_peaks=0, dtype="f32")
+    for r, wl in enumerate(wls):
+        u = R.tree_uniforms(wl.uniform_seed, B, N, 0)
+        tgt.copy_(to_device(wl.target, "bf16"))
+        dft.copy_(to_device(wl.draft, "bf16"))
+        toks.copy_(ints_to_device(wl.node_tokens))
+        ug.copy_(torch.from_numpy(np.ascontiguousarray(u, np.float32)))
+        acc.fill_(-7)
+        out.fill_(-7)
+        path.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        st = _check(wl, acc.cpu().numpy(), out.cpu().numpy(), path.cpu().numpy())
+        _say(f"  replay {r}: {st['mismatches']} mismatches")
+        a2, o2, p2 = _run_gpu(other, ws=ws)
+        _check(other, a2, o2, p2)
+    assert S.spec_workspace_status(ws) == 0
 
 
 def test_probability_rows():
