@@ -86,11 +86,13 @@ def test_greedy_chain_shapes(B, k, V, dtype):
     _run_greedy(W.greedy_chain(B=B, k=k, V=V, seed=B * 1000 + V, dtype=dtype))
 
 
-def test_greedy_chain_ties_masks_and_bad_tokens():
+@pytest.mark.parametrize("V", [3000, 2000])  # chunked kernel; one work-group per request
+def test_greedy_chain_ties_masks_and_bad_tokens(V):
     rng = np.random.default_rng(5)
-    B, k, V = 40, 5, 3000
+    B, k = 40, 5
     z = np.round(rng.standard_normal((B, k + 1, V)) * 1.2).astype(np.float32)  # many ties
     z[rng.random(z.shape) < 0.3] = -np.inf
+    z[3, 1] = -np.inf  # a wholly masked row: its argmax is index 0
     amax = np.argmax(z[:, :k], axis=-1)
     toks = np.where(rng.random((B, k)) < 0.8, amax, rng.integers(0, V, (B, k))).astype(np.int32)
     toks[0, 0] = -1

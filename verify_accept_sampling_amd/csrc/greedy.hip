@@ -13,6 +13,7 @@
 //          parent's argmax; the deepest accepted node (lowest index on ties)
 //          ends the path and its argmax is emitted (same page, section on the
 //          full inference loop, "Strict Acceptance").
+#include <algorithm>
 #include <climits>
 
 #include "device_common.h"
@@ -210,6 +211,49 @@ __global__ __launch_bounds__(kThreads) void k_greedy_chain(
   if (threadIdx.x == 0) accepted_len[b] = n;
 }
 
+// Small chains (up to 64 positions, every row of a request within
+// kSmallChainElems elements in all): one work-group per request of one wave
+// per row (at most kSmallChainWaves; wave w takes rows w, w + waves, ...),
+// lanes striding each row; the row argmaxes meet in shared memory and wave
+// 0 applies the greedy rule.  No partials and no ticket: one round trip of
+// row loads instead of three dependent ones.
+constexpr long kSmallChainElems = 16384;
+constexpr int kSmallChainWaves = 16;
+template <int DT, int NE>
+__global__ __launch_bounds__(kSmallChainWaves * kWaveSize) void k_greedy_chain_small(
+    const void* __restrict__ target, int k, int V, const int32_t* __restrict__ draft_tokens,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens) {
+  __shared__ int amax[kWaveSize];
+  const int n_pos = k + 1;
+  const int b = static_cast<int>(blockIdx.x);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int waves = static_cast<int>(blockDim.x >> 6);
+  const int my_tok = wave == 0 && lane < k ? draft_tokens[(long)b * k + lane] : -1;
+  const long n_groups = V / NE;
+  for (int j = wave; j < n_pos; j += waves) {
+    const void* rp = reinterpret_cast<const char*>(target) +
+                     ((long)b * n_pos + j) * (long)V * Elems<DT>::kBytes;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll 4
+    for (long g = lane; g < n_groups; g += kWaveSize) {  // ascending per lane
+      float x[NE];
+      load_group<DT, NE, true>(rp, g * NE, x);
+      argmax_update<NE>(bv, bi, x, g);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) am_merge(bv, bi, shfl_xor_f(bv, o), shfl_xor_i(bi, o));
+    if (lane == 0) amax[j] = bi == INT_MAX ? 0 : bi;  // all-(-inf) rows resolve to index 0
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int am = lane < n_pos ? amax[lane] : 0;
+  const uint64_t mm = __ballot(lane < k && my_tok != am);
+  const int n = mm != 0 ? __builtin_ctzll(mm) : k;
+  if (lane < n_pos) out_tokens[(long)b * n_pos + lane] = lane < n ? my_tok : lane == n ? am : -1;
+  if (lane == 0) accepted_len[b] = n;
+}
+
 template <int DT, int NE, int NMAX>
 __global__ __launch_bounds__(kThreads) void k_tree_greedy(
     const void* __restrict__ target, int n_nodes, int V, int C1, TreeArgsN<NMAX> tree, int D,
@@ -331,6 +375,11 @@ struct ChainKernel {
   }
 };
 template <int DT, int NE>
+struct SmallChainKernel {
+  static auto fn() { return &k_greedy_chain_small<DT, NE>; }
+  static int per_cu() { return 1; }
+};
+template <int DT, int NE>
 struct SmallTreeKernel {
   static auto fn() { return &k_tree_greedy<DT, NE, kSmallTree>; }
   static int per_cu() {
@@ -352,6 +401,10 @@ hipError_t launch_greedy_chain(const void* target, int dtype, int B, int k, int 
                                int32_t* out_tokens, void* ws, const WsLayout& L,
                                hipStream_t s) {
   const bool vec = rows_aligned(target, V, dtype);
+  if (k + 1 <= kWaveSize && (long)V * (k + 1) <= kSmallChainElems)
+    return launch_timed(kProfRowPass, pick_kernel<SmallChainKernel>(dtype, vec), dim3(B),
+                        dim3(kWaveSize * std::min(k + 1, kSmallChainWaves)), 0, s, target, k, V,
+                        draft_tokens, accepted_len, out_tokens);
   const auto kern = pick_kernel<ChainKernel>(dtype, vec);
   const int C1 = row_chunks(pick_per_cu<ChainKernel>(dtype, vec), (long)B * (k + 1), V, 1);
   char* w = static_cast<char*>(ws);
