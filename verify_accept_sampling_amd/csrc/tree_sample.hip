@@ -23,17 +23,22 @@
 //
 // Launches (none waits for another work-group: each reads what the kernels
 // before it on the stream wrote):
-//   k_tree_setup     one work-group: child lists, ranks, depths, the list of
-//                    nodes with children, and the children of rank >= 1 by
+//   k_tree_setup     one work-group (trees above kSmallTree nodes, or
+//                    probability rows; else work-group 0 of k_tree_stats):
+//                    child lists, ranks, depths, the lists of nodes with and
+//                    without children, and the children of rank >= 1 by
 //                    rank, from the parent array, into the workspace;
-//   k_tree_stats     (logits) float32 row statistic of every target row and
-//                    of the draft rows of nodes with children;
+//   k_tree_stats     (logits) the float64 statistic of both rows of every
+//                    node with children, per 16384-element chunk;
 //   k_tree_mass      one launch per round: per (request, child of rank i,
-//                    chunk) the chunk's sum of max(0, p - C_i q) at its
-//                    parent;
+//                    8192-element chunk) the chunk's sum of
+//                    max(0, p - C_i q) at its parent;
 //   k_tree_walk      one wave per request: the tests, the accepted path, the
-//                    outputs but the final token, and the draw state;
-//   k_tree_draw      per (request, chunk) the chunk's draw-weight total;
+//                    outputs but the final token, and the draw state; its
+//                    other work-groups compute the float32 statistics of
+//                    the leaves' target rows (logits; only the draw reads
+//                    them);
+//   k_tree_draw      per (request, chunk) the chunk's draw-weight totals;
 //                    the request's last work-group (completion ticket) then
 //                    picks the chunk by running total and the element by
 //                    the same per-chunk scan, on one wave.
@@ -196,7 +201,8 @@ __device__ __forceinline__ void ms64_merge(float& m, double& s, float m2, double
 // Row statistics of target row u and draft row u of request b.  Nodes with
 // children (`internal`): the float64 statistics k_tree_stats stored at
 // slots b*2N + u and b*2N + N + u (tree_xchunks(V) chunks each), merged in
-// chunk order.  A leaf: the
+// chunk order (plain sums when the chunks share their reference, as they
+// do unless a row's values exceed its first element by far).  A leaf: the
 // reference of its target row's float32 statistic, with S = 1 (its weights
 // are normalised by their own total).
 struct RowPair {
