@@ -790,12 +790,40 @@ __device__ __forceinline__ void tree_pick_wave(
     const TreeStat64* __restrict__ xstat, const double* __restrict__ dp, const double* tab,
     int32_t* __restrict__ out_tokens) {
   const int lane = threadIdx.x & 63;
+  // The chunk totals of the first kPickTiles tiles of 64 chunks (both
+  // entries) come into registers in one round trip, together with the row
+  // statistics' loads; tiles past them (rows beyond kPickTiles * 64
+  // chunks) are loaded as the scans reach them.
+  constexpr int kPickTiles = 8;
+  double r0[kPickTiles], r1[kPickTiles];
+#pragma unroll
+  for (int t = 0; t < kPickTiles; ++t) {
+    const int ch = t * kWaveSize + lane;
+    const long cc = min(ch, C2 - 1);  // unconditional loads
+    const double a0 = ld_dev_d(&dp[cc * 2]), a1 = ld_dev_d(&dp[cc * 2 + 1]);
+    r0[t] = ch < C2 ? a0 : 0.0;
+    r1[t] = ch < C2 ? a1 : 0.0;
+  }
+  RowPair rows{};
+  if (KIND == 0) rows = node_rows(xstat, part, b, N, st.node, V, C1, c, c1, tab, st.cf > 0.0);
+  const int n_tiles = (C2 + kWaveSize - 1) / kWaveSize;
+  auto entry = [&](int t, int w) {  // chunk t * 64 + lane's total, entry w
+    double v = 0.0;
+#pragma unroll
+    for (int i = 0; i < kPickTiles; ++i)
+      if (i == t) v = w ? r1[i] : r0[i];
+    if (t >= kPickTiles) {
+      const int ch = t * kWaveSize + lane;
+      v = ch < C2 ? ld_dev_d(&dp[(long)ch * 2 + w]) : 0.0;
+    }
+    return v;
+  };
   int which = 0;
   double C = st.cf;
   bool use_q = st.cf > 0.0;
   if (use_q) {  // empty residual: the weights before the last rejection
     double any = 0.0;
-    for (int ch = lane; ch < C2; ch += kWaveSize) any += ld_dev_d(&dp[(long)ch * 2]);
+    for (int t = 0; t < n_tiles; ++t) any += entry(t, 0);
     if (!(wave_sum_d(any) > 0.0)) {
       which = 1;
       C = st.cp;
@@ -806,17 +834,16 @@ __device__ __forceinline__ void tree_pick_wave(
   // chunk base + l, a wave scan per tile.  The grand total and the search
   // below run the same scans, so they see the same prefixes.
   const double u = (double)get_uniform(uniforms, seed, ctr0, b, st.node, 1, N - 1);
-  auto tile = [&](int base, double running, double& v, double& excl) {
-    const int ch = base + lane;
-    v = ch < C2 ? ld_dev_d(&dp[(long)ch * 2 + which]) : 0.0;
+  auto tile = [&](int t, double running, double& v, double& excl) {
+    v = entry(t, which);
     const double inc = wave_inclusive_scan_d(v);
     excl = running + (inc - v);
     return running + __shfl(inc, 63, 64);  // running total after the tile
   };
   double total = 0.0;
-  for (int base = 0; base < C2; base += kWaveSize) {  // wave-uniform
+  for (int t = 0; t < n_tiles; ++t) {  // wave-uniform
     double v, excl;
-    total = tile(base, total, v, excl);
+    total = tile(t, total, v, excl);
   }
   int tok = -1;
   if (total > 0.0) {
@@ -825,9 +852,10 @@ __device__ __forceinline__ void tree_pick_wave(
     // the chunks before it (past the end, a last-bit difference: the last).
     int sel = C2 - 1;
     double P = 0.0, running = 0.0;
-    for (int base = 0; base < C2; base += kWaveSize) {  // wave-uniform
+    for (int t = 0; t < n_tiles; ++t) {  // wave-uniform
+      const int base = t * kWaveSize;
       double v, excl;
-      const double after = tile(base, running, v, excl);
+      const double after = tile(t, running, v, excl);
       const uint64_t mh = __ballot(base + lane < C2 && excl + v > thr);
       if (mh != 0) {
         const int f = __builtin_ctzll(mh);
@@ -841,8 +869,6 @@ __device__ __forceinline__ void tree_pick_wave(
       }
       running = after;
     }
-    RowPair rows{};
-    if (KIND == 0) rows = node_rows(xstat, part, b, N, st.node, V, C1, c, c1, tab, st.cf > 0.0);
     const TermCoef k = term_coef<KIND>(rows, c1);
     const long eb = Elems<DT>::kBytes;
     const void* prow = static_cast<const char*>(target) + ((long)b * N + st.node) * V * eb;
