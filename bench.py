@@ -1007,7 +1007,9 @@ def bench_sample(args):
     need_rows = (np.minimum(acc_np + 1, k + 1) + np.minimum(acc_np + 1, k)).sum(axis=1)
     must_bytes = float(np.mean(need_rows * row_bytes + draw_bytes))
     full_bytes = float(np.mean(pass1_bytes + draw_bytes))
-    if args.path == "two_launch":
+    # the schedule that ran: two launches (row pass, draw) when asked for, or
+    # when auto picks them for a small row count; else the fused kernel
+    if "fused" not in kern:
         dom_name, dom, dom_bytes = "row_pass", kern["row_pass"], float(pass1_bytes)
     else:
         dom_name = "fused"
@@ -1032,7 +1034,9 @@ def bench_sample(args):
         "config": {"workload": wname, "B": B, "k": k, "V": V,
                    "logits": "bf16", "temperature": wl.temperature, "input_copies": len(copies),
                    "draw_arithmetic": "f64", "path": args.path},
-        "roofline": {"bound": "hbm", "kernel": KERNELS[args.path], "achieved": achieved,
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_sample_one" if dom_name == "fused" else "k_row_stats",
+                     "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes},
         "kernel_us": {"avg": dom["avg_us"], "p10": dom["p10_us"], "p50": dom["p50_us"],
@@ -1044,6 +1048,8 @@ def bench_sample(args):
                        "re-read of the rows drawn from (the early-exit schedule reads fewer: "
                        "must_read_bytes_per_launch, and traffic when measured)",
         "schedule": schedule,
+        "schedule_ran": "one launch (k_sample_one)" if dom_name == "fused"
+        else "two launches (k_row_stats, k_draw)",
         "must_read_bytes_per_launch": must_bytes,
         "achieved_gbps_over_must_read": must_bytes / (dom["avg_us"] * 1e-6) / 1e9
         if dom_name == "fused" else None,

@@ -174,8 +174,9 @@ int spec_verify_sample(const void* target, const void* draft, int dtype, int kin
  *   SPEC_SCHED_ONE_LAUNCH.
  * SPEC_SCHED_AUTO: SPEC_SCHED_EARLY_EXIT when the row pass needs more than
  *   one round of resident work-groups (B * (2k+1) * ceil(V / 65536) above
- *   five per compute unit), else SPEC_SCHED_ONE_LAUNCH: the faster of the two
- *   for the shape (every schedule gives the same outputs).
+ *   five per compute unit), SPEC_SCHED_TWO_LAUNCH when it needs at most a
+ *   third of one, else SPEC_SCHED_ONE_LAUNCH: the fastest for the shape as
+ *   measured (every schedule gives the same outputs).
  * Graph capture: on a stream that is being captured (hipStreamIsCapturing),
  * the one-launch schedules take their completion tags from a call epoch in
  * the workspace and add a one-thread kernel that advances it, so every

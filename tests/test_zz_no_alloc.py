@@ -117,8 +117,10 @@ def test_noalloc_probability_rows():
 def test_noalloc_give_up_does_not_outlive_its_call():
     _say("noalloc: forced give-up, then a normal call without reset")
     wl, tgt, dft, toks = _inputs(8, 4, 32000, 77)
+    # the one-launch schedule: its bounded waits are what the flag makes give up
     acc, out = S.spec_verify_sample_noalloc(tgt, dft, toks, wl.temperature,
-                                            seed=wl.uniform_seed, test_give_up=True)
+                                            seed=wl.uniform_seed, test_give_up=True,
+                                            schedule="one_launch")
     torch.cuda.synchronize()
     acc = acc.cpu().numpy()
     out = out.cpu().numpy()

@@ -1136,20 +1136,26 @@ static hipError_t launch_logits(const void* target, const void* draft, int B, in
   const long R = 2L * k + 1;
   auto* zr = reinterpret_cast<float*>(w + L.zrow);
   const long n_row = (long)B * R * C1;
-  if (mode.sched != SPEC_SCHED_TWO_LAUNCH) {
+  const long slots = (long)device_cus() * kOneLaunchGroupsPerCU;
+  // AUTO: early exit when the row pass takes more than one round of
+  // resident work-groups (then rows started after the first decisions can
+  // be skipped); with fewer rows every row is in flight from the start and
+  // the one-launch schedule is faster (B = 8, k = 4, V = 32000 bf16: 22.1
+  // us against 24.0 us with early exit); with at most a third of a round of
+  // rows, the two launches (row pass, then draw) are faster still: their
+  // draw work-groups start on known verdicts instead of waiting in the grid
+  // (per call: B = 8, k = 4, V = 32000: 19.8 against 20.7 us; B = 8, k = 8,
+  // V = 128256: 26.3 against 28.2; 816 rows, B = 24, k = 8, V = 128256:
+  // 46.0 against 42.3).
+  const int sched = mode.sched != SPEC_SCHED_AUTO ? mode.sched
+                    : n_row > slots              ? SPEC_SCHED_EARLY_EXIT
+                    : n_row * 3 > slots          ? SPEC_SCHED_ONE_LAUNCH
+                                                 : SPEC_SCHED_TWO_LAUNCH;
+  if (sched != SPEC_SCHED_TWO_LAUNCH) {
     auto* fl = reinterpret_cast<uint64_t*>(w + L.flag);
     // Early positions: as many as the first round of resident work-groups
     // streams (at least one).
     const long per_pos = (long)B * 2 * C1;
-    const long slots = (long)device_cus() * kOneLaunchGroupsPerCU;
-    // AUTO: early exit when the row pass takes more than one round of
-    // resident work-groups (then rows started after the first decisions can
-    // be skipped); with fewer rows every row is in flight from the start and
-    // the one-launch schedule is faster (B = 8, k = 4, V = 32000 bf16: 22.1
-    // us against 24.0 us with early exit).
-    const int sched = mode.sched != SPEC_SCHED_AUTO ? mode.sched
-                      : n_row > slots              ? SPEC_SCHED_EARLY_EXIT
-                                                   : SPEC_SCHED_ONE_LAUNCH;
     // Early exit needs no probe values beyond each request's stop.
     const bool exit_early = sched == SPEC_SCHED_EARLY_EXIT && probe == nullptr;
     // Measured at B = 64, k = 8, V = 128256 bf16 with early exit: E = 2, 3,
