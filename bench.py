@@ -407,12 +407,17 @@ def bench_greedy(args):
     t0 = to_dev(wl.target)
     copies = [t0] + [t0.clone() for _ in range(args.copies - 1)]
     ws = S.Workspace(dev)
+    # preallocated outputs, as a serving loop keeps them
+    n_out = (int(W.tree_depths(np.asarray(parent)).max()) + 1) if name == "tree" else rows
+    outs = (torch.empty(B, dtype=torch.int32, device=dev),
+            torch.empty(B, n_out, dtype=torch.int32, device=dev))
 
     def step(i):
         t = copies[i % len(copies)]
         if name == "tree":
-            return S.spec_verify_tree_greedy(t, parent, toks, want_path=False, workspace=ws)
-        return S.spec_verify_greedy(t, toks, workspace=ws)
+            return S.spec_verify_tree_greedy(t, parent, toks, want_path=False, workspace=ws,
+                                             out=outs)
+        return S.spec_verify_greedy(t, toks, workspace=ws, out=outs)
 
     for i in range(args.warmup):
         step(i)

@@ -374,3 +374,27 @@ def test_workspace_reuse_with_stale_partials(sample_path):
         assert int(buf[:PER_REQUEST_BYTES + 8].count_nonzero()) == 0
         assert S.spec_workspace_status(ws) == 0
         buf[COUNTER_BYTES:].fill_(0x5A)
+
+
+def test_greedy_bindings_write_preallocated_outputs():
+    """out= hands in the output tensors: they are written in place, returned,
+    and hold what freshly allocated outputs would."""
+    wl = W.greedy_chain(B=6, k=3, V=5000, seed=12, dtype="bf16")
+    t, tk = to_device(wl.target, "bf16"), ints_to_device(wl.draft_tokens)
+    ref = S.spec_verify_greedy(t, tk)
+    outs = (torch.full((6,), -9, dtype=torch.int32, device="cuda"),
+            torch.full((6, 4), -9, dtype=torch.int32, device="cuda"))
+    got = S.spec_verify_greedy(t, tk, out=outs)
+    assert got[0] is outs[0] and got[1] is outs[1]
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+    tw = W.tree_greedy(B=5, V=3000, seed=13)
+    tt, tn = to_device(tw.target, tw.dtype), ints_to_device(tw.node_tokens)
+    D = int(W.tree_depths(tw.parent).max())
+    ref = S.spec_verify_tree_greedy(tt, tw.parent.tolist(), tn)
+    outs = tuple(torch.full(shape, -9, dtype=torch.int32, device="cuda")
+                 for shape in ((5,), (5, D + 1), (5, D + 1)))
+    got = S.spec_verify_tree_greedy(tt, tw.parent.tolist(), tn, out=outs)
+    assert all(g is o for g, o in zip(got, outs))
+    assert all(torch.equal(r, g) for r, g in zip(ref, got))
+    with pytest.raises(ValueError):
+        S.spec_verify_greedy(t, tk, out=(outs[0], outs[1][:, :2]))

@@ -281,17 +281,20 @@ def spec_fill_uniforms(seed: int, counter0: int, n: int,
 
 
 def spec_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
-                       workspace: Optional[Workspace] = None):
+                       workspace: Optional[Workspace] = None, out=None):
     """Greedy chain verification.  target [B, k+1, V] (f32/bf16), draft_tokens
-    int32 [B, k].  Returns (accepted_len [B], out_tokens [B, k+1])."""
+    int32 [B, k].  out: optional preallocated (accepted_len, out_tokens),
+    written in place and returned.  Returns (accepted_len [B], out_tokens
+    [B, k+1])."""
     _need_cuda(target, "target")
     B, kp1, V = target.shape
     k = kp1 - 1
     _need_cuda(draft_tokens, "draft_tokens")
     if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, k):
         raise ValueError("draft_tokens must be int32 [B, k]")
-    acc = torch.empty(B, dtype=torch.int32, device=target.device)
-    out = torch.empty(B, kp1, dtype=torch.int32, device=target.device)
+    o_acc, o_out = (None, None) if out is None else out
+    acc = _out_arg(o_acc, (B,), torch.int32, target.device, "accepted_len")
+    out = _out_arg(o_out, (B, kp1), torch.int32, target.device, "out_tokens")
     lib = load_library()
     nbytes = spec_workspace_bytes(B, kp1, V)
     ws = _workspace(workspace, target.device, nbytes)
@@ -395,9 +398,22 @@ def spec_verify_sample_noalloc(target: torch.Tensor, draft: Optional[torch.Tenso
     return acc, tok
 
 
+_parent_cache: dict = {}
+
+
 def _parent_array(parent) -> "ctypes.Array":
-    vals = [int(v) for v in (parent.tolist() if hasattr(parent, "tolist") else parent)]
-    return (ctypes.c_int32 * len(vals))(*vals), len(vals)
+    """The parent array as int32 for the C call; the last few trees seen are
+    kept (a deployment verifies against one static tree), so a repeated tree
+    costs a tuple and a lookup."""
+    key = tuple(parent.tolist() if hasattr(parent, "tolist") else parent)
+    hit = _parent_cache.get(key)
+    if hit is None:
+        vals = [int(v) for v in key]
+        hit = ((ctypes.c_int32 * len(vals))(*vals), len(vals))
+        if len(_parent_cache) >= 8:
+            _parent_cache.pop(next(iter(_parent_cache)))
+        _parent_cache[key] = hit
+    return hit
 
 
 def spec_tree_depth(parent: Sequence[int]) -> int:
@@ -410,10 +426,12 @@ def spec_tree_depth(parent: Sequence[int]) -> int:
 
 def spec_verify_tree_greedy(target: torch.Tensor, parent: Sequence[int],
                             node_tokens: torch.Tensor, want_path: bool = True,
-                            workspace: Optional[Workspace] = None):
+                            workspace: Optional[Workspace] = None, out=None):
     """Greedy tree verification.  target [B, N, V], parent (host sequence of
-    N ints), node_tokens int32 [B, N].  Returns (accepted_len [B],
-    out_tokens [B, D+1], out_path [B, D+1] or None)."""
+    N ints), node_tokens int32 [B, N].  out: optional preallocated
+    (accepted_len, out_tokens[, out_path]), written in place and returned.
+    Returns (accepted_len [B], out_tokens [B, D+1], out_path [B, D+1] or
+    None)."""
     _need_cuda(target, "target")
     B, N, V = target.shape
     _need_cuda(node_tokens, "node_tokens")
@@ -426,9 +444,13 @@ def spec_verify_tree_greedy(target: torch.Tensor, parent: Sequence[int],
     if D < 0:
         _check(D)
     dev = target.device
-    acc = torch.empty(B, dtype=torch.int32, device=dev)
-    out = torch.empty(B, D + 1, dtype=torch.int32, device=dev)
-    path = torch.empty(B, D + 1, dtype=torch.int32, device=dev) if want_path else None
+    outs = tuple(out) if out is not None else ()
+    acc = _out_arg(outs[0] if outs else None, (B,), torch.int32, dev, "accepted_len")
+    out = _out_arg(outs[1] if outs else None, (B, D + 1), torch.int32, dev, "out_tokens")
+    if len(outs) > 2 and outs[2] is not None:
+        path = _out_arg(outs[2], (B, D + 1), torch.int32, dev, "out_path")
+    else:
+        path = torch.empty(B, D + 1, dtype=torch.int32, device=dev) if want_path else None
     lib = load_library()
     nbytes = spec_workspace_bytes(B, N, V)
     ws = _workspace(workspace, dev, nbytes)
