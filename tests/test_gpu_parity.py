@@ -398,3 +398,25 @@ def test_greedy_bindings_write_preallocated_outputs():
     assert all(torch.equal(r, g) for r, g in zip(ref, got))
     with pytest.raises(ValueError):
         S.spec_verify_greedy(t, tk, out=(outs[0], outs[1][:, :2]))
+
+
+def test_empty_batches_through_every_entry_point():
+    """B = 0 through the binding: every call returns empty outputs and
+    launches nothing."""
+    dev = "cuda"
+    k, V = 3, 1000
+    t = torch.zeros(0, k + 1, V, dtype=torch.bfloat16, device=dev)
+    d = torch.zeros(0, k, V, dtype=torch.bfloat16, device=dev)
+    tk = torch.zeros(0, k, dtype=torch.int32, device=dev)
+    acc, out = S.spec_verify_sample(t, d, tk, 0.8, seed=1)
+    assert acc.shape == (0,) and out.shape == (0, k + 1)
+    acc, out = S.spec_verify_greedy(t, tk)
+    assert acc.shape == (0,) and out.shape == (0, k + 1)
+    parent = [-1, 0, 0, 1]
+    tt = torch.zeros(0, 4, V, dtype=torch.bfloat16, device=dev)
+    nt = torch.zeros(0, 4, dtype=torch.int32, device=dev)
+    acc, out, path = S.spec_verify_tree_greedy(tt, parent, nt)
+    assert acc.shape == (0,) and out.shape == (0, 3)
+    acc, out, path = S.spec_verify_tree_sample(tt, tt.clone(), parent, nt, 0.8, seed=1)
+    assert acc.shape == (0,) and out.shape == (0, 3)
+    torch.cuda.synchronize()
