@@ -715,7 +715,7 @@ def bench_tree_sample(args):
         "value": B / (ms_step * 1e-3), "unit": "verified requests/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "f64", "data": "synthetic",
         "config": {"workload": "tree_sample_b16_n61_v128256_bf16_t0.7", "B": B, "nodes": N,
                    "V": V, "logits": "bf16", "temperature": wl.temperature,
                    "input_copies": len(copies), "draw_arithmetic": "f64"},
