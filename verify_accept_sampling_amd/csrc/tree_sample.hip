@@ -29,7 +29,7 @@
 //                    without children, and the children of rank >= 1 by
 //                    rank, from the parent array, into the workspace;
 //   k_tree_stats     (logits) the float64 statistic of both rows of every
-//                    node with children, per 16384-element chunk;
+//                    node with children, per kTreeStatChunk-element chunk;
 //   k_tree_mass      one launch per round: per (request, child of rank i,
 //                    8192-element chunk) the chunk's sum of
 //                    max(0, p - C_i q) at its parent;
