@@ -14,7 +14,8 @@ the C ABI.
   so the residual after a rejection is empty, and masked (-inf) logits
   with logits spread wide at a low temperature (the float64 statistics'
   reference handling); a call captured into a HIP graph and replayed on
-  new inputs, with eager calls of another shape in between.
+  new inputs, with eager calls of another shape in between; V = 300000
+  (more statistic chunks and draw chunks than the kernels keep at once).
 * Statistics: with every child's token drawn from the draft at its parent,
   the first emitted token follows the target's root distribution
   (chi-square over 40000 requests).
@@ -200,6 +201,20 @@ def test_masked_and_wide_low_temperature_logits(dt):
         node = int(path[b, n])
         tok = int(out[b, n])
         assert tok >= 0 and np.isfinite(zt[b, node, tok]), (b, node, tok)
+
+
+def test_large_vocabulary():
+    """V = 300000: more than 8 statistic chunks per row (the merges' second
+    batch) and more than 512 draw chunks (the pick's tiles past those it
+    keeps in registers)."""
+    _say("tree sampling: V=300000")
+    parent = np.array([-1, 0, 0, 1, 1], dtype=np.int32)
+    wl = W.tree_sample(B=6, V=300000, seed=61, uniform_seed=62, parent=parent, target_std=2.0,
+                       noise_std=1.0, temperature=1.0, n_peaks=0, dtype="bf16")
+    wl.node_tokens[::2, 1] = wl.V + 1  # rejected: draws from residuals over the whole row
+    acc, out, path = _run_gpu(wl)
+    st = _check(wl, acc, out, path)
+    assert st["mismatches"] == 0
 
 
 def test_graph_capture_and_replay():
