@@ -357,6 +357,42 @@ __device__ __forceinline__ void residual_state(const int* tables, const double* 
                                                double& M) {
   C = 0.0;
   M = 1.0;
+  constexpr int kFast = 8;  // ranks whose partials are loaded together
+  if (N <= kWaveSize && Cm <= kWaveSize && r <= kFast) {
+    // Small trees: the children of u from one load of the parent table
+    // (lane l: node l; a child's rank is its position among the set bits),
+    // then every needed rank's partials in one round trip, summed as
+    // wave_sum_fixed sums them (lane l holds entry l, then the butterfly):
+    // the same numbers as the loop below.
+    const int lane = threadIdx.x & 63;
+    const int pl = lane < N ? tree_tab(tables, kTabParent)[lane] : -1;
+    uint64_t kids = __ballot(lane > 0 && pl == u);
+    int js[kFast];
+#pragma unroll
+    for (int i = 0; i <= kFast; ++i) {  // js[i - 1]: the child of rank i
+      const int jj = kids ? __builtin_ctzll(kids) : -1;
+      if (kids) kids &= kids - 1;
+      if (i >= 1) js[i - 1] = jj;
+    }
+    double v[kFast];
+#pragma unroll
+    for (int i = 0; i < kFast; ++i) {
+      const int jj = js[i] >= 0 ? js[i] : 0;
+      const double x = mpart[((long)b * N + jj) * Cm + min(lane, Cm - 1)];
+      v[i] = lane < Cm ? x : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < kFast; ++i) {
+      if (i >= r || js[i] < 0) break;
+      const double cn = C + M;
+      const double F = wave_sum_d(v[i]);
+      if (F > 0.0) {
+        C = cn;
+        M = F;
+      }
+    }
+    return;
+  }
   int j = tree_tab(tables, kTabFirst)[u];
   for (int i = 0; i < r && j >= 0; ++i) {
     // state for child rank i + 1 from child rank i's rejection
