@@ -667,7 +667,7 @@ def bench_tree_sample(args):
         run(first + j, scratch)
     torch.cuda.synchronize()
     S.spec_profile_enable(False)
-    kinds = ("tree_stats", "tree_mass", "tree_walk", "tree_draw")
+    kinds = ("tree_stats", "tree_mass", "tree_walk", "tree_leaf", "tree_draw")
     kern = {}
     for kk in kinds:
         d = S.spec_profile_durations(kk)
@@ -683,17 +683,19 @@ def bench_tree_sample(args):
     row = V * 2
     stats_bytes = float(B * 2 * n_int * row)
     stats_ops = float(B * 2 * n_int * V * TREE_STAT_OPS_PER_ELEM)
-    leaf_bytes = float(B * (N - n_int) * row)
     acc_np = acc_all.cpu().numpy()
     path_np = path_all.cpu().numpy()
     out_np = out_all.cpu().numpy()
-    # draw: the stop node's target row, and its draft row after a rejection
-    drawn = 0
+    # draw: the stop node's target row, and its draft row after a rejection;
+    # a stop leaf's target row is also read once before, for its statistic
+    drawn = leaves = 0
     for jj in range(args.steps):
         for b in range(B):
             s_node = int(path_np[jj, b, acc_np[jj, b]])
             drawn += 2 if kids[s_node] else 1
+            leaves += 0 if kids[s_node] else 1
     draw_bytes = drawn / args.steps * row
+    leaf_bytes = leaves / args.steps * row
     mass_bytes = float(B * mass_units * 2 * row)
     step_bytes = stats_bytes + leaf_bytes + mass_bytes + draw_bytes
     st_us = kern["tree_stats"]["avg_us"]

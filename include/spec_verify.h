@@ -361,7 +361,8 @@ enum {
   SPEC_KERNEL_TREE_STATS = 5, /* tree sampling: row statistics */
   SPEC_KERNEL_TREE_MASS = 6,  /* tree sampling: residual-mass rounds */
   SPEC_KERNEL_TREE_WALK = 7,  /* tree sampling: table setup and the walk */
-  SPEC_KERNEL_TREE_DRAW = 8   /* tree sampling: draw weights and the pick */
+  SPEC_KERNEL_TREE_DRAW = 8,  /* tree sampling: draw weights and the pick */
+  SPEC_KERNEL_TREE_LEAF = 9   /* tree sampling: the stop leaves' row statistics */
 };
 int spec_profile_enable(int on);
 int spec_profile_read(int kind, long* launches, double* total_ms);

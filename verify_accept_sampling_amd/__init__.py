@@ -129,7 +129,8 @@ def load_library():
 
 
 KERNEL_KINDS = {"row_pass": 0, "draw": 1, "uniforms": 2, "fused": 3, "serving": 4,
-                "tree_stats": 5, "tree_mass": 6, "tree_walk": 7, "tree_draw": 8}
+                "tree_stats": 5, "tree_mass": 6, "tree_walk": 7, "tree_draw": 8,
+                "tree_leaf": 9}
 
 
 def spec_profile_enable(on: bool = True) -> None:

@@ -124,7 +124,7 @@ static_assert(SPEC_WORKSPACE_STATUS_OFFSET == kStatusWord * 4, "status word offs
 // has a tag of its own, so a tag left by an earlier call (or any other
 // content) is never taken for a current one.  The other regions are written
 // before they are read within each call.
-// Tree-sampling regions: the tree tables (ten int32 tables of kMaxNodes),
+// Tree-sampling regions: the tree tables (nine int32 tables of kMaxNodes),
 // the per-request draw state and the float64 row statistics.
 constexpr size_t kTreeTableBytes = 10 * (size_t)kMaxNodes * 4;
 constexpr size_t kTreeDrawBytes = 32;
@@ -216,7 +216,8 @@ constexpr int kProfTreeStats = 5; // tree sampling: row statistics
 constexpr int kProfTreeMass = 6;  // tree sampling: residual-mass rounds
 constexpr int kProfTreeWalk = 7;  // tree sampling: table setup and the walk
 constexpr int kProfTreeDraw = 8;  // tree sampling: draw weights and the pick
-constexpr int kProfKinds = 9;
+constexpr int kProfTreeLeaf = 9;  // tree sampling: the stop leaves' row statistics
+constexpr int kProfKinds = 10;
 // While timing is enabled, prof_begin hands out a start/stop event pair that
 // the launch itself stamps (hipExtLaunchKernel records them from the
 // kernel's dispatch, so the interval is the kernel alone); otherwise both

@@ -25,19 +25,21 @@
 // before it on the stream wrote):
 //   k_tree_setup     one work-group (trees above kSmallTree nodes, or
 //                    probability rows; else work-group 0 of k_tree_stats):
-//                    child lists, ranks, depths, the lists of nodes with and
-//                    without children, and the children of rank >= 1 by
-//                    rank, from the parent array, into the workspace;
+//                    child lists, ranks, depths, the list of nodes with
+//                    children, and the children of rank >= 1 by rank, from
+//                    the parent array, into the workspace;
 //   k_tree_stats     (logits) the float64 statistic of both rows of every
 //                    node with children, per kTreeStatChunk-element chunk;
 //   k_tree_mass      one launch per round: per (request, child of rank i,
 //                    8192-element chunk) the chunk's sum of
 //                    max(0, p - C_i q) at its parent;
 //   k_tree_walk      one wave per request: the tests, the accepted path, the
-//                    outputs but the final token, and the draw state; its
-//                    other work-groups compute the float32 statistics of
-//                    the leaves' target rows (logits; only the draw reads
-//                    them);
+//                    outputs but the final token, and the draw state (trees
+//                    of up to 64 nodes: every node's inputs in its own lane,
+//                    requested together, then a walk in registers);
+//   k_tree_leaf      (logits) per (request, chunk) the float32 statistic of
+//                    the target row of the leaf where the walk stopped, if
+//                    it stopped at a leaf (only the draw reads it);
 //   k_tree_draw      per (request, chunk) the chunk's draw-weight totals;
 //                    the request's last work-group (completion ticket) then
 //                    picks the chunk by running total and the element by
@@ -64,7 +66,6 @@ enum TreeTable {
   kTabRank,      // index among its siblings (0 = lowest)
   kTabDepth,
   kTabInternal,  // nodes with a child, ascending
-  kTabLeaf,      // nodes without a child, ascending
   kTabRanked,    // children of rank >= 1, by (rank, index)
   kTabRankOff,   // kTabRanked offset of rank r (entry r - 1), r = 1 .. max rank + 1
   kTabCount
@@ -126,8 +127,7 @@ __device__ __forceinline__ void tree_setup_block(const TreeArgsN<NMAX>& tree, in
   }
   __syncthreads();
   for (int j = threadIdx.x; j < N; j += kThreads) {
-    // The nodes with a child, ascending; those without, ascending; the
-    // children of rank >= 1 grouped by rank, ascending index within a
+    // The nodes with a child, ascending; the children of rank >= 1 grouped by rank, ascending index within a
     // rank; rank r's offset at entry r - 1 (r = 1 .. max rank + 1).
     // Entries past each list's length are 0.
     int n_int = 0, n_ranked = 0, max_rank = 0;
@@ -147,9 +147,7 @@ __device__ __forceinline__ void tree_setup_block(const TreeArgsN<NMAX>& tree, in
       }
     }
     if (nch[j] > 0) tables[kTabInternal * kMaxNodes + before_int] = j;
-    else tables[kTabLeaf * kMaxNodes + (j - before_int)] = j;  // leaves below j: j - before_int
     if (j >= n_int) tables[kTabInternal * kMaxNodes + j] = 0;
-    if (j >= N - n_int) tables[kTabLeaf * kMaxNodes + j] = 0;
     if (j >= 1 && rank[j] >= 1) tables[kTabRanked * kMaxNodes + lower_rank + same_rank_before] = j;
     if (j >= n_ranked) tables[kTabRanked * kMaxNodes + j] = 0;
     tables[kTabRankOff * kMaxNodes + j] = j <= max_rank ? off : 0;
@@ -560,19 +558,23 @@ __global__ __launch_bounds__(kThreads) void k_tree_stats(
   }
 }
 
-// Float32 statistic (part) of one chunk of a leaf's target row: its bonus
-// draw normalises its own weights, so only the reference is used.  Work
-// item i2 of B * n_leaf * C1.
+// The float32 statistic (reference, sum) of one chunk of C1 of the target
+// row of a leaf, the node where request b's walk stopped: the leaf's bonus
+// draw normalises its own weights, so only the reference is used.  One
+// work-group per (request, chunk); a request whose walk stopped at a node
+// with children (cf > 0: its rows have float64 statistics) has nothing to
+// do.  Only the stop leaf's row is read, one row per request.
 template <int DT, int NE>
-__device__ __forceinline__ void leaf_stats_block(const void* __restrict__ target, int N, int V,
-                                                 int C1, float c, int n_leaf,
-                                                 const int* __restrict__ tables,
-                                                 uint64_t* __restrict__ part, long i2) {
+__global__ __launch_bounds__(kThreads) void k_tree_leaf(const void* __restrict__ target, int N,
+                                                        int V, int C1, float c,
+                                                        const TreeDraw* __restrict__ tstate,
+                                                        uint64_t* __restrict__ part) {
+  const int chunk = static_cast<int>(blockIdx.x % C1);
+  const int b = static_cast<int>(blockIdx.x / C1);
+  const TreeDraw st = tstate[b];
+  if (st.cf > 0.0) return;  // work-group-uniform
+  const int node = st.node;
   const long eb = Elems<DT>::kBytes;
-  const int chunk = static_cast<int>(i2 % C1);
-  const int j = static_cast<int>((i2 / C1) % n_leaf);
-  const int b = static_cast<int>(i2 / C1 / n_leaf);
-  const int node = tree_tab(tables, kTabLeaf)[j];
   const void* rp = static_cast<const char*>(target) + ((long)b * N + node) * V * eb;
   const long n_groups = V / NE;
   const long gpc = (n_groups + C1 - 1) / C1;
@@ -696,6 +698,17 @@ inline size_t tree_walk_lds(int N) { return 256 * sizeof(double) + (3 + 2 * kWav
 // n_walk on instead compute the leaves' row statistics (logits), which only
 // the draw after this launch reads: streaming work beside the walk's
 // latency-bound waves.
+// Mass partials per node that the walk of a small tree keeps in registers.
+constexpr int kWalkLanePartials = 16;
+
+// Lane l's value of v in every lane (l wave-uniform).
+__device__ __forceinline__ double lane_value_d(double v, int l) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(bits), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), l);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int DT, int NE, int KIND>
 __global__ __launch_bounds__(kThreads) void k_tree_walk(
     const void* __restrict__ target, const void* __restrict__ draft, int B, int N, int V, int Cm,
@@ -704,14 +717,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
     const int* __restrict__ tables, const TreeStat64* __restrict__ xstat,
     const double* __restrict__ mpart, TreeDraw* __restrict__ tstate,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_path, int n_walk, int C1, float c, int n_leaf,
-    uint64_t* __restrict__ part) {
-  if ((int)blockIdx.x >= n_walk) {
-    if constexpr (KIND == 0)
-      leaf_stats_block<DT, NE>(target, N, V, C1, c, n_leaf, tables, part,
-                               (long)blockIdx.x - n_walk);
-    return;
-  }
+    int32_t* __restrict__ out_path) {
   extern __shared__ __align__(16) unsigned char walk_lds[];
   double* tab = reinterpret_cast<double*>(walk_lds);
   int* s_nchild = reinterpret_cast<int*>(tab + 256);
@@ -735,6 +741,72 @@ __global__ __launch_bounds__(kThreads) void k_tree_walk(
   int cur = 0, depth = 0;
   double cf = 0.0, cp = 0.0;
   if (lane == 0) path[0] = 0;
+  if (N <= kWaveSize && Cm <= kWalkLanePartials) {
+    // Small trees: lane j holds everything node j's test needs, requested
+    // together before the walk: its parent, token, uniform, the values of
+    // its token in its parent's rows, and F_j, the sum of its mass partials
+    // in the order wave_sum_fixed adds them (a wave holding them in lanes
+    // 0 .. Cm-1 and zeros above, halves added at distances 32, 16, .., 1;
+    // the zeros add exactly).  The walk itself then only moves registers.
+    const bool is_node = lane >= 1 && lane < N;
+    const int pj = is_node ? tree_tab(tables, kTabParent)[lane] : -1;
+    const int x = is_node ? tok[lane] : -1;
+    const bool valid = is_node && x >= 0 && x < V;
+    const double uj = is_node ? (double)get_uniform(uniforms, seed, ctr0, b, lane, 0, N - 1) : 0.0;
+    double f[kWalkLanePartials];
+    const double* mp = mpart + ((long)b * N + (is_node ? lane : 0)) * Cm;
+#pragma unroll
+    for (int i = 0; i < kWalkLanePartials; ++i) f[i] = i < Cm ? mp[i] : 0.0;
+#pragma unroll
+    for (int o = kWalkLanePartials / 2; o >= 1; o >>= 1)
+#pragma unroll
+      for (int i = 0; i < o; ++i) f[i] += f[i + o];
+    double px = 0.0, qx = 0.0;
+    if (is_node) {
+      RowPair rows{};
+      if (KIND == 0) rows = node_rows(xstat, nullptr, b, N, pj, V, 0, 0.f, c1, tab, true);
+      const TermCoef k = term_coef<KIND>(rows, c1);
+      const long ro = ((long)b * N + pj) * V * eb;
+      const int xs = valid ? x : 0;
+      px = tterm<KIND>(load_elem<DT>(static_cast<const char*>(target) + ro, xs), k.c1, k.c0p,
+                       k.ip, tab);
+      qx = tterm<KIND>(load_elem<DT>(static_cast<const char*>(draft) + ro, xs), k.c1, k.c0q,
+                       k.iq, tab);
+    }
+    for (;;) {
+      uint64_t kids = __ballot(pj == cur);  // children of cur, in index order
+      if (kids == 0) break;                 // a leaf: the bonus draw from its target row
+      double C = 0.0, M = 1.0;
+      int acc = -1;
+      for (bool first = true; kids != 0; first = false) {
+        const int ji = __builtin_ctzll(kids);
+        kids &= kids - 1;
+        if (!first) {
+          const double cn = C + M;
+          const double F = lane_value_d(f[0], ji);
+          if (F > 0.0) {
+            C = cn;
+            M = F;
+          }
+        }
+        const double pxi = lane_value_d(px, ji), qxi = lane_value_d(qx, ji);
+        const double ui = lane_value_d(uj, ji);
+        if (__builtin_amdgcn_readlane((int)valid, ji) &&
+            ui * qxi * M < fmax(0.0, pxi - C * qxi)) {
+          acc = ji;
+          break;
+        }
+      }
+      if (acc < 0) {  // every child rejected: draw from the residual
+        cf = C + M;
+        cp = C;
+        break;
+      }
+      cur = acc;
+      ++depth;
+      if (lane == 0) path[depth] = cur;
+    }
+  } else
   for (;;) {
     const int m = s_nchild[cur];
     if (m == 0) break;  // a leaf: the bonus draw from its target row
@@ -1067,15 +1139,17 @@ static hipError_t launch_tree_sample_t(const void* target, const void* draft, in
   }
   const int G = (C2 + kTreeChunksPerGroup - 1) / kTreeChunksPerGroup;
   const int wgs = (B + kWaves - 1) / kWaves;
-  // the leaves' row statistics (logits) ride in the walk's launch
-  const int n_leaf = N - shape.n_internal;
-  const long n_leaf_wgs = KIND == 0 ? (long)B * n_leaf * C1 : 0;
-  e = launch_timed(kProfTreeWalk, &k_tree_walk<DT, NE, KIND>, dim3((unsigned)(wgs + n_leaf_wgs)),
+  e = launch_timed(kProfTreeWalk, &k_tree_walk<DT, NE, KIND>, dim3((unsigned)wgs),
                    dim3(kThreads), tree_walk_lds(N), s, target, draft, B, N, V, Cm, shape.depth,
                    c1, node_tokens, uniforms, seed, ctr0, (const int*)tables,
                    (const TreeStat64*)xstat, (const double*)mpart, tstate, accepted_len,
-                   out_tokens, out_path, wgs, C1, c, n_leaf, part);
+                   out_tokens, out_path);
   if (e != hipSuccess) return e;
+  if (KIND == 0) {  // the stop leaves' row statistics (logits)
+    e = launch_timed(kProfTreeLeaf, &k_tree_leaf<DT, NE>, dim3((unsigned)((long)B * C1)),
+                     dim3(kThreads), 0, s, target, N, V, C1, c, (const TreeDraw*)tstate, part);
+    if (e != hipSuccess) return e;
+  }
   return launch_timed(kProfTreeDraw, &k_tree_draw<DT, NE, KIND>, dim3((unsigned)((long)B * G)),
                       dim3(kThreads), 0, s, target, draft, N, V, C1, C2, shape.depth, c, c1,
                       uniforms, seed, ctr0, (const TreeDraw*)tstate, (const uint64_t*)part,
