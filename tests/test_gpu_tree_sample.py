@@ -164,6 +164,23 @@ def test_wide_star_children_past_one_wave():
     assert all(path[b, 1] > 70 or acc[b] == 0 for b in range(0, wl.B, 2))
 
 
+@pytest.mark.parametrize("n_children", [63, 64])
+def test_star_at_the_lane_limit(n_children):
+    # 64 nodes (one per lane: the walk holds every node in registers) and
+    # 65 (tables in shared memory); the first 40 children are made to fail
+    # in even requests, so the walk applies 40 residual updates before the
+    # first child it can accept
+    _say(f"tree sampling: a {n_children}-child star, 40 forced rejections")
+    parent = np.array([-1] + [0] * n_children, dtype=np.int32)
+    wl = W.tree_sample(B=8, V=1024, seed=23, uniform_seed=24, parent=parent, target_std=2.0,
+                       noise_std=1.0, temperature=1.0, n_peaks=0, dtype="bf16")
+    wl.node_tokens[::2, 1:41] = wl.V + 1
+    acc, out, path = _run_gpu(wl)
+    st = _check(wl, acc, out, path)
+    assert st["mismatches"] == 0
+    assert all(path[b, 1] > 40 or acc[b] == 0 for b in range(0, wl.B, 2))
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_masked_and_wide_low_temperature_logits(dt):
     """The float64 row statistics' reference: rows whose first element is
